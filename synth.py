@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the preshuffled-B GEMM workloads.
+
+This module only draws random numbers and stores them in the input types
+(bf16 bit patterns, OCP e4m3fn codes, fp32 scales) using torch's own CPU
+conversions.  It holds none of the GEMM's arithmetic and is the one piece
+shared by the oracle side and the GPU side of every test and of the bench.
+
+Seeds follow ``seed = 1000*cfg + {0: A, 1: B, 2: scales}`` with numpy's PCG64.
+
+Workloads (the five configurations the library is measured and tested on):
+
+* ``bf16_small``   bf16 M=128, N=256, K=256; A, B ~ U(-1, 1).
+* ``bf16_large``   bf16 M=N=4096, K=8192; A, B ~ N(0, 1)/sqrt(K).
+* ``fp8_large``    e4m3 M=N=4096, K=8192; A, B ~ N(0, 1) quantised with the
+                   per-tensor scale amax/448.
+* ``fp8_decode``   e4m3 per-tensor, M in {1, 16}, N in {2048, 16384}, K=7168,
+                   split_k in {1, 2, 4, 8}; data as ``fp8_large``.
+* ``fp8_blockscale`` e4m3 M=16, N=16384, K=7168; N(0, 1) data quantised per
+                   block (A: per row per 128-K block, B: per 128x128 block) with
+                   scales U(0.5, 2) * amax_block / 448.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+CFG_BF16_SMALL = 0
+CFG_BF16_LARGE = 1
+CFG_FP8_LARGE = 2
+CFG_FP8_DECODE = 3
+CFG_FP8_BLOCKSCALE = 4
+
+WORKLOADS = {
+    "bf16_small": dict(cfg=CFG_BF16_SMALL, dtype="bf16", M=128, N=256, K=256),
+    "bf16_large": dict(cfg=CFG_BF16_LARGE, dtype="bf16", M=4096, N=4096, K=8192),
+    "fp8_large": dict(cfg=CFG_FP8_LARGE, dtype="fp8", M=4096, N=4096, K=8192),
+    "fp8_decode": dict(cfg=CFG_FP8_DECODE, dtype="fp8", Ms=(1, 16), Ns=(2048, 16384), K=7168,
+                       splits=(1, 2, 4, 8)),
+    "fp8_blockscale": dict(cfg=CFG_FP8_BLOCKSCALE, dtype="fp8", M=16, N=16384, K=7168,
+                           splits=(1, 2, 4, 8)),
+}
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def seed_of(cfg: int, which: int) -> int:
+    """which: 0 = A, 1 = B, 2 = scales."""
+    return 1000 * cfg + which
+
+
+# ----------------------------------------------------------- storage types
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16) via torch's conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP e4m3fn codes (uint8) via torch's conversion.  Callers clamp
+    to +-448 first; torch does not saturate."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def quantise_e4m3(x: np.ndarray, scale) -> np.ndarray:
+    """codes = e4m3(clamp(x / scale, -448, 448)); scale broadcasts against x."""
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.asarray(scale, dtype=np.float32),
+                -E4M3_MAX, E4M3_MAX)
+    return to_e4m3_codes(y)
+
+
+# ------------------------------------------------------------- generators
+
+def bf16_uniform(shape, seed, lo=-1.0, hi=1.0) -> np.ndarray:
+    return to_bf16_bits(rng(seed).uniform(lo, hi, size=shape).astype(np.float32))
+
+
+def bf16_normal(shape, seed, std=1.0) -> np.ndarray:
+    return to_bf16_bits((rng(seed).standard_normal(size=shape) * std).astype(np.float32))
+
+
+def fp8_per_tensor(shape, seed):
+    """N(0,1) data quantised with the per-tensor scale amax/448.
+
+    Returns (codes uint8, scale float32 array of shape (1,))."""
+    x = rng(seed).standard_normal(size=shape).astype(np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    s = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+    return quantise_e4m3(x, s), np.array([s], dtype=np.float32)
+
+
+def fp8_blockscale_a(M, K, seed_data, seed_scale):
+    """A [M][K] quantised per row per 128-K block; sA [M][K/128]."""
+    x = rng(seed_data).standard_normal(size=(M, K)).astype(np.float32)
+    kb = K // 128
+    amax = np.abs(x.reshape(M, kb, 128)).max(axis=2)
+    u = rng(seed_scale).uniform(0.5, 2.0, size=(M, kb)).astype(np.float32)
+    s = (u * amax / E4M3_MAX).astype(np.float32)
+    s[s == 0] = 1.0
+    codes = quantise_e4m3(x.reshape(M, kb, 128), s[:, :, None]).reshape(M, K)
+    return codes, s
+
+
+def fp8_blockscale_b(N, K, seed_data, seed_scale):
+    """B [N][K] quantised per 128x128 block; sB [N/128][K/128]."""
+    x = rng(seed_data).standard_normal(size=(N, K)).astype(np.float32)
+    nb, kb = N // 128, K // 128
+    blocks = x.reshape(nb, 128, kb, 128)
+    amax = np.abs(blocks).max(axis=(1, 3))
+    u = rng(seed_scale).uniform(0.5, 2.0, size=(nb, kb)).astype(np.float32)
+    s = (u * amax / E4M3_MAX).astype(np.float32)
+    s[s == 0] = 1.0
+    codes = quantise_e4m3(blocks, s[:, None, :, None]).reshape(N, K)
+    return codes, s
+
+
+def exact_ints(shape, seed, dtype: str, lo=-4, hi=4) -> np.ndarray:
+    """Uniform integers in [lo, hi], stored exactly as bf16 bits or e4m3 codes.
+
+    Every product and partial sum of such inputs is an exact fp32 number, so
+    any summation order gives the same bits."""
+    v = rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+    return to_bf16_bits(v) if dtype == "bf16" else to_e4m3_codes(v)
+
+
+def exact_block_scales(shape, seed) -> np.ndarray:
+    """Scales drawn from {0.5, 1, 2}: exact in every product."""
+    return rng(seed).choice(np.array([0.5, 1.0, 2.0], dtype=np.float32), size=shape)
+
+
+def workload_inputs(name: str, M=None, N=None, K=None):
+    """Inputs of a named workload: dict(A, B, sA, sB, dtype, scale_mode, M, N, K).
+
+    ``dtype`` is "bf16" or "fp8"; ``scale_mode`` is "none", "tensor" or "block128".
+    M/N/K override the workload's sizes (used for the decode family)."""
+    w = WORKLOADS[name]
+    cfg = w["cfg"]
+    M = M if M is not None else w.get("M")
+    N = N if N is not None else w.get("N")
+    K = K if K is not None else w.get("K")
+    sa, sb, ss = seed_of(cfg, 0), seed_of(cfg, 1), seed_of(cfg, 2)
+    if name == "bf16_small":
+        return dict(A=bf16_uniform((M, K), sa), B=bf16_uniform((N, K), sb), sA=None, sB=None,
+                    dtype="bf16", scale_mode="none", M=M, N=N, K=K)
+    if name == "bf16_large":
+        std = 1.0 / np.sqrt(K)
+        return dict(A=bf16_normal((M, K), sa, std), B=bf16_normal((N, K), sb, std), sA=None,
+                    sB=None, dtype="bf16", scale_mode="none", M=M, N=N, K=K)
+    if name in ("fp8_large", "fp8_decode"):
+        A, sA = fp8_per_tensor((M, K), sa)
+        B, sB = fp8_per_tensor((N, K), sb)
+        return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp8", scale_mode="tensor", M=M, N=N, K=K)
+    if name == "fp8_blockscale":
+        A, sA = fp8_blockscale_a(M, K, sa, ss)
+        B, sB = fp8_blockscale_b(N, K, sb, ss + 500)
+        return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp8", scale_mode="block128", M=M, N=N, K=K)
+    raise KeyError(name)

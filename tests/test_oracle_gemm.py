@@ -1,0 +1,275 @@
+"""Pins for the oracle GEMM (per-tensor, blockscale, split-K).
+
+The oracle is checked against things other than itself: exact rational
+arithmetic on tiny shapes, numpy's float64 matmul of independently decoded
+inputs (torch conversions) under the standard forward error bound of
+recursive fp32 summation (Higham, Accuracy and Stability of Numerical
+Algorithms, 2nd ed., section 3.1: |fl(sum) - sum| <= gamma_n * sum|terms|,
+gamma_n = n*u/(1-n*u), u = 2^-24), exact-integer inputs where every order of
+summation is exact, one-hot and identity operands, and split-K sums.
+Shapes are non-square (M != N != K) so that a transposed operand fails.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+U = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def dec_torch(codes, dtype):
+    """Independent decode through torch's storage types."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(codes).copy()).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def odt(orc, dtype):
+    return orc.BF16 if dtype == "bf16" else orc.FP8_E4M3
+
+
+def rand_codes(shape, seed, dtype):
+    if dtype == "bf16":
+        return synth.bf16_uniform(shape, seed)
+    codes, _ = synth.fp8_per_tensor(shape, seed)
+    return codes
+
+
+# ------------------------------------------------------- exact brute force
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 64), (3, 32, 64), (5, 16, 128), (7, 48, 192)])
+def test_tiny_against_exact_rationals(orc, dtype, M, N, K):
+    A = rand_codes((M, K), 11 + M, dtype)
+    B = rand_codes((N, K), 13 + N, dtype)
+    a = dec_torch(A, dtype)
+    b = dec_torch(B, dtype)
+    c32, c16 = orc.gemm(A, B, odt(orc, dtype))
+    for m in range(M):
+        for n in range(N):
+            exact = sum((Fraction(float(a[m, k])) * Fraction(float(b[n, k])) for k in range(K)),
+                        Fraction(0))
+            absum = sum(abs(float(a[m, k]) * float(b[n, k])) for k in range(K))
+            err = abs(Fraction(float(c32[m, n])) - exact)
+            assert err <= Fraction(gamma(K) * absum) + Fraction(1, 2**149), (m, n)
+            assert c16[m, n] == orc.bf16_round(float(c32[m, n]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_exact_integer_mode_is_exact(orc, dtype):
+    M, N, K = 9, 32, 256
+    A = synth.exact_ints((M, K), 1, dtype)
+    B = synth.exact_ints((N, K), 2, dtype)
+    a = dec_torch(A, dtype).astype(np.int64)
+    b = dec_torch(B, dtype).astype(np.int64)
+    exact = a @ b.T
+    s = np.float32(0.125)
+    mode = orc.SCALE_TENSOR if dtype == "fp8" else orc.SCALE_NONE
+    sA = np.array([s]) if dtype == "fp8" else None
+    sB = np.array([1.0]) if dtype == "fp8" else None
+    c32, c16 = orc.gemm(A, B, odt(orc, dtype), mode, sA, sB)
+    want = exact.astype(np.float64) * (0.125 if dtype == "fp8" else 1.0)
+    assert np.array_equal(c32.astype(np.float64), want)
+    ref16 = torch.from_numpy(want.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(c16.view(np.int16), ref16)
+
+
+# ------------------------------------------------- numpy float64 + bounds
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(17, 48, 320), (64, 96, 1024)])
+def test_random_against_fp64_matmul(orc, dtype, M, N, K):
+    A = rand_codes((M, K), 21, dtype)
+    B = rand_codes((N, K), 22, dtype)
+    a, b = dec_torch(A, dtype), dec_torch(B, dtype)
+    c64 = a @ b.T
+    bound = gamma(K) * (np.abs(a) @ np.abs(b).T)
+    c32, c16 = orc.gemm(A, B, odt(orc, dtype))
+    assert np.all(np.abs(c32 - c64) <= bound + 1e-30)
+    # the fp32 accumulation really is fp32 (not exact): some entry differs from fp64
+    assert np.any(c32.astype(np.float64) != c64)
+
+
+def test_per_tensor_scale_against_fp64(orc):
+    M, N, K = 24, 80, 512
+    A, sA = synth.fp8_per_tensor((M, K), 31)
+    B, sB = synth.fp8_per_tensor((N, K), 32)
+    a, b = dec_torch(A, "fp8"), dec_torch(B, "fp8")
+    s = float(sA[0]) * float(sB[0])
+    c64 = (a @ b.T) * s
+    bound = (gamma(K) + 3 * U) * (np.abs(a) @ np.abs(b).T) * s
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR, sA, sB)
+    assert np.all(np.abs(c32 - c64) <= bound + 1e-30)
+    # scales matter: a wrong scale would be far outside the bound
+    c32_unscaled, _ = orc.gemm(A, B, orc.FP8_E4M3)
+    assert np.max(np.abs(c32_unscaled - c64)) > 100 * np.max(bound)
+
+
+def test_blockscale_against_fp64(orc):
+    M, N, K = 6, 256, 512
+    A, sA = synth.fp8_blockscale_a(M, K, 41, 42)
+    B, sB = synth.fp8_blockscale_b(N, K, 43, 44)
+    a, b = dec_torch(A, "fp8"), dec_torch(B, "fp8")
+    KB = K // 128
+    c64 = np.zeros((M, N))
+    mag = np.zeros((M, N))
+    for kb in range(KB):
+        sl = slice(kb * 128, kb * 128 + 128)
+        blk = a[:, sl] @ b[:, sl].T
+        sc = sA[:, kb].astype(np.float64)[:, None] * np.repeat(sB[:, kb].astype(np.float64), 128)[None, :]
+        c64 += blk * sc
+        mag += (np.abs(a[:, sl]) @ np.abs(b[:, sl]).T) * sc
+    bound = (gamma(K + KB) + 3 * U) * mag
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB)
+    assert np.all(np.abs(c32 - c64) <= bound + 1e-30)
+    # the check is sensitive to the scale indexing: pairing block kb's data
+    # with another block's scales lands far outside the bound
+    alt = np.zeros((M, N))
+    for kb in range(KB):
+        sl = slice(kb * 128, kb * 128 + 128)
+        wk = KB - 1 - kb
+        sc = sA[:, wk].astype(np.float64)[:, None] * np.repeat(sB[:, wk].astype(np.float64), 128)[None, :]
+        alt += (a[:, sl] @ b[:, sl].T) * sc
+    assert np.max(np.abs(alt - c64) - bound) > 0
+
+
+def test_blockscale_uniform_scales_equal_per_tensor(orc):
+    M, N, K = 5, 128, 384
+    A = synth.exact_ints((M, K), 51, "fp8")
+    B = synth.exact_ints((N, K), 52, "fp8")
+    sA = np.full((M, K // 128), 0.5, np.float32)
+    sB = np.full((N // 128, K // 128), 2.0, np.float32)
+    c_blk, h_blk = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB)
+    c_ten, h_ten = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR, np.array([0.5]), np.array([2.0]))
+    assert np.array_equal(c_blk, c_ten) and np.array_equal(h_blk, h_ten)
+
+
+def test_blockscale_exact_against_integer_arithmetic(orc):
+    """Exact-integer data and scales in {0.5,1,2}: the blockscale result is
+    sum_kb (A_kb . B_kb) * sA[m][kb] * sB[n/128][kb] exactly."""
+    M, N, K = 4, 256, 640
+    A = synth.exact_ints((M, K), 61, "fp8")
+    B = synth.exact_ints((N, K), 62, "fp8")
+    sA = synth.exact_block_scales((M, K // 128), 63)
+    sB = synth.exact_block_scales((N // 128, K // 128), 64)
+    a = dec_torch(A, "fp8").astype(np.int64)
+    b = dec_torch(B, "fp8").astype(np.int64)
+    want = np.zeros((M, N), dtype=np.float64)
+    for kb in range(K // 128):
+        sl = slice(kb * 128, kb * 128 + 128)
+        for n in range(N):
+            want[:, n] += (a[:, sl] @ b[n, sl]) * sA[:, kb] * sB[n // 128, kb]
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB)
+    assert np.array_equal(c32.astype(np.float64), want)
+
+
+# ---------------------------------------------------- one-hot / identity
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_one_hot_rows_select_b_columns(orc, dtype):
+    M, N, K = 12, 64, 192
+    B = rand_codes((N, K), 71, dtype)
+    ks = np.random.Generator(np.random.PCG64(72)).integers(0, K, size=M)
+    one = 0x3F80 if dtype == "bf16" else 0x38
+    A = np.zeros((M, K), dtype=np.uint16 if dtype == "bf16" else np.uint8)
+    A[np.arange(M), ks] = one
+    if dtype == "fp8":
+        c32, c16 = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR, np.array([0.25]), np.array([0.5]))
+        want = dec_torch(B, "fp8")[:, ks].T * 0.125
+        assert np.array_equal(c32.astype(np.float64), want)
+    else:
+        c32, c16 = orc.gemm(A, B, orc.BF16)
+        assert np.array_equal(c16, B[:, ks].T)
+
+
+def test_identity_b_returns_a(orc):
+    M, K = 20, 128
+    A = synth.bf16_uniform((M, K), 81)
+    B = np.zeros((K, K), dtype=np.uint16)
+    B[np.arange(K), np.arange(K)] = 0x3F80
+    c32, c16 = orc.gemm(A, B, orc.BF16)
+    assert np.array_equal(c16, A)
+
+
+# ------------------------------------------------------------- split-K
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_splitk_exact_equals_unsplit(orc, dtype):
+    M, N, K = 16, 128, 1024
+    A = synth.exact_ints((M, K), 91, dtype)
+    B = synth.exact_ints((N, K), 92, dtype)
+    mode = orc.SCALE_TENSOR if dtype == "fp8" else orc.SCALE_NONE
+    sA = np.array([0.125]) if dtype == "fp8" else None
+    sB = np.array([1.0]) if dtype == "fp8" else None
+    c1, h1 = orc.gemm(A, B, odt(orc, dtype), mode, sA, sB)
+    for S in (2, 4, 8):
+        cS, hS, parts = orc.gemm(A, B, odt(orc, dtype), mode, sA, sB, split_k=S, want_partials=True)
+        assert np.array_equal(cS, c1) and np.array_equal(hS, h1)
+        assert np.array_equal(parts.sum(axis=0, dtype=np.float64), c1.astype(np.float64))
+
+
+def test_splitk_partials_are_slices_and_reduce_in_order(orc):
+    M, N, K = 3, 48, 768
+    A, sA = synth.fp8_per_tensor((M, K), 101)
+    B, sB = synth.fp8_per_tensor((N, K), 102)
+    S = 4
+    cS, hS, parts = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR, sA, sB, split_k=S,
+                             want_partials=True)
+    ch = K // S
+    for s in range(S):
+        ps, _ = orc.gemm(np.ascontiguousarray(A[:, s * ch:(s + 1) * ch]),
+                         np.ascontiguousarray(B[:, s * ch:(s + 1) * ch]),
+                         orc.FP8_E4M3, orc.SCALE_TENSOR, sA, sB)
+        assert np.array_equal(parts[s], ps)
+    tot = parts[0].copy()
+    for s in range(1, S):
+        tot = (tot + parts[s]).astype(np.float32)
+    assert np.array_equal(cS, tot)
+    lib = orc.lib()
+    assert all(hS.reshape(-1)[i] == lib.oracle_bf16_round(float(cS.reshape(-1)[i]))
+               for i in range(0, cS.size, 7))
+
+
+def test_splitk_blockscale_random_within_bound(orc):
+    M, N, K = 4, 128, 1024
+    A, sA = synth.fp8_blockscale_a(M, K, 111, 112)
+    B, sB = synth.fp8_blockscale_b(N, K, 113, 114)
+    c1, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB)
+    for S in (2, 4, 8):
+        cS, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB, split_k=S)
+        assert np.max(np.abs(cS - c1)) <= 1e-5 * np.max(np.abs(c1))
+
+
+# ---------------------------------------------------- rows / arguments
+
+def test_row_subset_matches_full(orc):
+    M, N, K = 33, 64, 256
+    A = synth.bf16_uniform((M, K), 121)
+    B = synth.bf16_uniform((N, K), 122)
+    c32, c16 = orc.gemm(A, B, orc.BF16)
+    rows = [32, 0, 17, 5]
+    r32, r16 = orc.gemm(A, B, orc.BF16, rows=rows)
+    assert np.array_equal(r32, c32[rows]) and np.array_equal(r16, c16[rows])
+
+
+def test_invalid_arguments_rejected(orc):
+    A = np.zeros((4, 256), np.uint8)
+    B = np.zeros((128, 256), np.uint8)
+    with pytest.raises(ValueError):
+        orc.gemm(A, B, orc.FP8_E4M3, split_k=3)           # K % split_k
+    with pytest.raises(ValueError):
+        orc.gemm(A, np.zeros((64, 256), np.uint8), orc.FP8_E4M3, orc.SCALE_BLOCK128,
+                 np.ones((4, 2)), np.ones((1, 2)))        # N % 128 for blockscale
+    with pytest.raises(ValueError):
+        orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR)   # scales missing
+    with pytest.raises(ValueError):
+        orc.gemm(A, B, orc.FP8_E4M3, rows=[4])           # row out of range
