@@ -1,0 +1,243 @@
+"""Python binding of the gfx950 preshuffled-B GEMM library (libdgp.so).
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in include/dgp.h.  torch supplies device memory (outputs
+are allocated as torch tensors when not given) and the stream (the current
+torch stream unless one is passed).  There is no fallback: if the compiled
+library is missing, every call raises.
+
+Element types follow the torch dtype of the operands: torch.bfloat16 ->
+DGP_BF16, torch.float8_e4m3fn -> DGP_FP8_E4M3.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdgp.so")
+
+BF16 = 0
+FP8_E4M3 = 1
+SCALE_NONE = 0
+SCALE_TENSOR = 1
+SCALE_BLOCK128 = 2
+
+STATUS = {0: "DGP_OK", 1: "DGP_ERR_NULL", 2: "DGP_ERR_SHAPE", 3: "DGP_ERR_ALIGN", 4: "DGP_ERR_DTYPE",
+          5: "DGP_ERR_SCALE_MODE", 6: "DGP_ERR_SPLITK", 7: "DGP_ERR_WORKSPACE", 8: "DGP_ERR_CONFIG",
+          9: "DGP_ERR_ARCH", 10: "DGP_ERR_HIP"}
+
+
+class DgpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.name}: {message}")
+
+
+class Config(ctypes.Structure):
+    """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair."""
+    _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
+                ("xcd_remap", ctypes.c_int), ("group_m", ctypes.c_int),
+                ("preload_vmem", ctypes.c_int), ("preload_dsrd", ctypes.c_int)]
+
+
+# Every symbol include/dgp.h and include/dgp_diag.h declare.
+EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
+           "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
+           "dgp_tile_of_workgroup", "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
+           "dgp_probe_stream_read")
+
+_lib = None
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdgp.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(or python dense_gemm_packer_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    sigs = {
+        "dgp_preshuffle_b": [_vp, _vp, _i64, _i64, _int, _vp],
+        "dgp_unshuffle_b": [_vp, _vp, _i64, _i64, _int, _vp],
+        "dgp_gemm_preshuffle": [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
+        "dgp_gemm_preshuffle_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp,
+                                       _sz, _vp, _vp],
+        "dgp_check_arch": [ctypes.c_char_p],
+        "dgp_tile_of_workgroup": [_i64, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_i64)],
+        "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
+        "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
+        "dgp_probe_copy": [_vp, _vp, _i64, _vp],
+        "dgp_probe_stream_read": [_vp, _i64, _vp, _vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = _int
+    L.dgp_splitk_workspace_bytes.argtypes = [_i64, _i64, _int]
+    L.dgp_splitk_workspace_bytes.restype = _sz
+    L.dgp_status_string.argtypes = [_int]
+    L.dgp_status_string.restype = ctypes.c_char_p
+    L.dgp_last_error.argtypes = []
+    L.dgp_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DgpError(status, lib().dgp_last_error().decode())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float8_e4m3fn)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, what: str):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _config(config):
+    if config is None:
+        return None
+    if isinstance(config, Config):
+        return ctypes.byref(config)
+    return ctypes.byref(Config(**config))
+
+
+# -------------------------------------------------------------- entry points
+
+def preshuffle_b(B: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Bs = dgp_preshuffle_b(B); B is [N][K] bf16 or e4m3, on the device."""
+    _dev(B, "B")
+    if out is None:
+        out = torch.empty_like(B)
+    _dev(out, "out")
+    _check(lib().dgp_preshuffle_b(_ptr(B), _ptr(out), B.shape[0], B.shape[1], dtype_code(B),
+                                  _stream_handle(stream)))
+    return out
+
+
+def unshuffle_b(Bs: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _dev(Bs, "Bs")
+    if out is None:
+        out = torch.empty_like(Bs)
+    _dev(out, "out")
+    _check(lib().dgp_unshuffle_b(_ptr(Bs), _ptr(out), Bs.shape[0], Bs.shape[1], dtype_code(Bs),
+                                 _stream_handle(stream)))
+    return out
+
+
+def _scale_mode(A, sA, scale_mode):
+    if scale_mode is not None:
+        return scale_mode
+    if dtype_code(A) == BF16:
+        return SCALE_NONE
+    return SCALE_TENSOR if sA is None or sA.numel() == 1 else SCALE_BLOCK128
+
+
+def gemm_preshuffle(A: torch.Tensor, Bs: torch.Tensor, sA: torch.Tensor | None = None,
+                    sB: torch.Tensor | None = None, scale_mode: int | None = None,
+                    out: torch.Tensor | None = None, config=None, stream=None) -> torch.Tensor:
+    """C = A * B^T (bf16 [M][N]) with Bs = preshuffle_b(B)."""
+    _dev(A, "A"), _dev(Bs, "Bs")
+    M, K = A.shape
+    N = Bs.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev(out, "out")
+    for s, name in ((sA, "sA"), (sB, "sB")):
+        if s is not None:
+            _dev(s, name)
+    mode = _scale_mode(A, sA, scale_mode)
+    _check(lib().dgp_gemm_preshuffle(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
+                                     _ptr(sA), _ptr(sB), _config(config), _stream_handle(stream)))
+    return out
+
+
+def splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:
+    return int(lib().dgp_splitk_workspace_bytes(M, N, split_k))
+
+
+def gemm_preshuffle_splitk(A: torch.Tensor, Bs: torch.Tensor, split_k: int,
+                           sA: torch.Tensor | None = None, sB: torch.Tensor | None = None,
+                           scale_mode: int | None = None, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, config=None,
+                           stream=None) -> torch.Tensor:
+    """Two-pass split-K C = A * B^T; workspace (fp32) is allocated if not given."""
+    _dev(A, "A"), _dev(Bs, "Bs")
+    M, K = A.shape
+    N = Bs.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev(out, "out")
+    need = splitk_workspace_bytes(M, N, split_k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=A.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    mode = _scale_mode(A, sA, scale_mode)
+    _check(lib().dgp_gemm_preshuffle_splitk(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
+                                            _ptr(sA), _ptr(sB), split_k, _ptr(workspace), ws_bytes,
+                                            _config(config), _stream_handle(stream)))
+    return out
+
+
+def check_arch(name: str) -> bool:
+    return lib().dgp_check_arch(name.encode()) == 0
+
+
+def status_string(status: int) -> str:
+    return lib().dgp_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- diagnostics
+
+def tile_of_workgroup(wg: int, tiles_m: int, tiles_n: int, splits: int, xcd_remap: int, group_m: int):
+    out = (ctypes.c_int64 * 3)()
+    _check(lib().dgp_tile_of_workgroup(wg, tiles_m, tiles_n, splits, xcd_remap, group_m, out))
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def probe_mfma_layout(which: int, a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty(64 * 4, dtype=torch.float32, device=a.device)
+    _check(lib().dgp_probe_mfma_layout(which, _ptr(a), _ptr(b), _ptr(out), _stream_handle(stream)))
+    return out.view(64, 4)
+
+
+def probe_lds_dma(src: torch.Tensor, perm: torch.Tensor, stream=None) -> torch.Tensor:
+    dst = torch.empty(1024, dtype=torch.uint8, device=src.device)
+    _check(lib().dgp_probe_lds_dma(_ptr(src), _ptr(perm), _ptr(dst), _stream_handle(stream)))
+    return dst
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().dgp_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream_handle(stream)))
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    _check(lib().dgp_probe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream_handle(stream)))

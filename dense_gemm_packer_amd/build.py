@@ -1,0 +1,74 @@
+"""Build the gfx950 HIP library libdgp.so in-tree (dense_gemm_packer_amd/libdgp.so).
+
+Each source under csrc/ is compiled with hipcc for gfx950 only, in parallel,
+then linked into one shared library.  Packed-fp32 VALU instructions are
+disabled for all device code.
+"""
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libdgp.so")
+SOURCES = ["dgp_api.cpp", "packer.hip", "gemm.hip", "reduce.hip", "probe.hip"]
+HEADERS = ["common.h", "launch.h"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in arch VGPRs: avoids accumulator copies at loop latches
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
+    return obj, msgs
+
+
+def build(force: bool = True, jobs: int = 0) -> str:
+    """Compile every source and link libdgp.so; returns the library path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    hdrs = [os.path.join(CSRC, h) for h in HEADERS] + [
+        os.path.join(HERE, "..", "include", h) for h in ("dgp.h", "dgp_diag.h")]
+    if not force and os.path.exists(LIB):
+        newest = max(os.path.getmtime(p) for p in srcs + hdrs)
+        if os.path.getmtime(LIB) >= newest:
+            return LIB
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for _, msgs in results:
+        if msgs.strip():
+            print(msgs, file=sys.stderr)
+    objs = [o for o, _ in results]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def asm(src: str, out: str) -> None:
+    """Write the gfx950 assembly of one source (for inspection)."""
+    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True)
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,470 @@
+// C-ABI layer of the gfx950 preshuffled-B GEMM library (include/dgp.h).
+//
+// Every entry point validates its arguments on the host first -- no HIP call
+// is made for a rejected call -- then checks the device architecture, picks a
+// compiled kernel and enqueues it on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dgp.h"
+#include "../../include/dgp_diag.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace dgp;
+
+namespace {
+
+thread_local char g_err[512];
+
+dgp_status fail(dgp_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dgp_status ok()
+{
+    g_err[0] = '\0';
+    return DGP_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == DGP_BF16 ? 2 : 1; }
+
+// Per-row byte limit: keeps every in-tile offset of the kernels in 32 bits.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 23;
+
+// ---------------------------------------------------------------- arch
+
+dgp_status check_device_arch()
+{
+    static int cached[64];   // 0 unknown, 1 gfx950, 2 other
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(DGP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64 && cached[dev] == 1)
+        return DGP_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+        return fail(DGP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    dgp_status st = dgp_check_arch(prop.gcnArchName);
+    if (dev >= 0 && dev < 64)
+        cached[dev] = st == DGP_OK ? 1 : 2;
+    if (st != DGP_OK)
+        return fail(DGP_ERR_ARCH, "device %d is %s; this library runs on gfx950 only", dev,
+                    prop.gcnArchName);
+    return DGP_OK;
+}
+
+dgp_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(DGP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ------------------------------------------------------- kernel choice
+
+struct Plan {
+    const KernelSpec *spec;
+    int tiles_m, tiles_n;
+    int remap, group_m;
+};
+
+bool spec_fits(const KernelSpec &k, int64_t Ks)
+{
+    if (k.family == kTiled)
+        return Ks % k.kt == 0;
+    return true;   // stream: any K range that is a multiple of 128 bytes
+}
+
+const KernelSpec *find_spec(int family, int dtype, int scale, int out, int tm, int tn, int kt, int p0, int p1)
+{
+    int n = 0;
+    const KernelSpec *t = kernel_table(&n);
+    for (int i = 0; i < n; ++i) {
+        const KernelSpec &k = t[i];
+        if (k.family == family && k.dtype == dtype && k.scale == scale && k.out == out && k.tm == tm &&
+            k.tn == tn && (kt <= 0 || k.kt == kt) && (p0 < 0 || k.p0 == p0) && (p1 < 0 || k.p1 == p1))
+            return &k;
+    }
+    return nullptr;
+}
+
+// Built-in per-shape choice.
+const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks)
+{
+    if (scale == DGP_SCALE_BLOCK128 || M <= 32) {
+        return find_spec(kStream, dtype, scale, out, 16, 64, -1, -1, -1);
+    }
+    const KernelSpec *k = nullptr;
+    if (M >= 1024 && N >= 1024)
+        k = find_spec(kTiled, dtype, scale, out, 256, 256, 128, 2, 4);
+    if (!k || !spec_fits(*k, Ks))
+        k = find_spec(kTiled, dtype, scale, out, 128, 128, 128, 2, 2);
+    return (k && spec_fits(*k, Ks)) ? k : nullptr;
+}
+
+// ---------------------------------------------------------- validation
+
+struct GemmCall {
+    const void *A, *Bs;
+    void *C;
+    int64_t M, N, K;
+    int dtype, scale;
+    const float *sA, *sB;
+    int split_k;
+    float *ws;
+    size_t ws_bytes;
+    const dgp_config *cfg;
+};
+
+dgp_status validate(const GemmCall &c, Plan *plan)
+{
+    if (c.dtype != DGP_BF16 && c.dtype != DGP_FP8_E4M3)
+        return fail(DGP_ERR_DTYPE, "dtype %d is neither DGP_BF16 nor DGP_FP8_E4M3", c.dtype);
+    if (c.M < 0 || c.N < 0 || c.K < 0)
+        return fail(DGP_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld", (long long)c.M, (long long)c.N,
+                    (long long)c.K);
+    if (c.scale < DGP_SCALE_NONE || c.scale > DGP_SCALE_BLOCK128)
+        return fail(DGP_ERR_SCALE_MODE, "unknown scale mode %d", c.scale);
+    if (c.dtype == DGP_BF16 && c.scale != DGP_SCALE_NONE)
+        return fail(DGP_ERR_SCALE_MODE, "bf16 takes DGP_SCALE_NONE");
+    if (c.dtype == DGP_FP8_E4M3 && c.scale == DGP_SCALE_NONE)
+        return fail(DGP_ERR_SCALE_MODE, "fp8 takes DGP_SCALE_TENSOR or DGP_SCALE_BLOCK128");
+    if (c.split_k < 1)
+        return fail(DGP_ERR_SPLITK, "split_k %d < 1", c.split_k);
+    if (c.cfg) {
+        if (c.cfg->preload_vmem < 0 || c.cfg->preload_dsrd < 0)
+            return fail(DGP_ERR_CONFIG, "preload must be a pair of non-negative integers (got %d, %d)",
+                        c.cfg->preload_vmem, c.cfg->preload_dsrd);
+        if (c.cfg->xcd_remap != 0 && c.cfg->xcd_remap != 1)
+            return fail(DGP_ERR_CONFIG, "xcd_remap must be 0 or 1");
+        if (c.cfg->xcd_remap == 1 && c.cfg->group_m < 1)
+            return fail(DGP_ERR_CONFIG, "group_m must be >= 1");
+    }
+    if (c.N % 16 != 0)
+        return fail(DGP_ERR_SHAPE, "N=%lld is not a multiple of 16 (preshuffle block rows)", (long long)c.N);
+    const int64_t Kb = c.K * elem_bytes(c.dtype);
+    if (Kb % 128 != 0)
+        return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld is not a multiple of 128", (long long)Kb);
+    if (Kb > kMaxRowBytes)
+        return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld exceeds %lld", (long long)Kb, (long long)kMaxRowBytes);
+    if (c.M > INT32_MAX / 2 || c.N > INT32_MAX / 2)
+        return fail(DGP_ERR_SHAPE, "M or N too large");
+    if (c.scale == DGP_SCALE_BLOCK128 && (c.K % 128 != 0 || c.N % 128 != 0))
+        return fail(DGP_ERR_SHAPE, "blockscale needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)",
+                    (long long)c.K, (long long)c.N);
+    if (c.K % c.split_k != 0)
+        return fail(DGP_ERR_SPLITK, "split_k=%d does not divide K=%lld", c.split_k, (long long)c.K);
+    const int64_t Ks = Kb / c.split_k;
+    if (Ks % 128 != 0)
+        return fail(DGP_ERR_SPLITK, "K range per split (%lld bytes) is not a multiple of 128", (long long)Ks);
+    if (c.scale == DGP_SCALE_BLOCK128 && (c.K / c.split_k) % 128 != 0)
+        return fail(DGP_ERR_SPLITK, "blockscale needs (K/split_k) %% 128 == 0");
+
+    if (c.M == 0 || c.N == 0) {
+        plan->spec = nullptr;
+        return ok();
+    }
+    if (!c.C)
+        return fail(DGP_ERR_NULL, "C is NULL");
+    if (!aligned16(c.C))
+        return fail(DGP_ERR_ALIGN, "C is not 16-byte aligned");
+    if (c.K == 0) {
+        plan->spec = nullptr;
+        return ok();
+    }
+    if (!c.A || !c.Bs)
+        return fail(DGP_ERR_NULL, "A or Bs is NULL");
+    if (!aligned16(c.A) || !aligned16(c.Bs))
+        return fail(DGP_ERR_ALIGN, "A and Bs must be 16-byte aligned");
+    if (c.scale != DGP_SCALE_NONE) {
+        if (!c.sA || !c.sB)
+            return fail(DGP_ERR_NULL, "scale mode needs sA and sB");
+        if (((uintptr_t)c.sA & 3u) || ((uintptr_t)c.sB & 3u))
+            return fail(DGP_ERR_ALIGN, "sA and sB must be 4-byte aligned");
+    }
+    if (c.split_k > 1) {
+        if (!c.ws)
+            return fail(DGP_ERR_WORKSPACE, "split_k > 1 needs a workspace");
+        if (!aligned16(c.ws))
+            return fail(DGP_ERR_ALIGN, "workspace is not 16-byte aligned");
+        const size_t need = dgp_splitk_workspace_bytes(c.M, c.N, c.split_k);
+        if (c.ws_bytes < need)
+            return fail(DGP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.ws_bytes, need);
+    }
+
+    const int out = c.split_k > 1 ? kOutPartial : kOutBf16;
+    const KernelSpec *spec = nullptr;
+    if (c.cfg && c.cfg->tile_m > 0) {
+        const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
+        spec = find_spec(fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n,
+                         fam == kTiled ? c.cfg->tile_k : -1, -1, -1);
+        if (!spec)
+            return fail(DGP_ERR_CONFIG, "no compiled kernel for tile %dx%dx%d with this dtype/scale",
+                        c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k);
+        if (!spec_fits(*spec, Ks))
+            return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
+                        spec->kt, (long long)Ks);
+        if (spec->pv != c.cfg->preload_vmem || spec->pd != c.cfg->preload_dsrd) {
+            int n = 0;
+            const KernelSpec *t = kernel_table(&n);
+            const KernelSpec *hinted = nullptr;
+            for (int i = 0; i < n; ++i)
+                if (t[i].family == spec->family && t[i].dtype == spec->dtype && t[i].scale == spec->scale &&
+                    t[i].out == spec->out && t[i].tm == spec->tm && t[i].tn == spec->tn &&
+                    t[i].kt == spec->kt && t[i].pv == c.cfg->preload_vmem && t[i].pd == c.cfg->preload_dsrd)
+                    hinted = &t[i];
+            if (!hinted)
+                return fail(DGP_ERR_CONFIG, "no compiled kernel with preload (%d, %d) for this tile",
+                            c.cfg->preload_vmem, c.cfg->preload_dsrd);
+            spec = hinted;
+        }
+    } else {
+        spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks);
+        if (!spec)
+            return fail(DGP_ERR_CONFIG, "no compiled kernel fits this shape");
+    }
+    plan->spec = spec;
+    plan->tiles_m = (int)((c.M + spec->tm - 1) / spec->tm);
+    plan->tiles_n = (int)((c.N + spec->tn - 1) / spec->tn);
+    if (c.cfg && c.cfg->tile_m > 0) {
+        plan->remap = c.cfg->xcd_remap;
+        plan->group_m = c.cfg->group_m < 1 ? 1 : c.cfg->group_m;
+    } else {
+        plan->remap = spec->family == kTiled ? 1 : 0;
+        plan->group_m = 4;
+    }
+    const int64_t grid = (int64_t)plan->tiles_m * plan->tiles_n * c.split_k;
+    if (grid > INT32_MAX)
+        return fail(DGP_ERR_SHAPE, "grid of %lld workgroups too large", (long long)grid);
+    return ok();
+}
+
+dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
+{
+    Plan plan{};
+    dgp_status st = validate(c, &plan);
+    if (st != DGP_OK)
+        return st;
+    if (c.M == 0 || c.N == 0)
+        return ok();
+    st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    if (c.K == 0)
+        return hip_status(launch_splitk_reduce(nullptr, c.C, c.M, c.N, 0, stream), "zero fill");
+
+    GemmArgs a{};
+    a.A = (const uint8_t *)c.A;
+    a.Bs = (const uint8_t *)c.Bs;
+    a.C = c.C;
+    a.ws = c.ws;
+    a.sA = c.sA;
+    a.sB = c.sB;
+    a.M = (int)c.M;
+    a.N = (int)c.N;
+    a.K = (int)c.K;
+    a.Kb = (int)(c.K * elem_bytes(c.dtype));
+    a.Ks = a.Kb / c.split_k;
+    a.tiles_m = plan.tiles_m;
+    a.tiles_n = plan.tiles_n;
+    a.splits = c.split_k;
+    a.remap = plan.remap;
+    a.group_m = plan.group_m;
+    const dim3 grid((unsigned)((int64_t)plan.tiles_m * plan.tiles_n * c.split_k));
+    plan.spec->launch(a, grid, stream);
+    st = hip_status(hipGetLastError(), "GEMM launch");
+    if (st != DGP_OK || c.split_k == 1)
+        return st;
+    return hip_status(launch_splitk_reduce(c.ws, c.C, c.M, c.N, c.split_k, stream), "split-K reduce launch");
+}
+
+dgp_status shuffle(const void *src, void *dst, int64_t N, int64_t K, int dtype, void *stream, bool inverse)
+{
+    if (dtype != DGP_BF16 && dtype != DGP_FP8_E4M3)
+        return fail(DGP_ERR_DTYPE, "dtype %d is neither DGP_BF16 nor DGP_FP8_E4M3", dtype);
+    if (N < 0 || K < 0)
+        return fail(DGP_ERR_SHAPE, "negative size N=%lld K=%lld", (long long)N, (long long)K);
+    const int64_t Kb = K * elem_bytes(dtype);
+    if (N % 16 != 0)
+        return fail(DGP_ERR_SHAPE, "N=%lld is not a multiple of 16", (long long)N);
+    if (Kb % 64 != 0)
+        return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld is not a multiple of 64", (long long)Kb);
+    if (Kb >= (int64_t(1) << 27))
+        return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld too large", (long long)Kb);
+    if (N / 16 > INT32_MAX)
+        return fail(DGP_ERR_SHAPE, "N too large");
+    if (N == 0 || K == 0)
+        return ok();
+    if (!src || !dst)
+        return fail(DGP_ERR_NULL, "source or destination is NULL");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(DGP_ERR_ALIGN, "source and destination must be 16-byte aligned");
+    const uintptr_t s = (uintptr_t)src, d = (uintptr_t)dst, n = (uintptr_t)(N * Kb);
+    if (s < d + n && d < s + n)
+        return fail(DGP_ERR_SHAPE, "source and destination overlap");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_preshuffle(src, dst, N, Kb, inverse, (hipStream_t)stream), "preshuffle launch");
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+dgp_status dgp_preshuffle_b(const void *B, void *Bs, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return shuffle(B, Bs, N, K, dtype, stream, false);
+}
+
+dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return shuffle(Bs, B, N, K, dtype, stream, true);
+}
+
+dgp_status dgp_gemm_preshuffle(const void *A, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                               int dtype, int scale_mode, const float *sA, const float *sB,
+                               const dgp_config *cfg, void *stream)
+{
+    GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, 1, nullptr, 0, cfg};
+    return run_gemm(c, (hipStream_t)stream);
+}
+
+size_t dgp_splitk_workspace_bytes(int64_t M, int64_t N, int split_k)
+{
+    if (split_k <= 1 || M <= 0 || N <= 0)
+        return 0;
+    return (size_t)split_k * (size_t)M * (size_t)N * sizeof(float);
+}
+
+dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
+                                      int64_t K, int dtype, int scale_mode, const float *sA,
+                                      const float *sB, int split_k, float *ws, size_t ws_bytes,
+                                      const dgp_config *cfg, void *stream)
+{
+    GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, split_k, ws, ws_bytes, cfg};
+    return run_gemm(c, (hipStream_t)stream);
+}
+
+dgp_status dgp_check_arch(const char *name)
+{
+    if (!name)
+        return DGP_ERR_ARCH;
+    // "gfx950" optionally followed by ":feature" suffixes.
+    if (strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':'))
+        return DGP_OK;
+    return DGP_ERR_ARCH;
+}
+
+const char *dgp_status_string(int s)
+{
+    switch (s) {
+    case DGP_OK: return "DGP_OK";
+    case DGP_ERR_NULL: return "DGP_ERR_NULL";
+    case DGP_ERR_SHAPE: return "DGP_ERR_SHAPE";
+    case DGP_ERR_ALIGN: return "DGP_ERR_ALIGN";
+    case DGP_ERR_DTYPE: return "DGP_ERR_DTYPE";
+    case DGP_ERR_SCALE_MODE: return "DGP_ERR_SCALE_MODE";
+    case DGP_ERR_SPLITK: return "DGP_ERR_SPLITK";
+    case DGP_ERR_WORKSPACE: return "DGP_ERR_WORKSPACE";
+    case DGP_ERR_CONFIG: return "DGP_ERR_CONFIG";
+    case DGP_ERR_ARCH: return "DGP_ERR_ARCH";
+    case DGP_ERR_HIP: return "DGP_ERR_HIP";
+    default: return "DGP_ERR_UNKNOWN";
+    }
+}
+
+const char *dgp_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------ diagnostics
+
+dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t splits, int xcd_remap,
+                                 int group_m, int64_t out[3])
+{
+    if (!out)
+        return fail(DGP_ERR_NULL, "out is NULL");
+    if (tiles_m < 1 || tiles_n < 1 || splits < 1 || wg < 0 || wg >= tiles_m * tiles_n * splits ||
+        (xcd_remap != 0 && xcd_remap != 1) || tiles_m * tiles_n * splits > INT32_MAX)
+        return fail(DGP_ERR_SHAPE, "bad tile-map arguments");
+    const TileCoord c = tile_of_workgroup<int64_t>(wg, tiles_m, tiles_n, splits, xcd_remap, group_m);
+    out[0] = c.tm;
+    out[1] = c.tn;
+    out[2] = c.s;
+    return ok();
+}
+
+dgp_status dgp_probe_mfma_layout(int which, const void *a, const void *b, float *out, void *stream)
+{
+    if (which != 0 && which != 1)
+        return fail(DGP_ERR_CONFIG, "which must be 0 or 1");
+    if (!a || !b || !out)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return fail(DGP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_mfma(which, a, b, out, (hipStream_t)stream), "probe launch");
+}
+
+dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, void *stream)
+{
+    if (!src || !perm || !dst)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(DGP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_lds_dma(src, perm, dst, (hipStream_t)stream), "probe launch");
+}
+
+dgp_status dgp_probe_copy(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(DGP_ERR_SHAPE, "bytes must be a non-negative multiple of 16");
+    if (bytes == 0)
+        return ok();
+    if (!src || !dst)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(DGP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_copy(src, dst, bytes, (hipStream_t)stream), "probe launch");
+}
+
+dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes < 0 || bytes % 4096 != 0)
+        return fail(DGP_ERR_SHAPE, "bytes must be a non-negative multiple of 4096");
+    if (bytes == 0)
+        return ok();
+    if (!src || !sink)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(src))
+        return fail(DGP_ERR_ALIGN, "source must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_stream_read(src, bytes, sink, (hipStream_t)stream), "probe launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI layer (dgp_api.cpp) and the
+// HIP kernels.  Not installed; callers use include/dgp.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgp {
+
+// Arguments shared by both GEMM kernel families.  All sizes are validated by
+// the host layer before a launch; byte quantities fit in 32 bits there.
+struct GemmArgs {
+    const uint8_t *A;     // [M][K] elements, row-major
+    const uint8_t *Bs;    // preshuffled B (dgp_preshuffle_b layout)
+    void *C;              // [M][N] bf16 (direct epilogue)
+    float *ws;            // [splits][M][N] fp32 (split-K partial epilogue)
+    const float *sA;      // per-tensor: 1 value; blockscale: [M][K/128]
+    const float *sB;      // per-tensor: 1 value; blockscale: [N/128][K/128]
+    int M, N;
+    int K;                // elements per row
+    int Kb;               // bytes per row of A and B
+    int Ks;               // bytes of K per split
+    int tiles_m, tiles_n, splits;
+    int remap, group_m;
+};
+
+// Kernel family selectors.
+enum Family { kTiled = 0, kStream = 1 };
+
+// One compiled kernel configuration.
+struct KernelSpec {
+    int family;
+    int dtype;      // 0 bf16, 1 fp8
+    int scale;      // 0 none, 1 tensor, 2 block128
+    int out;        // 0 bf16 direct, 1 fp32 partial
+    int tm, tn;     // workgroup output tile
+    int kt;         // K bytes per main-loop step (tiled) / per LDS panel (stream)
+    int waves;      // waves per workgroup
+    int p0, p1;     // family-specific: tiled = (wm, wn); stream = (strips per wave, depth)
+    int pv, pd;     // scheduling hint pair (tiled)
+    void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
+};
+
+// Table of every compiled GEMM kernel (defined in gemm.hip).
+const KernelSpec *kernel_table(int *count);
+
+hipError_t launch_preshuffle(const void *src, void *dst, int64_t N, int64_t Kb, bool inverse,
+                             hipStream_t stream);
+hipError_t launch_splitk_reduce(const float *ws, void *C, int64_t M, int64_t N, int splits,
+                                hipStream_t stream);
+
+// Probes (probe.hip).
+hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s);
+hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s);
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
+hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+
+}  // namespace dgp

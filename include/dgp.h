@@ -1,0 +1,178 @@
+/*
+ * dgp.h -- C ABI of the MI355X (gfx950) preshuffled-B GEMM library.
+ *
+ * The library computes C = A * B^T with B stored "preshuffled": reordered
+ * once, offline, into the order in which the matrix cores consume it.  The
+ * operation and its variants are the ones the following pages describe:
+ *
+ *   [P1] FlyDSL PR #1008, "Enable the gmem->LDS async copy for f16/bf16
+ *        preshuffle GEMM" -- the bf16 preshuffle GEMM, its A-tile async copy
+ *        into LDS, the A-tile granularity rule and the argument checks.
+ *   [P2] FlyDSL PR #974 and its follow-up commit "Reject tiles whose A tile is
+ *        only partially loaded" / "Restore per-k-step A-fragment LDS reads".
+ *   [P3] aiter PR #5148, "FlyDSL split-K preshuffle decode GEMM for small-M
+ *        shapes (FP8 + MX)" -- FP8 per-tensor and blockscale modes, the
+ *        two-pass split-K (fp32 workspace partials + reduce kernel) and the
+ *        direct split_k = 1 epilogue.
+ *
+ * Conventions for every entry point
+ *   - A is [M][K] row-major, B is [N][K] row-major (K contiguous): C = A*B^T,
+ *     C is [M][N] row-major bf16.  (m, k from A's shape and n from the weight's
+ *     first dimension, as in the blockscale reference reviewed on [P3].)
+ *   - Element types: DGP_BF16 (bf16 bit patterns, 2 bytes) or DGP_FP8_E4M3
+ *     (OCP e4m3fn codes, 1 byte).  Accumulation is always fp32.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees, synchronises or keeps a pointer past the
+ *     call.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and runs asynchronously: outputs are ready when the stream is.
+ *   - Scales are device pointers to fp32 as well (so a launch never needs a
+ *     host synchronisation).
+ *   - Every argument is validated on the host before any HIP call.  On a bad
+ *     argument the call returns a status != DGP_OK and enqueues nothing.
+ *   - Aliasing between an output and any input is not supported.
+ */
+#ifndef DGP_H
+#define DGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dgp_status {
+    DGP_OK = 0,
+    DGP_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    DGP_ERR_SHAPE = 2,       /* a size is negative or breaks a divisibility rule */
+    DGP_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                 */
+    DGP_ERR_DTYPE = 4,       /* unknown element type                             */
+    DGP_ERR_SCALE_MODE = 5,  /* unknown scale mode, or not valid for the dtype   */
+    DGP_ERR_SPLITK = 6,      /* split_k < 1 or does not divide the K range      */
+    DGP_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required          */
+    DGP_ERR_CONFIG = 8,      /* requested tile configuration not available       */
+    DGP_ERR_ARCH = 9,        /* current device is not gfx950                     */
+    DGP_ERR_HIP = 10         /* a HIP runtime call or kernel launch failed       */
+} dgp_status;
+
+typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1 } dgp_dtype;
+
+/* DGP_SCALE_NONE: bf16 only.  DGP_SCALE_TENSOR: fp8 only; sA, sB each point to
+ * one fp32 and C = bf16(acc * (sA*sB)).  DGP_SCALE_BLOCK128: fp8 only; sA is
+ * [M][K/128] fp32 (A per row per 128-wide K block), sB is [N/128][K/128] fp32
+ * (B per 128x128 block), both row-major; each 128-K block's fp32 partial sum
+ * is multiplied by sA[m][kb]*sB[n/128][kb] and added to the fp32 accumulator
+ * ([P3] "Summary"; scale shapes from the run_torch_blockscale review). */
+typedef enum dgp_scale_mode {
+    DGP_SCALE_NONE = 0,
+    DGP_SCALE_TENSOR = 1,
+    DGP_SCALE_BLOCK128 = 2
+} dgp_scale_mode;
+
+/* Optional tile configuration.  Pass NULL to use the built-in per-shape table.
+ *   tile_m, tile_n : output tile of one workgroup (must name a compiled tile)
+ *   tile_k         : K bytes staged per main-loop step (128 or 256)
+ *   xcd_remap      : 1 = map workgroup ids so neighbouring tiles share an XCD's
+ *                    L2 (output is bit-identical either way), 0 = plain raster
+ *   group_m        : tile rows per raster group when xcd_remap = 1 (>= 1)
+ *   preload        : scheduling hint pair -- the number of global loads and of
+ *                    LDS reads placed between matrix-core instructions; each
+ *                    >= 0 ([P1] "Changes" item 3 and its review: a pair of
+ *                    non-negative integers, rejected otherwise).  0,0 = none. */
+typedef struct dgp_config {
+    int tile_m;
+    int tile_n;
+    int tile_k;
+    int xcd_remap;
+    int group_m;
+    int preload_vmem;
+    int preload_dsrd;
+} dgp_config;
+
+/*
+ * dgp_preshuffle_b -- reorder B into the layout the GEMM reads.
+ *
+ * B ([N][K] of `dtype`, row-major) -> Bs (same byte count).  With
+ * Kb = K * element_bytes, Bs is a sequence of 1024-byte blocks, one per
+ * (nb, kb) for nb < N/16, kb < Kb/64, block index nb*(Kb/64) + kb; inside a
+ * block, byte g*256 + nn*16 + j (g < 4, nn < 16, j < 16) holds byte
+ * kb*64 + g*16 + j of row nb*16 + nn.  A wave reading 16 bytes per lane from
+ * one block therefore receives one 16x16 matrix-core operand tile: lane l gets
+ * row 16*nb + l%16 of B, K-bytes 64*kb + 16*(l/16) .. +15.  The pages name this
+ * preshuffled layout ([P1] title and file table, [P3] "bpreshuffle") without
+ * writing it out; this is the library's own definition.  The layout is
+ * byte-granular, so one packer serves both element types.
+ *
+ * Requires N % 16 == 0, (K * element_bytes) % 64 == 0, N, K >= 0, B and Bs
+ * 16-byte aligned and not overlapping.  Run it ONCE per weight: Bs is always
+ * treated as already preshuffled and no other entry point shuffles B again
+ * (preshuffling twice corrupts the result, the hazard flagged on [P3]).
+ */
+dgp_status dgp_preshuffle_b(const void *B, void *Bs, int64_t N, int64_t K, int dtype, void *stream);
+
+/* dgp_unshuffle_b -- the inverse permutation (Bs -> B).  Same rules. */
+dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dtype, void *stream);
+
+/*
+ * dgp_gemm_preshuffle -- C = A * B^T, single pass, bf16 output.
+ *
+ * A: [M][K] `dtype`, Bs: dgp_preshuffle_b(B), C: [M][N] bf16.  fp32
+ * accumulation; scales per `scale_mode` (see dgp_scale_mode) applied in the
+ * epilogue; the result is rounded to bf16 once, to nearest-even ([P1]
+ * "Performance": bf16 in, bf16 out; [P3] "What's included": direct-output
+ * epilogue for every scale mode).
+ *
+ * Requires M, N, K >= 0; N % 16 == 0; (K*element_bytes) % 128 == 0 (bf16:
+ * K % 64, fp8: K % 128 -- the fp8 matrix-core step is 128 deep); blockscale
+ * also N % 128 == 0 and K % 128 == 0 (rejected, never rounded up: the review
+ * on [P3] flags the silent ceil-division); A, Bs, C 16-byte aligned.
+ * M = 0 or N = 0 is a no-op returning DGP_OK.  The device must be gfx950.
+ */
+dgp_status dgp_gemm_preshuffle(const void *A, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
+                               int dtype, int scale_mode, const float *sA, const float *sB,
+                               const dgp_config *cfg, void *stream);
+
+/* Bytes of fp32 workspace dgp_gemm_preshuffle_splitk needs:
+ * split_k * M * N * 4 for split_k > 1, 0 for split_k == 1. */
+size_t dgp_splitk_workspace_bytes(int64_t M, int64_t N, int split_k);
+
+/*
+ * dgp_gemm_preshuffle_splitk -- two-pass split-K GEMM for decode-sized M.
+ *
+ * Pass 1 splits K into split_k equal contiguous ranges; each range's fp32
+ * partial (scales applied) is written to ws[s][M][N].  Pass 2, a second kernel
+ * on the same stream, sums the partials in order s = 0..split_k-1 in fp32 and
+ * rounds to bf16 once ([P3] "What's included" and its file table: fp32
+ * workspace partials, a reduction kernel that downcasts once, a two-pass
+ * driver).  split_k == 1 takes the direct epilogue and ignores ws ([P3]: the
+ * single-pass split_k = 1 epilogue).
+ *
+ * Requires everything dgp_gemm_preshuffle does, plus split_k >= 1,
+ * K % split_k == 0 and ((K/split_k)*element_bytes) % 128 == 0 (blockscale:
+ * (K/split_k) % 128 == 0); for split_k > 1, ws != NULL, 16-byte aligned, and
+ * ws_bytes >= dgp_splitk_workspace_bytes(M, N, split_k).  ws is scratch owned
+ * by the caller; its contents after the call are unspecified.
+ */
+dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
+                                      int64_t K, int dtype, int scale_mode, const float *sA,
+                                      const float *sB, int split_k, float *ws, size_t ws_bytes,
+                                      const dgp_config *cfg, void *stream);
+
+/* dgp_check_arch -- DGP_OK if `gcn_arch_name` (as reported by the HIP device
+ * properties, e.g. "gfx950:sramecc+:xnack-") names gfx950, else DGP_ERR_ARCH.
+ * Pure host function.  The async global->LDS copy the GEMM depends on exists
+ * on gfx950 only ([P1] review: fail early off gfx950). */
+dgp_status dgp_check_arch(const char *gcn_arch_name);
+
+/* dgp_status_string -- static, human-readable name of a status code. */
+const char *dgp_status_string(int status);
+
+/* dgp_last_error -- detail message of the last failing call on this thread
+ * (static thread-local storage; empty string if none). */
+const char *dgp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGP_H */

@@ -1,0 +1,74 @@
+/*
+ * dgp_diag.h -- diagnostic entry points of the gfx950 preshuffled-B GEMM
+ * library: the workgroup -> tile map, and small probe kernels used to check
+ * hardware facts the GEMM relies on and to measure the roofline walls.
+ * Same conventions as dgp.h (device pointers owned by the caller, async on
+ * `stream`, host-side validation first).
+ */
+#ifndef DGP_DIAG_H
+#define DGP_DIAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dgp.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * dgp_tile_of_workgroup -- host mirror of the device workgroup -> tile map.
+ *
+ * For a grid of tiles_m x tiles_n x splits workgroups, returns in out[0..2]
+ * the (tile_m index, tile_n index, split index) that workgroup `wg` computes.
+ * With xcd_remap = 1 the ids are first regrouped so that the workgroups the
+ * hardware places on one XCD (ids congruent mod 8 -- 8 XCDs on gfx950) get
+ * consecutive logical ids, and logical ids are rastered in groups of group_m
+ * tile rows, keeping tiles that share A rows or B columns on one XCD's L2.
+ * This is the workgroup-order swizzle exposed as xcd_swizzle on [P1]
+ * "Performance" and re-derived from the linear workgroup id in the attention
+ * XCD-remap commit on [P2]; the map is a bijection, so the output is
+ * bit-identical with or without it.  Returns DGP_ERR_SHAPE for bad arguments.
+ */
+dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t splits,
+                                 int xcd_remap, int group_m, int64_t out[3]);
+
+/*
+ * dgp_probe_mfma_layout -- run each matrix-core instruction the GEMM uses once
+ * on operands the caller supplies and store the raw accumulator registers.
+ *   which = 0: v_mfma_f32_16x16x32_bf16   (a, b: 64 lanes x 16 bytes)
+ *   which = 1: v_mfma_f32_16x16x128_f8f6f4 with e4m3 operands (64 lanes x 32 bytes)
+ * a, b: device buffers of 64*16 (which 0) or 64*32 (which 1) bytes, lane-major.
+ * out: device buffer of 64*4 fp32 (lane-major, 4 accumulator registers).
+ */
+dgp_status dgp_probe_mfma_layout(int which, const void *a, const void *b, float *out, void *stream);
+
+/*
+ * dgp_probe_lds_dma -- one wave copies 64 x 16 bytes from src (lane l reads
+ * the 16 bytes at src + perm[l]*16) into LDS with the async global->LDS load
+ * the GEMM uses, then copies LDS bytes 0..1023 to dst unchanged, revealing
+ * where each lane's bytes landed.  src: >= 1024 bytes, perm: 64 int32 in
+ * [0, 64), dst: 1024 bytes.
+ */
+dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, void *stream);
+
+/*
+ * dgp_probe_copy -- plain 16-byte-per-thread device copy of `bytes` bytes
+ * (bytes % 16 == 0).  The reference kernel of known traffic used to calibrate
+ * hardware byte counters.
+ */
+dgp_status dgp_probe_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/*
+ * dgp_probe_stream_read -- read `bytes` bytes (bytes % 4096 == 0) with
+ * 16-byte non-temporal loads and write one 32-bit xor-fold per workgroup to
+ * `sink` (>= 4096 uint32).  Measures the attainable HBM read rate.
+ */
+dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGP_DIAG_H */

@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+run the library through its C ABI (via the binding) and compare with the
+oracle."""
+import numpy as np
+import torch
+
+import dense_gemm_packer_amd as dgp
+import oracle
+
+DEV = "cuda:0"
+
+
+def dev_codes(codes: np.ndarray, dtype: str) -> torch.Tensor:
+    """bf16 bit patterns (uint16) or e4m3 codes (uint8) -> device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
+    t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn)
+    return t.to(DEV)
+
+
+def dev_f32(x) -> torch.Tensor | None:
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to(DEV)
+
+
+def host_bits(c: torch.Tensor) -> np.ndarray:
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def odt(dtype: str) -> int:
+    return oracle.BF16 if dtype == "bf16" else oracle.FP8_E4M3
+
+
+def omode(mode: str) -> int:
+    return {"none": oracle.SCALE_NONE, "tensor": oracle.SCALE_TENSOR, "block128": oracle.SCALE_BLOCK128}[mode]
+
+
+def dmode(mode: str) -> int:
+    return {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128}[mode]
+
+
+def run_gpu(A, B, dtype, mode, sA=None, sB=None, split_k=1, config=None, Bs_dev=None):
+    """Preshuffle B and run the GEMM on the device; returns C as bf16 bits."""
+    a = dev_codes(A, dtype)
+    if Bs_dev is None:
+        Bs_dev = dgp.preshuffle_b(dev_codes(B, dtype))
+    if split_k == 1 and config is None:
+        c = dgp.gemm_preshuffle(a, Bs_dev, dev_f32(sA), dev_f32(sB), dmode(mode))
+    else:
+        c = dgp.gemm_preshuffle_splitk(a, Bs_dev, split_k, dev_f32(sA), dev_f32(sB), dmode(mode),
+                                       config=config)
+    torch.cuda.synchronize()
+    return host_bits(c)
+
+
+def run_oracle(A, B, dtype, mode, sA=None, sB=None, split_k=1, rows=None):
+    return oracle.gemm(A, B, odt(dtype), omode(mode), sA, sB, split_k=split_k, rows=rows)
+
+
+def assert_close(c_gpu_bits, c_ref_f32, tol=1e-2, what=""):
+    """max |C_gpu - C_ref| <= tol * max |C_ref| (bf16 output vs fp32 oracle)."""
+    g = bf16_to_f32(c_gpu_bits).astype(np.float64)
+    r = c_ref_f32.astype(np.float64)
+    assert g.shape == r.shape
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    bound = tol * max(np.max(np.abs(r)), 1e-30)
+    err = np.max(np.abs(g - r)) if g.size else 0.0
+    assert err <= bound, f"{what}: max err {err:.4g} > {bound:.4g}"
+    return err / max(np.max(np.abs(r)), 1e-30)

@@ -1,0 +1,73 @@
+"""Hardware facts the GEMM relies on, checked on the device: the register
+layout of the two matrix-core instructions, and where the async
+global->LDS copy puts each lane's 16 bytes."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_packer_amd as dgp
+from gpu_common import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_mfma_bf16_16x16x32_layout():
+    """First operand lane l: row l%16, K 8*(l//16)+j; second operand lane l:
+    column l%16, same K; result lane l: rows 4*(l//16)+r, column l%16."""
+    g = np.random.Generator(np.random.PCG64(1))
+    X = g.integers(-3, 4, size=(16, 32)).astype(np.float32)   # first operand, 16 x K
+    Y = g.integers(-3, 4, size=(32, 16)).astype(np.float32)   # second operand, K x 16
+    a = np.zeros((64, 8), np.float32)
+    b = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        for j in range(8):
+            a[l, j] = X[l % 16, 8 * (l // 16) + j]
+            b[l, j] = Y[8 * (l // 16) + j, l % 16]
+    ta = torch.from_numpy(_bf16_bits(a).view(np.uint8).copy()).to(DEV)
+    tb = torch.from_numpy(_bf16_bits(b).view(np.uint8).copy()).to(DEV)
+    out = dgp.probe_mfma_layout(0, ta, tb).cpu().numpy()
+    D = X @ Y
+    want = np.array([[D[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)], np.float32)
+    assert np.array_equal(out, want)
+
+
+def test_mfma_fp8_16x16x128_layout():
+    """e4m3 operands, 32 bytes per lane assembled as the library does: bytes
+    0..15 = K 16*(l//16)+j, bytes 16..31 = K 64+16*(l//16)+j.  Any K order the
+    hardware uses is shared by both operands, so the product must come out
+    exact; the result layout is as for bf16."""
+    g = np.random.Generator(np.random.PCG64(2))
+    X = g.integers(-4, 5, size=(16, 128)).astype(np.float32)
+    Y = g.integers(-4, 5, size=(128, 16)).astype(np.float32)
+    a = np.zeros((64, 32), np.float32)
+    b = np.zeros((64, 32), np.float32)
+    for l in range(64):
+        ks = [16 * (l // 16) + j for j in range(16)] + [64 + 16 * (l // 16) + j for j in range(16)]
+        a[l] = X[l % 16, ks]
+        b[l] = Y[ks, l % 16]
+    to8 = lambda v: torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).contiguous().to(DEV)
+    out = dgp.probe_mfma_layout(1, to8(a), to8(b)).cpu().numpy()
+    D = X @ Y
+    want = np.array([[D[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)], np.float32)
+    assert np.array_equal(out, want)
+
+
+def test_lds_dma_destination_is_linear_per_lane():
+    g = np.random.Generator(np.random.PCG64(3))
+    src = g.integers(0, 256, size=1024, dtype=np.uint8)
+    perm = g.permutation(64).astype(np.int32)
+    out = dgp.probe_lds_dma(torch.from_numpy(src).to(DEV), torch.from_numpy(perm).to(DEV)).cpu().numpy()
+    want = np.concatenate([src[16 * p:16 * p + 16] for p in perm])
+    assert np.array_equal(out, want)
+
+
+def test_probe_copy_copies():
+    x = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(x)
+    dgp.probe_copy(x, y)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)

@@ -1,0 +1,201 @@
+"""GEMM parity on the device against the oracle, element by element.
+
+Shapes span several tiles and ragged tails (M and N not multiples of the
+tile), every compiled kernel configuration is forced at least once, and the
+degenerate cases (M = 1, K = 0, empty) are covered.  The bar: exact-integer
+inputs are bit-exact; random inputs satisfy max|C - C_ref| <= 1e-2*max|C_ref|
+with C_ref the oracle's fp32 value before rounding."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_packer_amd as dgp
+import oracle
+import synth
+from gpu_common import (DEV, assert_close, dev_codes, dev_f32, dmode, host_bits, run_gpu,
+                        run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+TILED = [(256, 256), (128, 256), (128, 128)]
+
+
+def rand_inputs(dtype, mode, M, N, K, seed):
+    if dtype == "bf16":
+        return synth.bf16_uniform((M, K), seed), synth.bf16_uniform((N, K), seed + 1), None, None
+    if mode == "tensor":
+        A, sA = synth.fp8_per_tensor((M, K), seed)
+        B, sB = synth.fp8_per_tensor((N, K), seed + 1)
+        return A, B, sA, sB
+    A, sA = synth.fp8_blockscale_a(M, K, seed, seed + 2)
+    B, sB = synth.fp8_blockscale_b(N, K, seed + 1, seed + 3)
+    return A, B, sA, sB
+
+
+def exact_inputs(dtype, mode, M, N, K, seed):
+    A = synth.exact_ints((M, K), seed, dtype)
+    B = synth.exact_ints((N, K), seed + 1, dtype)
+    if mode == "none":
+        return A, B, None, None
+    if mode == "tensor":
+        return A, B, np.array([0.125], np.float32), np.array([1.0], np.float32)
+    return (A, B, synth.exact_block_scales((M, K // 128), seed + 2),
+            synth.exact_block_scales((N // 128, K // 128), seed + 3))
+
+
+CASES = [  # dtype, mode, M, N, K
+    ("bf16", "none", 128, 256, 256),
+    ("bf16", "none", 300, 272, 512),
+    ("bf16", "none", 1, 64, 128),
+    ("bf16", "none", 16, 528, 1024),
+    ("bf16", "none", 40, 144, 384),
+    ("bf16", "none", 1030, 1040, 640),
+    ("fp8", "tensor", 128, 256, 256),
+    ("fp8", "tensor", 300, 272, 1024),
+    ("fp8", "tensor", 1, 2048, 896),
+    ("fp8", "tensor", 16, 528, 1024),
+    ("fp8", "tensor", 1030, 1040, 1280),
+    ("fp8", "block128", 16, 256, 1024),
+    ("fp8", "block128", 1, 384, 512),
+    ("fp8", "block128", 33, 128, 768),
+]
+
+
+@pytest.mark.parametrize("dtype,mode,M,N,K", CASES)
+def test_random_within_tolerance(dtype, mode, M, N, K):
+    A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 7 + M)
+    got = run_gpu(A, B, dtype, mode, sA, sB)
+    c32, _ = run_oracle(A, B, dtype, mode, sA, sB)
+    assert_close(got, c32, what=f"{dtype} {mode} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype,mode,M,N,K", CASES)
+def test_exact_integers_bit_exact(dtype, mode, M, N, K):
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 11 + N)
+    got = run_gpu(A, B, dtype, mode, sA, sB)
+    _, c16 = run_oracle(A, B, dtype, mode, sA, sB)
+    assert np.array_equal(got, c16)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor")])
+@pytest.mark.parametrize("tile", TILED)
+@pytest.mark.parametrize("split_k", [1, 2])
+def test_every_tiled_config(dtype, mode, tile, split_k):
+    M, N = 2 * tile[0] + 44, 2 * tile[1] + 48   # ragged in both dimensions
+    K = 1024 if dtype == "fp8" else 512
+    cfg = dgp.Config(tile[0], tile[1], 128, 1, 4, 0, 0)
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 5)
+    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
+    _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+    assert np.array_equal(got, c16)
+    A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 6)
+    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
+    c32, _ = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+    assert_close(got, c32)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
+@pytest.mark.parametrize("M", [1, 16, 20])
+@pytest.mark.parametrize("split_k", [1, 2, 4, 8])
+def test_stream_splitk(dtype, mode, M, split_k):
+    N, K = 384, 2048
+    cfg = dgp.Config(16, 64, 0, 0, 1, 0, 0)
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 3)
+    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
+    _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+    assert np.array_equal(got, c16)
+    A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 4)
+    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
+    c32, _ = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+    assert_close(got, c32)
+
+
+def test_stream_multi_panel():
+    """K range larger than one LDS panel of A (several panels per split)."""
+    M, N, K = 16, 256, 24576
+    A, B, sA, sB = exact_inputs("fp8", "tensor", M, N, K, 9)
+    got = run_gpu(A, B, "fp8", "tensor", sA, sB, split_k=1, config=dgp.Config(16, 64, 0, 0, 1, 0, 0))
+    _, c16 = run_oracle(A, B, "fp8", "tensor", sA, sB)
+    assert np.array_equal(got, c16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_one_hot_rows_bit_exact(dtype):
+    M, N, K = 64, 320, 1024
+    B = synth.bf16_uniform((N, K), 1) if dtype == "bf16" else synth.fp8_per_tensor((N, K), 1)[0]
+    ks = np.random.Generator(np.random.PCG64(2)).integers(0, K, size=M)
+    A = np.zeros((M, K), dtype=np.uint16 if dtype == "bf16" else np.uint8)
+    A[np.arange(M), ks] = 0x3F80 if dtype == "bf16" else 0x38
+    mode = "none" if dtype == "bf16" else "tensor"
+    sA = None if dtype == "bf16" else np.array([0.5], np.float32)
+    sB = None if dtype == "bf16" else np.array([0.25], np.float32)
+    for cfg in (None, dgp.Config(16, 64, 0, 0, 1, 0, 0), dgp.Config(128, 128, 128, 1, 4, 0, 0)):
+        got = run_gpu(A, B, dtype, mode, sA, sB, config=cfg) if cfg else run_gpu(A, B, dtype, mode, sA, sB)
+        _, c16 = run_oracle(A, B, dtype, mode, sA, sB)
+        assert np.array_equal(got, c16)
+    if dtype == "bf16":
+        assert np.array_equal(got, B[:, ks].T)
+
+
+def test_identity_b_returns_a():
+    M, K = 300, 512
+    A = synth.bf16_uniform((M, K), 3)
+    B = np.zeros((K, K), np.uint16)
+    B[np.arange(K), np.arange(K)] = 0x3F80
+    for cfg in (None, dgp.Config(256, 256, 128, 1, 4, 0, 0)):
+        got = run_gpu(A, B, "bf16", "none", config=cfg) if cfg else run_gpu(A, B, "bf16", "none")
+        assert np.array_equal(got, A)
+
+
+@pytest.mark.parametrize("tile", TILED)
+def test_xcd_remap_is_bit_identical(tile):
+    M, N, K = 1100, 1072, 512
+    A, B, _, _ = rand_inputs("bf16", "none", M, N, K, 8)
+    outs = []
+    for remap, group in ((0, 1), (1, 1), (1, 4), (1, 8)):
+        outs.append(run_gpu(A, B, "bf16", "none", config=dgp.Config(tile[0], tile[1], 128, remap, group, 0, 0)))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_negative_control_corrupted_weight_diverges():
+    M, N, K = 64, 256, 512
+    A, B, _, _ = rand_inputs("bf16", "none", M, N, K, 12)
+    Bs = dgp.preshuffle_b(dev_codes(B, "bf16"))
+    raw = Bs.view(torch.uint8).view(-1)
+    raw[12345] ^= 0x40
+    got = run_gpu(A, B, "bf16", "none", Bs_dev=Bs)
+    c32, c16 = run_oracle(A, B, "bf16", "none")
+    assert not np.array_equal(got, c16)
+    # and a double preshuffle (the hazard of shuffling an already-preshuffled B) corrupts C
+    Bss = dgp.preshuffle_b(dgp.preshuffle_b(dev_codes(B, "bf16")))
+    got = run_gpu(A, B, "bf16", "none", Bs_dev=Bss)
+    err = np.max(np.abs((got.astype(np.uint32) << 16).view(np.float32) - c32))
+    assert err > 1e-2 * np.max(np.abs(c32))
+
+
+def test_k_zero_gives_zeros_and_empty_is_noop():
+    A = torch.zeros((5, 0), dtype=torch.bfloat16, device=DEV)
+    Bs = torch.zeros((32, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((5, 32), 7.0, dtype=torch.bfloat16, device=DEV)
+    dgp.gemm_preshuffle(A, Bs, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    A = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV)
+    Bs = torch.zeros((32, 128), dtype=torch.bfloat16, device=DEV)
+    assert dgp.gemm_preshuffle(A, Bs).shape == (0, 32)
+
+
+def test_binding_rejects_bad_arguments():
+    A = torch.zeros((16, 128), dtype=torch.float8_e4m3fn, device=DEV)
+    Bs = torch.zeros((128, 128), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.ones(1, device=DEV)
+    with pytest.raises(dgp.DgpError) as e:
+        dgp.gemm_preshuffle_splitk(A, Bs, 3, s, s)
+    assert e.value.name == "DGP_ERR_SPLITK"
+    with pytest.raises(dgp.DgpError) as e:
+        dgp.gemm_preshuffle(A, Bs, s, s, config=dgp.Config(100, 64, 128, 1, 4, 0, 0))
+    assert e.value.name == "DGP_ERR_CONFIG"
+    with pytest.raises(dgp.DgpError) as e:
+        dgp.gemm_preshuffle(A, Bs, s, s, config=dgp.Config(128, 128, 128, 1, 4, -1, 2))
+    assert e.value.name == "DGP_ERR_CONFIG"

@@ -1,0 +1,202 @@
+"""Host-side tests of the C-ABI library: it loads, exports every symbol the
+headers declare, and rejects every invalid argument with the documented
+status before making any HIP call (only invalid calls are made here, so no
+device is touched).  Also: the workgroup -> tile map is a bijection, and the
+product path shares nothing with the oracle."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, SCALE, SPLITK, WS, CONFIG, ARCH, HIP = range(11)
+BF16, FP8 = 0, 1
+NONE, TENSOR, BLOCK = 0, 1, 2
+P = 0x10000          # aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def dgp():
+    import dense_gemm_packer_amd as d
+    if not os.path.exists(d.LIB_PATH):
+        from dense_gemm_packer_amd import build
+        build.build()
+    return d
+
+
+@pytest.fixture(scope="module")
+def L(dgp):
+    return dgp.lib()
+
+
+def declared_symbols():
+    names = set()
+    for h in os.listdir(INCLUDE):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(dgp_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol(dgp, L):
+    names = declared_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(dgp.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", dgp.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dgp_\w+)", out))
+    assert names <= exported
+
+
+def test_check_arch(L):
+    assert L.dgp_check_arch(b"gfx950") == OK
+    assert L.dgp_check_arch(b"gfx950:sramecc+:xnack-") == OK
+    for bad in (b"gfx942", b"gfx942:sramecc+:xnack-", b"gfx9500", b"gfx90a", b"", None):
+        assert L.dgp_check_arch(bad) == ARCH
+
+
+def test_status_strings(L):
+    names = ["DGP_OK", "DGP_ERR_NULL", "DGP_ERR_SHAPE", "DGP_ERR_ALIGN", "DGP_ERR_DTYPE",
+             "DGP_ERR_SCALE_MODE", "DGP_ERR_SPLITK", "DGP_ERR_WORKSPACE", "DGP_ERR_CONFIG",
+             "DGP_ERR_ARCH", "DGP_ERR_HIP"]
+    for i, n in enumerate(names):
+        assert L.dgp_status_string(i).decode() == n
+    assert L.dgp_status_string(99).decode() == "DGP_ERR_UNKNOWN"
+
+
+def gemm(L, A=P, Bs=P, C=P, M=16, N=128, K=256, dtype=FP8, scale=TENSOR, sA=P, sB=P, cfg=None):
+    return L.dgp_gemm_preshuffle(A, Bs, C, M, N, K, dtype, scale, sA, sB, cfg, None)
+
+
+def splitk(L, split, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(A=P, Bs=P, C=P, M=16, N=128, K=1024, dtype=FP8, scale=TENSOR, sA=P, sB=P)
+    a.update(kw)
+    return L.dgp_gemm_preshuffle_splitk(a["A"], a["Bs"], a["C"], a["M"], a["N"], a["K"], a["dtype"],
+                                        a["scale"], a["sA"], a["sB"], split, ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), DTYPE),
+    (dict(M=-1), SHAPE), (dict(N=-16), SHAPE), (dict(K=-128), SHAPE),
+    (dict(dtype=BF16, scale=TENSOR), SCALE), (dict(dtype=FP8, scale=NONE), SCALE), (dict(scale=5), SCALE),
+    (dict(N=24), SHAPE),                                  # N % 16
+    (dict(dtype=BF16, scale=NONE, K=32), SHAPE),          # K*2 bytes % 128
+    (dict(K=192), SHAPE),                                 # fp8 K % 128
+    (dict(scale=BLOCK, N=64), SHAPE),                     # blockscale N % 128
+    (dict(C=0), NULL), (dict(A=0), NULL), (dict(Bs=0), NULL),
+    (dict(sA=0), NULL), (dict(sB=0), NULL),
+    (dict(A=P + 8), ALIGN), (dict(Bs=P + 4), ALIGN), (dict(C=P + 2), ALIGN), (dict(sA=P + 1), ALIGN),
+])
+def test_gemm_rejects(L, kw, status):
+    assert gemm(L, **kw) == status
+    assert L.dgp_last_error().decode() != ""
+
+
+def test_empty_problems_are_noops(L):
+    assert gemm(L, M=0, A=0, Bs=0, C=0) == OK
+    assert gemm(L, N=0, A=0, Bs=0, C=0) == OK
+
+
+def test_config_validation(dgp, L):
+    Cfg = dgp.Config
+    bad = [Cfg(256, 256, 128, 1, 4, -1, 0), Cfg(256, 256, 128, 1, 4, 0, -3), Cfg(256, 256, 128, 2, 4, 0, 0),
+           Cfg(256, 256, 128, 1, 0, 0, 0), Cfg(100, 100, 128, 1, 4, 0, 0), Cfg(256, 256, 64, 1, 4, 0, 0),
+           Cfg(256, 256, 128, 1, 4, 3, 3)]
+    for c in bad:
+        assert gemm(L, M=4096, N=4096, K=8192, cfg=ctypes.byref(c)) == CONFIG, (c.tile_m, c.preload_vmem)
+
+
+def test_splitk_validation(L):
+    assert splitk(L, 0) == SPLITK
+    assert splitk(L, 3) == SPLITK                          # 3 does not divide K=1024
+    assert splitk(L, 16) == SPLITK                         # 64-byte K range per split
+    assert splitk(L, 2, ws=0) == WS
+    assert splitk(L, 2, ws_bytes=2 * 16 * 128 * 4 - 1) == WS
+    assert splitk(L, 2, ws=P + 4) == ALIGN
+    assert L.dgp_splitk_workspace_bytes(16, 16384, 8) == 8 * 16 * 16384 * 4
+    assert L.dgp_splitk_workspace_bytes(16, 16384, 1) == 0
+    assert L.dgp_splitk_workspace_bytes(0, 16384, 4) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, P + 4096 * 64, 24, 64, FP8), SHAPE),              # N % 16
+    ((P, P + 4096 * 64, 16, 48, FP8), SHAPE),              # K bytes % 64
+    ((P, P + 4096 * 64, 16, 16, BF16), SHAPE),             # 32 bytes
+    ((P, P + 512, 16, 64, FP8), SHAPE),                    # overlap
+    ((0, P, 16, 64, FP8), NULL), ((P, 0, 16, 64, FP8), NULL),
+    ((P + 8, P + 65536, 16, 64, FP8), ALIGN),
+    ((P, P + 65536, 16, 64, 3), DTYPE),
+    ((P, P + 65536, -16, 64, FP8), SHAPE),
+])
+def test_preshuffle_rejects(L, args, status):
+    assert L.dgp_preshuffle_b(*args, None) == status
+    assert L.dgp_unshuffle_b(*args, None) == status
+
+
+def test_preshuffle_empty_is_noop(L):
+    assert L.dgp_preshuffle_b(0, 0, 0, 64, FP8, None) == OK
+    assert L.dgp_preshuffle_b(0, 0, 16, 0, FP8, None) == OK
+
+
+def test_probe_validation(L):
+    assert L.dgp_probe_mfma_layout(2, P, P, P, None) == CONFIG
+    assert L.dgp_probe_mfma_layout(0, 0, P, P, None) == NULL
+    assert L.dgp_probe_copy(P, P, 17, None) == SHAPE
+    assert L.dgp_probe_copy(P, P, 0, None) == OK
+    assert L.dgp_probe_stream_read(P, 4095, P, None) == SHAPE
+
+
+@pytest.mark.parametrize("remap,group_m", [(0, 1), (1, 1), (1, 4), (1, 8)])
+def test_tile_map_is_a_bijection(dgp, remap, group_m):
+    for tm in (1, 2, 3, 7, 16):
+        for tn in (1, 5, 16):
+            for sp in (1, 2, 3, 8):
+                W = tm * tn * sp
+                seen = {dgp.tile_of_workgroup(w, tm, tn, sp, remap, group_m) for w in range(W)}
+                assert len(seen) == W
+                assert all(0 <= a < tm and 0 <= b < tn and 0 <= c < sp for a, b, c in seen)
+
+
+def test_tile_map_remap_groups_xcd_neighbours(dgp):
+    # 16 x 16 tiles, group_m 4: the 32 workgroups the hardware deals to XCD 0
+    # (ids 0, 8, 16, ...) cover a 4 x 8 block of tiles.
+    tiles = {dgp.tile_of_workgroup(w, 16, 16, 1, 1, 4)[:2] for w in range(0, 256, 8)}
+    assert {t[0] for t in tiles} == {0, 1, 2, 3} and {t[1] for t in tiles} == set(range(8))
+    # without remap the same ids are a plain raster
+    assert dgp.tile_of_workgroup(17, 16, 16, 1, 0, 4) == (1, 1, 0)
+
+
+def test_tile_map_rejects_bad_arguments(dgp):
+    with pytest.raises(dgp.DgpError):
+        dgp.tile_of_workgroup(6, 2, 3, 1, 1, 4)
+    with pytest.raises(dgp.DgpError):
+        dgp.tile_of_workgroup(0, 0, 3, 1, 1, 4)
+
+
+def test_product_shares_nothing_with_the_oracle(dgp):
+    pkg = os.path.join(ROOT, "dense_gemm_packer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text.replace("no oracle", "")), f
+    deps = subprocess.run(["ldd", dgp.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".c", ".py")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "dense_gemm_packer_amd" not in text.replace("dense_gemm_packer_amd/csrc", "")
+
+
+def test_binding_fails_loudly_without_the_library(dgp, monkeypatch, tmp_path):
+    monkeypatch.setattr(dgp, "_lib", None)
+    monkeypatch.setattr(dgp, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        dgp.lib()
