@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the preshuffled-B GEMM on one MI355X (gfx950).
+
+One step = one call of the hot path on the headline workload: the bf16 GEMM
+C[4096][4096] = A[4096][8192] * B^T with B preshuffled (the preshuffle runs
+once per weight, before the timed region, and is timed on its own).  Inputs
+are seeded synthetic data resident in HBM before the timed region starts.
+
+Prints ONE JSON line: throughput (TFLOP/s), the roofline of the dominant
+kernel (the GEMM itself, timed per launch with HIP events on its launch
+stream), the CPU oracle timed on a bounded row sample, and secondary figures
+(fp8 GEMM, fp8 split-K decode and blockscale decode in GB/s against the HBM
+wall, the packer) measured in the same run.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 (published)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+MALL_BYTES = 256 << 20         # Infinity Cache; cold-cache rotation exceeds 2x this
+METRIC = "TFLOP/s (large M) and GB/s (decode M≤16) at 1 GPU; % of MFMA / HBM roofline"
+PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_4096x4096x8192_traffic.md")
+KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm.hip", "dense_gemm_packer_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if
+    missing or taken on a different version of the kernel source."""
+    try:
+        kv = {}
+        with open(PROFILE_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip().strip("-* `")] = v.strip().strip("`")
+        if kv.get("source_sha256") != kernel_source_sha():
+            return None
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of C in the CPU oracle sample")
+    ap.add_argument("--profile-traffic", action="store_true",
+                    help="run only a 256 MiB probe copy and a few GEMM launches (for counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_packer_amd as dgp
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(codes, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn).to(dev)
+
+    # ------------------------------------------------------------ headline
+    w = synth.workload_inputs("bf16_large")
+    M, N, K = w["M"], w["N"], w["K"]
+    A = to_dev(w["A"], "bf16")
+    B = to_dev(w["B"], "bf16")
+    Bs = dgp.preshuffle_b(B)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    if args.profile_traffic:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dgp.probe_copy(src, dst)
+        for _ in range(3):
+            dgp.gemm_preshuffle(A, Bs, out=C)
+        torch.cuda.synchronize()
+        log("profile-traffic: 3 x probe copy of 256 MiB, 3 x GEMM bf16 4096x4096x8192")
+        return 0
+
+    for _ in range(args.warmup):
+        dgp.gemm_preshuffle(A, Bs, out=C)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        dgp.gemm_preshuffle(A, Bs, out=C)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    launch_avg_ms = float(np.mean(launch_ms))
+    achieved = flops / (launch_avg_ms * 1e-3) / 1e12
+    log(f"bf16 GEMM {M}x{N}x{K}: {ms_per_step*1e3:.1f} us/step wall, {launch_avg_ms*1e3:.1f} us/launch "
+        f"(median {np.median(launch_ms)*1e3:.1f}, min {np.min(launch_ms)*1e3:.1f}) -> {achieved:.0f} TFLOP/s")
+
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gemm_tiled_kernel bf16 256x256x128 (8 waves)",
+                "per_launch": f"{flops:.4g} FLOP = 2*M*N*K"}
+
+    # --------------------------------------------------------- CPU oracle
+    cpu = None
+    c_gpu = C.view(torch.int16).cpu().numpy().view(np.uint16)
+    if not args.no_cpu:
+        import oracle
+        rows = np.linspace(0, M - 1, min(args.cpu_rows, M)).astype(np.int64)
+        threads = oracle.default_threads()
+        t = time.perf_counter()
+        c32, _ = oracle.gemm(w["A"], w["B"], oracle.BF16, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t
+        g = (c_gpu[rows].astype(np.uint32) << 16).view(np.float32)
+        rel = float(np.max(np.abs(g - c32)) / np.max(np.abs(c32)))
+        cpu = {"value": round(2.0 * len(rows) * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{len(rows)} of {M} rows of C (all N={N} columns, K={K}), {dt:.1f} s; "
+                         f"GPU vs oracle on these rows: max|err|/max|C| = {rel:.2e}"}
+        log(f"oracle: {len(rows)} rows in {dt:.1f} s on {threads} threads; parity {rel:.2e}")
+        if rel > 1e-2:
+            log("PARITY FAILURE against the oracle on the sampled rows")
+            return 1
+
+    secondary = {}
+    if not args.no_secondary:
+        secondary = run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs, A, C, M, N, K)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(K) rounded to bf16)",
+        "config": {"workload": "bf16 GEMM C=A*B^T, M=N=4096, K=8192, B preshuffled, fp32 accumulate, bf16 out",
+                   "M": M, "N": N, "K": K, "tile": "256x256x128", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def graph_time_us(torch, fn, iters):
+    """Per-iteration GPU time of fn(i), i = 0..iters-1, captured in one HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * iters)
+
+
+def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C_bf16, M, N, K):
+    out = {}
+    # Packer on the headline weight: read + write 2*N*K*2 bytes.
+    B_raw = dgp.unshuffle_b(Bs_bf16)
+    dst = torch.empty_like(B_raw)
+    us = graph_time_us(torch, lambda i: dgp.preshuffle_b(B_raw, out=dst), 10)
+    out["packer_bf16_4096x8192"] = {"us": round(us, 2), "GB/s": round(2 * N * K * 2 / (us * 1e-6) / 1e9, 1)}
+    assert torch.equal(dst.view(torch.int16), Bs_bf16.view(torch.int16))
+    del B_raw, dst
+
+    # HBM wall: streaming read of 1 GiB.
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    us = graph_time_us(torch, lambda i: dgp.probe_stream_read(buf, sink), 5)
+    wall_gbs = (1 << 30) / (us * 1e-6) / 1e9
+    out["hbm_stream_read_1GiB"] = {"us": round(us, 1), "GB/s": round(wall_gbs, 1)}
+    del buf
+
+    # fp8 per-tensor GEMM, M=N=4096, K=8192.
+    w = synth.workload_inputs("fp8_large")
+    A8 = to_dev(w["A"], "fp8")
+    Bs8 = dgp.preshuffle_b(to_dev(w["B"], "fp8"))
+    sA = torch.from_numpy(w["sA"]).to(dev)
+    sB = torch.from_numpy(w["sB"]).to(dev)
+    C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, out=C8), 10)
+    tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
+    out["fp8_gemm_4096x4096x8192"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+                                      "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+    del A8, Bs8, C8
+
+    # fp8 split-K decode (per-tensor) and blockscale decode, cold cache.
+    dec = {}
+    for mode in ("tensor", "block128"):
+        name = "fp8_decode" if mode == "tensor" else "fp8_blockscale"
+        Ms = (1, 16) if mode == "tensor" else (16,)
+        Ns = (2048, 16384) if mode == "tensor" else (16384,)
+        for n_ in Ns:
+            base = synth.workload_inputs(name, M=16, N=n_)
+            kk = base["K"]
+            Bs_one = dgp.preshuffle_b(to_dev(base["B"], "fp8"))
+            copies = max(2, int(np.ceil(2 * MALL_BYTES / (n_ * kk))) + 1)
+            Bss = [Bs_one] + [Bs_one.clone() for _ in range(copies - 1)]
+            sBt = torch.from_numpy(np.ascontiguousarray(base["sB"])).to(dev)
+            for m_ in Ms:
+                A_ = to_dev(base["A"][:m_], "fp8")
+                sAt = torch.from_numpy(np.ascontiguousarray(base["sA"][:m_] if mode == "block128"
+                                                            else base["sA"])).to(dev)
+                best = None
+                for split in (1, 2, 4, 8):
+                    Cs = [torch.empty((m_, n_), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+                    wsb = dgp.splitk_workspace_bytes(m_, n_, split)
+                    wss = [torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev) for _ in range(copies)]
+                    iters = copies * max(1, 20 // copies)
+
+                    def fn(i, split=split, Cs=Cs, wss=wss, A_=A_, sAt=sAt):
+                        j = i % copies
+                        dgp.gemm_preshuffle_splitk(A_, Bss[j], split, sAt, sBt, out=Cs[j],
+                                                   workspace=wss[j] if split > 1 else None)
+                    us = graph_time_us(torch, fn, iters)
+                    nbytes = m_ * kk + n_ * kk + 2 * m_ * n_
+                    nbytes += 8 if mode == "tensor" else 4 * (m_ * kk // 128 + (n_ // 128) * (kk // 128))
+                    gbs = nbytes / (us * 1e-6) / 1e9
+                    key = f"{mode} M={m_} N={n_} K={kk} split={split}"
+                    dec[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                "frac_measured_wall": round(gbs / wall_gbs, 4)}
+                    if best is None or gbs > best[1]:
+                        best = (split, gbs)
+                    del Cs, wss
+                dec[f"best {mode} M={m_} N={n_}"] = {"split": best[0], "GB/s": round(best[1], 1),
+                                                     "frac_hbm": round(best[1] / PEAK_HBM_GBS, 4)}
+            del Bss, Bs_one
+    out["decode_cold_cache"] = dec
+    for k, v in dec.items():
+        if k.startswith("best"):
+            print(f"  {k}: {v}", file=sys.stderr)
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())
