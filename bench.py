@@ -65,8 +65,8 @@ def read_traffic():
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of C in the CPU oracle sample")
@@ -137,7 +137,7 @@ def main():
     traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_tiled_kernel bf16 256x256x128 (8 waves)",
+                "kernel": "gemm_tiled_kernel<bf16, 256x256 tile, 1x8 waves, 128-byte k-tile, prefetch 2, LDS read-ahead 8>",
                 "per_launch": f"{flops:.4g} FLOP = 2*M*N*K"}
 
     # --------------------------------------------------------- CPU oracle

@@ -38,16 +38,17 @@ class DgpError(RuntimeError):
 
 
 class Config(ctypes.Structure):
-    """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair."""
+    """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair, waves_m, prefetch."""
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("xcd_remap", ctypes.c_int), ("group_m", ctypes.c_int),
-                ("preload_vmem", ctypes.c_int), ("preload_dsrd", ctypes.c_int)]
+                ("preload_vmem", ctypes.c_int), ("preload_dsrd", ctypes.c_int),
+                ("waves_m", ctypes.c_int), ("prefetch", ctypes.c_int)]
 
 
 # Every symbol include/dgp.h and include/dgp_diag.h declare.
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
-           "dgp_tile_of_workgroup", "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
+           "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
            "dgp_probe_stream_read")
 
 _lib = None
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
                                        _sz, _vp, _vp],
         "dgp_check_arch": [ctypes.c_char_p],
         "dgp_tile_of_workgroup": [_i64, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_i64)],
+        "dgp_kernel_count": [],
+        "dgp_kernel_info": [_int, ctypes.POINTER(Config), ctypes.POINTER(_int), ctypes.POINTER(_int),
+                            ctypes.POINTER(_int)],
         "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
@@ -219,6 +223,17 @@ def tile_of_workgroup(wg: int, tiles_m: int, tiles_n: int, splits: int, xcd_rema
     out = (ctypes.c_int64 * 3)()
     _check(lib().dgp_tile_of_workgroup(wg, tiles_m, tiles_n, splits, xcd_remap, group_m, out))
     return int(out[0]), int(out[1]), int(out[2])
+
+
+def kernels():
+    """Every compiled GEMM kernel: list of (Config, dtype, scale_mode, split_out)."""
+    L = lib()
+    out = []
+    for i in range(L.dgp_kernel_count()):
+        cfg, dt, sm, so = Config(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(L.dgp_kernel_info(i, ctypes.byref(cfg), ctypes.byref(dt), ctypes.byref(sm), ctypes.byref(so)))
+        out.append((cfg, dt.value, sm.value, so.value))
+    return out
 
 
 def probe_mfma_layout(which: int, a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:

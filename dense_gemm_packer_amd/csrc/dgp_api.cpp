@@ -89,14 +89,21 @@ bool spec_fits(const KernelSpec &k, int64_t Ks)
     return true;   // stream: any K range that is a multiple of 128 bytes
 }
 
-const KernelSpec *find_spec(int family, int dtype, int scale, int out, int tm, int tn, int kt, int p0, int p1)
+// A kernel-table query; -1 in a field means "any".
+struct Query {
+    int family, dtype, scale, out, tm, tn;
+    int kt = -1, wm = -1, depth = -1, pv = -1, pd = -1;
+};
+
+const KernelSpec *find_spec(const Query &q)
 {
     int n = 0;
     const KernelSpec *t = kernel_table(&n);
     for (int i = 0; i < n; ++i) {
         const KernelSpec &k = t[i];
-        if (k.family == family && k.dtype == dtype && k.scale == scale && k.out == out && k.tm == tm &&
-            k.tn == tn && (kt <= 0 || k.kt == kt) && (p0 < 0 || k.p0 == p0) && (p1 < 0 || k.p1 == p1))
+        if (k.family == q.family && k.dtype == q.dtype && k.scale == q.scale && k.out == q.out && k.tm == q.tm &&
+            k.tn == q.tn && (q.kt < 0 || k.kt == q.kt) && (q.wm < 0 || k.p0 == q.wm) &&
+            (q.depth < 0 || k.depth == q.depth) && (q.pv < 0 || k.pv == q.pv) && (q.pd < 0 || k.pd == q.pd))
             return &k;
     }
     return nullptr;
@@ -105,14 +112,19 @@ const KernelSpec *find_spec(int family, int dtype, int scale, int out, int tm, i
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks)
 {
-    if (scale == DGP_SCALE_BLOCK128 || M <= 32) {
-        return find_spec(kStream, dtype, scale, out, 16, 64, -1, -1, -1);
-    }
+    if (scale == DGP_SCALE_BLOCK128 || M <= 32)
+        return find_spec(Query{kStream, dtype, scale, out, 16, 64});
     const KernelSpec *k = nullptr;
-    if (M >= 1024 && N >= 1024)
-        k = find_spec(kTiled, dtype, scale, out, 256, 256, 128, 2, 4);
-    if (!k || !spec_fits(*k, Ks))
-        k = find_spec(kTiled, dtype, scale, out, 128, 128, 128, 2, 2);
+    if (M >= 1024 && N >= 1024) {
+        Query q{kTiled, dtype, scale, out, 256, 256};
+        q.kt = 128, q.wm = 1, q.depth = 2, q.pv = 0, q.pd = 8;
+        k = find_spec(q);
+    }
+    if (!k || !spec_fits(*k, Ks)) {
+        Query q{kTiled, dtype, scale, out, 128, 128};
+        q.kt = 128, q.pv = 0, q.pd = 4;
+        k = find_spec(q);
+    }
     return (k && spec_fits(*k, Ks)) ? k : nullptr;
 }
 
@@ -210,28 +222,31 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     const KernelSpec *spec = nullptr;
     if (c.cfg && c.cfg->tile_m > 0) {
         const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
-        spec = find_spec(fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n,
-                         fam == kTiled ? c.cfg->tile_k : -1, -1, -1);
+        if (c.cfg->waves_m < 0 || c.cfg->prefetch < 0)
+            return fail(DGP_ERR_CONFIG, "waves_m and prefetch must be >= 0");
+        Query q{fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n};
+        if (fam == kTiled) {
+            q.kt = c.cfg->tile_k;
+            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;
+            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
+            // (0, 0) = this tile's tuned default hints; any other pair must
+            // name a compiled kernel exactly.
+            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0) {
+                q.pv = c.cfg->preload_vmem;
+                q.pd = c.cfg->preload_dsrd;
+            }
+        } else if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0) {
+            return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
+        }
+        spec = find_spec(q);
         if (!spec)
-            return fail(DGP_ERR_CONFIG, "no compiled kernel for tile %dx%dx%d with this dtype/scale",
-                        c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k);
+            return fail(DGP_ERR_CONFIG,
+                        "no compiled kernel for tile %dx%dx%d (waves_m %d, prefetch %d, preload %d,%d) with this "
+                        "dtype/scale", c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k, c.cfg->waves_m,
+                        c.cfg->prefetch, c.cfg->preload_vmem, c.cfg->preload_dsrd);
         if (!spec_fits(*spec, Ks))
             return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
                         spec->kt, (long long)Ks);
-        if (spec->pv != c.cfg->preload_vmem || spec->pd != c.cfg->preload_dsrd) {
-            int n = 0;
-            const KernelSpec *t = kernel_table(&n);
-            const KernelSpec *hinted = nullptr;
-            for (int i = 0; i < n; ++i)
-                if (t[i].family == spec->family && t[i].dtype == spec->dtype && t[i].scale == spec->scale &&
-                    t[i].out == spec->out && t[i].tm == spec->tm && t[i].tn == spec->tn &&
-                    t[i].kt == spec->kt && t[i].pv == c.cfg->preload_vmem && t[i].pd == c.cfg->preload_dsrd)
-                    hinted = &t[i];
-            if (!hinted)
-                return fail(DGP_ERR_CONFIG, "no compiled kernel with preload (%d, %d) for this tile",
-                            c.cfg->preload_vmem, c.cfg->preload_dsrd);
-            spec = hinted;
-        }
     } else {
         spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks);
         if (!spec)
@@ -245,7 +260,7 @@ dgp_status validate(const GemmCall &c, Plan *plan)
         plan->group_m = c.cfg->group_m < 1 ? 1 : c.cfg->group_m;
     } else {
         plan->remap = spec->family == kTiled ? 1 : 0;
-        plan->group_m = 4;
+        plan->group_m = 8;
     }
     const int64_t grid = (int64_t)plan->tiles_m * plan->tiles_n * c.split_k;
     if (grid > INT32_MAX)
@@ -406,6 +421,37 @@ dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, i
     out[0] = c.tm;
     out[1] = c.tn;
     out[2] = c.s;
+    return ok();
+}
+
+int dgp_kernel_count(void)
+{
+    int n = 0;
+    kernel_table(&n);
+    return n;
+}
+
+dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mode, int *split_out)
+{
+    int n = 0;
+    const KernelSpec *t = kernel_table(&n);
+    if (index < 0 || index >= n)
+        return fail(DGP_ERR_SHAPE, "kernel index %d out of range [0, %d)", index, n);
+    if (!cfg || !dtype || !scale_mode || !split_out)
+        return fail(DGP_ERR_NULL, "NULL output");
+    const KernelSpec &k = t[index];
+    cfg->tile_m = k.tm;
+    cfg->tile_n = k.tn;
+    cfg->tile_k = k.family == kTiled ? k.kt : 0;
+    cfg->xcd_remap = k.family == kTiled ? 1 : 0;
+    cfg->group_m = 8;
+    cfg->preload_vmem = k.pv;
+    cfg->preload_dsrd = k.pd;
+    cfg->waves_m = k.family == kTiled ? k.p0 : 0;
+    cfg->prefetch = k.family == kTiled ? k.depth : 0;
+    *dtype = k.dtype;
+    *scale_mode = k.scale;
+    *split_out = k.out == kOutPartial ? 1 : 0;
     return ok();
 }
 

@@ -137,14 +137,18 @@ struct TiledShape {
     static_assert(kCH <= 4, "B block offsets must fit the 12-bit immediate");
 };
 
-template <int DT, int TM, int TN, int WM, int WN, int KT, int SCALE, int OUT, int PV, int PD>
+template <int DT, int TM, int TN, int WM, int WN, int KT, int DEPTH, int SCALE, int OUT, int PV, int PD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 gemm_tiled_kernel(const GemmArgs p)
 {
     using S = TiledShape<DT, TM, TN, WM, WN, KT>;
     using Frag = typename Op<DT>::Frag;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * S::kBufBytes];
+    static_assert(DEPTH >= 1 && (DEPTH + 1) * TM * KT <= 160 * 1024, "A ring must fit in LDS");
+    // Prefetch distance DEPTH k-tiles: a ring of DEPTH+1 A buffers in LDS and
+    // DEPTH sets of B registers.
+    constexpr int kRing = DEPTH + 1;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * S::kBufBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -187,73 +191,141 @@ gemm_tiled_kernel(const GemmArgs p)
         for (int j = 0; j < S::kNT; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One set of B registers: the fragments of chunk c of k-tile t are
-    // reloaded with chunk c of tile t+1 as soon as the MFMAs of chunk c have
-    // consumed them, so every B load still has one whole k-tile of compute
-    // to land in.
-    i32x4 breg[S::kNT][S::kCH];
+    // B registers: DEPTH sets.  The fragments of chunk c of k-tile t (set
+    // t % DEPTH) are reloaded with chunk c of tile t+DEPTH as soon as the MFMAs
+    // of chunk c have consumed them, so every B load has DEPTH whole k-tiles
+    // of compute to land in.
+    i32x4 breg[DEPTH][S::kNT][S::kCH];
 
-    auto load_b = [&](int ch, uint32_t koff) {
+    auto load_b = [&](auto setc, int ch, uint32_t koff) {
+        constexpr int SET = decltype(setc)::value;
 #pragma unroll
         for (int nt = 0; nt < S::kNT; ++nt)
-            breg[nt][ch] = load16<kAuxNone>(rB, b_voff[nt] + ch * 1024 + koff * 16u);
+            breg[SET][nt][ch] = load16<kAuxNone>(rB, b_voff[nt] + ch * 1024 + koff * 16u);
     };
     auto dma_a = [&](uint32_t buf_off, uint32_t koff) {
 #pragma unroll
         for (int j = 0; j < S::kDmaPerWave; ++j)
             lds_dma16(rA, lds + buf_off + (j * S::kWaves + wave) * 1024, dma_voff[j], koff);
     };
+    auto kofs = [&](int t) {   // first K byte of tile t, clamped to the last tile
+        return kbase + (uint32_t)(t < ntiles ? t : ntiles - 1) * KT;
+    };
 
-    // Prologue: A and B of k-tile 0 (A first: the wait below relies on it).
-    dma_a(0, kbase);
+    // Prologue: A and B of tiles 0..DEPTH-1, in the exact order the loop body
+    // issues them (A copy, then B chunk by chunk), so the compiler's load
+    // counters agree on the loop-entry and back-edge paths.
+    auto prologue_tile = [&](auto setc) {
+        constexpr int D = decltype(setc)::value;
+        dma_a((uint32_t)D * S::kBufBytes, kofs(D));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ch = 0; ch < S::kCH; ++ch)
-        load_b(ch, kbase);
+        for (int ch = 0; ch < S::kCH; ++ch) {
+            load_b(setc, ch, kofs(D));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    prologue_tile(std::integral_constant<int, 0>{});
+    if constexpr (DEPTH > 1)
+        prologue_tile(std::integral_constant<int, (DEPTH > 1 ? 1 : 0)>{});
+    if constexpr (DEPTH > 2)
+        prologue_tile(std::integral_constant<int, (DEPTH > 2 ? 2 : 0)>{});
+    if constexpr (DEPTH > 3)
+        prologue_tile(std::integral_constant<int, (DEPTH > 3 ? 3 : 0)>{});
+    static_assert(DEPTH <= 4, "prologue and loop unrolled for DEPTH <= 4");
 
-    for (int t = 0; t < ntiles; ++t) {
-        const uint32_t cur = (uint32_t)(t & 1) * S::kBufBytes;
-        // This wave's A copy of tile t has landed once at most kBLoads loads
-        // (the B loads issued after it) are outstanding, and every earlier
-        // LDS read has completed; the barrier then certifies both for all
-        // waves, so tile t is readable and the other buffer is free.
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(S::kBLoads) : "memory");
-        // Prefetch tile t+1 (clamped: the last step repeats the last tile so
-        // that every step issues the same loads and the counts stay exact).
-        const uint32_t knext = kbase + (uint32_t)(t + 1 < ntiles ? t + 1 : ntiles - 1) * KT;
-        dma_a(cur ^ (uint32_t)S::kBufBytes, knext);
+    // Loads issued after the A copy of tile t, when step t begins: the B
+    // loads of tile t, then DEPTH-1 more tiles of A copies and B loads.
+    constexpr int kAfter = S::kBLoads + (DEPTH - 1) * (S::kDmaPerWave + S::kBLoads);
+    static_assert(kAfter <= 63, "vmcnt field is 6 bits");
+
+    uint32_t cur = 0;                                   // LDS offset of tile t
+    uint32_t nxt = (uint32_t)DEPTH * S::kBufBytes;      // LDS offset of tile t+DEPTH
+    auto step = [&](auto setc, int t) {
+        // This wave's A copy of tile t has landed once at most kAfter loads are
+        // outstanding, and every earlier LDS read has completed; the barrier
+        // certifies both for all waves, so tile t is readable and the buffer
+        // of tile t-1 is free for tile t+DEPTH.
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAfter) : "memory");
+        const uint32_t knext = kofs(t + DEPTH);
+        dma_a(nxt, knext);
 
         const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+        constexpr int SET = decltype(setc)::value;
+        // A fragments in MFMA order: fragment f = (step f / kMT, row tile f % kMT).
+        constexpr int kFr = S::kSteps * S::kMT;
+        auto frag_at = [&](int f) {
+            return lds_frag<DT>(abase + ((f % S::kMT) * S::kCH + (f / S::kMT) * S::kStepCh) * 1024);
+        };
 #pragma unroll
-        for (int st = 0; st < S::kSteps; ++st) {
+        for (int f = 0; f < kFr; ++f) {
+            const int st = f / S::kMT, mt = f % S::kMT;
+            const Frag a = frag_at(f);
 #pragma unroll
-            for (int mt = 0; mt < S::kMT; ++mt) {
-                const Frag a = lds_frag<DT>(abase + (mt * S::kCH + st * S::kStepCh) * 1024);
-#pragma unroll
-                for (int nt = 0; nt < S::kNT; ++nt) {
-                    Frag b;
-                    if constexpr (DT == kDtypeBf16)
-                        b = breg[nt][st];
-                    else
-                        b = cat(breg[nt][2 * st], breg[nt][2 * st + 1]);
-                    acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
-                }
+            for (int nt = 0; nt < S::kNT; ++nt) {
+                Frag b;
+                if constexpr (DT == kDtypeBf16)
+                    b = breg[SET][nt][st];
+                else
+                    b = cat(breg[SET][nt][2 * st], breg[SET][nt][2 * st + 1]);
+                acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
             }
+            if (mt == S::kMT - 1) {
 #pragma unroll
-            for (int cc = 0; cc < S::kStepCh; ++cc)
-                load_b(st * S::kStepCh + cc, knext);
-            if constexpr (PV > 0 || PD > 0) {
-                // Interleave, per MFMA, PD LDS reads and PV global loads.
-#pragma unroll
-                for (int i = 0; i < S::kMT * S::kNT; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if constexpr (PD > 0)
-                        __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
-                    if constexpr (PV > 0)
-                        __builtin_amdgcn_sched_group_barrier(0x020, PV, 0);
-                }
+                for (int cc = 0; cc < S::kStepCh; ++cc)
+                    load_b(setc, st * S::kStepCh + cc, knext);
             }
         }
+        if constexpr (PD > 0) {
+            // Software-pipeline the A fragments: the LDS reads of PD fragments
+            // first, then for every fragment its MFMAs followed by the reads of
+            // the fragment PD places ahead -- each read gets PD fragments'
+            // worth of MFMAs to land.  With PV > 0, one global load (B reload
+            // or A copy) is placed after every PV MFMAs.
+            constexpr int kRA = PD < kFr ? PD : kFr;
+            constexpr int kRd = S::kStepCh;   // LDS reads per fragment
+            __builtin_amdgcn_sched_group_barrier(0x100, kRA * kRd, 0);
+#pragma unroll
+            for (int f = 0; f < kFr; ++f) {
+                if constexpr (PV > 0) {
+                    static_assert(PV <= S::kNT && S::kNT % PV == 0, "PV must divide the MFMAs per fragment");
+#pragma unroll
+                    for (int m = 0; m < S::kNT / PV; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, PV, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
+                }
+                if (f + kRA < kFr)
+                    __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+            }
+        }
+        cur = cur + S::kBufBytes == kRing * S::kBufBytes ? 0 : cur + S::kBufBytes;
+        nxt = nxt + S::kBufBytes == kRing * S::kBufBytes ? 0 : nxt + S::kBufBytes;
+    };
+
+    // Main loop, unrolled by DEPTH so that the B register set of every step is
+    // a compile-time index; the remaining ntiles % DEPTH steps follow.
+    int t = 0;
+    for (; t + DEPTH <= ntiles; t += DEPTH) {
+        step(std::integral_constant<int, 0>{}, t);
+        if constexpr (DEPTH > 1)
+            step(std::integral_constant<int, (DEPTH > 1 ? 1 : 0)>{}, t + 1);
+        if constexpr (DEPTH > 2)
+            step(std::integral_constant<int, (DEPTH > 2 ? 2 : 0)>{}, t + 2);
+        if constexpr (DEPTH > 3)
+            step(std::integral_constant<int, (DEPTH > 3 ? 3 : 0)>{}, t + 3);
     }
+    if constexpr (DEPTH > 1)
+        if (t < ntiles)
+            step(std::integral_constant<int, 0>{}, t++);
+    if constexpr (DEPTH > 2)
+        if (t < ntiles)
+            step(std::integral_constant<int, (DEPTH > 2 ? 1 : 0)>{}, t++);
+    if constexpr (DEPTH > 3)
+        if (t < ntiles)
+            step(std::integral_constant<int, (DEPTH > 3 ? 2 : 0)>{}, t++);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: scale once, round once.
@@ -432,10 +504,10 @@ gemm_stream_kernel(const GemmArgs p, int panel)
 
 // ============================================================ registry
 
-template <int DT, int TM, int TN, int WM, int WN, int KT, int SCALE, int OUT, int PV, int PD>
+template <int DT, int TM, int TN, int WM, int WN, int KT, int DEPTH, int SCALE, int OUT, int PV, int PD>
 void launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    gemm_tiled_kernel<DT, TM, TN, WM, WN, KT, SCALE, OUT, PV, PD><<<grid, WM * WN * 64, 0, s>>>(a);
+    gemm_tiled_kernel<DT, TM, TN, WM, WN, KT, DEPTH, SCALE, OUT, PV, PD><<<grid, WM * WN * 64, 0, s>>>(a);
 }
 
 template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
@@ -461,30 +533,32 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
 }
 
-#define DGP_TILED(DT, TM, TN, WM, WN, KT, SC, OUT, PV, PD)                                   \
-    {kTiled, DT, SC, OUT, TM, TN, KT, WM * WN, WM, WN, PV, PD,                                \
-     &launch_tiled<DT, TM, TN, WM, WN, KT, SC, OUT, PV, PD>}
+#define DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, OUT, PV, PD)                            \
+    {kTiled, DT, SC, OUT, TM, TN, KT, WM * WN, WM, WN, PV, PD, DEPTH,                         \
+     &launch_tiled<DT, TM, TN, WM, WN, KT, DEPTH, SC, OUT, PV, PD>}
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
-    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0,           \
+    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH,    \
      &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
 
-#define DGP_TILED_BOTH_OUT(DT, TM, TN, WM, WN, KT, SC, PV, PD)                                \
-    DGP_TILED(DT, TM, TN, WM, WN, KT, SC, kOutBf16, PV, PD),                                  \
-        DGP_TILED(DT, TM, TN, WM, WN, KT, SC, kOutPartial, PV, PD)
+#define DGP_TILED_BOTH_OUT(DT, TM, TN, WM, WN, KT, DEPTH, SC, PV, PD)                         \
+    DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutBf16, PV, PD),                           \
+        DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutPartial, PV, PD)
 #define DGP_STREAM_BOTH_OUT(DT, NW, SPW, DEPTH, SC)                                           \
     DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutBf16), DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutPartial)
 
 static const KernelSpec kKernels[] = {
-    // large tiles, bf16: 8 waves (2 per SIMD) of 128x64 or 64x128, or 4 waves of 64x128 / 64x64
-    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, 128, kScaleNone, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 4, 2, 128, kScaleNone, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 256, 2, 2, 128, kScaleNone, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 128, 2, 2, 128, kScaleNone, 0, 0),
+    // large tiles, bf16 (tm, tn, waves m x n, k-tile bytes, prefetch depth, scale, preload pair)
+    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 1, 8, 128, 2, kScaleNone, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 1, 8, 128, 2, kScaleNone, 0, 0),
+    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, 128, 2, kScaleNone, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 256, 1, 4, 128, 2, kScaleNone, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 128, 2, 2, 128, 2, kScaleNone, 0, 4),
     // large tiles, fp8 per-tensor
-    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, kScaleTensor, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 4, 2, 128, kScaleTensor, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 2, 2, 128, kScaleTensor, 0, 0),
-    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, kScaleTensor, 0, 0),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleTensor, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleTensor, 0, 0),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, 2, kScaleTensor, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 1, 4, 128, 2, kScaleTensor, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleTensor, 0, 4),
     // streaming (decode-sized M)
     DGP_STREAM_BOTH_OUT(kDtypeBf16, 4, 1, 16, kScaleNone),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleTensor),

@@ -38,6 +38,7 @@ struct KernelSpec {
     int waves;      // waves per workgroup
     int p0, p1;     // family-specific: tiled = (wm, wn); stream = (strips per wave, depth)
     int pv, pd;     // scheduling hint pair (tiled)
+    int depth;      // prefetch distance: k-tiles (tiled) / steps (stream)
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
 };
 

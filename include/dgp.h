@@ -75,10 +75,18 @@ typedef enum dgp_scale_mode {
  *   xcd_remap      : 1 = map workgroup ids so neighbouring tiles share an XCD's
  *                    L2 (output is bit-identical either way), 0 = plain raster
  *   group_m        : tile rows per raster group when xcd_remap = 1 (>= 1)
- *   preload        : scheduling hint pair -- the number of global loads and of
- *                    LDS reads placed between matrix-core instructions; each
- *                    >= 0 ([P1] "Changes" item 3 and its review: a pair of
- *                    non-negative integers, rejected otherwise).  0,0 = none. */
+ *   preload        : scheduling hint pair ([P1] "Changes" item 3 and its
+ *                    review: a pair of non-negative integers, rejected
+ *                    otherwise).  preload_dsrd = A fragments read from LDS
+ *                    ahead of the matrix-core instructions that consume them;
+ *                    preload_vmem = matrix-core instructions between two global
+ *                    loads (0: loads placed by the compiler).  (0, 0) selects
+ *                    the tile's tuned default; any other pair must name a
+ *                    compiled kernel.
+ *   waves_m        : waves along M inside the workgroup (0 = any compiled
+ *                    layout for this tile).
+ *   prefetch       : k-tiles loaded ahead of the one being multiplied (0 = any
+ *                    compiled depth for this tile). */
 typedef struct dgp_config {
     int tile_m;
     int tile_n;
@@ -87,6 +95,8 @@ typedef struct dgp_config {
     int group_m;
     int preload_vmem;
     int preload_dsrd;
+    int waves_m;
+    int prefetch;
 } dgp_config;
 
 /*

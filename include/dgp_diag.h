@@ -35,6 +35,17 @@ dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, i
                                  int xcd_remap, int group_m, int64_t out[3]);
 
 /*
+ * dgp_kernel_info -- describe compiled GEMM kernel number `index`
+ * (0 <= index < dgp_kernel_count()).  Fills *cfg with the configuration that
+ * selects exactly this kernel through dgp_gemm_preshuffle[_splitk] (xcd_remap
+ * and group_m set to the defaults), and *dtype, *scale_mode with the element
+ * type and scale mode it computes; *split_out = 1 if it is the fp32-partial
+ * (split_k > 1) variant, 0 if it writes bf16 C directly.  Pure host function.
+ */
+int dgp_kernel_count(void);
+dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mode, int *split_out);
+
+/*
  * dgp_probe_mfma_layout -- run each matrix-core instruction the GEMM uses once
  * on operands the caller supplies and store the raw accumulator registers.
  *   which = 0: v_mfma_f32_16x16x32_bf16   (a, b: 64 lanes x 16 bytes)

@@ -17,7 +17,7 @@ from gpu_common import (DEV, assert_close, dev_codes, dev_f32, dmode, host_bits,
 
 pytestmark = pytest.mark.gpu
 
-TILED = [(256, 256), (128, 256), (128, 128)]
+TILED = [(256, 256, 1, 8), (256, 256, 2, 8), (128, 256, 1, 8), (128, 128, 2, 4)]
 
 
 def rand_inputs(dtype, mode, M, N, K, seed):
@@ -77,21 +77,39 @@ def test_exact_integers_bit_exact(dtype, mode, M, N, K):
     assert np.array_equal(got, c16)
 
 
-@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor")])
-@pytest.mark.parametrize("tile", TILED)
-@pytest.mark.parametrize("split_k", [1, 2])
-def test_every_tiled_config(dtype, mode, tile, split_k):
-    M, N = 2 * tile[0] + 44, 2 * tile[1] + 48   # ragged in both dimensions
-    K = 1024 if dtype == "fp8" else 512
-    cfg = dgp.Config(tile[0], tile[1], 128, 1, 4, 0, 0)
-    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 5)
-    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
-    _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
-    assert np.array_equal(got, c16)
-    A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 6)
-    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
-    c32, _ = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
-    assert_close(got, c32)
+def test_every_compiled_kernel():
+    """Each kernel of the compiled table, selected exactly through its config,
+    on inputs ragged in M and N: exact integers bit-exact, random data within
+    tolerance.  Split-output kernels run with split_k = 2."""
+    names = {0: "none", 1: "tensor", 2: "block128"}
+    for cfg, dt, sm, split_out in dgp.kernels():
+        dtype = "bf16" if dt == dgp.BF16 else "fp8"
+        mode = names[sm]
+        if cfg.tile_m == 16:
+            M, N = 37, 384
+        else:
+            M, N = 2 * cfg.tile_m + 44, 2 * cfg.tile_n + 128
+        K = 1024 if dtype == "fp8" else 512
+        split = 2 if split_out else 1
+        what = f"{dtype} {mode} tile {cfg.tile_m}x{cfg.tile_n}x{cfg.tile_k} wm{cfg.waves_m} d{cfg.prefetch} s{split}"
+        A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 5)
+        got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
+        _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
+        assert np.array_equal(got, c16), what
+        A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 6)
+        got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
+        c32, _ = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
+        assert_close(got, c32, what=what)
+
+
+def test_k_tile_counts_not_multiple_of_prefetch_depth():
+    """ntiles % depth != 0 exercises the steps after the unrolled main loop."""
+    for k in (128, 384, 640, 896):     # 1, 3, 5, 7 fp8 k-tiles of 128 bytes
+        for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dgp.FP8_E4M3 and not so]:
+            A, B, sA, sB = exact_inputs("fp8", "tensor", 300, 528, k, 13)
+            got = run_gpu(A, B, "fp8", "tensor", sA, sB, config=cfg)
+            _, c16 = run_oracle(A, B, "fp8", "tensor", sA, sB)
+            assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch)
 
 
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
@@ -142,7 +160,7 @@ def test_identity_b_returns_a():
     A = synth.bf16_uniform((M, K), 3)
     B = np.zeros((K, K), np.uint16)
     B[np.arange(K), np.arange(K)] = 0x3F80
-    for cfg in (None, dgp.Config(256, 256, 128, 1, 4, 0, 0)):
+    for cfg in (None, dgp.Config(256, 256, 128, 1, 8, 0, 8, 1, 2), dgp.Config(256, 256, 128, 1, 8, 0, 8, 2, 2)):
         got = run_gpu(A, B, "bf16", "none", config=cfg) if cfg else run_gpu(A, B, "bf16", "none")
         assert np.array_equal(got, A)
 
@@ -153,7 +171,8 @@ def test_xcd_remap_is_bit_identical(tile):
     A, B, _, _ = rand_inputs("bf16", "none", M, N, K, 8)
     outs = []
     for remap, group in ((0, 1), (1, 1), (1, 4), (1, 8)):
-        outs.append(run_gpu(A, B, "bf16", "none", config=dgp.Config(tile[0], tile[1], 128, remap, group, 0, 0)))
+        outs.append(run_gpu(A, B, "bf16", "none",
+                            config=dgp.Config(tile[0], tile[1], 128, remap, group, 0, tile[3], tile[2], 2)))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
 

@@ -46,7 +46,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol(dgp, L):
     names = declared_symbols()
-    assert len(names) >= 13
+    assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
     assert set(dgp.EXPORTS) == names
@@ -171,6 +171,27 @@ def test_tile_map_remap_groups_xcd_neighbours(dgp):
     assert {t[0] for t in tiles} == {0, 1, 2, 3} and {t[1] for t in tiles} == set(range(8))
     # without remap the same ids are a plain raster
     assert dgp.tile_of_workgroup(17, 16, 16, 1, 0, 4) == (1, 1, 0)
+
+
+def test_kernel_table(dgp, L):
+    ks = dgp.kernels()
+    assert len(ks) == L.dgp_kernel_count() > 0
+    seen = set()
+    for cfg, dt, sm, split_out in ks:
+        key = (cfg.tile_m, cfg.tile_n, cfg.tile_k, cfg.waves_m, cfg.prefetch, cfg.preload_vmem,
+               cfg.preload_dsrd, dt, sm, split_out)
+        assert key not in seen
+        seen.add(key)
+        assert (dt, sm) in ((0, 0), (1, 1), (1, 2))
+        if cfg.tile_m > 16:
+            # the A-tile granularity rule: whole 16-byte loads per thread
+            assert (cfg.tile_m * cfg.tile_k) % 1024 == 0 and cfg.prefetch >= 1
+    with pytest.raises(dgp.DgpError):
+        import ctypes
+        c = dgp.Config()
+        i = ctypes.c_int()
+        dgp._check(L.dgp_kernel_info(len(ks), ctypes.byref(c), ctypes.byref(i), ctypes.byref(i),
+                                     ctypes.byref(i)))
 
 
 def test_tile_map_rejects_bad_arguments(dgp):
