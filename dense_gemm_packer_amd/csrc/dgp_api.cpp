@@ -101,8 +101,9 @@ const KernelSpec *find_spec(const Query &q)
     const KernelSpec *t = kernel_table(&n);
     for (int i = 0; i < n; ++i) {
         const KernelSpec &k = t[i];
+        const int wm = k.family == kTiled ? k.p0 : k.waves;
         if (k.family == q.family && k.dtype == q.dtype && k.scale == q.scale && k.out == q.out && k.tm == q.tm &&
-            k.tn == q.tn && (q.kt < 0 || k.kt == q.kt) && (q.wm < 0 || k.p0 == q.wm) &&
+            k.tn == q.tn && (q.kt < 0 || k.kt == q.kt) && (q.wm < 0 || wm == q.wm) &&
             (q.depth < 0 || k.depth == q.depth) && (q.pv < 0 || k.pv == q.pv) && (q.pd < 0 || k.pd == q.pd))
             return &k;
     }
@@ -235,8 +236,11 @@ dgp_status validate(const GemmCall &c, Plan *plan)
                 q.pv = c.cfg->preload_vmem;
                 q.pd = c.cfg->preload_dsrd;
             }
-        } else if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0) {
-            return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
+        } else {
+            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0)
+                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
+            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;   // matched against waves per workgroup
+            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
         }
         spec = find_spec(q);
         if (!spec)
@@ -447,8 +451,8 @@ dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mo
     cfg->group_m = 8;
     cfg->preload_vmem = k.pv;
     cfg->preload_dsrd = k.pd;
-    cfg->waves_m = k.family == kTiled ? k.p0 : 0;
-    cfg->prefetch = k.family == kTiled ? k.depth : 0;
+    cfg->waves_m = k.family == kTiled ? k.p0 : k.waves;
+    cfg->prefetch = k.depth;
     *dtype = k.dtype;
     *scale_mode = k.scale;
     *split_out = k.out == kOutPartial ? 1 : 0;

@@ -164,6 +164,10 @@ gemm_tiled_kernel(const GemmArgs p)
 
     // A: rows m0.. of A; rows >= M are past num_records and load as zero.
     const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    // Where the copy puts each lane's 16 bytes: instruction j of this wave
+    // fills LDS block blk = j*waves + wave = (row group rg, 64-byte chunk ch),
+    // lane l landing at byte 16*l with row 16*rg + l%16, K-bytes
+    // 64*ch + 16*(l/16) -- the lane's global address selects the bytes.
     uint32_t dma_voff[S::kDmaPerWave];
 #pragma unroll
     for (int j = 0; j < S::kDmaPerWave; ++j) {
@@ -559,9 +563,10 @@ static const KernelSpec kKernels[] = {
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 1, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleTensor, 0, 4),
-    // streaming (decode-sized M)
+    // streaming (decode-sized M): waves per workgroup, strips per wave, ring depth
     DGP_STREAM_BOTH_OUT(kDtypeBf16, 4, 1, 16, kScaleNone),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleTensor),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 2, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
 };
 

@@ -44,21 +44,26 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const i32x4 *__restrict
         dst[i] = src[i];
 }
 
-__global__ __launch_bounds__(256) void probe_stream_read_kernel(const i32x4 *__restrict__ src, int64_t n16,
-                                                                uint32_t *__restrict__ sink)
+constexpr int kStreamThreads = 512;
+constexpr int kStreamUnroll = 8;   // 16-byte loads in flight per thread
+
+// Streaming read: round i of workgroup b covers the 64 KiB chunk i*grid + b;
+// thread t reads bytes chunk + u*8192 + 16*t for u < 8 (8 loads in flight per
+// thread, 64 KiB per workgroup), non-temporal.
+__global__ __launch_bounds__(kStreamThreads) void probe_stream_read_kernel(const uint8_t *__restrict__ src,
+                                                                           int64_t bytes, uint32_t *__restrict__ sink)
 {
-    // Grid-stride 16-byte non-temporal loads, four in flight per thread.
-    const int64_t stride = (int64_t)gridDim.x * 256;
+    constexpr int64_t kChunk = (int64_t)kStreamThreads * 16 * kStreamUnroll;
+    const int64_t chunks = bytes / kChunk;
     i32x4 x = {0, 0, 0, 0};
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += 4 * stride) {
-        i32x4 v[4];
+    for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+        const auto r = make_rsrc(src + c * kChunk, (uint32_t)kChunk);
+        i32x4 v[kStreamUnroll];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = i + u * stride;
-            v[u] = j < n16 ? __builtin_nontemporal_load(src + j) : i32x4{0, 0, 0, 0};
-        }
+        for (int u = 0; u < kStreamUnroll; ++u)
+            v[u] = load16<kAuxNonTemporal>(r, (uint32_t)(u * kStreamThreads * 16 + threadIdx.x * 16));
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kStreamUnroll; ++u)
             x ^= v[u];
     }
     const uint32_t f = (uint32_t)(x.x ^ x.y ^ x.z ^ x.w);
@@ -92,13 +97,12 @@ hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStrea
 
 hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s)
 {
-    const int64_t n16 = bytes / 16;
-    if (n16 == 0)
+    // Whole 64 KiB chunks are read; the tail (bytes % 64 KiB) is not.
+    const int64_t chunks = bytes / ((int64_t)kStreamThreads * 16 * kStreamUnroll);
+    if (chunks == 0)
         return hipSuccess;
-    int64_t blocks = (n16 + 1023) / 1024;
-    if (blocks > 4096)
-        blocks = 4096;
-    probe_stream_read_kernel<<<(unsigned)blocks, 256, 0, s>>>((const i32x4 *)src, n16, sink);
+    const int64_t blocks = chunks < 1024 ? chunks : 1024;
+    probe_stream_read_kernel<<<(unsigned)blocks, kStreamThreads, 0, s>>>((const uint8_t *)src, bytes, sink);
     return hipGetLastError();
 }
 

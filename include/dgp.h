@@ -83,10 +83,13 @@ typedef enum dgp_scale_mode {
  *                    loads (0: loads placed by the compiler).  (0, 0) selects
  *                    the tile's tuned default; any other pair must name a
  *                    compiled kernel.
- *   waves_m        : waves along M inside the workgroup (0 = any compiled
- *                    layout for this tile).
- *   prefetch       : k-tiles loaded ahead of the one being multiplied (0 = any
- *                    compiled depth for this tile). */
+ *   waves_m        : tiled kernels: waves along M inside the workgroup; the
+ *                    16-row streaming kernel (tile_m = 16): waves per
+ *                    workgroup, each owning tile_n / (16 * waves) strips
+ *                    (0 = any compiled layout for this tile).
+ *   prefetch       : tiled kernels: k-tiles loaded ahead of the one being
+ *                    multiplied; streaming kernel: MFMA steps of loads in
+ *                    flight per wave (0 = any compiled depth for this tile). */
 typedef struct dgp_config {
     int tile_m;
     int tile_n;
