@@ -164,6 +164,9 @@ def main():
     secondary = {}
     if not args.no_secondary:
         secondary = run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs, A, C, M, N, K)
+        wall = secondary["mfma_wall_bf16"]["workload_data"]
+        roofline["measured_wall"] = wall
+        roofline["frac_measured_wall"] = round(achieved / wall, 4)
 
     line = {
         "metric": METRIC,
@@ -231,6 +234,32 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["hbm_stream_read_1GiB"] = {"us": round(us, 1), "GB/s": round(wall_gbs, 1)}
     del buf
 
+    # MFMA walls: a register-only matrix-core loop (512 workgroups x 4 waves,
+    # two waves per SIMD like the GEMM) timed like the GEMMs.  On the
+    # workload's own operand bytes it gives the rate the chip sustains at the
+    # clock it holds for that data; constant operands (1.0) give the rate near
+    # the spec clock.
+    def mfma_wall(which, data_bytes):
+        rounds = 1024 if which == 0 else 512
+        need = dgp.MFMA_PEAK_OPERAND_BYTES[which]
+        res = {}
+        for kind in ("workload_data", "constant_1.0"):
+            if kind == "workload_data":
+                ops = data_bytes[:need].clone()
+            else:
+                ops = torch.empty(need, dtype=torch.uint8, device=dev)
+                if which == 0:
+                    ops.view(torch.int16).fill_(0x3F80)
+                else:
+                    ops.fill_(0x38)
+            flop = dgp.MFMA_PEAK_FLOP[which] * 512 * 4 * rounds * 64
+            us = graph_time_us(torch, lambda i: dgp.probe_mfma_peak(which, rounds, 512, ops, sink), 8)
+            res[kind] = round(flop / (us * 1e-6) / 1e12, 1)
+        return res
+
+    out["mfma_wall_bf16"] = mfma_wall(0, A_bf16.view(torch.uint8).reshape(-1))
+    out["mfma_wall_bf16"]["frac_of_peak"] = round(out["mfma_wall_bf16"]["workload_data"] / PEAK_BF16_TFLOPS, 4)
+
     # fp8 per-tensor GEMM, M=N=4096, K=8192.
     w = synth.workload_inputs("fp8_large")
     A8 = to_dev(w["A"], "fp8")
@@ -238,10 +267,13 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     sA = torch.from_numpy(w["sA"]).to(dev)
     sB = torch.from_numpy(w["sB"]).to(dev)
     C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    out["mfma_wall_fp8"] = mfma_wall(1, A8.view(torch.uint8).reshape(-1))
+    out["mfma_wall_fp8"]["frac_of_peak"] = round(out["mfma_wall_fp8"]["workload_data"] / PEAK_FP8_TFLOPS, 4)
     us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, out=C8), 10)
     tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
     out["fp8_gemm_4096x4096x8192"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
-                                      "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+                                      "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                                      "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4)}
     del A8, Bs8, C8
 
     # fp8 split-K decode (per-tensor) and blockscale decode, cold cache.

@@ -49,7 +49,7 @@ class Config(ctypes.Structure):
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
            "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
-           "dgp_probe_stream_read")
+           "dgp_probe_stream_read", "dgp_probe_mfma_peak")
 
 _lib = None
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
         "dgp_probe_stream_read": [_vp, _i64, _vp, _vp],
+        "dgp_probe_mfma_peak": [_int, _int, _int, _vp, _vp, _vp],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -256,3 +257,19 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
 def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     _check(lib().dgp_probe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream_handle(stream)))
+
+
+# FLOP per matrix-core instruction of dgp_probe_mfma_peak (which = 0, 1), and
+# the operand buffer it reads (256 sets x 16 fragments x 64 lanes x 16|32 B).
+MFMA_PEAK_FLOP = (16384, 65536)
+MFMA_PEAK_OPERAND_BYTES = (256 * 16 * 64 * 16, 256 * 16 * 64 * 32)
+
+
+def probe_mfma_peak(which: int, rounds: int, blocks: int, operands: torch.Tensor, sink: torch.Tensor,
+                    stream=None) -> int:
+    """Launch the register-only MFMA loop on `operands`; returns the FLOP it performs."""
+    _dev(operands, "operands")
+    if operands.numel() * operands.element_size() < MFMA_PEAK_OPERAND_BYTES[which]:
+        raise ValueError(f"operands must hold {MFMA_PEAK_OPERAND_BYTES[which]} bytes")
+    _check(lib().dgp_probe_mfma_peak(which, rounds, blocks, _ptr(operands), _ptr(sink), _stream_handle(stream)))
+    return blocks * 4 * rounds * 64 * MFMA_PEAK_FLOP[which]

@@ -517,4 +517,21 @@ dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink,
     return hip_status(launch_probe_stream_read(src, bytes, sink, (hipStream_t)stream), "probe launch");
 }
 
+dgp_status dgp_probe_mfma_peak(int which, int rounds, int blocks, const void *operands, uint32_t *sink,
+                               void *stream)
+{
+    if (which != 0 && which != 1)
+        return fail(DGP_ERR_CONFIG, "which must be 0 or 1");
+    if (rounds < 1 || rounds > (1 << 24) || blocks < 1 || blocks > 65536)
+        return fail(DGP_ERR_SHAPE, "rounds must be in [1, 2^24] and blocks in [1, 65536]");
+    if (!operands || !sink)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(operands))
+        return fail(DGP_ERR_ALIGN, "operands must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_mfma_peak(which, rounds, blocks, operands, sink, (hipStream_t)stream), "probe launch");
+}
+
 }  // extern "C"

@@ -55,5 +55,7 @@ hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out
 hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
 hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void *ops, uint32_t *sink,
+                                  hipStream_t s);
 
 }  // namespace dgp

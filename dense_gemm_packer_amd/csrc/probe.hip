@@ -1,7 +1,10 @@
 // Probe kernels: check the hardware facts the GEMM relies on (matrix-core
 // register layouts, where the async global->LDS copy puts each lane's bytes)
 // and measure the walls the GEMM is judged against (a plain copy of known
-// traffic for counter calibration, a streaming read for the HBM wall).
+// traffic for counter calibration, a streaming read for the HBM wall, a
+// register-only matrix-core loop for the sustained MFMA rate).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -71,6 +74,59 @@ __global__ __launch_bounds__(kStreamThreads) void probe_stream_read_kernel(const
         sink[blockIdx.x & 4095] = f;
 }
 
+constexpr int kPeakThreads = 256;   // 4 waves per workgroup
+constexpr int kPeakSets = 256;      // operand sets in the caller's buffer
+
+// Sustained matrix-core rate on given operands: each wave loads 8 A and 8 B
+// fragments (operand set wave % kPeakSets of the caller's buffer) into
+// registers, then issues rounds x 64 MFMAs over 8 independent accumulators,
+// pairing every B fragment with every A fragment in turn, with no memory
+// traffic in the loop.  The matrix units draw more power on operands that
+// toggle, so the rate depends on the data: random operands hold a lower
+// clock than constant ones.  which = 0: v_mfma_f32_16x16x32_bf16,
+// 1: the e4m3 16x16x128 form.
+template <int WHICH>
+__global__ __launch_bounds__(kPeakThreads) void probe_mfma_peak_kernel(int rounds, const uint8_t *__restrict__ ops,
+                                                                       uint32_t *sink)
+{
+    constexpr int kFB = WHICH == 0 ? 16 : 32;   // bytes per lane per fragment
+    using F = typename std::conditional<WHICH == 0, i32x4, i32x8>::type;
+    const int l = threadIdx.x & 63;
+    const int set = (int)((blockIdx.x * (kPeakThreads / 64) + (threadIdx.x >> 6)) % kPeakSets);
+    const uint8_t *base = ops + (size_t)set * 16 * 64 * kFB + l * kFB;
+    F af[8], bf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        af[j] = *reinterpret_cast<const F *>(base + j * 64 * kFB);
+        bf[j] = *reinterpret_cast<const F *>(base + (8 + j) * 64 * kFB);
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (WHICH == 0)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf[j]),
+                                                                     __builtin_bit_cast(bf16x8, af[(j + s) & 7]),
+                                                                     acc[j], 0, 0, 0);
+                else
+                    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[(j + s) & 7], acc[j],
+                                                                              0, 0, 0, 0, 0, 0);
+            }
+        }
+    }
+    float f = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        f += acc[j].x + acc[j].y + acc[j].z + acc[j].w;
+    if (f == 1.2345e-7f)   // practically never true; keeps the products alive
+        sink[blockIdx.x & 4095] = (uint32_t)l;
+}
+
 hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s)
 {
     probe_mfma_kernel<<<1, 64, 0, s>>>(which, (const uint8_t *)a, (const uint8_t *)b, out);
@@ -92,6 +148,16 @@ hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStrea
     if (blocks > 65536)
         blocks = 65536;
     probe_copy_kernel<<<(unsigned)blocks, 256, 0, s>>>((const i32x4 *)src, (i32x4 *)dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void *ops, uint32_t *sink,
+                                  hipStream_t s)
+{
+    if (which == 0)
+        probe_mfma_peak_kernel<0><<<blocks, kPeakThreads, 0, s>>>(rounds, (const uint8_t *)ops, sink);
+    else
+        probe_mfma_peak_kernel<1><<<blocks, kPeakThreads, 0, s>>>(rounds, (const uint8_t *)ops, sink);
     return hipGetLastError();
 }
 

@@ -71,3 +71,17 @@ def test_probe_copy_copies():
     dgp.probe_copy(x, y)
     torch.cuda.synchronize()
     assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_probe_mfma_peak_runs_and_leaves_sink(which):
+    # The register-only loop touches memory only on a practically impossible
+    # value, so the sink stays as written; the FLOP count is the documented one.
+    ops = torch.randint(0, 255, (dgp.MFMA_PEAK_OPERAND_BYTES[which],), dtype=torch.uint8, device=DEV)
+    ops[ops == 0x7F] = 0   # no e4m3 NaN codes
+    ops[ops == 0xFF] = 0
+    sink = torch.full((4096,), 7, dtype=torch.int32, device=DEV)
+    flop = dgp.probe_mfma_peak(which, 16, 8, ops, sink)
+    torch.cuda.synchronize()
+    assert flop == 8 * 4 * 16 * 64 * (16384 if which == 0 else 65536)
+    assert bool((sink == 7).all())

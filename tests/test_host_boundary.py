@@ -151,6 +151,13 @@ def test_probe_validation(L):
     assert L.dgp_probe_copy(P, P, 17, None) == SHAPE
     assert L.dgp_probe_copy(P, P, 0, None) == OK
     assert L.dgp_probe_stream_read(P, 4095, P, None) == SHAPE
+    assert L.dgp_probe_mfma_peak(2, 1, 1, P, P, None) == CONFIG
+    assert L.dgp_probe_mfma_peak(0, 0, 1, P, P, None) == SHAPE
+    assert L.dgp_probe_mfma_peak(1, 1, 0, P, P, None) == SHAPE
+    assert L.dgp_probe_mfma_peak(0, 1, 65537, P, P, None) == SHAPE
+    assert L.dgp_probe_mfma_peak(0, 1, 1, 0, P, None) == NULL
+    assert L.dgp_probe_mfma_peak(0, 1, 1, P, 0, None) == NULL
+    assert L.dgp_probe_mfma_peak(0, 1, 1, P + 8, P, None) == ALIGN
 
 
 @pytest.mark.parametrize("remap,group_m", [(0, 1), (1, 1), (1, 4), (1, 8)])
