@@ -38,17 +38,18 @@ class DgpError(RuntimeError):
 
 
 class Config(ctypes.Structure):
-    """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair, waves_m, prefetch."""
+    """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair, waves_m, prefetch, schedule."""
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("xcd_remap", ctypes.c_int), ("group_m", ctypes.c_int),
                 ("preload_vmem", ctypes.c_int), ("preload_dsrd", ctypes.c_int),
-                ("waves_m", ctypes.c_int), ("prefetch", ctypes.c_int)]
+                ("waves_m", ctypes.c_int), ("prefetch", ctypes.c_int), ("schedule", ctypes.c_int)]
 
 
 # Every symbol include/dgp.h and include/dgp_diag.h declare.
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
-           "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
+           "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
+           "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
            "dgp_probe_stream_read", "dgp_probe_mfma_peak")
 
 _lib = None
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "dgp_kernel_count": [],
         "dgp_kernel_info": [_int, ctypes.POINTER(Config), ctypes.POINTER(_int), ctypes.POINTER(_int),
                             ctypes.POINTER(_int)],
+        "dgp_select_kernel": [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(Config), ctypes.POINTER(_int)],
         "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
@@ -235,6 +237,30 @@ def kernels():
         _check(L.dgp_kernel_info(i, ctypes.byref(cfg), ctypes.byref(dt), ctypes.byref(sm), ctypes.byref(so)))
         out.append((cfg, dt.value, sm.value, so.value))
     return out
+
+
+def select_kernel(M: int, N: int, K: int, dtype: int, scale_mode: int, split_k: int = 1, config=None) -> int:
+    """Table index of the GEMM kernel such a call would launch (-1: none)."""
+    idx = ctypes.c_int()
+    cfg = None if config is None else (config if isinstance(config, Config) else Config(**config))
+    _check(lib().dgp_select_kernel(M, N, K, dtype, scale_mode, split_k,
+                                   None if cfg is None else ctypes.byref(cfg), ctypes.byref(idx)))
+    return idx.value
+
+
+def describe_kernel(index: int) -> str:
+    """One-line description of compiled kernel `index`."""
+    cfg, dt, sm, so = kernels()[index]
+    dts = "bf16" if dt == BF16 else "fp8"
+    if cfg.tile_m == 16:
+        return (f"gemm_stream_kernel<{dts}, 16x{cfg.tile_n} tile, {cfg.waves_m} waves, "
+                f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
+    sched = {1: f"interleaved, LDS read-ahead {cfg.preload_dsrd}", 2: "ping-pong",
+             3: f"A and B in LDS, LDS read-ahead {cfg.preload_dsrd}"}[cfg.schedule]
+    kname = {1: "tiled", 2: "pingpong", 3: "lds"}[cfg.schedule]
+    return (f"gemm_{kname}_kernel<{dts}, {cfg.tile_m}x{cfg.tile_n} tile, "
+            f"{cfg.tile_k}-byte k-tile, waves_m {cfg.waves_m}, prefetch {cfg.prefetch}, {sched}"
+            f"{', fp32 partials' if so else ''}>")
 
 
 def probe_mfma_layout(which: int, a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:

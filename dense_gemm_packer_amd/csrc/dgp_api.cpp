@@ -92,7 +92,7 @@ bool spec_fits(const KernelSpec &k, int64_t Ks)
 // A kernel-table query; -1 in a field means "any".
 struct Query {
     int family, dtype, scale, out, tm, tn;
-    int kt = -1, wm = -1, depth = -1, pv = -1, pd = -1;
+    int kt = -1, wm = -1, depth = -1, pv = -1, pd = -1, sched = -1;
 };
 
 const KernelSpec *find_spec(const Query &q)
@@ -104,7 +104,8 @@ const KernelSpec *find_spec(const Query &q)
         const int wm = k.family == kTiled ? k.p0 : k.waves;
         if (k.family == q.family && k.dtype == q.dtype && k.scale == q.scale && k.out == q.out && k.tm == q.tm &&
             k.tn == q.tn && (q.kt < 0 || k.kt == q.kt) && (q.wm < 0 || wm == q.wm) &&
-            (q.depth < 0 || k.depth == q.depth) && (q.pv < 0 || k.pv == q.pv) && (q.pd < 0 || k.pd == q.pd))
+            (q.depth < 0 || k.depth == q.depth) && (q.pv < 0 || k.pv == q.pv) && (q.pd < 0 || k.pd == q.pd) &&
+            (q.sched < 0 || k.sched == q.sched))
             return &k;
     }
     return nullptr;
@@ -141,7 +142,71 @@ struct GemmCall {
     float *ws;
     size_t ws_bytes;
     const dgp_config *cfg;
+    bool select_only = false;   // shapes and configuration only: no buffers checked
 };
+
+// Kernel choice for a validated call: the configured tile, or the built-in
+// per-shape table.
+dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
+{
+    const int out = c.split_k > 1 ? kOutPartial : kOutBf16;
+    const KernelSpec *spec = nullptr;
+    if (c.cfg && c.cfg->tile_m > 0) {
+        const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
+        if (c.cfg->waves_m < 0 || c.cfg->prefetch < 0)
+            return fail(DGP_ERR_CONFIG, "waves_m and prefetch must be >= 0");
+        if (c.cfg->schedule < 0 || c.cfg->schedule > kSchedBothLds)
+            return fail(DGP_ERR_CONFIG, "schedule must be 0, 1, 2 or 3 (got %d)", c.cfg->schedule);
+        Query q{fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n};
+        if (fam == kTiled) {
+            q.kt = c.cfg->tile_k;
+            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;
+            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
+            // (0, 0) = this tile's tuned default hints; any other pair must
+            // name a compiled kernel exactly.
+            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0) {
+                q.pv = c.cfg->preload_vmem;
+                q.pd = c.cfg->preload_dsrd;
+            }
+            if (c.cfg->schedule > 0)
+                q.sched = c.cfg->schedule;
+        } else {
+            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0)
+                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
+            if (c.cfg->schedule != 0)
+                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel has no schedule choice");
+            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;   // matched against waves per workgroup
+            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
+        }
+        spec = find_spec(q);
+        if (!spec)
+            return fail(DGP_ERR_CONFIG,
+                        "no compiled kernel for tile %dx%dx%d (waves_m %d, prefetch %d, preload %d,%d, schedule %d) "
+                        "with this dtype/scale", c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k, c.cfg->waves_m,
+                        c.cfg->prefetch, c.cfg->preload_vmem, c.cfg->preload_dsrd, c.cfg->schedule);
+        if (!spec_fits(*spec, Ks))
+            return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
+                        spec->kt, (long long)Ks);
+    } else {
+        spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks);
+        if (!spec)
+            return fail(DGP_ERR_CONFIG, "no compiled kernel fits this shape");
+    }
+    plan->spec = spec;
+    plan->tiles_m = (int)((c.M + spec->tm - 1) / spec->tm);
+    plan->tiles_n = (int)((c.N + spec->tn - 1) / spec->tn);
+    if (c.cfg && c.cfg->tile_m > 0) {
+        plan->remap = c.cfg->xcd_remap;
+        plan->group_m = c.cfg->group_m < 1 ? 1 : c.cfg->group_m;
+    } else {
+        plan->remap = spec->family == kTiled ? 1 : 0;
+        plan->group_m = 8;
+    }
+    const int64_t grid = (int64_t)plan->tiles_m * plan->tiles_n * c.split_k;
+    if (grid > INT32_MAX)
+        return fail(DGP_ERR_SHAPE, "grid of %lld workgroups too large", (long long)grid);
+    return ok();
+}
 
 dgp_status validate(const GemmCall &c, Plan *plan)
 {
@@ -187,10 +252,12 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     if (c.scale == DGP_SCALE_BLOCK128 && (c.K / c.split_k) % 128 != 0)
         return fail(DGP_ERR_SPLITK, "blockscale needs (K/split_k) %% 128 == 0");
 
-    if (c.M == 0 || c.N == 0) {
+    if (c.M == 0 || c.N == 0 || (c.select_only && c.K == 0)) {
         plan->spec = nullptr;
         return ok();
     }
+    if (c.select_only)
+        return select_kernel(c, Ks, plan);
     if (!c.C)
         return fail(DGP_ERR_NULL, "C is NULL");
     if (!aligned16(c.C))
@@ -219,57 +286,7 @@ dgp_status validate(const GemmCall &c, Plan *plan)
             return fail(DGP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.ws_bytes, need);
     }
 
-    const int out = c.split_k > 1 ? kOutPartial : kOutBf16;
-    const KernelSpec *spec = nullptr;
-    if (c.cfg && c.cfg->tile_m > 0) {
-        const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
-        if (c.cfg->waves_m < 0 || c.cfg->prefetch < 0)
-            return fail(DGP_ERR_CONFIG, "waves_m and prefetch must be >= 0");
-        Query q{fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n};
-        if (fam == kTiled) {
-            q.kt = c.cfg->tile_k;
-            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;
-            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
-            // (0, 0) = this tile's tuned default hints; any other pair must
-            // name a compiled kernel exactly.
-            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0) {
-                q.pv = c.cfg->preload_vmem;
-                q.pd = c.cfg->preload_dsrd;
-            }
-        } else {
-            if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0)
-                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
-            q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;   // matched against waves per workgroup
-            q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
-        }
-        spec = find_spec(q);
-        if (!spec)
-            return fail(DGP_ERR_CONFIG,
-                        "no compiled kernel for tile %dx%dx%d (waves_m %d, prefetch %d, preload %d,%d) with this "
-                        "dtype/scale", c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k, c.cfg->waves_m,
-                        c.cfg->prefetch, c.cfg->preload_vmem, c.cfg->preload_dsrd);
-        if (!spec_fits(*spec, Ks))
-            return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
-                        spec->kt, (long long)Ks);
-    } else {
-        spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks);
-        if (!spec)
-            return fail(DGP_ERR_CONFIG, "no compiled kernel fits this shape");
-    }
-    plan->spec = spec;
-    plan->tiles_m = (int)((c.M + spec->tm - 1) / spec->tm);
-    plan->tiles_n = (int)((c.N + spec->tn - 1) / spec->tn);
-    if (c.cfg && c.cfg->tile_m > 0) {
-        plan->remap = c.cfg->xcd_remap;
-        plan->group_m = c.cfg->group_m < 1 ? 1 : c.cfg->group_m;
-    } else {
-        plan->remap = spec->family == kTiled ? 1 : 0;
-        plan->group_m = 8;
-    }
-    const int64_t grid = (int64_t)plan->tiles_m * plan->tiles_n * c.split_k;
-    if (grid > INT32_MAX)
-        return fail(DGP_ERR_SHAPE, "grid of %lld workgroups too large", (long long)grid);
-    return ok();
+    return select_kernel(c, Ks, plan);
 }
 
 dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
@@ -453,9 +470,29 @@ dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mo
     cfg->preload_dsrd = k.pd;
     cfg->waves_m = k.family == kTiled ? k.p0 : k.waves;
     cfg->prefetch = k.depth;
+    cfg->schedule = k.sched;
     *dtype = k.dtype;
     *scale_mode = k.scale;
     *split_out = k.out == kOutPartial ? 1 : 0;
+    return ok();
+}
+
+dgp_status dgp_select_kernel(int64_t M, int64_t N, int64_t K, int dtype, int scale_mode, int split_k,
+                             const dgp_config *cfg, int *index)
+{
+    if (!index)
+        return fail(DGP_ERR_NULL, "NULL index");
+    GemmCall c{nullptr, nullptr, nullptr, M, N, K, dtype, scale_mode, nullptr, nullptr, split_k, nullptr, 0, cfg};
+    c.select_only = true;
+    Plan plan{};
+    const dgp_status st = validate(c, &plan);
+    if (st != DGP_OK)
+        return st;
+    *index = -1;
+    if (plan.spec) {
+        int n = 0;
+        *index = (int)(plan.spec - kernel_table(&n));
+    }
     return ok();
 }
 

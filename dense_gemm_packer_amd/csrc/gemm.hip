@@ -347,6 +347,340 @@ gemm_tiled_kernel(const GemmArgs p)
     }
 }
 
+// ============================================================ both in LDS
+
+// gemm_lds_kernel -- large M with both operands staged in LDS.  Per 128-byte
+// k-tile the A tile (TM rows) and the preshuffled B tile (TN/16 strips) go
+// global -> LDS with the async buffer load, into a two-stage ring; the waves
+// (WM x WN, each owning TM/WM rows x TN/WN columns) read their A and B
+// fragments from LDS.  The preshuffled B needs no swizzle in LDS: a 1 KiB
+// block of Bs is copied as-is (one fully coalesced load per wave) and is
+// already in operand order, so the B reads are as conflict-free as the A
+// reads.  Against gemm_tiled_kernel this moves the B stream off the VGPR
+// return path: all global traffic is LDS-bound copies, and one B fragment
+// feeds TM/WM/16 MFMAs instead of one wave's private column strip.
+//
+// Step t: every wave waits for its copies of tile t (the only loads in
+// flight), the barrier makes tile t visible to all waves and certifies that
+// tile t-1's stage is no longer read, the copies of tile t+1 go into that
+// stage, and the MFMAs of tile t run.  All of a k-tile's B fragments are
+// read first, then the A fragments PD ahead of the MFMAs that use them.
+template <int DT, int TM, int TN, int WM, int WN, int SCALE, int OUT, int PD>
+__global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
+                               amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
+gemm_lds_kernel(const GemmArgs p)
+{
+    constexpr int KT = 128;
+    using S = TiledShape<DT, TM, TN, WM, WN, KT>;
+    using Frag = typename Op<DT>::Frag;
+    constexpr int kABytes = TM * KT, kBBytes = TN * KT, kStage = kABytes + kBBytes;
+    constexpr int kBBlocks = (TN / 16) * S::kCH;
+    constexpr int kBDmaPerWave = kBBlocks / S::kWaves;
+    static_assert(kBBlocks % S::kWaves == 0, "B tile must split into whole copies per wave");
+    static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
+    const int m0 = (int)tc.tm * TM;
+    const int n0 = (int)tc.tn * TN;
+    const int split = (int)tc.s;
+    const uint32_t Kb = (uint32_t)p.Kb;
+    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
+    const int ntiles = p.Ks / KT;
+
+    // A copies: instruction j fills A block j*waves + wave = (row group, chunk),
+    // as in gemm_tiled_kernel.  Rows >= M load as zero.
+    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    uint32_t a_voff[S::kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < S::kDmaPerWave; ++j) {
+        const int blk = j * S::kWaves + wave;
+        a_voff[j] = (uint32_t)((blk / S::kCH) * 16 + (lane & 15)) * Kb +
+                    (uint32_t)((blk % S::kCH) * 64 + (lane >> 4) * 16);
+    }
+    // B copies: instruction j copies B block j*waves + wave = (strip sb of the
+    // tile, chunk ch) of Bs unchanged; strips >= N/16 load as zero.
+    const int strip0 = n0 / 16;
+    const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb,
+                              clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
+    uint32_t b_voff[kBDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kBDmaPerWave; ++j) {
+        const int blk = j * S::kWaves + wave;
+        b_voff[j] = (uint32_t)(blk / S::kCH) * 16u * Kb + (uint32_t)(blk % S::kCH) * 1024u + (uint32_t)lane * 16u;
+    }
+
+    float scale = 1.0f;
+    if constexpr (SCALE == kScaleTensor)
+        scale = p.sA[0] * p.sB[0];
+
+    f32x4 acc[S::kMT][S::kNT];
+#pragma unroll
+    for (int i = 0; i < S::kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < S::kNT; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto copy_tile = [&](uint32_t stage_off, int t) {
+        const uint32_t koff = kbase + (uint32_t)t * KT;
+#pragma unroll
+        for (int j = 0; j < S::kDmaPerWave; ++j)
+            lds_dma16(rA, lds + stage_off + (j * S::kWaves + wave) * 1024, a_voff[j], koff);
+#pragma unroll
+        for (int j = 0; j < kBDmaPerWave; ++j)
+            lds_dma16(rB, lds + stage_off + kABytes + (j * S::kWaves + wave) * 1024, b_voff[j], koff * 16u);
+    };
+
+    copy_tile(0, 0);
+    constexpr int kFr = S::kSteps * S::kMT;
+    constexpr int kRA = PD < kFr ? PD : kFr;
+    for (int t = 0; t < ntiles; ++t) {
+        const uint32_t cur = (uint32_t)(t & 1) * kStage;
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (t + 1 < ntiles)
+            copy_tile(kStage - cur, t + 1);
+        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+        const uint8_t *bbase = lds + cur + kABytes + (wn * S::kNT * S::kCH) * 1024 + lane * 16;
+        Frag bfr[S::kSteps][S::kNT];
+#pragma unroll
+        for (int st = 0; st < S::kSteps; ++st)
+#pragma unroll
+            for (int nt = 0; nt < S::kNT; ++nt)
+                bfr[st][nt] = lds_frag<DT>(bbase + (nt * S::kCH + st * S::kStepCh) * 1024);
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+            const int st = f / S::kMT, mt = f % S::kMT;
+            const Frag a = lds_frag<DT>(abase + (mt * S::kCH + st * S::kStepCh) * 1024);
+#pragma unroll
+            for (int nt = 0; nt < S::kNT; ++nt)
+                acc[mt][nt] = mfma_op(bfr[st][nt], a, acc[mt][nt]);
+        }
+        // B fragments and the first kRA A fragments, then per A fragment its
+        // MFMAs and the read of the fragment kRA places ahead.
+        constexpr int kRd = S::kStepCh;
+        __builtin_amdgcn_sched_group_barrier(0x100, (S::kSteps * S::kNT + kRA) * kRd, 0);
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
+            if (f + kRA < kFr)
+                __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+    for (int mt = 0; mt < S::kMT; ++mt) {
+        const int m = m0 + (wm * S::kMT + mt) * 16 + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < S::kNT; ++nt) {
+            const int n = n0 + (wn * S::kNT + nt) * 16 + (lane >> 4) * 4;
+            f32x4 v = acc[mt][nt];
+            if constexpr (SCALE == kScaleTensor)
+                v = v * scale;
+            store_tile<OUT>(p, split, m, n, v);
+        }
+    }
+}
+
+// ============================================================ ping-pong
+
+// gemm_pingpong_kernel -- the 256 x 256 tile of gemm_tiled_kernel (8 waves,
+// each owning 256 rows x 32 columns, 128-byte k-tiles, a ring of three A
+// buffers in LDS, preshuffled B straight into VGPRs) with a different
+// schedule.  Every k-tile is cut into two phases of 512 matrix-core cycles
+// per wave: bf16 phase p is MFMA k-step p over all 16 row tiles, fp8 phase p
+// is the single 128-deep k-step over row tiles 8p..8p+7.  A phase is split
+// into a memory part M -- issue this phase's share of the global loads, read
+// the phase's 16 A fragments from LDS and wait for them -- and a compute part
+// C that only issues MFMAs.  Waves 0-3 (one per SIMD) and waves 4-7 (the
+// other wave of each SIMD) run half a phase apart, separated by workgroup
+// barriers, so on every SIMD one wave issues an unbroken run of MFMAs while
+// the other does its memory work: the memory instructions and their waits
+// never sit in front of a ready MFMA.  Between two barriers group 0 is in
+// M(t,p) while group 1 is in C of the phase before, and the other way round.
+//
+// Load pipeline per wave (program order, vmcnt counts in-order completion):
+// the prologue issues A(0), then [B(0) half 0, A(1) half 0], [B(0) half 1,
+// A(1) half 1]; M(t,p) issues [B(t+1) half p, A(t+2) half p] (2 + 2 loads;
+// half p of B is the 64-byte chunk p, half p of A is copy instructions 2p,
+// 2p+1).  At the end of M(t,0), vmcnt(6) means B(t) has landed; at the end of
+// M(t,1), vmcnt(8) means this wave's A(t+1) copy has landed, and the barrier
+// that follows (before any wave reads tile t+1) makes that hold for all
+// waves.  A(t+2) goes to the buffer of tile t-1, whose last reader (group 1,
+// M(t-1,1)) finished before the barrier that opens M(t,0).
+template <int DT, int SCALE, int OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+gemm_pingpong_kernel(const GemmArgs p)
+{
+    constexpr int TM = 256, TN = 256, WM = 1, WN = 8, KT = 128;
+    using S = TiledShape<DT, TM, TN, WM, WN, KT>;
+    using Frag = typename Op<DT>::Frag;
+    static_assert(S::kCH == 2 && S::kNT == 2 && S::kMT == 16 && S::kDmaPerWave == 4, "fixed shape");
+    constexpr int kRing = 3;
+    constexpr int kFrP = DT == kDtypeBf16 ? 16 : 8;   // A fragments per phase: 16 LDS reads either way
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * S::kBufBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
+    const int m0 = (int)tc.tm * TM;
+    const int n0 = (int)tc.tn * TN;
+    const int split = (int)tc.s;
+    const uint32_t Kb = (uint32_t)p.Kb;
+    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
+    const int ntiles = p.Ks / KT;
+
+    // A copy: instruction j of this wave fills LDS block blk = j*8 + wave
+    // (row group blk/2, 64-byte chunk blk%2), as in gemm_tiled_kernel.
+    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    uint32_t dma_voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int blk = j * 8 + wave;
+        dma_voff[j] = (uint32_t)((blk / 2) * 16 + (lane & 15)) * Kb + (uint32_t)((blk % 2) * 64 + (lane >> 4) * 16);
+    }
+    const int strip0 = (n0 + wave * 32) / 16;
+    const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb,
+                              clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
+    uint32_t b_voff[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+        b_voff[nt] = (uint32_t)nt * 16u * Kb + (uint32_t)lane * 16u;
+
+    float scale = 1.0f;
+    if constexpr (SCALE == kScaleTensor)
+        scale = p.sA[0] * p.sB[0];
+
+    f32x4 acc[16][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    i32x4 breg[2][2][2];   // [set = tile % 2][strip][64-byte chunk]
+    Frag fr[kFrP];
+
+    auto kofs = [&](int t) { return kbase + (uint32_t)(t < ntiles ? t : ntiles - 1) * KT; };
+    auto load_b_half = [&](auto setc, int h, uint32_t koff) {
+        constexpr int SET = decltype(setc)::value;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            breg[SET][nt][h] = load16<kAuxNone>(rB, b_voff[nt] + h * 1024 + koff * 16u);
+    };
+    auto dma_half = [&](uint32_t buf_off, int h, uint32_t koff) {
+#pragma unroll
+        for (int j = 2 * h; j < 2 * h + 2; ++j)
+            lds_dma16(rA, lds + buf_off + (j * 8 + wave) * 1024, dma_voff[j], koff);
+    };
+    auto read_frags = [&](uint32_t buf_off, int ph) {
+        const uint8_t *abase = lds + buf_off + lane * 16;
+#pragma unroll
+        for (int f = 0; f < kFrP; ++f) {
+            if constexpr (DT == kDtypeBf16)
+                fr[f] = lds_frag<DT>(abase + (f * 2 + ph) * 1024);
+            else
+                fr[f] = lds_frag<DT>(abase + ((8 * ph + f) * 2) * 1024);
+        }
+    };
+    auto compute = [&](auto setc, auto phc) {
+        constexpr int SET = decltype(setc)::value, PH = decltype(phc)::value;
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int f = 0; f < kFrP; ++f) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                if constexpr (DT == kDtypeBf16)
+                    acc[f][nt] = mfma_op(breg[SET][nt][PH], fr[f], acc[f][nt]);
+                else
+                    acc[8 * PH + f][nt] = mfma_op(cat(breg[SET][nt][0], breg[SET][nt][1]), fr[f],
+                                                  acc[8 * PH + f][nt]);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // Prologue: A(0); then B(0) and A(1) in the per-phase order.
+    dma_half(0, 0, kofs(0));
+    dma_half(0, 1, kofs(0));
+    __builtin_amdgcn_sched_barrier(0);
+    load_b_half(std::integral_constant<int, 0>{}, 0, kofs(0));
+    dma_half(S::kBufBytes, 0, kofs(1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_b_half(std::integral_constant<int, 0>{}, 1, kofs(0));
+    dma_half(S::kBufBytes, 1, kofs(1));
+    __builtin_amdgcn_sched_barrier(0);
+    // A(0) has landed for every wave.
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave >= 4)   // group 1 starts half a phase behind
+        asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t cur = 0;                          // LDS offset of tile t
+    uint32_t nxt = 2u * S::kBufBytes;          // LDS offset of tile t+2
+    auto tile_step = [&](auto setc, int t) {
+        constexpr int SET = decltype(setc)::value;
+        const std::integral_constant<int, SET ^ 1> nset{};
+        const uint32_t kb1 = kofs(t + 1), ka2 = kofs(t + 2);
+        // M(t,0)
+        load_b_half(nset, 0, kb1);
+        dma_half(nxt, 0, ka2);
+        read_frags(cur, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // C(t,0)
+        compute(setc, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // M(t,1)
+        load_b_half(nset, 1, kb1);
+        dma_half(nxt, 1, ka2);
+        read_frags(cur, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // C(t,1)
+        compute(setc, std::integral_constant<int, 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        cur = cur + S::kBufBytes == kRing * S::kBufBytes ? 0 : cur + S::kBufBytes;
+        nxt = nxt + S::kBufBytes == kRing * S::kBufBytes ? 0 : nxt + S::kBufBytes;
+    };
+
+    int t = 0;
+    for (; t + 2 <= ntiles; t += 2) {
+        tile_step(std::integral_constant<int, 0>{}, t);
+        tile_step(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t < ntiles)
+        tile_step(std::integral_constant<int, 0>{}, t);
+    if (wave < 4)   // group 0 matches group 1's extra barrier
+        asm volatile("s_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+        const int m = m0 + mt * 16 + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = n0 + (wave * 2 + nt) * 16 + (lane >> 4) * 4;
+            f32x4 v = acc[mt][nt];
+            if constexpr (SCALE == kScaleTensor)
+                v = v * scale;
+            store_tile<OUT>(p, split, m, n, v);
+        }
+    }
+}
+
 // =============================================================== stream
 
 // Largest K range (bytes) of the 16 A rows held in LDS at once.
@@ -514,6 +848,18 @@ void launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_tiled_kernel<DT, TM, TN, WM, WN, KT, DEPTH, SCALE, OUT, PV, PD><<<grid, WM * WN * 64, 0, s>>>(a);
 }
 
+template <int DT, int TM, int TN, int WM, int WN, int SCALE, int OUT, int PD>
+void launch_lds(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    gemm_lds_kernel<DT, TM, TN, WM, WN, SCALE, OUT, PD><<<grid, WM * WN * 64, 0, s>>>(a);
+}
+
+template <int DT, int SCALE, int OUT>
+void launch_pingpong(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    gemm_pingpong_kernel<DT, SCALE, OUT><<<grid, 512, 0, s>>>(a);
+}
+
 template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
 void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
@@ -538,28 +884,40 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
 }
 
 #define DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, OUT, PV, PD)                            \
-    {kTiled, DT, SC, OUT, TM, TN, KT, WM * WN, WM, WN, PV, PD, DEPTH,                         \
+    {kTiled, DT, SC, OUT, TM, TN, KT, WM * WN, WM, WN, PV, PD, DEPTH, kSchedInterleaved,      \
      &launch_tiled<DT, TM, TN, WM, WN, KT, DEPTH, SC, OUT, PV, PD>}
+#define DGP_PINGPONG(DT, SC, OUT)                                                             \
+    {kTiled, DT, SC, OUT, 256, 256, 128, 8, 1, 8, 0, 0, 2, kSchedPingPong,                     \
+     &launch_pingpong<DT, SC, OUT>}
+#define DGP_LDS(DT, TM, TN, WM, WN, SC, OUT, PD)                                              \
+    {kTiled, DT, SC, OUT, TM, TN, 128, WM * WN, WM, WN, 0, PD, 1, kSchedBothLds,               \
+     &launch_lds<DT, TM, TN, WM, WN, SC, OUT, PD>}
+#define DGP_LDS_BOTH_OUT(DT, TM, TN, WM, WN, SC, PD)                                          \
+    DGP_LDS(DT, TM, TN, WM, WN, SC, kOutBf16, PD), DGP_LDS(DT, TM, TN, WM, WN, SC, kOutPartial, PD)
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
-    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH,    \
+    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
      &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
 
 #define DGP_TILED_BOTH_OUT(DT, TM, TN, WM, WN, KT, DEPTH, SC, PV, PD)                         \
     DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutBf16, PV, PD),                           \
         DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutPartial, PV, PD)
+#define DGP_PINGPONG_BOTH_OUT(DT, SC) DGP_PINGPONG(DT, SC, kOutBf16), DGP_PINGPONG(DT, SC, kOutPartial)
 #define DGP_STREAM_BOTH_OUT(DT, NW, SPW, DEPTH, SC)                                           \
     DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutBf16), DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutPartial)
 
 static const KernelSpec kKernels[] = {
-    // large tiles, bf16 (tm, tn, waves m x n, k-tile bytes, prefetch depth, scale, preload pair)
+    // large tiles, bf16 (tm, tn, waves m x n, k-tile bytes, prefetch depth, scale, preload pair);
+    // within one tile the first entry is the tuned default
     DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 1, 8, 128, 2, kScaleNone, 0, 8),
-    DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 1, 8, 128, 2, kScaleNone, 0, 0),
+    DGP_PINGPONG_BOTH_OUT(kDtypeBf16, kScaleNone),
+    DGP_LDS_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, kScaleNone, 4),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, 128, 2, kScaleNone, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 256, 1, 4, 128, 2, kScaleNone, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 128, 2, 2, 128, 2, kScaleNone, 0, 4),
     // large tiles, fp8 per-tensor
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleTensor, 0, 8),
-    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleTensor, 0, 0),
+    DGP_PINGPONG_BOTH_OUT(kDtypeFp8, kScaleTensor),
+    DGP_LDS_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, kScaleTensor, 4),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 1, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleTensor, 0, 4),

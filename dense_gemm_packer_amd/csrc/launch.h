@@ -27,6 +27,9 @@ struct GemmArgs {
 // Kernel family selectors.
 enum Family { kTiled = 0, kStream = 1 };
 
+// Wave schedules of the tiled family (dgp_config.schedule).
+enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3 };
+
 // One compiled kernel configuration.
 struct KernelSpec {
     int family;
@@ -39,6 +42,7 @@ struct KernelSpec {
     int p0, p1;     // family-specific: tiled = (wm, wn); stream = (strips per wave, depth)
     int pv, pd;     // scheduling hint pair (tiled)
     int depth;      // prefetch distance: k-tiles (tiled) / steps (stream)
+    int sched;      // tiled: kSchedInterleaved or kSchedPingPong; stream: 0
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
 };
 

@@ -89,7 +89,20 @@ typedef enum dgp_scale_mode {
  *                    (0 = any compiled layout for this tile).
  *   prefetch       : tiled kernels: k-tiles loaded ahead of the one being
  *                    multiplied; streaming kernel: MFMA steps of loads in
- *                    flight per wave (0 = any compiled depth for this tile). */
+ *                    flight per wave (0 = any compiled depth for this tile).
+ *   schedule       : tiled kernels: how one workgroup's waves order their
+ *                    work.  1 = interleaved: every wave mixes its LDS reads,
+ *                    global loads and MFMAs, placed by the preload hints;
+ *                    2 = ping-pong: each k-tile is cut into two phases, and
+ *                    the two waves of every SIMD take turns, one issuing an
+ *                    unbroken run of MFMAs while the other does its loads
+ *                    (preload must be (0, 0)); 3 = both in LDS: A and the
+ *                    preshuffled B tile both go global -> LDS with the async
+ *                    copy (two stages), and the waves read both operands from
+ *                    LDS; 0 = the tile's tuned default.
+ *                    Must be 0 for the streaming kernel.  Zero-initialising
+ *                    the whole struct and setting tile_m = 0 selects the
+ *                    built-in table, like NULL. */
 typedef struct dgp_config {
     int tile_m;
     int tile_n;
@@ -100,6 +113,7 @@ typedef struct dgp_config {
     int preload_dsrd;
     int waves_m;
     int prefetch;
+    int schedule;
 } dgp_config;
 
 /*

@@ -46,6 +46,20 @@ int dgp_kernel_count(void);
 dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mode, int *split_out);
 
 /*
+ * dgp_select_kernel -- which compiled GEMM kernel a call would launch.
+ *
+ * Runs the shape and configuration checks of dgp_gemm_preshuffle_splitk
+ * (dgp_gemm_preshuffle when split_k = 1) for these arguments -- no buffers,
+ * no device -- and stores in *index the table index (as numbered by
+ * dgp_kernel_info) of the GEMM kernel that call would launch, or -1 when it
+ * would launch none (M = 0, N = 0 or K = 0).  Returns the status the GEMM
+ * entry point would return for a shape or configuration error.
+ * Pure host function.
+ */
+dgp_status dgp_select_kernel(int64_t M, int64_t N, int64_t K, int dtype, int scale_mode, int split_k,
+                             const dgp_config *config, int *index);
+
+/*
  * dgp_probe_mfma_layout -- run each matrix-core instruction the GEMM uses once
  * on operands the caller supplies and store the raw accumulator registers.
  *   which = 0: v_mfma_f32_16x16x32_bf16   (a, b: 64 lanes x 16 bytes)

@@ -102,14 +102,20 @@ def test_every_compiled_kernel():
         assert_close(got, c32, what=what)
 
 
-def test_k_tile_counts_not_multiple_of_prefetch_depth():
-    """ntiles % depth != 0 exercises the steps after the unrolled main loop."""
-    for k in (128, 384, 640, 896):     # 1, 3, 5, 7 fp8 k-tiles of 128 bytes
-        for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dgp.FP8_E4M3 and not so]:
-            A, B, sA, sB = exact_inputs("fp8", "tensor", 300, 528, k, 13)
-            got = run_gpu(A, B, "fp8", "tensor", sA, sB, config=cfg)
-            _, c16 = run_oracle(A, B, "fp8", "tensor", sA, sB)
-            assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
+    """ntiles % depth != 0 exercises the steps after the unrolled main loop
+    (1, 2, 3, 5, 7 k-tiles of 128 bytes)."""
+    eb = 2 if dtype == "bf16" else 1
+    mode = "none" if dtype == "bf16" else "tensor"
+    dcode = dgp.BF16 if dtype == "bf16" else dgp.FP8_E4M3
+    for tiles in (1, 2, 3, 5, 7):
+        k = tiles * 128 // eb
+        for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dcode and not so]:
+            A, B, sA, sB = exact_inputs(dtype, mode, 300, 528, k, 13)
+            got = run_gpu(A, B, dtype, mode, sA, sB, config=cfg)
+            _, c16 = run_oracle(A, B, dtype, mode, sA, sB)
+            assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
@@ -175,6 +181,33 @@ def test_xcd_remap_is_bit_identical(tile):
                             config=dgp.Config(tile[0], tile[1], 128, remap, group, 0, tile[3], tile[2], 2)))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+SCHED_CFG = {2: (1, 2), 3: (2, 1)}   # schedule -> (waves_m, prefetch) of its 256x256 kernel
+
+
+@pytest.mark.parametrize("sched", [2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_schedules_ragged_splitk_and_remap(dtype, sched):
+    """The ping-pong and both-in-LDS schedules on a ragged multi-tile grid:
+    exact integers bit-exact for split_k 1 and 3 (3 splits of 5 k-tiles each)
+    under every tile map; random data within tolerance."""
+    wm, pf = SCHED_CFG[sched]
+    mode = "none" if dtype == "bf16" else "tensor"
+    M, N = 3 * 256 + 17, 2 * 256 + 48
+    K = 15 * 128 // (2 if dtype == "bf16" else 1)
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 21)
+    outs = []
+    for split in (1, 3):
+        for remap, group in ((0, 1), (1, 1), (1, 8)):
+            cfg = dgp.Config(256, 256, 128, remap, group, 0, 0, wm, pf, sched)
+            got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
+            _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
+            assert np.array_equal(got, c16), (split, remap, group)
+    A, B, sA, sB = rand_inputs(dtype, mode, M, N, K, 22)
+    got = run_gpu(A, B, dtype, mode, sA, sB, config=dgp.Config(256, 256, 128, 1, 8, 0, 0, wm, pf, sched))
+    c32, _ = run_oracle(A, B, dtype, mode, sA, sB)
+    assert_close(got, c32)
 
 
 def test_negative_control_corrupted_weight_diverges():

@@ -186,7 +186,7 @@ def test_kernel_table(dgp, L):
     seen = set()
     for cfg, dt, sm, split_out in ks:
         key = (cfg.tile_m, cfg.tile_n, cfg.tile_k, cfg.waves_m, cfg.prefetch, cfg.preload_vmem,
-               cfg.preload_dsrd, dt, sm, split_out)
+               cfg.preload_dsrd, cfg.schedule, dt, sm, split_out)
         assert key not in seen
         seen.add(key)
         assert (dt, sm) in ((0, 0), (1, 1), (1, 2))
@@ -199,6 +199,46 @@ def test_kernel_table(dgp, L):
         i = ctypes.c_int()
         dgp._check(L.dgp_kernel_info(len(ks), ctypes.byref(c), ctypes.byref(i), ctypes.byref(i),
                                      ctypes.byref(i)))
+
+
+def test_every_kernel_is_selected_by_its_reported_config(dgp):
+    # The configuration dgp_kernel_info reports must select exactly that
+    # kernel, so iterating the table really runs every compiled kernel.
+    for i, (cfg, dt, sm, split_out) in enumerate(dgp.kernels()):
+        M = 37 if cfg.tile_m == 16 else 2 * cfg.tile_m + 44
+        N = 384 if cfg.tile_m == 16 else 2 * cfg.tile_n + 128
+        K = 1024 if dt == dgp.FP8_E4M3 else 512
+        assert dgp.select_kernel(M, N, K, dt, sm, 2 if split_out else 1, cfg) == i, dgp.describe_kernel(i)
+        assert dgp.describe_kernel(i)
+
+
+def test_default_selection(dgp):
+    # Headline shapes take a 256x256 tile, decode-sized M and blockscale the
+    # 16-row streaming kernel; empty calls launch nothing.
+    for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
+        cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
+        assert (cfg.tile_m, cfg.tile_n) == (256, 256)
+        assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dt, sm, 4)][0].tile_m == 16
+    assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)][0].tile_m == 16
+    assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
+    assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
+
+
+def test_schedule_validation(dgp):
+    base = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8)
+    for sched in (1, 2, 3):
+        i = dgp.select_kernel(1024, 1024, 1024, dgp.BF16, dgp.SCALE_NONE, 1, dgp.Config(**base, schedule=sched))
+        assert dgp.kernels()[i][0].schedule == sched
+    bad = (dgp.Config(**base, schedule=4), dgp.Config(**base, schedule=-1),
+           dgp.Config(**base, schedule=2, preload_dsrd=8),
+           dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 1))
+    for cfg in bad:
+        with pytest.raises(dgp.DgpError) as e:
+            dgp.select_kernel(1024, 1024, 1024, dgp.BF16, dgp.SCALE_NONE, 1, cfg)
+        assert e.value.name == "DGP_ERR_CONFIG"
+    with pytest.raises(dgp.DgpError) as e:
+        dgp.select_kernel(1024, 1000, 1024, dgp.BF16, dgp.SCALE_NONE)
+    assert e.value.name == "DGP_ERR_SHAPE"
 
 
 def test_tile_map_rejects_bad_arguments(dgp):
