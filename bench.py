@@ -30,7 +30,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 MALL_BYTES = 256 << 20         # Infinity Cache; cold-cache rotation exceeds 2x this
 METRIC = "TFLOP/s (large M) and GB/s (decode M≤16) at 1 GPU; % of MFMA / HBM roofline"
 PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_4096x4096x8192_traffic.md")
-KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm.hip", "dense_gemm_packer_amd/csrc/common.h"]
+KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_tiled.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
+                  "dense_gemm_packer_amd/csrc/common.h"]
 
 
 def log(*a):
@@ -137,7 +138,7 @@ def main():
     traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_tiled_kernel<bf16, 256x256 tile, 1x8 waves, 128-byte k-tile, prefetch 2, LDS read-ahead 8>",
+                "kernel": dgp.describe_kernel(dgp.select_kernel(M, N, K, dgp.BF16, dgp.SCALE_NONE)),
                 "per_launch": f"{flops:.4g} FLOP = 2*M*N*K"}
 
     # --------------------------------------------------------- CPU oracle
@@ -274,6 +275,27 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["fp8_gemm_4096x4096x8192"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
                                       "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                                       "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4)}
+    out["fp8_gemm_4096x4096x8192"]["kernel"] = dgp.describe_kernel(
+        dgp.select_kernel(4096, 4096, 8192, dgp.FP8_E4M3, dgp.SCALE_TENSOR))
+
+    # Context only: the vendor library (hipBLASLt through torch) on the same
+    # shapes and bytes, in the same process, with B in its own row-major
+    # layout.  Not part of the path and not a baseline.
+    vend = {}
+    try:
+        Bb = dgp.unshuffle_b(Bs_bf16)
+        us = graph_time_us(torch, lambda i: torch.nn.functional.linear(A_bf16, Bb), 10)
+        vend["bf16_4096x4096x8192_TFLOP/s"] = round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)
+        del Bb
+        B8 = dgp.unshuffle_b(Bs8)
+        one = torch.ones((), device=dev)
+        us = graph_time_us(torch, lambda i: torch._scaled_mm(A8, B8.t(), scale_a=one, scale_b=one,
+                                                             out_dtype=torch.bfloat16), 10)
+        vend["fp8_4096x4096x8192_TFLOP/s"] = round(2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12, 1)
+        del B8
+    except Exception as e:   # a torch build without these paths: report, do not fail
+        vend["error"] = repr(e)[:200]
+    out["vendor_library_same_process"] = vend
     del A8, Bs8, C8
 
     # fp8 split-K decode (per-tensor) and blockscale decode, cold cache.

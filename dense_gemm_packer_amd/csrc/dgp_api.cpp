@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "../../include/dgp.h"
 #include "../../include/dgp_diag.h"
@@ -16,6 +17,25 @@
 #include "launch.h"
 
 using namespace dgp;
+
+namespace dgp {
+
+const KernelSpec *kernel_table(int *count)
+{
+    static const std::vector<KernelSpec> all = [] {
+        std::vector<KernelSpec> v;
+        int n = 0;
+        const KernelSpec *t = tiled_kernels(&n);
+        v.insert(v.end(), t, t + n);
+        t = stream_kernels(&n);
+        v.insert(v.end(), t, t + n);
+        return v;
+    }();
+    *count = (int)all.size();
+    return all.data();
+}
+
+}  // namespace dgp
 
 namespace {
 

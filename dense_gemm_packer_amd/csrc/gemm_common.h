@@ -1,0 +1,101 @@
+// Device helpers shared by the GEMM kernel families (gemm_tiled.hip,
+// gemm_stream.hip): matrix-core operations, LDS fragment reads, the async
+// global->LDS copy, and the epilogue store.
+//
+// Matrix-core operands.  bf16 uses v_mfma_f32_16x16x32_bf16 (the K32 MFMA
+// selected for bf16 on gfx950, FlyDSL PR #1008 review excerpt) and fp8 the
+// 128-deep v_mfma_f32_16x16x128_f8f6f4 (same excerpt; scale operands left at
+// 0, which selects the unscaled form).  The preshuffled B fragment is passed
+// as the instruction's FIRST operand and the A fragment as its second, so the
+// instruction produces the 16x16 tile of C^T: lane l holds
+// C[m = l%16][n = 4*(l/16) + r], r = 0..3 -- four consecutive columns of one
+// row, written with a single 8-byte (bf16) or 16-byte (fp32) store.  Both
+// operands use the same in-register K order, so any K permutation the
+// hardware applies inside one instruction is applied to both alike.
+//
+// A in LDS.  The A tile is stored in the same 1 KiB operand blocks as the
+// preshuffled B: block (row group rg, 64-byte K chunk c) holds, at byte
+// 16*l, the 16 bytes of row 16*rg + l%16 at K-bytes 64*c + 16*(l/16).  The
+// writer (the async copy, whose LDS side is linear per wave) realises this
+// permutation through the global addresses of its lanes; the reader reads
+// 16 consecutive bytes per lane.  Writer and reader share the one mapping,
+// and both sides touch 64 distinct 16-byte bank groups per wave: no bank
+// conflicts by construction.  (The pages keep a row-major tile with an XOR
+// swizzle whose writer and reader had to be made to agree, FlyDSL PR #1008
+// "Changes" item 2; this mapping is the same idea -- a 16-byte-granular LDS
+// permutation known to both sides -- chosen for the operand order.)
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dgp {
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ inline f32x4 mfma_op(const i32x4 &b, const i32x4 &a, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                   __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+}
+
+__device__ inline f32x4 mfma_op(const i32x8 &b, const i32x8 &a, const f32x4 &c)
+{
+    // cbsz = blgp = 0: both operands OCP e4m3; zero scale operands: unscaled.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline i32x8 cat(const i32x4 &lo, const i32x4 &hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int DT>
+struct Op;
+template <>
+struct Op<kDtypeBf16> {
+    using Frag = i32x4;
+    static constexpr int kBlocks = 1;   // 1 KiB operand blocks per MFMA step (64 K-bytes)
+};
+template <>
+struct Op<kDtypeFp8> {
+    using Frag = i32x8;
+    static constexpr int kBlocks = 2;   // 128 K-bytes
+};
+
+template <int DT>
+__device__ inline typename Op<DT>::Frag lds_frag(const uint8_t *p)
+{
+    if constexpr (DT == kDtypeBf16) {
+        return *reinterpret_cast<const i32x4 *>(p);
+    } else {
+        return cat(*reinterpret_cast<const i32x4 *>(p), *reinterpret_cast<const i32x4 *>(p + 1024));
+    }
+}
+
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_dst, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// ------------------------------------------------------------- epilogue
+
+template <int OUT>
+__device__ inline void store_tile(const GemmArgs &p, int split, int m, int n, f32x4 v)
+{
+    if (m >= p.M || n >= p.N)
+        return;
+    if constexpr (OUT == kOutBf16) {
+        u32x2 packed;
+        packed.x = pack_bf16x2(v.x, v.y);
+        packed.y = pack_bf16x2(v.z, v.w);
+        *reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(p.C) + ((int64_t)m * p.N + n) * 2) = packed;
+    } else {
+        *reinterpret_cast<f32x4 *>(p.ws + ((int64_t)split * p.M + m) * p.N + n) = v;
+    }
+}
+
+}  // namespace dgp

@@ -1,0 +1,218 @@
+// Decode-sized-M GEMM kernel for C = A * B^T with B preshuffled
+// (include/dgp.h) and its table entries.  Operand layout and epilogue:
+// gemm_common.h.
+//
+// gemm_stream_kernel -- decode-sized M (aiter PR #5148, "Summary": split-K
+//    preshuffle GEMM for small M).  A workgroup owns 16 rows of C and a few
+//    16-column strips; the A rows of its K range sit in LDS and each wave
+//    streams its strips of B through a deep ring of in-flight 16-byte loads.
+//    It also carries the FP8 blockscale mode for any M.
+
+#include "gemm_common.h"
+
+namespace dgp {
+
+// =============================================================== stream
+
+// Largest K range (bytes) of the 16 A rows held in LDS at once.
+constexpr int kStreamPanelMax = 8192;
+
+template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+gemm_stream_kernel(const GemmArgs p, int panel)
+{
+    using Frag = typename Op<DT>::Frag;
+    constexpr int kStepCh = Op<DT>::kBlocks;
+    constexpr int kStepBytes = 64 * kStepCh;
+    constexpr int kScaleCols = kStreamPanelMax / 128;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_a[];   // 16 * panel bytes
+    __shared__ float lds_sa[SCALE == kScaleBlock ? 16 : 1][kScaleCols];
+    __shared__ float lds_sb[SCALE == kScaleBlock ? NW * SPW : 1][kScaleCols];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
+    const int m0 = (int)tc.tm * 16;
+    const int strip_wg = (int)tc.tn * (NW * SPW);
+    const int strip_w = strip_wg + wave * SPW;
+    const int split = (int)tc.s;
+    const uint32_t Kb = (uint32_t)p.Kb;
+    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
+    const int nsteps = panel / kStepBytes;
+    const int kblocks_row = p.K / 128;   // blockscale: scale columns per row
+
+    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
+    const auto rB = make_rsrc(p.Bs + (int64_t)strip_w * 16 * Kb,
+                              clamp_bytes((int64_t)(p.N / 16 - strip_w) * 16 * Kb));
+    uint32_t b_voff[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        b_voff[sp] = (uint32_t)sp * 16u * Kb + (uint32_t)lane * 16u;
+
+    float tscale = 1.0f;
+    if constexpr (SCALE == kScaleTensor)
+        tscale = p.sA[0] * p.sB[0];
+
+    f32x4 acc[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    i32x4 breg[DEPTH][SPW][kStepCh];
+    auto load_step = [&](int d, int st, uint32_t pk) {
+        const uint32_t soff = (pk + (uint32_t)st * kStepBytes) * 16u;
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int cc = 0; cc < kStepCh; ++cc)
+                breg[d][sp][cc] = load16<kAuxNonTemporal>(rB, b_voff[sp] + cc * 1024 + soff);
+    };
+
+    for (int p0 = 0; p0 < p.Ks; p0 += panel) {
+        const uint32_t pk = kbase + (uint32_t)p0;   // first K byte of this panel
+        if (p0 > 0)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+        // Blockscale: fetch this panel's scales into registers now (written
+        // to LDS once the copies below are in flight).  Entry i of the sA
+        // tile is (row i / cols, block i % cols); of the sB tile, (strip of
+        // the workgroup i / cols, block i % cols).
+        constexpr int kSaPer = SCALE == kScaleBlock ? (16 * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
+        constexpr int kSbPer = SCALE == kScaleBlock ? (NW * SPW * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
+        float sa_v[kSaPer], sb_v[kSbPer];
+        const int cols = panel / 128, kb0 = (int)(pk / 128u);
+        if constexpr (SCALE == kScaleBlock) {
+#pragma unroll
+            for (int u = 0; u < kSaPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                const int r = i / cols, c = i % cols;
+                sa_v[u] = (i < 16 * cols && m0 + r < p.M) ? p.sA[(int64_t)(m0 + r) * kblocks_row + kb0 + c] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kSbPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                const int st = i / cols, c = i % cols;
+                const int strip = strip_wg + st;
+                sb_v[u] = (i < NW * SPW * cols && strip < p.N / 16)
+                              ? p.sB[(int64_t)(strip * 16 / 128) * kblocks_row + kb0 + c]
+                              : 0.f;
+            }
+        }
+
+        // A rows m0..m0+15 of this panel -> LDS, one 1 KiB operand block per
+        // 64-byte K chunk (blocks dealt round-robin to the waves).
+        for (int c = wave; c < panel / 64; c += NW)
+            lds_dma16(rA, lds_a + c * 1024, a_voff, pk + (uint32_t)c * 64u);
+        // Fill the ring of in-flight B loads (clamped to the last step).
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            load_step(d, d < nsteps ? d : nsteps - 1, pk);
+
+        if constexpr (SCALE == kScaleBlock) {
+#pragma unroll
+            for (int u = 0; u < kSaPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                if (i < 16 * cols)
+                    lds_sa[i / cols][i % cols] = sa_v[u];
+            }
+#pragma unroll
+            for (int u = 0; u < kSbPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                if (i < NW * SPW * cols)
+                    lds_sb[i / cols][i % cols] = sb_v[u];
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DEPTH * SPW * kStepCh) : "memory");
+
+        for (int st0 = 0; st0 < nsteps; st0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int st = st0 + d;
+                if (st < nsteps) {
+                    const Frag a = lds_frag<DT>(lds_a + (st * kStepCh) * 1024 + lane * 16);
+#pragma unroll
+                    for (int sp = 0; sp < SPW; ++sp) {
+                        Frag b;
+                        if constexpr (DT == kDtypeBf16)
+                            b = breg[d][sp][0];
+                        else
+                            b = cat(breg[d][sp][0], breg[d][sp][1]);
+                        if constexpr (SCALE == kScaleBlock) {
+                            // One MFMA is exactly one 128-wide K block: scale its
+                            // fp32 partial, then add (blockscale, aiter PR #5148).
+                            const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
+                            const float s = __fmul_rn(lds_sa[lane & 15][st], lds_sb[wave * SPW + sp][st]);
+                            acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, s));
+                            acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, s));
+                            acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, s));
+                            acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, s));
+                        } else {
+                            acc[sp] = mfma_op(b, a, acc[sp]);
+                        }
+                    }
+                }
+                const int nx = st + DEPTH < nsteps ? st + DEPTH : nsteps - 1;
+                load_step(d, nx, pk);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int m = m0 + (lane & 15);
+        const int n = (strip_w + sp) * 16 + (lane >> 4) * 4;
+        f32x4 v = acc[sp];
+        if constexpr (SCALE == kScaleTensor)
+            v = v * tscale;
+        store_tile<OUT>(p, split, m, n, v);
+    }
+}
+
+template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
+void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    constexpr int kStepBytes = 64 * Op<DT>::kBlocks;
+    // Panel: the whole K range of a split if its 16 rows fit, else the
+    // largest step multiple <= kStreamPanelMax that divides it (the host
+    // layer only accepts K ranges for which one exists).
+    int panel = a.Ks;
+    if (panel > kStreamPanelMax) {
+        panel = kStreamPanelMax - kStreamPanelMax % kStepBytes;
+        while (panel > kStepBytes && a.Ks % panel != 0)
+            panel -= kStepBytes;
+    }
+    const size_t lds = (size_t)16 * panel;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void *)gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 16 * kStreamPanelMax);
+        attr_set = true;
+    }
+    gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
+}
+
+#define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
+    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
+     &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
+
+#define DGP_STREAM_BOTH_OUT(DT, NW, SPW, DEPTH, SC)                                           \
+    DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutBf16), DGP_STREAM(DT, NW, SPW, DEPTH, SC, kOutPartial)
+
+static const KernelSpec kStreamKernels[] = {
+    // streaming (decode-sized M): waves per workgroup, strips per wave, ring depth
+    DGP_STREAM_BOTH_OUT(kDtypeBf16, 4, 1, 16, kScaleNone),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleTensor),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 2, 8, kScaleTensor),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
+};
+
+const KernelSpec *stream_kernels(int *count)
+{
+    *count = (int)(sizeof(kStreamKernels) / sizeof(kStreamKernels[0]));
+    return kStreamKernels;
+}
+
+}  // namespace dgp

@@ -46,7 +46,11 @@ struct KernelSpec {
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
 };
 
-// Table of every compiled GEMM kernel (defined in gemm.hip).
+// The compiled GEMM kernels: the tiled family (gemm_tiled.hip), the
+// streaming family (gemm_stream.hip), and both in one table, tiled first
+// (dgp_api.cpp) -- the numbering dgp_kernel_info uses.
+const KernelSpec *tiled_kernels(int *count);
+const KernelSpec *stream_kernels(int *count);
 const KernelSpec *kernel_table(int *count);
 
 hipError_t launch_preshuffle(const void *src, void *dst, int64_t N, int64_t Kb, bool inverse,
