@@ -14,22 +14,29 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdgp.so")
-SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_stream.hip", "reduce.hip", "probe.hip"]
-HEADERS = ["common.h", "launch.h"]
+SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_lds.hip", "gemm_stream.hip", "reduce.hip", "probe.hip"]
+HEADERS = ["common.h", "launch.h", "gemm_common.h"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in arch VGPRs: avoids accumulator copies at loop latches
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# Keep MFMA accumulators in arch VGPRs (avoids accumulator copies at loop
+# latches) everywhere except in the kernels that need the AGPRs for them.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC_SOURCES = {"gemm_lds.hip"}
+
+
+def flags(src):
+    """hipcc flags for one source file."""
+    return CFLAGS + ([] if src in AGPR_ACC_SOURCES else VGPR_FORM)
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *flags(src), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -66,7 +73,7 @@ def build(force: bool = True, jobs: int = 0) -> str:
 
 def asm(src: str, out: str) -> None:
     """Write the gfx950 assembly of one source (for inspection)."""
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *flags(src), "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out]
     subprocess.run(cmd, check=True)
 
 

@@ -27,6 +27,8 @@ const KernelSpec *kernel_table(int *count)
         int n = 0;
         const KernelSpec *t = tiled_kernels(&n);
         v.insert(v.end(), t, t + n);
+        t = lds_kernels(&n);
+        v.insert(v.end(), t, t + n);
         t = stream_kernels(&n);
         v.insert(v.end(), t, t + n);
         return v;

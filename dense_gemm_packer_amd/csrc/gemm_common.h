@@ -98,4 +98,29 @@ __device__ inline void store_tile(const GemmArgs &p, int split, int m, int n, f3
     }
 }
 
+// Per-wave counts of a TM x TN workgroup tile split over WM x WN waves, with
+// KT-byte k-tiles (the tiled kernel families).
+template <int DT, int TM, int TN, int WM, int WN, int KT>
+struct TiledShape {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kMT = TM / WM / 16;             // 16-row tiles per wave
+    static constexpr int kNT = TN / WN / 16;             // 16-column strips per wave
+    static constexpr int kCH = KT / 64;                  // 64-byte K chunks per k-tile
+    static constexpr int kStepCh = Op<DT>::kBlocks;
+    static constexpr int kSteps = kCH / kStepCh;         // MFMA k-steps per k-tile
+    static constexpr int kABlocks = (TM / 16) * kCH;     // 1 KiB A blocks per k-tile
+    static constexpr int kDmaPerWave = kABlocks / kWaves;
+    static constexpr int kBufBytes = TM * KT;
+    static constexpr int kBLoads = kNT * kCH;            // B loads per wave per k-tile
+    static_assert(TM % (16 * WM) == 0 && TN % (16 * WN) == 0, "tile must split into 16x16 wave tiles");
+    // The A-tile granularity rule of FlyDSL PR #974's follow-up commit (item 1):
+    // the tile must split into whole 16-byte loads per thread, i.e.
+    // TM*KT % (threads*16) == 0 -- with fewer loads the tail of the tile is
+    // never fetched and the kernel computes on stale LDS.
+    static_assert((TM * KT) % (kThreads * 16) == 0, "A tile must split into whole 16-byte loads");
+    static_assert(kCH % kStepCh == 0, "k-tile must hold whole MFMA steps");
+    static_assert(kCH <= 4, "B block offsets must fit the 12-bit immediate");
+};
+
 }  // namespace dgp

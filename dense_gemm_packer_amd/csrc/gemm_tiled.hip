@@ -1,6 +1,7 @@
 // Large-M GEMM kernels for C = A * B^T with B preshuffled (include/dgp.h):
-// the tiled family -- the interleaved gemm_tiled_kernel, the ping-pong and
-// both-in-LDS schedules of the 256 x 256 tile -- and their table entries.
+// the interleaved gemm_tiled_kernel and the ping-pong schedule of the
+// 256 x 256 tile, and their table entries (the both-in-LDS schedule:
+// gemm_lds.hip).
 // Operand layout and epilogue: gemm_common.h.
 //
 // gemm_tiled_kernel -- large M (the compute-bound path of FlyDSL PR #1008,
@@ -19,28 +20,6 @@ namespace dgp {
 
 // ================================================================ tiled
 
-template <int DT, int TM, int TN, int WM, int WN, int KT>
-struct TiledShape {
-    static constexpr int kWaves = WM * WN;
-    static constexpr int kThreads = kWaves * 64;
-    static constexpr int kMT = TM / WM / 16;             // 16-row tiles per wave
-    static constexpr int kNT = TN / WN / 16;             // 16-column strips per wave
-    static constexpr int kCH = KT / 64;                  // 64-byte K chunks per k-tile
-    static constexpr int kStepCh = Op<DT>::kBlocks;
-    static constexpr int kSteps = kCH / kStepCh;         // MFMA k-steps per k-tile
-    static constexpr int kABlocks = (TM / 16) * kCH;     // 1 KiB A blocks per k-tile
-    static constexpr int kDmaPerWave = kABlocks / kWaves;
-    static constexpr int kBufBytes = TM * KT;
-    static constexpr int kBLoads = kNT * kCH;            // B loads per wave per k-tile
-    static_assert(TM % (16 * WM) == 0 && TN % (16 * WN) == 0, "tile must split into 16x16 wave tiles");
-    // The A-tile granularity rule of FlyDSL PR #974's follow-up commit (item 1):
-    // the tile must split into whole 16-byte loads per thread, i.e.
-    // TM*KT % (threads*16) == 0 -- with fewer loads the tail of the tile is
-    // never fetched and the kernel computes on stale LDS.
-    static_assert((TM * KT) % (kThreads * 16) == 0, "A tile must split into whole 16-byte loads");
-    static_assert(kCH % kStepCh == 0, "k-tile must hold whole MFMA steps");
-    static_assert(kCH <= 4, "B block offsets must fit the 12-bit immediate");
-};
 
 template <int DT, int TM, int TN, int WM, int WN, int KT, int DEPTH, int SCALE, int OUT, int PV, int PD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
@@ -238,145 +217,6 @@ gemm_tiled_kernel(const GemmArgs p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: scale once, round once.
-#pragma unroll
-    for (int mt = 0; mt < S::kMT; ++mt) {
-        const int m = m0 + (wm * S::kMT + mt) * 16 + (lane & 15);
-#pragma unroll
-        for (int nt = 0; nt < S::kNT; ++nt) {
-            const int n = n0 + (wn * S::kNT + nt) * 16 + (lane >> 4) * 4;
-            f32x4 v = acc[mt][nt];
-            if constexpr (SCALE == kScaleTensor)
-                v = v * scale;
-            store_tile<OUT>(p, split, m, n, v);
-        }
-    }
-}
-
-// ============================================================ both in LDS
-
-// gemm_lds_kernel -- large M with both operands staged in LDS.  Per 128-byte
-// k-tile the A tile (TM rows) and the preshuffled B tile (TN/16 strips) go
-// global -> LDS with the async buffer load, into a two-stage ring; the waves
-// (WM x WN, each owning TM/WM rows x TN/WN columns) read their A and B
-// fragments from LDS.  The preshuffled B needs no swizzle in LDS: a 1 KiB
-// block of Bs is copied as-is (one fully coalesced load per wave) and is
-// already in operand order, so the B reads are as conflict-free as the A
-// reads.  Against gemm_tiled_kernel this moves the B stream off the VGPR
-// return path: all global traffic is LDS-bound copies, and one B fragment
-// feeds TM/WM/16 MFMAs instead of one wave's private column strip.
-//
-// Step t: every wave waits for its copies of tile t (the only loads in
-// flight), the barrier makes tile t visible to all waves and certifies that
-// tile t-1's stage is no longer read, the copies of tile t+1 go into that
-// stage, and the MFMAs of tile t run.  All of a k-tile's B fragments are
-// read first, then the A fragments PD ahead of the MFMAs that use them.
-template <int DT, int TM, int TN, int WM, int WN, int SCALE, int OUT, int PD>
-__global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
-                               amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
-gemm_lds_kernel(const GemmArgs p)
-{
-    constexpr int KT = 128;
-    using S = TiledShape<DT, TM, TN, WM, WN, KT>;
-    using Frag = typename Op<DT>::Frag;
-    constexpr int kABytes = TM * KT, kBBytes = TN * KT, kStage = kABytes + kBBytes;
-    constexpr int kBBlocks = (TN / 16) * S::kCH;
-    constexpr int kBDmaPerWave = kBBlocks / S::kWaves;
-    static_assert(kBBlocks % S::kWaves == 0, "B tile must split into whole copies per wave");
-    static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-
-    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
-    const int m0 = (int)tc.tm * TM;
-    const int n0 = (int)tc.tn * TN;
-    const int split = (int)tc.s;
-    const uint32_t Kb = (uint32_t)p.Kb;
-    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
-    const int ntiles = p.Ks / KT;
-
-    // A copies: instruction j fills A block j*waves + wave = (row group, chunk),
-    // as in gemm_tiled_kernel.  Rows >= M load as zero.
-    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
-    uint32_t a_voff[S::kDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < S::kDmaPerWave; ++j) {
-        const int blk = j * S::kWaves + wave;
-        a_voff[j] = (uint32_t)((blk / S::kCH) * 16 + (lane & 15)) * Kb +
-                    (uint32_t)((blk % S::kCH) * 64 + (lane >> 4) * 16);
-    }
-    // B copies: instruction j copies B block j*waves + wave = (strip sb of the
-    // tile, chunk ch) of Bs unchanged; strips >= N/16 load as zero.
-    const int strip0 = n0 / 16;
-    const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb,
-                              clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
-    uint32_t b_voff[kBDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kBDmaPerWave; ++j) {
-        const int blk = j * S::kWaves + wave;
-        b_voff[j] = (uint32_t)(blk / S::kCH) * 16u * Kb + (uint32_t)(blk % S::kCH) * 1024u + (uint32_t)lane * 16u;
-    }
-
-    float scale = 1.0f;
-    if constexpr (SCALE == kScaleTensor)
-        scale = p.sA[0] * p.sB[0];
-
-    f32x4 acc[S::kMT][S::kNT];
-#pragma unroll
-    for (int i = 0; i < S::kMT; ++i)
-#pragma unroll
-        for (int j = 0; j < S::kNT; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto copy_tile = [&](uint32_t stage_off, int t) {
-        const uint32_t koff = kbase + (uint32_t)t * KT;
-#pragma unroll
-        for (int j = 0; j < S::kDmaPerWave; ++j)
-            lds_dma16(rA, lds + stage_off + (j * S::kWaves + wave) * 1024, a_voff[j], koff);
-#pragma unroll
-        for (int j = 0; j < kBDmaPerWave; ++j)
-            lds_dma16(rB, lds + stage_off + kABytes + (j * S::kWaves + wave) * 1024, b_voff[j], koff * 16u);
-    };
-
-    copy_tile(0, 0);
-    constexpr int kFr = S::kSteps * S::kMT;
-    constexpr int kRA = PD < kFr ? PD : kFr;
-    for (int t = 0; t < ntiles; ++t) {
-        const uint32_t cur = (uint32_t)(t & 1) * kStage;
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (t + 1 < ntiles)
-            copy_tile(kStage - cur, t + 1);
-        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
-        const uint8_t *bbase = lds + cur + kABytes + (wn * S::kNT * S::kCH) * 1024 + lane * 16;
-        Frag bfr[S::kSteps][S::kNT];
-#pragma unroll
-        for (int st = 0; st < S::kSteps; ++st)
-#pragma unroll
-            for (int nt = 0; nt < S::kNT; ++nt)
-                bfr[st][nt] = lds_frag<DT>(bbase + (nt * S::kCH + st * S::kStepCh) * 1024);
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-            const int st = f / S::kMT, mt = f % S::kMT;
-            const Frag a = lds_frag<DT>(abase + (mt * S::kCH + st * S::kStepCh) * 1024);
-#pragma unroll
-            for (int nt = 0; nt < S::kNT; ++nt)
-                acc[mt][nt] = mfma_op(bfr[st][nt], a, acc[mt][nt]);
-        }
-        // B fragments and the first kRA A fragments, then per A fragment its
-        // MFMAs and the read of the fragment kRA places ahead.
-        constexpr int kRd = S::kStepCh;
-        __builtin_amdgcn_sched_group_barrier(0x100, (S::kSteps * S::kNT + kRA) * kRd, 0);
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-            __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
-            if (f + kRA < kFr)
-                __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
 #pragma unroll
     for (int mt = 0; mt < S::kMT; ++mt) {
         const int m = m0 + (wm * S::kMT + mt) * 16 + (lane & 15);
@@ -592,12 +432,6 @@ void launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_tiled_kernel<DT, TM, TN, WM, WN, KT, DEPTH, SCALE, OUT, PV, PD><<<grid, WM * WN * 64, 0, s>>>(a);
 }
 
-template <int DT, int TM, int TN, int WM, int WN, int SCALE, int OUT, int PD>
-void launch_lds(const GemmArgs &a, dim3 grid, hipStream_t s)
-{
-    gemm_lds_kernel<DT, TM, TN, WM, WN, SCALE, OUT, PD><<<grid, WM * WN * 64, 0, s>>>(a);
-}
-
 template <int DT, int SCALE, int OUT>
 void launch_pingpong(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
@@ -610,11 +444,6 @@ void launch_pingpong(const GemmArgs &a, dim3 grid, hipStream_t s)
 #define DGP_PINGPONG(DT, SC, OUT)                                                             \
     {kTiled, DT, SC, OUT, 256, 256, 128, 8, 1, 8, 0, 0, 2, kSchedPingPong,                     \
      &launch_pingpong<DT, SC, OUT>}
-#define DGP_LDS(DT, TM, TN, WM, WN, SC, OUT, PD)                                              \
-    {kTiled, DT, SC, OUT, TM, TN, 128, WM * WN, WM, WN, 0, PD, 1, kSchedBothLds,               \
-     &launch_lds<DT, TM, TN, WM, WN, SC, OUT, PD>}
-#define DGP_LDS_BOTH_OUT(DT, TM, TN, WM, WN, SC, PD)                                          \
-    DGP_LDS(DT, TM, TN, WM, WN, SC, kOutBf16, PD), DGP_LDS(DT, TM, TN, WM, WN, SC, kOutPartial, PD)
 #define DGP_TILED_BOTH_OUT(DT, TM, TN, WM, WN, KT, DEPTH, SC, PV, PD)                         \
     DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutBf16, PV, PD),                           \
         DGP_TILED(DT, TM, TN, WM, WN, KT, DEPTH, SC, kOutPartial, PV, PD)
@@ -625,14 +454,12 @@ static const KernelSpec kTiledKernels[] = {
     // within one tile the first entry is the tuned default
     DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 1, 8, 128, 2, kScaleNone, 0, 8),
     DGP_PINGPONG_BOTH_OUT(kDtypeBf16, kScaleNone),
-    DGP_LDS_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, kScaleNone, 4),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 256, 256, 2, 4, 128, 2, kScaleNone, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 256, 1, 4, 128, 2, kScaleNone, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeBf16, 128, 128, 2, 2, 128, 2, kScaleNone, 0, 4),
     // large tiles, fp8 per-tensor
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleTensor, 0, 8),
     DGP_PINGPONG_BOTH_OUT(kDtypeFp8, kScaleTensor),
-    DGP_LDS_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, kScaleTensor, 4),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 1, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleTensor, 0, 4),

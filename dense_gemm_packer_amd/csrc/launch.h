@@ -46,10 +46,12 @@ struct KernelSpec {
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
 };
 
-// The compiled GEMM kernels: the tiled family (gemm_tiled.hip), the
-// streaming family (gemm_stream.hip), and both in one table, tiled first
+// The compiled GEMM kernels: the tiled family (gemm_tiled.hip), its
+// both-in-LDS schedule (gemm_lds.hip), the streaming family
+// (gemm_stream.hip), and all of them in one table in that order
 // (dgp_api.cpp) -- the numbering dgp_kernel_info uses.
 const KernelSpec *tiled_kernels(int *count);
+const KernelSpec *lds_kernels(int *count);
 const KernelSpec *stream_kernels(int *count);
 const KernelSpec *kernel_table(int *count);
 
