@@ -252,6 +252,9 @@ def describe_kernel(index: int) -> str:
     """One-line description of compiled kernel `index`."""
     cfg, dt, sm, so = kernels()[index]
     dts = "bf16" if dt == BF16 else "fp8"
+    if cfg.tile_m == 16 and cfg.tile_n == 16:
+        return (f"gemm_ksplit_kernel<{dts}, 16x16 tile, K split over {cfg.waves_m} waves, "
+                f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
     if cfg.tile_m == 16:
         return (f"gemm_stream_kernel<{dts}, 16x{cfg.tile_n} tile, {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")

@@ -134,10 +134,16 @@ const KernelSpec *find_spec(const Query &q)
 }
 
 // Built-in per-shape choice.
-const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks)
+const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    if (scale == DGP_SCALE_BLOCK128 || M <= 32)
+    if (scale == DGP_SCALE_BLOCK128 || M <= 32) {
+        // Narrow weights: when the 64-column streaming tile would give fewer
+        // than 128 workgroups, one strip per workgroup with K split over its
+        // waves spreads the stream wider (measured faster up to that point).
+        if (N * split_k < 128 * 64)
+            return find_spec(Query{kStream, dtype, scale, out, 16, 16});
         return find_spec(Query{kStream, dtype, scale, out, 16, 64});
+    }
     const KernelSpec *k = nullptr;
     if (M >= 1024 && N >= 1024) {
         Query q{kTiled, dtype, scale, out, 256, 256};
@@ -210,7 +216,7 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
             return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
                         spec->kt, (long long)Ks);
     } else {
-        spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks);
+        spec = default_spec(c.dtype, c.scale, out, c.M, c.N, Ks, c.split_k);
         if (!spec)
             return fail(DGP_ERR_CONFIG, "no compiled kernel fits this shape");
     }

@@ -171,6 +171,116 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     }
 }
 
+// gemm_ksplit_kernel -- decode-sized M over few columns.  A workgroup owns a
+// 16-row x 16-column tile of C (one strip of Bs) and divides its K range into
+// NW contiguous slices of whole MFMA steps, one per wave, so a narrow weight
+// still spreads over many waves without a second pass: N = 2048 gives 128
+// workgroups of NW waves where the 64-column streaming tile gives 32.  Each
+// wave streams its slice of A and B straight into registers through a ring
+// of DEPTH MFMA steps of in-flight loads (A rows >= M and the B strip past N
+// load as zero), then the NW partial tiles are added in LDS in wave order --
+// a fixed order, so results are reproducible -- and wave 0 runs the epilogue.
+// Blockscale: one fp8 MFMA step is exactly one 128-wide K block, scaled as in
+// gemm_stream_kernel with the scales read straight from global memory.
+template <int DT, int NW, int DEPTH, int SCALE, int OUT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+gemm_ksplit_kernel(const GemmArgs p)
+{
+    using Frag = typename Op<DT>::Frag;
+    constexpr int kStepCh = Op<DT>::kBlocks;
+    constexpr int kStepBytes = 64 * kStepCh;
+    __shared__ f32x4 red[NW][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
+    const int m0 = (int)tc.tm * 16;
+    const int strip = (int)tc.tn;
+    const int split = (int)tc.s;
+    const uint32_t Kb = (uint32_t)p.Kb;
+    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
+    const int nsteps = p.Ks / kStepBytes;
+    // This wave's steps [s0, s1): the first nsteps % NW waves take one more.
+    const int per = nsteps / NW, extra = nsteps % NW;
+    const int s0 = wave * per + (wave < extra ? wave : extra);
+    const int s1 = s0 + per + (wave < extra ? 1 : 0);
+    const int kblocks_row = p.K / 128;   // blockscale: scale columns per row
+
+    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
+    const auto rB = make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip) * 16 * Kb));
+    const uint32_t b_voff = (uint32_t)lane * 16u;
+    const int m = m0 + (lane & 15);
+    const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? p.sA + (int64_t)m * kblocks_row : nullptr;
+    const float *sb_row = SCALE == kScaleBlock ? p.sB + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    i32x4 areg[DEPTH][kStepCh], breg[DEPTH][kStepCh];
+    // Step st of the split: K bytes kbase + st*kStepBytes; A chunk cc of it is
+    // one 16-row x 64-byte operand read, B chunk cc one 1 KiB block of the strip.
+    auto load_step = [&](int d, int st) {
+        const uint32_t k = kbase + (uint32_t)st * kStepBytes;
+#pragma unroll
+        for (int cc = 0; cc < kStepCh; ++cc) {
+            areg[d][cc] = load16<kAuxNone>(rA, a_voff + k + cc * 64u);
+            breg[d][cc] = load16<kAuxNonTemporal>(rB, b_voff + k * 16u + cc * 1024u);
+        }
+    };
+    // Clamp target of the ring: the slice's last step, or for an empty slice
+    // (nsteps < NW) the split's last step -- loaded, never used.
+    const int last = (s1 > s0 ? s1 : nsteps) - 1;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        load_step(d, s0 + d < s1 ? s0 + d : last);
+    for (int st0 = s0; st0 < s1; st0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int st = st0 + d;
+            if (st < s1) {
+                Frag a, b;
+                if constexpr (DT == kDtypeBf16) {
+                    a = areg[d][0];
+                    b = breg[d][0];
+                } else {
+                    a = cat(areg[d][0], areg[d][1]);
+                    b = cat(breg[d][0], breg[d][1]);
+                }
+                if constexpr (SCALE == kScaleBlock) {
+                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
+                    const float sa = sa_row ? sa_row[kb] : 0.f;
+                    const float sc = __fmul_rn(sa, sb_row[kb]);
+                    const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
+                    acc.x = __fadd_rn(acc.x, __fmul_rn(part.x, sc));
+                    acc.y = __fadd_rn(acc.y, __fmul_rn(part.y, sc));
+                    acc.z = __fadd_rn(acc.z, __fmul_rn(part.z, sc));
+                    acc.w = __fadd_rn(acc.w, __fmul_rn(part.w, sc));
+                } else {
+                    acc = mfma_op(b, a, acc);
+                }
+                load_step(d, st + DEPTH < s1 ? st + DEPTH : last);
+            }
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const f32x4 u = red[w][lane];
+            v.x = __fadd_rn(v.x, u.x);
+            v.y = __fadd_rn(v.y, u.y);
+            v.z = __fadd_rn(v.z, u.z);
+            v.w = __fadd_rn(v.w, u.w);
+        }
+        if constexpr (SCALE == kScaleTensor)
+            v = v * (p.sA[0] * p.sB[0]);
+        store_tile<OUT>(p, split, m, strip * 16 + (lane >> 4) * 4, v);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
 void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
@@ -194,6 +304,16 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
 }
 
+template <int DT, int NW, int DEPTH, int SCALE, int OUT>
+void launch_ksplit(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    gemm_ksplit_kernel<DT, NW, DEPTH, SCALE, OUT><<<grid, NW * 64, 0, s>>>(a);
+}
+
+#define DGP_KSPLIT(DT, NW, DEPTH, SC, OUT)                                                    \
+    {kStream, DT, SC, OUT, 16, 16, 0, NW, 1, DEPTH, 0, 0, DEPTH, 0, &launch_ksplit<DT, NW, DEPTH, SC, OUT>}
+#define DGP_KSPLIT_BOTH_OUT(DT, NW, DEPTH, SC)                                                \
+    DGP_KSPLIT(DT, NW, DEPTH, SC, kOutBf16), DGP_KSPLIT(DT, NW, DEPTH, SC, kOutPartial)
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
     {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
      &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
@@ -207,6 +327,10 @@ static const KernelSpec kStreamKernels[] = {
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 2, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
+    // one strip per workgroup, K split over the waves: waves, ring depth
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock),
 };
 
 const KernelSpec *stream_kernels(int *count)

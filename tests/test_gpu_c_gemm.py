@@ -118,12 +118,14 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
+@pytest.mark.parametrize("tile_n", [64, 16])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
-def test_stream_splitk(dtype, mode, M, split_k):
+def test_stream_splitk(dtype, mode, M, split_k, tile_n):
+    """Decode kernels: the 16x64 streaming tile and the 16x16 K-split tile."""
     N, K = 384, 2048
-    cfg = dgp.Config(16, 64, 0, 0, 1, 0, 0)
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
     A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 3)
     got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
     _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
@@ -132,6 +134,25 @@ def test_stream_splitk(dtype, mode, M, split_k):
     got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
     c32, _ = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
     assert_close(got, c32)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
+def test_ksplit_uneven_and_empty_slices(dtype, mode):
+    """K-split kernel: step counts not divisible by the 8 waves and fewer
+    steps than waves (some waves own no K), with splits.  (bf16 steps are 64
+    bytes and K rows must be whole 128 bytes, so its counts are even.)"""
+    cfg = dgp.Config(16, 16, 0, 0, 1, 0, 0)
+    step = 32 if dtype == "bf16" else 128    # K elements per MFMA step
+    cases = (((18, 1), (26, 1), (2, 1), (6, 1), (36, 2), (20, 2)) if dtype == "bf16" else
+             ((9, 1), (13, 1), (1, 1), (3, 1), (5, 1), (18, 2), (10, 2)))
+    for steps, split in cases:
+        K = steps * step
+        if mode == "block128" and (K // split) % 128:
+            continue
+        A, B, sA, sB = exact_inputs(dtype, mode, 5, 256, K, 31)
+        got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
+        _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
+        assert np.array_equal(got, c16), (steps, split)
 
 
 def test_stream_multi_panel():

@@ -218,7 +218,11 @@ def test_default_selection(dgp):
     for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
         cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
         assert (cfg.tile_m, cfg.tile_n) == (256, 256)
-        assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dt, sm, 4)][0].tile_m == 16
+        assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dt, sm, 4)][0].tile_n == 64
+        # narrow weights: one strip per workgroup, K split over its waves
+        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 1)][0].tile_n == 16
+        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
+        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 64
     assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)][0].tile_m == 16
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
