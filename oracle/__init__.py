@@ -19,6 +19,7 @@ FP8_E4M3 = 1
 SCALE_NONE = 0
 SCALE_TENSOR = 1
 SCALE_BLOCK128 = 2
+SCALE_MX128 = 3
 
 _lib = None
 
@@ -34,6 +35,8 @@ def lib():
         L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
         L.oracle_e4m3_decode.restype = ctypes.c_float
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_decode.restype = ctypes.c_float
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
         L.oracle_bf16_round.restype = ctypes.c_uint16
         L.oracle_bf16_round.argtypes = [ctypes.c_float]
         for name in ("oracle_preshuffle_b", "oracle_unshuffle_b"):
@@ -65,6 +68,10 @@ def bf16_decode(h):
 
 def e4m3_decode(b):
     return lib().oracle_e4m3_decode(int(b))
+
+
+def e8m0_decode(e):
+    return lib().oracle_e8m0_decode(int(e))
 
 
 def bf16_round(f):
@@ -109,6 +116,9 @@ def gemm(A, B, dtype, scale_mode=SCALE_NONE, sA=None, sB=None, split_k=1, rows=N
          want_partials=False, nthreads=0):
     """C = A * B^T on unshuffled B.
 
+    Scales: per-tensor and blockscale take fp32 arrays; mxfp8 (SCALE_MX128)
+    takes E8M0 bytes, sA [M][K/128] and sB [N][K/128].
+
     Returns (c_f32, c_bf16[, partials]): the fp32 value before rounding, the
     bf16 bit patterns, and (optionally) the per-split fp32 partials
     [split_k][nrows][N].  ``rows`` selects rows of C (default: all).
@@ -118,8 +128,9 @@ def gemm(A, B, dtype, scale_mode=SCALE_NONE, sA=None, sB=None, split_k=1, rows=N
     M, K = A.shape
     N = B.shape[0]
     assert B.shape[1] == K
-    sA_ = None if sA is None else np.ascontiguousarray(np.asarray(sA, dtype=np.float32))
-    sB_ = None if sB is None else np.ascontiguousarray(np.asarray(sB, dtype=np.float32))
+    sdt = np.uint8 if scale_mode == SCALE_MX128 else np.float32   # E8M0 bytes or fp32 scales
+    sA_ = None if sA is None else np.ascontiguousarray(np.asarray(sA, dtype=sdt))
+    sB_ = None if sB is None else np.ascontiguousarray(np.asarray(sB, dtype=sdt))
     rows_ = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     nrows = M if rows_ is None else rows_.size
     c32 = np.empty((nrows, N), dtype=np.float32)

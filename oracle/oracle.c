@@ -17,7 +17,9 @@
  *  - Scale modes (aiter PR #5148, "Summary" / "What's included"): none (bf16),
  *    FP8 per-tensor (one fp32 scale each for A and B), FP8 blockscale (A per
  *    row per 128-wide K block, B per 128x128 block; shapes [M][K/128] and
- *    [N/128][K/128] from the run_torch_blockscale review comment).
+ *    [N/128][K/128] from the run_torch_blockscale review comment), and the MX
+ *    mode mxfp8 (same PR, "What's included": 128-element blocks with one E8M0
+ *    scale each, applied by the hardware-scaled matrix instruction).
  *  - Split-K (aiter PR #5148, "What's included" and the file table): each of
  *    split_k K-chunks produces fp32 partials in a workspace and a second pass
  *    reduces them in fp32, rounding to the output type once.
@@ -34,6 +36,12 @@
  *    fp32 sum.
  *  - split s covers K range [s*K/S, (s+1)*K/S); partials carry the scales; the
  *    reduce adds P_0 + P_1 + ... + P_{S-1} in that order.
+ *  - mxfp8: an E8M0 byte e means 2^(e-127) (e = 255: NaN), as in the OCP
+ *    microscaling format; A has one scale per row per 128-K block ([M][K/128]
+ *    bytes) and B one per row of B, i.e. per output column, per 128-K block
+ *    ([N][K/128] bytes), both row-major.  As for blockscale, each block's
+ *    fp32 partial sum p is scaled and added: acc += p * 2^(eA-127) * 2^(eB-127),
+ *    the power of two applied exactly (ldexpf).
  *
  * Build: plain C11, -O2 -ffp-contract=off, no fast-math (so that every fp32
  * multiply and add rounds separately, in the order written here).
@@ -46,7 +54,7 @@
 #include <unistd.h>
 
 enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1 };
-enum { ORC_SCALE_NONE = 0, ORC_SCALE_TENSOR = 1, ORC_SCALE_BLOCK128 = 2 };
+enum { ORC_SCALE_NONE = 0, ORC_SCALE_TENSOR = 1, ORC_SCALE_BLOCK128 = 2, ORC_SCALE_MX128 = 3 };
 
 /* ---------------------------------------------------------------- decode */
 
@@ -78,6 +86,15 @@ float oracle_e4m3_decode(uint8_t b)
 }
 
 /* ------------------------------------------------------------ fp32 -> bf16 */
+
+/* E8M0 scale byte (OCP microscaling): 2^(e-127); e = 255 encodes NaN.  The
+ * smallest, 2^-127, is an fp32 subnormal and exact. */
+float oracle_e8m0_decode(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexpf(1.0f, (int)e - 127);
+}
 
 /* Round to nearest, ties to even, on the bit pattern: add 0x7FFF plus the
  * lowest kept bit, then truncate.  Overflow carries into the exponent and
@@ -145,7 +162,8 @@ typedef struct {
     const float *b;      /* decoded B, [N][K] (unshuffled) */
     int64_t M, N, K;
     int scale_mode;
-    const float *sA, *sB;
+    const float *sA, *sB;      /* per-tensor and blockscale scales */
+    const uint8_t *eA, *eB;    /* mxfp8 E8M0 scales */
     int split_k;
     const int64_t *rows; /* rows of C to compute; NULL = 0..nrows-1 */
     int64_t nrows;
@@ -161,6 +179,22 @@ static float partial_sum(const gemm_job *j, int64_t m, int64_t n, int64_t k0, in
 {
     const float *arow = j->a + m * j->K;
     const float *brow = j->b + n * j->K;
+    if (j->scale_mode == ORC_SCALE_MX128) {
+        int64_t kblocks = j->K / 128;
+        float acc = 0.0f;
+        for (int64_t kb = k0 / 128; kb < k1 / 128; ++kb) {
+            float p = 0.0f;
+            for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+                p += arow[k] * brow[k];
+            uint8_t ea = j->eA[m * kblocks + kb], eb = j->eB[n * kblocks + kb];
+            if (ea == 255 || eb == 255)
+                p = NAN;
+            else
+                p = ldexpf(p, ((int)ea - 127) + ((int)eb - 127));
+            acc += p;
+        }
+        return acc;
+    }
     if (j->scale_mode == ORC_SCALE_BLOCK128) {
         int64_t kblocks = j->K / 128;
         float acc = 0.0f;
@@ -226,12 +260,14 @@ static float *decode_all(const void *src, int64_t count, int dtype)
 
 /*
  * Compute rows of C.  A is [M][K] and B is [N][K] (unshuffled), both of
- * element type dtype (bf16 bit patterns or e4m3 codes).  rows lists which rows
+ * element type dtype (bf16 bit patterns or e4m3 codes).  sA, sB: fp32 scales
+ * (per-tensor, blockscale) or E8M0 bytes (mxfp8), unused for scale mode none.
+ * rows lists which rows
  * of C to produce (NULL: all M rows, nrows must equal M).  Outputs are indexed
  * by position in rows.  Returns 0, or -1 on an invalid argument.
  */
 int oracle_gemm_rows(const void *A, const void *B, int64_t M, int64_t N, int64_t K,
-                     int dtype, int scale_mode, const float *sA, const float *sB,
+                     int dtype, int scale_mode, const void *sA, const void *sB,
                      int split_k, const int64_t *rows, int64_t nrows,
                      float *out_f32, uint16_t *out_bf16, float *partials, int nthreads)
 {
@@ -239,7 +275,9 @@ int oracle_gemm_rows(const void *A, const void *B, int64_t M, int64_t N, int64_t
         return -1;
     if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3)
         return -1;
-    if (scale_mode < ORC_SCALE_NONE || scale_mode > ORC_SCALE_BLOCK128)
+    if (scale_mode < ORC_SCALE_NONE || scale_mode > ORC_SCALE_MX128)
+        return -1;
+    if (scale_mode == ORC_SCALE_MX128 && (dtype != ORC_FP8_E4M3 || K % 128 != 0 || (K / split_k) % 128 != 0))
         return -1;
     if (scale_mode != ORC_SCALE_NONE && (!sA || !sB))
         return -1;
@@ -268,7 +306,9 @@ int oracle_gemm_rows(const void *A, const void *B, int64_t M, int64_t N, int64_t
     if (nthreads > nrows)
         nthreads = nrows > 0 ? (int)nrows : 1;
 
-    gemm_job base = {a, b, M, N, K, scale_mode, sA, sB, split_k, rows, nrows,
+    const int mx = scale_mode == ORC_SCALE_MX128;
+    gemm_job base = {a, b, M, N, K, scale_mode, mx ? NULL : (const float *)sA, mx ? NULL : (const float *)sB,
+                     mx ? (const uint8_t *)sA : NULL, mx ? (const uint8_t *)sB : NULL, split_k, rows, nrows,
                      out_f32, out_bf16, partials, 0, 0};
     gemm_job *jobs = (gemm_job *)malloc(sizeof(gemm_job) * (size_t)nthreads);
     pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);

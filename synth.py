@@ -31,6 +31,7 @@ CFG_BF16_LARGE = 1
 CFG_FP8_LARGE = 2
 CFG_FP8_DECODE = 3
 CFG_FP8_BLOCKSCALE = 4
+CFG_FP8_MX128 = 5         # microscaling (mxfp8) decode, the first adjacent workload
 
 WORKLOADS = {
     "bf16_small": dict(cfg=CFG_BF16_SMALL, dtype="bf16", M=128, N=256, K=256),
@@ -40,6 +41,7 @@ WORKLOADS = {
                        splits=(1, 2, 4, 8)),
     "fp8_blockscale": dict(cfg=CFG_FP8_BLOCKSCALE, dtype="fp8", M=16, N=16384, K=7168,
                            splits=(1, 2, 4, 8)),
+    "fp8_mx128": dict(cfg=CFG_FP8_MX128, dtype="fp8", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
 }
 
 
@@ -119,6 +121,30 @@ def fp8_blockscale_b(N, K, seed_data, seed_scale):
     return codes, s
 
 
+def fp8_mx128(R, K, seed_data, seed_mag):
+    """Rows [R][K] in the microscaling format with 128-element blocks: codes
+    (e4m3) and one E8M0 byte per row per block ([R][K/128] uint8).
+
+    Data: N(0,1) times a per-block magnitude 2^u, u uniform in {-4..4}, so the
+    block scales differ.  Scale rule of the OCP microscaling format: shared
+    exponent floor(log2(amax)) - 8 (8 = largest e4m3 exponent), stored biased
+    by 127; elements x / 2^(shared exponent), saturated to +-448."""
+    kb = K // 128
+    x = rng(seed_data).standard_normal(size=(R, kb, 128)).astype(np.float32)
+    x *= np.exp2(rng(seed_mag).integers(-4, 5, size=(R, kb, 1))).astype(np.float32)
+    amax = np.abs(x).max(axis=2)
+    shared = np.floor(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64) - 8
+    e = np.clip(shared + 127, 0, 254).astype(np.uint8)
+    scale = np.exp2(e.astype(np.float64) - 127).astype(np.float32)
+    codes = quantise_e4m3(x, scale[:, :, None]).reshape(R, K)
+    return codes, e
+
+
+def exact_e8m0_scales(shape, seed) -> np.ndarray:
+    """E8M0 bytes from {126, 127, 128} (scales 0.5, 1, 2): exact in every product."""
+    return rng(seed).choice(np.array([126, 127, 128], dtype=np.uint8), size=shape)
+
+
 def exact_ints(shape, seed, dtype: str, lo=-4, hi=4) -> np.ndarray:
     """Uniform integers in [lo, hi], stored exactly as bf16 bits or e4m3 codes.
 
@@ -136,7 +162,8 @@ def exact_block_scales(shape, seed) -> np.ndarray:
 def workload_inputs(name: str, M=None, N=None, K=None):
     """Inputs of a named workload: dict(A, B, sA, sB, dtype, scale_mode, M, N, K).
 
-    ``dtype`` is "bf16" or "fp8"; ``scale_mode`` is "none", "tensor" or "block128".
+    ``dtype`` is "bf16" or "fp8"; ``scale_mode`` is "none", "tensor", "block128"
+    or "mx128" (E8M0 byte scales, sA [M][K/128], sB [N][K/128]).
     M/N/K override the workload's sizes (used for the decode family)."""
     w = WORKLOADS[name]
     cfg = w["cfg"]
@@ -159,4 +186,8 @@ def workload_inputs(name: str, M=None, N=None, K=None):
         A, sA = fp8_blockscale_a(M, K, sa, ss)
         B, sB = fp8_blockscale_b(N, K, sb, ss + 500)
         return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp8", scale_mode="block128", M=M, N=N, K=K)
+    if name == "fp8_mx128":
+        A, sA = fp8_mx128(M, K, sa, ss)
+        B, sB = fp8_mx128(N, K, sb, ss + 500)
+        return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp8", scale_mode="mx128", M=M, N=N, K=K)
     raise KeyError(name)

@@ -273,3 +273,119 @@ def test_invalid_arguments_rejected(orc):
         orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR)   # scales missing
     with pytest.raises(ValueError):
         orc.gemm(A, B, orc.FP8_E4M3, rows=[4])           # row out of range
+
+
+# ---------------------------------------------------- mxfp8 (E8M0, 128-K blocks)
+
+def test_e8m0_decode_exhaustive(orc):
+    """Every E8M0 byte against its definition, 2^(e-127) with e = 255 NaN,
+    computed with Python's exact ldexp."""
+    import math
+    for e in range(256):
+        got = orc.e8m0_decode(e)
+        if e == 255:
+            assert math.isnan(got)
+        else:
+            assert got == math.ldexp(1.0, e - 127), e
+
+
+def _mx_scale(e):
+    return np.exp2(e.astype(np.float64) - 127)
+
+
+def test_mx128_against_fp64(orc):
+    """Random microscaled data: within the recursive-summation bound of the
+    fp64 blockwise result sum_kb (A_kb . B_kb) * 2^(eA-127) * 2^(eB-127), and
+    pairing the blocks with another block's scales lands outside it."""
+    M, N, K = 6, 48, 640
+    A, eA = synth.fp8_mx128(M, K, 141, 142)
+    B, eB = synth.fp8_mx128(N, K, 143, 144)
+    assert len(np.unique(eA)) > 3 and len(np.unique(eB)) > 3   # the scales do vary
+    a, b = dec_torch(A, "fp8"), dec_torch(B, "fp8")
+    KB = K // 128
+    c64, mag, alt = np.zeros((M, N)), np.zeros((M, N)), np.zeros((M, N))
+    for kb in range(KB):
+        sl = slice(kb * 128, kb * 128 + 128)
+        sc = _mx_scale(eA[:, kb])[:, None] * _mx_scale(eB[:, kb])[None, :]
+        c64 += (a[:, sl] @ b[:, sl].T) * sc
+        mag += (np.abs(a[:, sl]) @ np.abs(b[:, sl]).T) * sc
+        wk = KB - 1 - kb
+        alt += (a[:, sl] @ b[:, sl].T) * (_mx_scale(eA[:, wk])[:, None] * _mx_scale(eB[:, wk])[None, :])
+    bound = (gamma(K + KB) + U) * mag
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB)
+    assert np.all(np.abs(c32 - c64) <= bound + 1e-30)
+    assert np.max(np.abs(alt - c64) - bound) > 0
+
+
+def test_mx128_exact_against_integer_arithmetic(orc):
+    """Exact-integer data, E8M0 scales in {126,127,128}: exact, and with every
+    scale 127 (1.0) it equals the unscaled product."""
+    M, N, K = 5, 40, 512
+    A = synth.exact_ints((M, K), 151, "fp8")
+    B = synth.exact_ints((N, K), 152, "fp8")
+    eA = synth.exact_e8m0_scales((M, K // 128), 153)
+    eB = synth.exact_e8m0_scales((N, K // 128), 154)
+    a = dec_torch(A, "fp8").astype(np.int64)
+    b = dec_torch(B, "fp8").astype(np.int64)
+    want = np.zeros((M, N))
+    for kb in range(K // 128):
+        sl = slice(kb * 128, kb * 128 + 128)
+        want += (a[:, sl] @ b[:, sl].T) * _mx_scale(eA[:, kb])[:, None] * _mx_scale(eB[:, kb])[None, :]
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB)
+    assert np.array_equal(c32.astype(np.float64), want)
+    ones_a = np.full_like(eA, 127)
+    ones_b = np.full_like(eB, 127)
+    c_mx, h_mx = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, ones_a, ones_b)
+    c_pl, h_pl = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_TENSOR, np.array([1.0]), np.array([1.0]))
+    assert np.array_equal(c_mx, c_pl) and np.array_equal(h_mx, h_pl)
+
+
+def test_mx128_b_scale_is_per_output_column(orc):
+    """B's scales index [n][kb]: doubling one row of B's scales (one output
+    column) doubles exactly that column and nothing else."""
+    M, N, K = 4, 32, 256
+    A = synth.exact_ints((M, K), 161, "fp8")
+    B = synth.exact_ints((N, K), 162, "fp8")
+    eA = np.full((M, K // 128), 127, np.uint8)
+    eB = np.full((N, K // 128), 127, np.uint8)
+    base, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB)
+    eB2 = eB.copy()
+    eB2[7, :] = 128
+    c, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB2)
+    assert np.array_equal(c[:, 7], 2 * base[:, 7])
+    assert np.array_equal(np.delete(c, 7, axis=1), np.delete(base, 7, axis=1))
+
+
+def test_mx128_nan_scale_poisons_its_row(orc):
+    M, N, K = 3, 16, 256
+    A = synth.exact_ints((M, K), 171, "fp8")
+    B = synth.exact_ints((N, K), 172, "fp8")
+    eA = np.full((M, K // 128), 127, np.uint8)
+    eB = np.full((N, K // 128), 127, np.uint8)
+    eA[1, 1] = 255
+    c, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB)
+    assert np.all(np.isnan(c[1])) and np.all(np.isfinite(c[[0, 2]]))
+
+
+def test_mx128_splitk_exact_equals_unsplit(orc):
+    M, N, K = 3, 24, 1024
+    A = synth.exact_ints((M, K), 181, "fp8")
+    B = synth.exact_ints((N, K), 182, "fp8")
+    eA = synth.exact_e8m0_scales((M, K // 128), 183)
+    eB = synth.exact_e8m0_scales((N, K // 128), 184)
+    c1, h1 = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB)
+    for S in (2, 4, 8):
+        cS, hS, parts = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_MX128, eA, eB, split_k=S, want_partials=True)
+        assert np.array_equal(cS, c1) and np.array_equal(hS, h1)
+        assert parts.shape == (S, M, N)
+
+
+def test_mx128_invalid_arguments_rejected(orc):
+    A8 = np.zeros((2, 256), np.uint8)
+    e = np.full((2, 2), 127, np.uint8)
+    with pytest.raises(ValueError):   # bf16 has no MX mode here
+        orc.gemm(np.zeros((2, 256), np.uint16), np.zeros((2, 256), np.uint16), orc.BF16, orc.SCALE_MX128, e, e)
+    with pytest.raises(ValueError):   # K not a whole number of 128-blocks
+        orc.gemm(np.zeros((2, 192), np.uint8), np.zeros((2, 192), np.uint8), orc.FP8_E4M3, orc.SCALE_MX128, e, e)
+    with pytest.raises(ValueError):   # split ranges must be whole blocks
+        orc.gemm(A8, np.zeros((2, 256), np.uint8), orc.FP8_E4M3, orc.SCALE_MX128, e, e, split_k=4)
