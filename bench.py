@@ -298,10 +298,10 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["vendor_library_same_process"] = vend
     del A8, Bs8, C8
 
-    # fp8 split-K decode (per-tensor) and blockscale decode, cold cache.
+    # fp8 split-K decode (per-tensor), blockscale and mxfp8 decode, cold cache.
     dec = {}
-    for mode in ("tensor", "block128"):
-        name = "fp8_decode" if mode == "tensor" else "fp8_blockscale"
+    for mode in ("tensor", "block128", "mx128"):
+        name = {"tensor": "fp8_decode", "block128": "fp8_blockscale", "mx128": "fp8_mx128"}[mode]
         Ms = (1, 16) if mode == "tensor" else (16,)
         Ns = (2048, 16384) if mode == "tensor" else (16384,)
         for n_ in Ns:
@@ -313,7 +313,7 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
             sBt = torch.from_numpy(np.ascontiguousarray(base["sB"])).to(dev)
             for m_ in Ms:
                 A_ = to_dev(base["A"][:m_], "fp8")
-                sAt = torch.from_numpy(np.ascontiguousarray(base["sA"][:m_] if mode == "block128"
+                sAt = torch.from_numpy(np.ascontiguousarray(base["sA"][:m_] if mode != "tensor"
                                                             else base["sA"])).to(dev)
                 best = None
                 for split in (1, 2, 4, 8):
@@ -328,7 +328,8 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                                                    workspace=wss[j] if split > 1 else None)
                     us = graph_time_us(torch, fn, iters)
                     nbytes = m_ * kk + n_ * kk + 2 * m_ * n_
-                    nbytes += 8 if mode == "tensor" else 4 * (m_ * kk // 128 + (n_ // 128) * (kk // 128))
+                    nbytes += {"tensor": 8, "block128": 4 * (m_ * kk // 128 + (n_ // 128) * (kk // 128)),
+                               "mx128": m_ * kk // 128 + n_ * kk // 128}[mode]
                     gbs = nbytes / (us * 1e-6) / 1e9
                     key = f"{mode} M={m_} N={n_} K={kk} split={split}"
                     dec[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),

@@ -24,6 +24,7 @@ FP8_E4M3 = 1
 SCALE_NONE = 0
 SCALE_TENSOR = 1
 SCALE_BLOCK128 = 2
+SCALE_MX128 = 3
 
 STATUS = {0: "DGP_OK", 1: "DGP_ERR_NULL", 2: "DGP_ERR_SHAPE", 3: "DGP_ERR_ALIGN", 4: "DGP_ERR_DTYPE",
           5: "DGP_ERR_SCALE_MODE", 6: "DGP_ERR_SPLITK", 7: "DGP_ERR_WORKSPACE", 8: "DGP_ERR_CONFIG",
@@ -49,7 +50,7 @@ class Config(ctypes.Structure):
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
            "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
-           "dgp_probe_mfma_layout", "dgp_probe_lds_dma", "dgp_probe_copy",
+           "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_copy",
            "dgp_probe_stream_read", "dgp_probe_mfma_peak")
 
 _lib = None
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "dgp_select_kernel": [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(Config), ctypes.POINTER(_int)],
         "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
+        "dgp_probe_mfma_scaled": [_vp, _vp, _vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
         "dgp_probe_stream_read": [_vp, _i64, _vp, _vp],
         "dgp_probe_mfma_peak": [_int, _int, _int, _vp, _vp, _vp],
@@ -159,10 +161,14 @@ def unshuffle_b(Bs: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 
 
 def _scale_mode(A, sA, scale_mode):
+    """The scale mode of a call: given, or inferred from the scales (none for
+    bf16; uint8 E8M0 scales -> mxfp8; one fp32 -> per-tensor; else blockscale)."""
     if scale_mode is not None:
         return scale_mode
     if dtype_code(A) == BF16:
         return SCALE_NONE
+    if sA is not None and sA.dtype == torch.uint8:
+        return SCALE_MX128
     return SCALE_TENSOR if sA is None or sA.numel() == 1 else SCALE_BLOCK128
 
 
@@ -269,6 +275,13 @@ def describe_kernel(index: int) -> str:
 def probe_mfma_layout(which: int, a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty(64 * 4, dtype=torch.float32, device=a.device)
     _check(lib().dgp_probe_mfma_layout(which, _ptr(a), _ptr(b), _ptr(out), _stream_handle(stream)))
+    return out.view(64, 4)
+
+
+def probe_mfma_scaled(a: torch.Tensor, b: torch.Tensor, sa: torch.Tensor, sb: torch.Tensor,
+                      stream=None) -> torch.Tensor:
+    out = torch.empty(64 * 4, dtype=torch.float32, device=a.device)
+    _check(lib().dgp_probe_mfma_scaled(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(out), _stream_handle(stream)))
     return out.view(64, 4)
 
 

@@ -19,6 +19,7 @@ constexpr int kDtypeFp8 = 1;
 constexpr int kScaleNone = 0;
 constexpr int kScaleTensor = 1;
 constexpr int kScaleBlock = 2;
+constexpr int kScaleMx = 3;         // mxfp8: E8M0 byte per 128-K block per row of A / of B
 constexpr int kOutBf16 = 0;         // direct epilogue: bf16 C
 constexpr int kOutPartial = 1;      // split-K pass 1: fp32 partials
 

@@ -136,7 +136,7 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    if (scale == DGP_SCALE_BLOCK128 || M <= 32) {
+    if (scale == DGP_SCALE_BLOCK128 || scale == DGP_SCALE_MX128 || M <= 32) {
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
         // waves spreads the stream wider (measured faster up to that point).
@@ -165,7 +165,7 @@ struct GemmCall {
     void *C;
     int64_t M, N, K;
     int dtype, scale;
-    const float *sA, *sB;
+    const void *sA, *sB;
     int split_k;
     float *ws;
     size_t ws_bytes;
@@ -243,12 +243,12 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     if (c.M < 0 || c.N < 0 || c.K < 0)
         return fail(DGP_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld", (long long)c.M, (long long)c.N,
                     (long long)c.K);
-    if (c.scale < DGP_SCALE_NONE || c.scale > DGP_SCALE_BLOCK128)
+    if (c.scale < DGP_SCALE_NONE || c.scale > DGP_SCALE_MX128)
         return fail(DGP_ERR_SCALE_MODE, "unknown scale mode %d", c.scale);
     if (c.dtype == DGP_BF16 && c.scale != DGP_SCALE_NONE)
         return fail(DGP_ERR_SCALE_MODE, "bf16 takes DGP_SCALE_NONE");
     if (c.dtype == DGP_FP8_E4M3 && c.scale == DGP_SCALE_NONE)
-        return fail(DGP_ERR_SCALE_MODE, "fp8 takes DGP_SCALE_TENSOR or DGP_SCALE_BLOCK128");
+        return fail(DGP_ERR_SCALE_MODE, "fp8 takes DGP_SCALE_TENSOR, DGP_SCALE_BLOCK128 or DGP_SCALE_MX128");
     if (c.split_k < 1)
         return fail(DGP_ERR_SPLITK, "split_k %d < 1", c.split_k);
     if (c.cfg) {
@@ -272,13 +272,15 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     if (c.scale == DGP_SCALE_BLOCK128 && (c.K % 128 != 0 || c.N % 128 != 0))
         return fail(DGP_ERR_SHAPE, "blockscale needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)",
                     (long long)c.K, (long long)c.N);
+    if (c.scale == DGP_SCALE_MX128 && c.K % 128 != 0)
+        return fail(DGP_ERR_SHAPE, "mxfp8 needs K %% 128 == 0 (K=%lld)", (long long)c.K);
     if (c.K % c.split_k != 0)
         return fail(DGP_ERR_SPLITK, "split_k=%d does not divide K=%lld", c.split_k, (long long)c.K);
     const int64_t Ks = Kb / c.split_k;
     if (Ks % 128 != 0)
         return fail(DGP_ERR_SPLITK, "K range per split (%lld bytes) is not a multiple of 128", (long long)Ks);
-    if (c.scale == DGP_SCALE_BLOCK128 && (c.K / c.split_k) % 128 != 0)
-        return fail(DGP_ERR_SPLITK, "blockscale needs (K/split_k) %% 128 == 0");
+    if ((c.scale == DGP_SCALE_BLOCK128 || c.scale == DGP_SCALE_MX128) && (c.K / c.split_k) % 128 != 0)
+        return fail(DGP_ERR_SPLITK, "block scales need (K/split_k) %% 128 == 0");
 
     if (c.M == 0 || c.N == 0 || (c.select_only && c.K == 0)) {
         plan->spec = nullptr;
@@ -301,8 +303,8 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     if (c.scale != DGP_SCALE_NONE) {
         if (!c.sA || !c.sB)
             return fail(DGP_ERR_NULL, "scale mode needs sA and sB");
-        if (((uintptr_t)c.sA & 3u) || ((uintptr_t)c.sB & 3u))
-            return fail(DGP_ERR_ALIGN, "sA and sB must be 4-byte aligned");
+        if (c.scale != DGP_SCALE_MX128 && (((uintptr_t)c.sA & 3u) || ((uintptr_t)c.sB & 3u)))
+            return fail(DGP_ERR_ALIGN, "fp32 scales sA and sB must be 4-byte aligned");
     }
     if (c.split_k > 1) {
         if (!c.ws)
@@ -403,7 +405,7 @@ dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dt
 }
 
 dgp_status dgp_gemm_preshuffle(const void *A, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
-                               int dtype, int scale_mode, const float *sA, const float *sB,
+                               int dtype, int scale_mode, const void *sA, const void *sB,
                                const dgp_config *cfg, void *stream)
 {
     GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, 1, nullptr, 0, cfg};
@@ -418,8 +420,8 @@ size_t dgp_splitk_workspace_bytes(int64_t M, int64_t N, int split_k)
 }
 
 dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
-                                      int64_t K, int dtype, int scale_mode, const float *sA,
-                                      const float *sB, int split_k, float *ws, size_t ws_bytes,
+                                      int64_t K, int dtype, int scale_mode, const void *sA,
+                                      const void *sB, int split_k, float *ws, size_t ws_bytes,
                                       const dgp_config *cfg, void *stream)
 {
     GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, split_k, ws, ws_bytes, cfg};
@@ -536,6 +538,19 @@ dgp_status dgp_probe_mfma_layout(int which, const void *a, const void *b, float 
     if (st != DGP_OK)
         return st;
     return hip_status(launch_probe_mfma(which, a, b, out, (hipStream_t)stream), "probe launch");
+}
+
+dgp_status dgp_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
+                                 void *stream)
+{
+    if (!a || !b || !sa || !sb || !out)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return fail(DGP_ERR_ALIGN, "a, b and out must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_mfma_scaled(a, b, sa, sb, out, (hipStream_t)stream), "probe launch");
 }
 
 dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, void *stream)

@@ -47,6 +47,17 @@ __device__ inline f32x4 mfma_op(const i32x8 &b, const i32x8 &a, const f32x4 &c)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Hardware-scaled e4m3 MFMA (mxfp8): eb, ea are E8M0 bytes (2^(e-127)) for the
+// B fragment (first operand: lane l's byte scales row l%16 of it) and the A
+// fragment (second operand: column l%16) over the K block lane l / 16 selects;
+// in the operand order of this library that block is K [32q, 32q+32) of the
+// 128-deep step, so an MX scale that is constant over the step (128-element
+// blocks) applies to the whole step.
+__device__ inline f32x4 mfma_mx(const i32x8 &b, const i32x8 &a, const f32x4 &c, int eb, int ea)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea);
+}
+
 __device__ inline i32x8 cat(const i32x4 &lo, const i32x4 &hi)
 {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

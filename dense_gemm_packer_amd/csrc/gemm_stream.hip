@@ -28,6 +28,9 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds_a[];   // 16 * panel bytes
     __shared__ float lds_sa[SCALE == kScaleBlock ? 16 : 1][kScaleCols];
     __shared__ float lds_sb[SCALE == kScaleBlock ? NW * SPW : 1][kScaleCols];
+    // mxfp8: E8M0 bytes of the panel, per A row and per column of the workgroup.
+    __shared__ uint8_t lds_xa[SCALE == kScaleMx ? 16 : 1][kScaleCols];
+    __shared__ uint8_t lds_xb[SCALE == kScaleMx ? NW * SPW * 16 : 1][kScaleCols];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -53,7 +56,7 @@ gemm_stream_kernel(const GemmArgs p, int panel)
 
     float tscale = 1.0f;
     if constexpr (SCALE == kScaleTensor)
-        tscale = p.sA[0] * p.sB[0];
+        tscale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
 
     f32x4 acc[SPW];
 #pragma unroll
@@ -88,7 +91,7 @@ gemm_stream_kernel(const GemmArgs p, int panel)
             for (int u = 0; u < kSaPer; ++u) {
                 const int i = threadIdx.x + u * NW * 64;
                 const int r = i / cols, c = i % cols;
-                sa_v[u] = (i < 16 * cols && m0 + r < p.M) ? p.sA[(int64_t)(m0 + r) * kblocks_row + kb0 + c] : 0.f;
+                sa_v[u] = (i < 16 * cols && m0 + r < p.M) ? static_cast<const float *>(p.sA)[(int64_t)(m0 + r) * kblocks_row + kb0 + c] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < kSbPer; ++u) {
@@ -96,8 +99,30 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                 const int st = i / cols, c = i % cols;
                 const int strip = strip_wg + st;
                 sb_v[u] = (i < NW * SPW * cols && strip < p.N / 16)
-                              ? p.sB[(int64_t)(strip * 16 / 128) * kblocks_row + kb0 + c]
+                              ? static_cast<const float *>(p.sB)[(int64_t)(strip * 16 / 128) * kblocks_row + kb0 + c]
                               : 0.f;
+            }
+        }
+
+        // mxfp8: this panel's E8M0 bytes into registers (rows >= M and columns
+        // >= N get 127 = 1.0; their data is zero).
+        constexpr int kXaPer = SCALE == kScaleMx ? (16 * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
+        constexpr int kXbPer = SCALE == kScaleMx ? (NW * SPW * 16 * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
+        uint32_t xa_v[kXaPer], xb_v[kXbPer];
+        if constexpr (SCALE == kScaleMx) {
+            const uint8_t *xa = static_cast<const uint8_t *>(p.sA), *xb = static_cast<const uint8_t *>(p.sB);
+#pragma unroll
+            for (int u = 0; u < kXaPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                const int r = i / cols, c = i % cols;
+                xa_v[u] = (i < 16 * cols && m0 + r < p.M) ? xa[(int64_t)(m0 + r) * kblocks_row + kb0 + c] : 127u;
+            }
+#pragma unroll
+            for (int u = 0; u < kXbPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                const int col = i / cols, c = i % cols;
+                const int n = strip_wg * 16 + col;
+                xb_v[u] = (i < NW * SPW * 16 * cols && n < p.N) ? xb[(int64_t)n * kblocks_row + kb0 + c] : 127u;
             }
         }
 
@@ -124,6 +149,20 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                     lds_sb[i / cols][i % cols] = sb_v[u];
             }
         }
+        if constexpr (SCALE == kScaleMx) {
+#pragma unroll
+            for (int u = 0; u < kXaPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                if (i < 16 * cols)
+                    lds_xa[i / cols][i % cols] = (uint8_t)xa_v[u];
+            }
+#pragma unroll
+            for (int u = 0; u < kXbPer; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                if (i < NW * SPW * 16 * cols)
+                    lds_xb[i / cols][i % cols] = (uint8_t)xb_v[u];
+            }
+        }
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DEPTH * SPW * kStepCh) : "memory");
 
         for (int st0 = 0; st0 < nsteps; st0 += DEPTH) {
@@ -148,6 +187,9 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                             acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, s));
                             acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, s));
                             acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, s));
+                        } else if constexpr (SCALE == kScaleMx) {
+                            acc[sp] = mfma_mx(b, a, acc[sp], lds_xb[(wave * SPW + sp) * 16 + (lane & 15)][st],
+                                              lds_xa[lane & 15][st]);
                         } else {
                             acc[sp] = mfma_op(b, a, acc[sp]);
                         }
@@ -212,8 +254,14 @@ gemm_ksplit_kernel(const GemmArgs p)
     const auto rB = make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip) * 16 * Kb));
     const uint32_t b_voff = (uint32_t)lane * 16u;
     const int m = m0 + (lane & 15);
-    const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? p.sA + (int64_t)m * kblocks_row : nullptr;
-    const float *sb_row = SCALE == kScaleBlock ? p.sB + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
+    const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
+    const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
+    // mxfp8: this lane's A row and B column E8M0 rows (A rows >= M: none).
+    const uint8_t *xa_row = (SCALE == kScaleMx && m < p.M)
+                                ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
+    const uint8_t *xb_row = SCALE == kScaleMx
+                                ? static_cast<const uint8_t *>(p.sB) + (int64_t)(strip * 16 + (lane & 15)) * kblocks_row
+                                : nullptr;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     i32x4 areg[DEPTH][kStepCh], breg[DEPTH][kStepCh];
@@ -255,6 +303,9 @@ gemm_ksplit_kernel(const GemmArgs p)
                     acc.y = __fadd_rn(acc.y, __fmul_rn(part.y, sc));
                     acc.z = __fadd_rn(acc.z, __fmul_rn(part.z, sc));
                     acc.w = __fadd_rn(acc.w, __fmul_rn(part.w, sc));
+                } else if constexpr (SCALE == kScaleMx) {
+                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
+                    acc = mfma_mx(b, a, acc, xb_row[kb], xa_row ? xa_row[kb] : 127);
                 } else {
                     acc = mfma_op(b, a, acc);
                 }
@@ -275,7 +326,7 @@ gemm_ksplit_kernel(const GemmArgs p)
             v.w = __fadd_rn(v.w, u.w);
         }
         if constexpr (SCALE == kScaleTensor)
-            v = v * (p.sA[0] * p.sB[0]);
+            v = v * (static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0]);
         store_tile<OUT>(p, split, m, strip * 16 + (lane >> 4) * 4, v);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -327,10 +378,12 @@ static const KernelSpec kStreamKernels[] = {
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 2, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleMx),
     // one strip per workgroup, K split over the waves: waves, ring depth
     DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx),
 };
 
 const KernelSpec *stream_kernels(int *count)

@@ -70,7 +70,7 @@ gemm_tiled_kernel(const GemmArgs p)
 
     float scale = 1.0f;
     if constexpr (SCALE == kScaleTensor)
-        scale = p.sA[0] * p.sB[0];
+        scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
 
     f32x4 acc[S::kMT][S::kNT];
 #pragma unroll
@@ -299,7 +299,7 @@ gemm_pingpong_kernel(const GemmArgs p)
 
     float scale = 1.0f;
     if constexpr (SCALE == kScaleTensor)
-        scale = p.sA[0] * p.sB[0];
+        scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
 
     f32x4 acc[16][2];
 #pragma unroll

@@ -14,8 +14,8 @@ struct GemmArgs {
     const uint8_t *Bs;    // preshuffled B (dgp_preshuffle_b layout)
     void *C;              // [M][N] bf16 (direct epilogue)
     float *ws;            // [splits][M][N] fp32 (split-K partial epilogue)
-    const float *sA;      // per-tensor: 1 value; blockscale: [M][K/128]
-    const float *sB;      // per-tensor: 1 value; blockscale: [N/128][K/128]
+    const void *sA;       // per-tensor: 1 fp32; blockscale: [M][K/128] fp32; mxfp8: [M][K/128] E8M0
+    const void *sB;       // per-tensor: 1 fp32; blockscale: [N/128][K/128] fp32; mxfp8: [N][K/128] E8M0
     int M, N;
     int K;                // elements per row
     int Kb;               // bytes per row of A and B
@@ -34,7 +34,7 @@ enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3 };
 struct KernelSpec {
     int family;
     int dtype;      // 0 bf16, 1 fp8
-    int scale;      // 0 none, 1 tensor, 2 block128
+    int scale;      // 0 none, 1 tensor, 2 block128, 3 mxfp8 (E8M0, 128-K blocks)
     int out;        // 0 bf16 direct, 1 fp32 partial
     int tm, tn;     // workgroup output tile
     int kt;         // K bytes per main-loop step (tiled) / per LDS panel (stream)
@@ -63,6 +63,8 @@ hipError_t launch_splitk_reduce(const float *ws, void *C, int64_t M, int64_t N, 
 // Probes (probe.hip).
 hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s);
 hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s);
+hipError_t launch_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
+                                    hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
 hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void *ops, uint32_t *sink,

@@ -27,6 +27,20 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(int which, const uint8_t
     *reinterpret_cast<f32x4 *>(out + l * 4) = acc;
 }
 
+// One hardware-scaled e4m3 MFMA: lane l supplies E8M0 scale byte sa[l] for
+// its A fragment (src1 here, as in the GEMM) and sb[l] for its B fragment
+// (src0), each in byte 0 of a 32-bit operand (op_sel 0).
+__global__ __launch_bounds__(64) void probe_mfma_scaled_kernel(const uint8_t *a, const uint8_t *b,
+                                                               const uint8_t *sa, const uint8_t *sb, float *out)
+{
+    const int l = threadIdx.x;
+    const i32x8 x = *reinterpret_cast<const i32x8 *>(a + l * 32);
+    const i32x8 y = *reinterpret_cast<const i32x8 *>(b + l * 32);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(y, x, acc, 0, 0, 0, (int)sb[l], 0, (int)sa[l]);
+    *reinterpret_cast<f32x4 *>(out + l * 4) = acc;
+}
+
 __global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint8_t *src, const int32_t *perm, uint8_t *dst)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[1024];
@@ -130,6 +144,14 @@ __global__ __launch_bounds__(kPeakThreads) void probe_mfma_peak_kernel(int round
 hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s)
 {
     probe_mfma_kernel<<<1, 64, 0, s>>>(which, (const uint8_t *)a, (const uint8_t *)b, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
+                                    hipStream_t s)
+{
+    probe_mfma_scaled_kernel<<<1, 64, 0, s>>>((const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sa,
+                                              (const uint8_t *)sb, out);
     return hipGetLastError();
 }
 

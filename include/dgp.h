@@ -57,16 +57,23 @@ typedef enum dgp_status {
 
 typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1 } dgp_dtype;
 
-/* DGP_SCALE_NONE: bf16 only.  DGP_SCALE_TENSOR: fp8 only; sA, sB each point to
- * one fp32 and C = bf16(acc * (sA*sB)).  DGP_SCALE_BLOCK128: fp8 only; sA is
- * [M][K/128] fp32 (A per row per 128-wide K block), sB is [N/128][K/128] fp32
- * (B per 128x128 block), both row-major; each 128-K block's fp32 partial sum
- * is multiplied by sA[m][kb]*sB[n/128][kb] and added to the fp32 accumulator
- * ([P3] "Summary"; scale shapes from the run_torch_blockscale review). */
+/* DGP_SCALE_NONE: bf16 only; sA, sB unused.  DGP_SCALE_TENSOR: fp8 only; sA,
+ * sB each point to one fp32 and C = bf16(acc * (sA*sB)).  DGP_SCALE_BLOCK128:
+ * fp8 only; sA is [M][K/128] fp32 (A per row per 128-wide K block), sB is
+ * [N/128][K/128] fp32 (B per 128x128 block), both row-major; each 128-K
+ * block's fp32 partial sum is multiplied by sA[m][kb]*sB[n/128][kb] and added
+ * to the fp32 accumulator ([P3] "Summary"; scale shapes from the
+ * run_torch_blockscale review).  DGP_SCALE_MX128 (mxfp8): fp8 only; sA is
+ * [M][K/128] and sB [N][K/128] bytes, both row-major, each an E8M0 scale
+ * 2^(e-127) (255: NaN) for one row of A or one row of B (= one column of C)
+ * over one 128-wide K block; the matrix-core instruction applies them to each
+ * block's products ([P3] "What's included": mxfp8 with 128-element blocks on
+ * the hardware-scaled MFMA).  fp32 scales must be 4-byte aligned. */
 typedef enum dgp_scale_mode {
     DGP_SCALE_NONE = 0,
     DGP_SCALE_TENSOR = 1,
-    DGP_SCALE_BLOCK128 = 2
+    DGP_SCALE_BLOCK128 = 2,
+    DGP_SCALE_MX128 = 3
 } dgp_scale_mode;
 
 /* Optional tile configuration.  Pass NULL to use the built-in per-shape table.
@@ -152,11 +159,12 @@ dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dt
  * Requires M, N, K >= 0; N % 16 == 0; (K*element_bytes) % 128 == 0 (bf16:
  * K % 64, fp8: K % 128 -- the fp8 matrix-core step is 128 deep); blockscale
  * also N % 128 == 0 and K % 128 == 0 (rejected, never rounded up: the review
- * on [P3] flags the silent ceil-division); A, Bs, C 16-byte aligned.
+ * on [P3] flags the silent ceil-division), mxfp8 K % 128 == 0; A, Bs, C
+ * 16-byte aligned.  sA, sB: device pointers to the scales of `scale_mode`.
  * M = 0 or N = 0 is a no-op returning DGP_OK.  The device must be gfx950.
  */
 dgp_status dgp_gemm_preshuffle(const void *A, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
-                               int dtype, int scale_mode, const float *sA, const float *sB,
+                               int dtype, int scale_mode, const void *sA, const void *sB,
                                const dgp_config *cfg, void *stream);
 
 /* Bytes of fp32 workspace dgp_gemm_preshuffle_splitk needs:
@@ -175,14 +183,14 @@ size_t dgp_splitk_workspace_bytes(int64_t M, int64_t N, int split_k);
  * single-pass split_k = 1 epilogue).
  *
  * Requires everything dgp_gemm_preshuffle does, plus split_k >= 1,
- * K % split_k == 0 and ((K/split_k)*element_bytes) % 128 == 0 (blockscale:
- * (K/split_k) % 128 == 0); for split_k > 1, ws != NULL, 16-byte aligned, and
+ * K % split_k == 0 and ((K/split_k)*element_bytes) % 128 == 0 (blockscale and
+ * mxfp8: (K/split_k) % 128 == 0); for split_k > 1, ws != NULL, 16-byte aligned, and
  * ws_bytes >= dgp_splitk_workspace_bytes(M, N, split_k).  ws is scratch owned
  * by the caller; its contents after the call are unspecified.
  */
 dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
-                                      int64_t K, int dtype, int scale_mode, const float *sA,
-                                      const float *sB, int split_k, float *ws, size_t ws_bytes,
+                                      int64_t K, int dtype, int scale_mode, const void *sA,
+                                      const void *sB, int split_k, float *ws, size_t ws_bytes,
                                       const dgp_config *cfg, void *stream);
 
 /* dgp_check_arch -- DGP_OK if `gcn_arch_name` (as reported by the HIP device

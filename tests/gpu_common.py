@@ -23,6 +23,15 @@ def dev_f32(x) -> torch.Tensor | None:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to(DEV)
 
 
+def dev_scales(x, mode: str) -> torch.Tensor | None:
+    """Scales to the device: E8M0 bytes for mx128, fp32 otherwise."""
+    if x is None:
+        return None
+    if mode == "mx128":
+        return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.uint8))).to(DEV)
+    return dev_f32(x)
+
+
 def host_bits(c: torch.Tensor) -> np.ndarray:
     return c.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -36,11 +45,13 @@ def odt(dtype: str) -> int:
 
 
 def omode(mode: str) -> int:
-    return {"none": oracle.SCALE_NONE, "tensor": oracle.SCALE_TENSOR, "block128": oracle.SCALE_BLOCK128}[mode]
+    return {"none": oracle.SCALE_NONE, "tensor": oracle.SCALE_TENSOR, "block128": oracle.SCALE_BLOCK128,
+            "mx128": oracle.SCALE_MX128}[mode]
 
 
 def dmode(mode: str) -> int:
-    return {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128}[mode]
+    return {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128,
+            "mx128": dgp.SCALE_MX128}[mode]
 
 
 def run_gpu(A, B, dtype, mode, sA=None, sB=None, split_k=1, config=None, Bs_dev=None):
@@ -49,10 +60,10 @@ def run_gpu(A, B, dtype, mode, sA=None, sB=None, split_k=1, config=None, Bs_dev=
     if Bs_dev is None:
         Bs_dev = dgp.preshuffle_b(dev_codes(B, dtype))
     if split_k == 1 and config is None:
-        c = dgp.gemm_preshuffle(a, Bs_dev, dev_f32(sA), dev_f32(sB), dmode(mode))
+        c = dgp.gemm_preshuffle(a, Bs_dev, dev_scales(sA, mode), dev_scales(sB, mode), dmode(mode))
     else:
-        c = dgp.gemm_preshuffle_splitk(a, Bs_dev, split_k, dev_f32(sA), dev_f32(sB), dmode(mode),
-                                       config=config)
+        c = dgp.gemm_preshuffle_splitk(a, Bs_dev, split_k, dev_scales(sA, mode), dev_scales(sB, mode),
+                                       dmode(mode), config=config)
     torch.cuda.synchronize()
     return host_bits(c)
 

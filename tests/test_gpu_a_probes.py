@@ -56,6 +56,49 @@ def test_mfma_fp8_16x16x128_layout():
     assert np.array_equal(out, want)
 
 
+@pytest.mark.parametrize("per_group", [False, True])
+def test_mfma_scaled_e8m0_semantics(per_group):
+    """Hardware-scaled e4m3 MFMA with the library's operand assembly (lane l:
+    bytes 0..15 = K 16*(l//16)+j, bytes 16..31 = K 64+16*(l//16)+j).  The
+    scales act on 32-wide K blocks in that logical K order, [32q, 32q+32),
+    and lane 16q+i supplies block q's scale for row i of the first operand
+    (B fragment) and column i of the second (A fragment) -- so the byte order
+    of the preshuffled layout is the instruction's own K order.  With
+    per_group False the four blocks of a row/column share one scale (the
+    128-K block of the mxfp8 mode); with True they differ.  Exact small
+    integers and scales 2^-2..2^2: every product and sum is exact."""
+    g = np.random.Generator(np.random.PCG64(4 + per_group))
+    X = g.integers(-4, 5, size=(16, 128)).astype(np.float32)   # first operand: 16 rows x K
+    Y = g.integers(-4, 5, size=(128, 16)).astype(np.float32)   # second operand: K x 16
+    if per_group:
+        sb = g.integers(125, 130, size=64).astype(np.uint8)
+        sa = g.integers(125, 130, size=64).astype(np.uint8)
+    else:
+        sb = np.tile(g.integers(125, 130, size=16), 4).astype(np.uint8)
+        sa = np.tile(g.integers(125, 130, size=16), 4).astype(np.uint8)
+    xa = np.zeros((64, 32), np.float32)   # first-operand lanes (rows of X)
+    yb = np.zeros((64, 32), np.float32)   # second-operand lanes (columns of Y)
+    groups = []
+    for l in range(64):
+        ks = [16 * (l // 16) + j for j in range(16)] + [64 + 16 * (l // 16) + j for j in range(16)]
+        xa[l] = X[l % 16, ks]
+        yb[l] = Y[ks, l % 16]
+    for q in range(4):
+        groups.append(list(range(32 * q, 32 * q + 32)))
+    to8 = lambda v: torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).contiguous().to(DEV)
+    u8 = lambda v: torch.from_numpy(v).to(DEV)
+    # the probe passes its `b` buffer as the first operand and `a` as the second
+    out = dgp.probe_mfma_scaled(to8(yb), to8(xa), u8(sa), u8(sb)).cpu().numpy()
+    D = np.zeros((16, 16))
+    for q in range(4):
+        ks = groups[q]
+        sub = X[:, ks].astype(np.float64) @ Y[ks, :].astype(np.float64)
+        D += sub * np.exp2(sb[16 * q:16 * q + 16].astype(np.float64) - 127)[:, None] \
+                 * np.exp2(sa[16 * q:16 * q + 16].astype(np.float64) - 127)[None, :]
+    want = np.array([[D[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)], np.float32)
+    assert np.array_equal(out, want)
+
+
 def test_lds_dma_destination_is_linear_per_lane():
     g = np.random.Generator(np.random.PCG64(3))
     src = g.integers(0, 256, size=1024, dtype=np.uint8)

@@ -27,6 +27,10 @@ def rand_inputs(dtype, mode, M, N, K, seed):
         A, sA = synth.fp8_per_tensor((M, K), seed)
         B, sB = synth.fp8_per_tensor((N, K), seed + 1)
         return A, B, sA, sB
+    if mode == "mx128":
+        A, sA = synth.fp8_mx128(M, K, seed, seed + 2)
+        B, sB = synth.fp8_mx128(N, K, seed + 1, seed + 3)
+        return A, B, sA, sB
     A, sA = synth.fp8_blockscale_a(M, K, seed, seed + 2)
     B, sB = synth.fp8_blockscale_b(N, K, seed + 1, seed + 3)
     return A, B, sA, sB
@@ -39,6 +43,9 @@ def exact_inputs(dtype, mode, M, N, K, seed):
         return A, B, None, None
     if mode == "tensor":
         return A, B, np.array([0.125], np.float32), np.array([1.0], np.float32)
+    if mode == "mx128":
+        return (A, B, synth.exact_e8m0_scales((M, K // 128), seed + 2),
+                synth.exact_e8m0_scales((N, K // 128), seed + 3))
     return (A, B, synth.exact_block_scales((M, K // 128), seed + 2),
             synth.exact_block_scales((N // 128, K // 128), seed + 3))
 
@@ -58,6 +65,10 @@ CASES = [  # dtype, mode, M, N, K
     ("fp8", "block128", 16, 256, 1024),
     ("fp8", "block128", 1, 384, 512),
     ("fp8", "block128", 33, 128, 768),
+    ("fp8", "mx128", 16, 256, 1024),
+    ("fp8", "mx128", 1, 2048, 896),
+    ("fp8", "mx128", 37, 144, 768),
+    ("fp8", "mx128", 300, 272, 512),
 ]
 
 
@@ -81,7 +92,7 @@ def test_every_compiled_kernel():
     """Each kernel of the compiled table, selected exactly through its config,
     on inputs ragged in M and N: exact integers bit-exact, random data within
     tolerance.  Split-output kernels run with split_k = 2."""
-    names = {0: "none", 1: "tensor", 2: "block128"}
+    names = {0: "none", 1: "tensor", 2: "block128", 3: "mx128"}
     for cfg, dt, sm, split_out in dgp.kernels():
         dtype = "bf16" if dt == dgp.BF16 else "fp8"
         mode = names[sm]
@@ -119,7 +130,8 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
 
 
 @pytest.mark.parametrize("tile_n", [64, 16])
-@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
+                                        ("fp8", "mx128")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
 def test_stream_splitk(dtype, mode, M, split_k, tile_n):
@@ -136,7 +148,8 @@ def test_stream_splitk(dtype, mode, M, split_k, tile_n):
     assert_close(got, c32)
 
 
-@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128")])
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
+                                        ("fp8", "mx128")])
 def test_ksplit_uneven_and_empty_slices(dtype, mode):
     """K-split kernel: step counts not divisible by the 8 waves and fewer
     steps than waves (some waves own no K), with splits.  (bf16 steps are 64
@@ -147,7 +160,7 @@ def test_ksplit_uneven_and_empty_slices(dtype, mode):
              ((9, 1), (13, 1), (1, 1), (3, 1), (5, 1), (18, 2), (10, 2)))
     for steps, split in cases:
         K = steps * step
-        if mode == "block128" and (K // split) % 128:
+        if mode in ("block128", "mx128") and (K // split) % 128:
             continue
         A, B, sA, sB = exact_inputs(dtype, mode, 5, 256, K, 31)
         got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
@@ -229,6 +242,31 @@ def test_schedules_ragged_splitk_and_remap(dtype, sched):
     got = run_gpu(A, B, dtype, mode, sA, sB, config=dgp.Config(256, 256, 128, 1, 8, 0, 0, wm, pf, sched))
     c32, _ = run_oracle(A, B, dtype, mode, sA, sB)
     assert_close(got, c32)
+
+
+@pytest.mark.parametrize("tile_n", [64, 16])
+def test_mx128_scale_indexing(tile_n):
+    """mxfp8 scales reach the right operands: doubling one column's B scale
+    row doubles exactly that column of C, and a NaN A scale poisons exactly
+    its row (E8M0 255)."""
+    M, N, K = 5, 128, 512
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
+    A, B, eA, eB = exact_inputs("fp8", "mx128", M, N, K, 41)
+    eA[:] = 127
+    eB[:] = 127
+    base = run_gpu(A, B, "fp8", "mx128", eA, eB, config=cfg)
+    eB2 = eB.copy()
+    eB2[37, :] = 128
+    got = run_gpu(A, B, "fp8", "mx128", eA, eB2, config=cfg)
+    _, want = run_oracle(A, B, "fp8", "mx128", eA, eB2)
+    assert np.array_equal(got, want)
+    f = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f(got)[:, 37], 2 * f(base)[:, 37])
+    assert np.array_equal(np.delete(got, 37, axis=1), np.delete(base, 37, axis=1))
+    eA2 = eA.copy()
+    eA2[3, 2] = 255
+    got = f(run_gpu(A, B, "fp8", "mx128", eA2, eB, config=cfg))
+    assert np.all(np.isnan(got[3])) and np.all(np.isfinite(np.delete(got, 3, axis=0)))
 
 
 def test_negative_control_corrupted_weight_diverges():

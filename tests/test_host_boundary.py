@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 
 OK, NULL, SHAPE, ALIGN, DTYPE, SCALE, SPLITK, WS, CONFIG, ARCH, HIP = range(11)
 BF16, FP8 = 0, 1
-NONE, TENSOR, BLOCK = 0, 1, 2
+NONE, TENSOR, BLOCK, MX = 0, 1, 2, 3
 P = 0x10000          # aligned fake device address (never dereferenced)
 
 
@@ -90,6 +90,8 @@ def splitk(L, split, ws=P, ws_bytes=1 << 30, **kw):
     (dict(dtype=BF16, scale=NONE, K=32), SHAPE),          # K*2 bytes % 128
     (dict(K=192), SHAPE),                                 # fp8 K % 128
     (dict(scale=BLOCK, N=64), SHAPE),                     # blockscale N % 128
+    (dict(dtype=BF16, scale=MX, K=64), SCALE),            # mxfp8 is fp8 only
+    (dict(scale=MX, sA=0), NULL),                          # E8M0 bytes need pointers too
     (dict(C=0), NULL), (dict(A=0), NULL), (dict(Bs=0), NULL),
     (dict(sA=0), NULL), (dict(sB=0), NULL),
     (dict(A=P + 8), ALIGN), (dict(Bs=P + 4), ALIGN), (dict(C=P + 2), ALIGN), (dict(sA=P + 1), ALIGN),
@@ -97,6 +99,15 @@ def splitk(L, split, ws=P, ws_bytes=1 << 30, **kw):
 def test_gemm_rejects(L, kw, status):
     assert gemm(L, **kw) == status
     assert L.dgp_last_error().decode() != ""
+
+
+def test_mx128_accepts_byte_aligned_scales_and_any_n16(dgp):
+    # E8M0 scales are bytes (no 4-byte alignment) and B's are per column, so
+    # N need only be a multiple of 16; split ranges must be whole 128-K blocks.
+    assert dgp.select_kernel(16, 48, 1024, dgp.FP8_E4M3, dgp.SCALE_MX128) >= 0
+    with pytest.raises(dgp.DgpError) as e:
+        dgp.select_kernel(16, 48, 1024, dgp.FP8_E4M3, dgp.SCALE_MX128, 16)   # 64-K ranges
+    assert e.value.name == "DGP_ERR_SPLITK"
 
 
 def test_empty_problems_are_noops(L):
@@ -189,7 +200,7 @@ def test_kernel_table(dgp, L):
                cfg.preload_dsrd, cfg.schedule, dt, sm, split_out)
         assert key not in seen
         seen.add(key)
-        assert (dt, sm) in ((0, 0), (1, 1), (1, 2))
+        assert (dt, sm) in ((0, 0), (1, 1), (1, 2), (1, 3))
         if cfg.tile_m > 16:
             # the A-tile granularity rule: whole 16-byte loads per thread
             assert (cfg.tile_m * cfg.tile_k) % 1024 == 0 and cfg.prefetch >= 1
