@@ -298,23 +298,26 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["vendor_library_same_process"] = vend
     del A8, Bs8, C8
 
-    # fp8 split-K decode (per-tensor), blockscale and mxfp8 decode, cold cache.
+    # Decode-sized M, cold cache: fp8 per-tensor, blockscale, mxfp8, and bf16.
     dec = {}
-    for mode in ("tensor", "block128", "mx128"):
-        name = {"tensor": "fp8_decode", "block128": "fp8_blockscale", "mx128": "fp8_mx128"}[mode]
-        Ms = (1, 16) if mode == "tensor" else (16,)
-        Ns = (2048, 16384) if mode == "tensor" else (16384,)
+    for mode in ("tensor", "block128", "mx128", "bf16"):
+        name = {"tensor": "fp8_decode", "block128": "fp8_blockscale", "mx128": "fp8_mx128",
+                "bf16": "bf16_decode"}[mode]
+        edt = "bf16" if mode == "bf16" else "fp8"
+        eb = 2 if mode == "bf16" else 1
+        Ms = (1, 16) if mode in ("tensor", "bf16") else (16,)
+        Ns = (2048, 16384) if mode in ("tensor", "bf16") else (16384,)
         for n_ in Ns:
             base = synth.workload_inputs(name, M=16, N=n_)
             kk = base["K"]
-            Bs_one = dgp.preshuffle_b(to_dev(base["B"], "fp8"))
-            copies = max(2, int(np.ceil(2 * MALL_BYTES / (n_ * kk))) + 1)
+            Bs_one = dgp.preshuffle_b(to_dev(base["B"], edt))
+            copies = max(2, int(np.ceil(2 * MALL_BYTES / (n_ * kk * eb))) + 1)
             Bss = [Bs_one] + [Bs_one.clone() for _ in range(copies - 1)]
-            sBt = torch.from_numpy(np.ascontiguousarray(base["sB"])).to(dev)
+            sBt = None if base["sB"] is None else torch.from_numpy(np.ascontiguousarray(base["sB"])).to(dev)
             for m_ in Ms:
-                A_ = to_dev(base["A"][:m_], "fp8")
-                sAt = torch.from_numpy(np.ascontiguousarray(base["sA"][:m_] if mode != "tensor"
-                                                            else base["sA"])).to(dev)
+                A_ = to_dev(base["A"][:m_], edt)
+                sAt = None if base["sA"] is None else torch.from_numpy(np.ascontiguousarray(
+                    base["sA"][:m_] if mode != "tensor" else base["sA"])).to(dev)
                 best = None
                 for split in (1, 2, 4, 8):
                     Cs = [torch.empty((m_, n_), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
@@ -327,9 +330,9 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                         dgp.gemm_preshuffle_splitk(A_, Bss[j], split, sAt, sBt, out=Cs[j],
                                                    workspace=wss[j] if split > 1 else None)
                     us = graph_time_us(torch, fn, iters)
-                    nbytes = m_ * kk + n_ * kk + 2 * m_ * n_
+                    nbytes = (m_ * kk + n_ * kk) * eb + 2 * m_ * n_
                     nbytes += {"tensor": 8, "block128": 4 * (m_ * kk // 128 + (n_ // 128) * (kk // 128)),
-                               "mx128": m_ * kk // 128 + n_ * kk // 128}[mode]
+                               "mx128": m_ * kk // 128 + n_ * kk // 128, "bf16": 0}[mode]
                     gbs = nbytes / (us * 1e-6) / 1e9
                     key = f"{mode} M={m_} N={n_} K={kk} split={split}"
                     dec[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),

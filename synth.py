@@ -32,6 +32,7 @@ CFG_FP8_LARGE = 2
 CFG_FP8_DECODE = 3
 CFG_FP8_BLOCKSCALE = 4
 CFG_FP8_MX128 = 5         # microscaling (mxfp8) decode, the first adjacent workload
+CFG_BF16_DECODE = 6       # bf16 weights at decode M, the second adjacent workload
 
 WORKLOADS = {
     "bf16_small": dict(cfg=CFG_BF16_SMALL, dtype="bf16", M=128, N=256, K=256),
@@ -42,6 +43,8 @@ WORKLOADS = {
     "fp8_blockscale": dict(cfg=CFG_FP8_BLOCKSCALE, dtype="fp8", M=16, N=16384, K=7168,
                            splits=(1, 2, 4, 8)),
     "fp8_mx128": dict(cfg=CFG_FP8_MX128, dtype="fp8", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
+    "bf16_decode": dict(cfg=CFG_BF16_DECODE, dtype="bf16", Ms=(1, 16), Ns=(2048, 16384), K=7168,
+                        splits=(1, 2, 4, 8)),
 }
 
 
@@ -174,7 +177,7 @@ def workload_inputs(name: str, M=None, N=None, K=None):
     if name == "bf16_small":
         return dict(A=bf16_uniform((M, K), sa), B=bf16_uniform((N, K), sb), sA=None, sB=None,
                     dtype="bf16", scale_mode="none", M=M, N=N, K=K)
-    if name == "bf16_large":
+    if name in ("bf16_large", "bf16_decode"):
         std = 1.0 / np.sqrt(K)
         return dict(A=bf16_normal((M, K), sa, std), B=bf16_normal((N, K), sb, std), sA=None,
                     sB=None, dtype="bf16", scale_mode="none", M=M, N=N, K=K)
