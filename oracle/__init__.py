@@ -16,10 +16,12 @@ from . import build as _build
 
 BF16 = 0
 FP8_E4M3 = 1
+FP4_E2M1 = 2
 SCALE_NONE = 0
 SCALE_TENSOR = 1
 SCALE_BLOCK128 = 2
 SCALE_MX128 = 3
+SCALE_MX32 = 4
 
 _lib = None
 
@@ -35,6 +37,8 @@ def lib():
         L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
         L.oracle_e4m3_decode.restype = ctypes.c_float
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_decode.restype = ctypes.c_float
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e8m0_decode.restype = ctypes.c_float
         L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
         L.oracle_bf16_round.restype = ctypes.c_uint16
@@ -68,6 +72,10 @@ def bf16_decode(h):
 
 def e4m3_decode(b):
     return lib().oracle_e4m3_decode(int(b))
+
+
+def e2m1_decode(nibble):
+    return lib().oracle_e2m1_decode(int(nibble))
 
 
 def e8m0_decode(e):
@@ -117,7 +125,9 @@ def gemm(A, B, dtype, scale_mode=SCALE_NONE, sA=None, sB=None, split_k=1, rows=N
     """C = A * B^T on unshuffled B.
 
     Scales: per-tensor and blockscale take fp32 arrays; mxfp8 (SCALE_MX128)
-    takes E8M0 bytes, sA [M][K/128] and sB [N][K/128].
+    takes E8M0 bytes, sA [M][K/128] and sB [N][K/128]; mxfp4 (FP4_E2M1 with
+    SCALE_MX32) takes A and B as packed bytes [rows][K/2] and E8M0 bytes
+    sA [M][K/32], sB [N][K/32].
 
     Returns (c_f32, c_bf16[, partials]): the fp32 value before rounding, the
     bf16 bit patterns, and (optionally) the per-split fp32 partials
@@ -128,7 +138,9 @@ def gemm(A, B, dtype, scale_mode=SCALE_NONE, sA=None, sB=None, split_k=1, rows=N
     M, K = A.shape
     N = B.shape[0]
     assert B.shape[1] == K
-    sdt = np.uint8 if scale_mode == SCALE_MX128 else np.float32   # E8M0 bytes or fp32 scales
+    if dtype == FP4_E2M1:    # packed pairs: the arrays hold K/2 bytes per row
+        K *= 2
+    sdt = np.uint8 if scale_mode in (SCALE_MX128, SCALE_MX32) else np.float32   # E8M0 bytes or fp32
     sA_ = None if sA is None else np.ascontiguousarray(np.asarray(sA, dtype=sdt))
     sB_ = None if sB is None else np.ascontiguousarray(np.asarray(sB, dtype=sdt))
     rows_ = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))

@@ -19,7 +19,9 @@
  *    row per 128-wide K block, B per 128x128 block; shapes [M][K/128] and
  *    [N/128][K/128] from the run_torch_blockscale review comment), and the MX
  *    mode mxfp8 (same PR, "What's included": 128-element blocks with one E8M0
- *    scale each, applied by the hardware-scaled matrix instruction).
+ *    scale each, applied by the hardware-scaled matrix instruction) and mxfp4
+ *    (same list: 4-bit packed elements, 32-element blocks with one E8M0 scale
+ *    each).
  *  - Split-K (aiter PR #5148, "What's included" and the file table): each of
  *    split_k K-chunks produces fp32 partials in a workspace and a second pass
  *    reduces them in fp32, rounding to the output type once.
@@ -42,6 +44,12 @@
  *    ([N][K/128] bytes), both row-major.  As for blockscale, each block's
  *    fp32 partial sum p is scaled and added: acc += p * 2^(eA-127) * 2^(eB-127),
  *    the power of two applied exactly (ldexpf).
+ *  - mxfp4: elements are OCP E2M1 (1 sign, 2 exponent bits with bias 1, 1
+ *    mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), packed two per byte with
+ *    element 2j in the low nibble of byte j and 2j+1 in the high nibble; K
+ *    counts elements, a row is K/2 bytes.  Scales as for mxfp8 but per 32-K
+ *    block: A [M][K/32], B [N][K/32] E8M0 bytes; each 32-block's fp32 partial
+ *    is scaled and added.
  *
  * Build: plain C11, -O2 -ffp-contract=off, no fast-math (so that every fp32
  * multiply and add rounds separately, in the order written here).
@@ -53,8 +61,8 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1 };
-enum { ORC_SCALE_NONE = 0, ORC_SCALE_TENSOR = 1, ORC_SCALE_BLOCK128 = 2, ORC_SCALE_MX128 = 3 };
+enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1, ORC_FP4_E2M1 = 2 };
+enum { ORC_SCALE_NONE = 0, ORC_SCALE_TENSOR = 1, ORC_SCALE_BLOCK128 = 2, ORC_SCALE_MX128 = 3, ORC_SCALE_MX32 = 4 };
 
 /* ---------------------------------------------------------------- decode */
 
@@ -82,6 +90,17 @@ float oracle_e4m3_decode(uint8_t b)
         mag = ldexpf((float)m, -9);
     else
         mag = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* OCP 4-bit float E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa
+ * bit; exponent field 0 is subnormal (m * 0.5).  All 16 codes are finite. */
+float oracle_e2m1_decode(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int m = nibble & 1;
+    float mag = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
     return sign ? -mag : mag;
 }
 
@@ -179,12 +198,13 @@ static float partial_sum(const gemm_job *j, int64_t m, int64_t n, int64_t k0, in
 {
     const float *arow = j->a + m * j->K;
     const float *brow = j->b + n * j->K;
-    if (j->scale_mode == ORC_SCALE_MX128) {
-        int64_t kblocks = j->K / 128;
+    if (j->scale_mode == ORC_SCALE_MX128 || j->scale_mode == ORC_SCALE_MX32) {
+        const int64_t bs = j->scale_mode == ORC_SCALE_MX128 ? 128 : 32;   /* block size */
+        int64_t kblocks = j->K / bs;
         float acc = 0.0f;
-        for (int64_t kb = k0 / 128; kb < k1 / 128; ++kb) {
+        for (int64_t kb = k0 / bs; kb < k1 / bs; ++kb) {
             float p = 0.0f;
-            for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+            for (int64_t k = kb * bs; k < kb * bs + bs; ++k)
                 p += arow[k] * brow[k];
             uint8_t ea = j->eA[m * kblocks + kb], eb = j->eB[n * kblocks + kb];
             if (ea == 255 || eb == 255)
@@ -250,18 +270,23 @@ static float *decode_all(const void *src, int64_t count, int dtype)
         const uint16_t *h = (const uint16_t *)src;
         for (int64_t i = 0; i < count; ++i)
             dst[i] = oracle_bf16_decode(h[i]);
-    } else {
+    } else if (dtype == ORC_FP8_E4M3) {
         const uint8_t *q = (const uint8_t *)src;
         for (int64_t i = 0; i < count; ++i)
             dst[i] = oracle_e4m3_decode(q[i]);
+    } else {   /* E2M1, two per byte, element 2j in the low nibble */
+        const uint8_t *q = (const uint8_t *)src;
+        for (int64_t i = 0; i < count; ++i)
+            dst[i] = oracle_e2m1_decode((uint8_t)((q[i / 2] >> (4 * (i & 1))) & 0xF));
     }
     return dst;
 }
 
 /*
  * Compute rows of C.  A is [M][K] and B is [N][K] (unshuffled), both of
- * element type dtype (bf16 bit patterns or e4m3 codes).  sA, sB: fp32 scales
- * (per-tensor, blockscale) or E8M0 bytes (mxfp8), unused for scale mode none.
+ * element type dtype (bf16 bit patterns, e4m3 codes, or packed e2m1 pairs --
+ * K elements = K/2 bytes per row).  sA, sB: fp32 scales (per-tensor,
+ * blockscale) or E8M0 bytes (mxfp8, mxfp4), unused for scale mode none.
  * rows lists which rows
  * of C to produce (NULL: all M rows, nrows must equal M).  Outputs are indexed
  * by position in rows.  Returns 0, or -1 on an invalid argument.
@@ -273,9 +298,14 @@ int oracle_gemm_rows(const void *A, const void *B, int64_t M, int64_t N, int64_t
 {
     if (M < 0 || N < 0 || K < 0 || nrows < 0 || split_k < 1)
         return -1;
-    if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3)
+    if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3 && dtype != ORC_FP4_E2M1)
         return -1;
-    if (scale_mode < ORC_SCALE_NONE || scale_mode > ORC_SCALE_MX128)
+    if (scale_mode < ORC_SCALE_NONE || scale_mode > ORC_SCALE_MX32)
+        return -1;
+    /* e2m1 comes with its 32-block scales and nothing else */
+    if ((dtype == ORC_FP4_E2M1) != (scale_mode == ORC_SCALE_MX32))
+        return -1;
+    if (scale_mode == ORC_SCALE_MX32 && (K % 32 != 0 || (K / split_k) % 32 != 0 || K % 2 != 0))
         return -1;
     if (scale_mode == ORC_SCALE_MX128 && (dtype != ORC_FP8_E4M3 || K % 128 != 0 || (K / split_k) % 128 != 0))
         return -1;
@@ -306,7 +336,7 @@ int oracle_gemm_rows(const void *A, const void *B, int64_t M, int64_t N, int64_t
     if (nthreads > nrows)
         nthreads = nrows > 0 ? (int)nrows : 1;
 
-    const int mx = scale_mode == ORC_SCALE_MX128;
+    const int mx = scale_mode == ORC_SCALE_MX128 || scale_mode == ORC_SCALE_MX32;
     gemm_job base = {a, b, M, N, K, scale_mode, mx ? NULL : (const float *)sA, mx ? NULL : (const float *)sB,
                      mx ? (const uint8_t *)sA : NULL, mx ? (const uint8_t *)sB : NULL, split_k, rows, nrows,
                      out_f32, out_bf16, partials, 0, 0};

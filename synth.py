@@ -33,6 +33,7 @@ CFG_FP8_DECODE = 3
 CFG_FP8_BLOCKSCALE = 4
 CFG_FP8_MX128 = 5         # microscaling (mxfp8) decode, the first adjacent workload
 CFG_BF16_DECODE = 6       # bf16 weights at decode M, the second adjacent workload
+CFG_FP4_MX32 = 7          # mxfp4 decode, the fourth adjacent workload
 
 WORKLOADS = {
     "bf16_small": dict(cfg=CFG_BF16_SMALL, dtype="bf16", M=128, N=256, K=256),
@@ -45,6 +46,7 @@ WORKLOADS = {
     "fp8_mx128": dict(cfg=CFG_FP8_MX128, dtype="fp8", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
     "bf16_decode": dict(cfg=CFG_BF16_DECODE, dtype="bf16", Ms=(1, 16), Ns=(2048, 16384), K=7168,
                         splits=(1, 2, 4, 8)),
+    "fp4_mx32": dict(cfg=CFG_FP4_MX32, dtype="fp4", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
 }
 
 
@@ -70,6 +72,27 @@ def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     to +-448 first; torch does not saturate."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
     return t.view(torch.uint8).numpy().copy()
+
+
+E2M1_MAX = 6.0
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+
+def to_e2m1_codes(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP E2M1 codes (uint8, one per element): round to nearest on the
+    grid 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating at 6."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(E2M1_MAX))
+    idx = np.searchsorted(_E2M1_MIDS, a, side="left")
+    at_mid = (idx < len(_E2M1_MIDS)) & (a == _E2M1_MIDS[np.minimum(idx, len(_E2M1_MIDS) - 1)])
+    code = idx + (at_mid & (idx % 2 == 1))
+    return (code + 8 * (x < 0)).astype(np.uint8)
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """[rows][K] E2M1 codes -> [rows][K/2] bytes, element 2j in the low nibble."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
 def quantise_e4m3(x: np.ndarray, scale) -> np.ndarray:
@@ -143,6 +166,23 @@ def fp8_mx128(R, K, seed_data, seed_mag):
     return codes, e
 
 
+def fp4_mx32(R, K, seed_data, seed_mag):
+    """Rows [R][K] in mxfp4: packed E2M1 bytes [R][K/2] and one E8M0 byte per
+    row per 32-element block ([R][K/32]).  Data N(0,1) times a per-block
+    magnitude 2^u, u uniform in {-4..4}; scale rule of the OCP microscaling
+    format, shared exponent floor(log2(amax)) - 2 (2 = largest E2M1
+    exponent), elements saturated to +-6."""
+    kb = K // 32
+    x = rng(seed_data).standard_normal(size=(R, kb, 32)).astype(np.float32)
+    x *= np.exp2(rng(seed_mag).integers(-4, 5, size=(R, kb, 1))).astype(np.float32)
+    amax = np.abs(x).max(axis=2)
+    shared = np.floor(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64) - 2
+    e = np.clip(shared + 127, 0, 254).astype(np.uint8)
+    scale = np.exp2(e.astype(np.float64) - 127).astype(np.float32)
+    codes = to_e2m1_codes(x / scale[:, :, None]).reshape(R, K)
+    return pack_e2m1(codes), e
+
+
 def exact_e8m0_scales(shape, seed) -> np.ndarray:
     """E8M0 bytes from {126, 127, 128} (scales 0.5, 1, 2): exact in every product."""
     return rng(seed).choice(np.array([126, 127, 128], dtype=np.uint8), size=shape)
@@ -154,6 +194,8 @@ def exact_ints(shape, seed, dtype: str, lo=-4, hi=4) -> np.ndarray:
     Every product and partial sum of such inputs is an exact fp32 number, so
     any summation order gives the same bits."""
     v = rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+    if dtype == "fp4":    # packed pairs: shape[-1] elements -> shape[-1]/2 bytes
+        return pack_e2m1(to_e2m1_codes(v))
     return to_bf16_bits(v) if dtype == "bf16" else to_e4m3_codes(v)
 
 
@@ -189,6 +231,10 @@ def workload_inputs(name: str, M=None, N=None, K=None):
         A, sA = fp8_blockscale_a(M, K, sa, ss)
         B, sB = fp8_blockscale_b(N, K, sb, ss + 500)
         return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp8", scale_mode="block128", M=M, N=N, K=K)
+    if name == "fp4_mx32":
+        A, sA = fp4_mx32(M, K, sa, ss)
+        B, sB = fp4_mx32(N, K, sb, ss + 500)
+        return dict(A=A, B=B, sA=sA, sB=sB, dtype="fp4", scale_mode="mx32", M=M, N=N, K=K)
     if name == "fp8_mx128":
         A, sA = fp8_mx128(M, K, sa, ss)
         B, sB = fp8_mx128(N, K, sb, ss + 500)

@@ -389,3 +389,119 @@ def test_mx128_invalid_arguments_rejected(orc):
         orc.gemm(np.zeros((2, 192), np.uint8), np.zeros((2, 192), np.uint8), orc.FP8_E4M3, orc.SCALE_MX128, e, e)
     with pytest.raises(ValueError):   # split ranges must be whole blocks
         orc.gemm(A8, np.zeros((2, 256), np.uint8), orc.FP8_E4M3, orc.SCALE_MX128, e, e, split_k=4)
+
+
+# ---------------------------------------------------- mxfp4 (E2M1 pairs, 32-K blocks)
+
+def _e2m1_table():
+    """code -> value from the golden file (OCP MX specification values)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "e2m1_ocp_values.txt")
+    t = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            c, v = line.split()
+            t[int(c, 16)] = float(v)
+    assert len(t) == 16
+    return t
+
+
+def dec_fp4_table(packed):
+    """Unpack [rows][K/2] bytes (element 2j low nibble) through the golden table."""
+    t = _e2m1_table()
+    lut = np.array([t[c] for c in range(16)], np.float64)
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.float64)
+    out[..., 0::2] = lut[p & 0xF]
+    out[..., 1::2] = lut[p >> 4]
+    return out
+
+
+def test_e2m1_decode_exhaustive_against_ocp_table(orc):
+    t = _e2m1_table()
+    for c in range(16):
+        got = orc.e2m1_decode(c)
+        assert got == t[c] and np.signbit(got) == np.signbit(t[c]), c
+
+
+def test_fp4_nibble_order_one_hot(orc):
+    """A one-hot A row at element k picks B[:, k]: pins that element k of a row
+    lives in byte k/2.  (Which nibble of the byte holds the even element is a
+    relabeling of K applied alike to A and B that never crosses a 32-element
+    scale block, so it cannot change C; the library's convention -- even
+    element in the low nibble -- is the packing in synth.pack_e2m1.)"""
+    M, N, K = 8, 16, 64
+    B = synth.exact_ints((N, K), 191, "fp4")
+    b = dec_fp4_table(B)
+    ks = [0, 1, 2, 33, 62, 63, 17, 40]
+    codes = np.zeros((M, K), np.uint8)
+    codes[np.arange(M), ks] = 0x2            # 1.0
+    A = synth.pack_e2m1(codes)
+    eA = np.full((M, K // 32), 127, np.uint8)
+    eB = np.full((N, K // 32), 127, np.uint8)
+    c32, _ = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB)
+    assert np.array_equal(c32.astype(np.float64), b[:, ks].T)
+
+
+def test_mx32_against_fp64(orc):
+    M, N, K = 5, 40, 512
+    A, eA = synth.fp4_mx32(M, K, 201, 202)
+    B, eB = synth.fp4_mx32(N, K, 203, 204)
+    assert len(np.unique(eA)) > 3
+    a, b = dec_fp4_table(A), dec_fp4_table(B)
+    KB = K // 32
+    c64, mag, alt = np.zeros((M, N)), np.zeros((M, N)), np.zeros((M, N))
+    for kb in range(KB):
+        sl = slice(kb * 32, kb * 32 + 32)
+        sc = _mx_scale(eA[:, kb])[:, None] * _mx_scale(eB[:, kb])[None, :]
+        c64 += (a[:, sl] @ b[:, sl].T) * sc
+        mag += (np.abs(a[:, sl]) @ np.abs(b[:, sl]).T) * sc
+        wk = (kb + 1) % KB
+        alt += (a[:, sl] @ b[:, sl].T) * (_mx_scale(eA[:, wk])[:, None] * _mx_scale(eB[:, wk])[None, :])
+    bound = (gamma(K + KB) + U) * mag
+    c32, _ = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB)
+    assert np.all(np.abs(c32 - c64) <= bound + 1e-30)
+    assert np.max(np.abs(alt - c64) - bound) > 0
+
+
+def test_mx32_exact_integers_and_per_column_scale(orc):
+    M, N, K = 4, 24, 256
+    A = synth.exact_ints((M, K), 211, "fp4")
+    B = synth.exact_ints((N, K), 212, "fp4")
+    eA = synth.exact_e8m0_scales((M, K // 32), 213)
+    eB = synth.exact_e8m0_scales((N, K // 32), 214)
+    a, b = dec_fp4_table(A), dec_fp4_table(B)
+    want = np.zeros((M, N))
+    for kb in range(K // 32):
+        sl = slice(kb * 32, kb * 32 + 32)
+        want += (a[:, sl] @ b[:, sl].T) * _mx_scale(eA[:, kb])[:, None] * _mx_scale(eB[:, kb])[None, :]
+    c32, _ = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB)
+    assert np.array_equal(c32.astype(np.float64), want)
+    eB2 = eB.copy()
+    eB2[5] = np.minimum(eB2[5] + 1, 254)
+    c2, _ = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB2)
+    assert np.array_equal(c2[:, 5], 2 * c32[:, 5])
+    assert np.array_equal(np.delete(c2, 5, axis=1), np.delete(c32, 5, axis=1))
+
+
+def test_mx32_splitk_exact_equals_unsplit(orc):
+    M, N, K = 3, 16, 512
+    A = synth.exact_ints((M, K), 221, "fp4")
+    B = synth.exact_ints((N, K), 222, "fp4")
+    eA = synth.exact_e8m0_scales((M, K // 32), 223)
+    eB = synth.exact_e8m0_scales((N, K // 32), 224)
+    c1, h1 = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB)
+    for S in (2, 4, 8):
+        cS, hS = orc.gemm(A, B, orc.FP4_E2M1, orc.SCALE_MX32, eA, eB, split_k=S)
+        assert np.array_equal(cS, c1) and np.array_equal(hS, h1)
+
+
+def test_mx32_invalid_arguments_rejected(orc):
+    A = np.zeros((2, 64), np.uint8)
+    e = np.full((2, 4), 127, np.uint8)
+    with pytest.raises(ValueError):   # e2m1 takes only its 32-block scales
+        orc.gemm(A, A, orc.FP4_E2M1, orc.SCALE_MX128, e, e)
+    with pytest.raises(ValueError):   # and the 32-block mode only e2m1
+        orc.gemm(np.zeros((2, 128), np.uint8), np.zeros((2, 128), np.uint8), orc.FP8_E4M3, orc.SCALE_MX32, e, e)
+    with pytest.raises(ValueError):   # split ranges must be whole 32-blocks
+        orc.gemm(A, A, orc.FP4_E2M1, orc.SCALE_MX32, e, e, split_k=8)
