@@ -91,7 +91,8 @@ def main():
 
     def to_dev(codes, dtype):
         t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
-        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn).to(dev)
+        return t.view({"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
+                       "fp4": torch.float4_e2m1fn_x2}[dtype]).to(dev)
 
     # ------------------------------------------------------------ headline
     w = synth.workload_inputs("bf16_large")
@@ -298,15 +299,15 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["vendor_library_same_process"] = vend
     del A8, Bs8, C8
 
-    # Decode-sized M, cold cache: fp8 per-tensor, blockscale, mxfp8, and bf16.
+    # Decode-sized M, cold cache: fp8 per-tensor, blockscale, mxfp8, mxfp4, and bf16.
     dec = {}
-    for mode in ("tensor", "block128", "mx128", "bf16"):
+    for mode in ("tensor", "block128", "mx128", "mx32", "bf16"):
         name = {"tensor": "fp8_decode", "block128": "fp8_blockscale", "mx128": "fp8_mx128",
-                "bf16": "bf16_decode"}[mode]
-        edt = "bf16" if mode == "bf16" else "fp8"
-        eb = 2 if mode == "bf16" else 1
-        Ms = (1, 16) if mode in ("tensor", "bf16") else (16,)
-        Ns = (2048, 16384) if mode in ("tensor", "bf16") else (16384,)
+                "mx32": "fp4_mx32", "bf16": "bf16_decode"}[mode]
+        edt = {"bf16": "bf16", "mx32": "fp4"}.get(mode, "fp8")
+        eb = {"bf16": 2.0, "mx32": 0.5}.get(mode, 1.0)     # bytes per element
+        Ms = (1, 16) if mode in ("tensor", "bf16", "mx32") else (16,)
+        Ns = (2048, 16384) if mode in ("tensor", "bf16", "mx32") else (16384,)
         for n_ in Ns:
             base = synth.workload_inputs(name, M=16, N=n_)
             kk = base["K"]
@@ -330,9 +331,10 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                         dgp.gemm_preshuffle_splitk(A_, Bss[j], split, sAt, sBt, out=Cs[j],
                                                    workspace=wss[j] if split > 1 else None)
                     us = graph_time_us(torch, fn, iters)
-                    nbytes = (m_ * kk + n_ * kk) * eb + 2 * m_ * n_
+                    nbytes = int((m_ * kk + n_ * kk) * eb) + 2 * m_ * n_
                     nbytes += {"tensor": 8, "block128": 4 * (m_ * kk // 128 + (n_ // 128) * (kk // 128)),
-                               "mx128": m_ * kk // 128 + n_ * kk // 128, "bf16": 0}[mode]
+                               "mx128": m_ * kk // 128 + n_ * kk // 128,
+                               "mx32": m_ * kk // 32 + n_ * kk // 32, "bf16": 0}[mode]
                     gbs = nbytes / (us * 1e-6) / 1e9
                     key = f"{mode} M={m_} N={n_} K={kk} split={split}"
                     dec[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),

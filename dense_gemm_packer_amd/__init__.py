@@ -7,7 +7,9 @@ torch stream unless one is passed).  There is no fallback: if the compiled
 library is missing, every call raises.
 
 Element types follow the torch dtype of the operands: torch.bfloat16 ->
-DGP_BF16, torch.float8_e4m3fn -> DGP_FP8_E4M3.
+DGP_BF16, torch.float8_e4m3fn -> DGP_FP8_E4M3, torch.float4_e2m1fn_x2 (two
+E2M1 values per byte; a [rows][K/2] tensor holds K elements per row) ->
+DGP_FP4_E2M1.
 """
 from __future__ import annotations
 
@@ -21,10 +23,12 @@ LIB_PATH = os.path.join(_HERE, "libdgp.so")
 
 BF16 = 0
 FP8_E4M3 = 1
+FP4_E2M1 = 2
 SCALE_NONE = 0
 SCALE_TENSOR = 1
 SCALE_BLOCK128 = 2
 SCALE_MX128 = 3
+SCALE_MX32 = 4
 
 STATUS = {0: "DGP_OK", 1: "DGP_ERR_NULL", 2: "DGP_ERR_SHAPE", 3: "DGP_ERR_ALIGN", 4: "DGP_ERR_DTYPE",
           5: "DGP_ERR_SCALE_MODE", 6: "DGP_ERR_SPLITK", 7: "DGP_ERR_WORKSPACE", 8: "DGP_ERR_CONFIG",
@@ -80,7 +84,7 @@ def lib() -> ctypes.CDLL:
         "dgp_select_kernel": [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(Config), ctypes.POINTER(_int)],
         "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
-        "dgp_probe_mfma_scaled": [_vp, _vp, _vp, _vp, _vp, _vp],
+        "dgp_probe_mfma_scaled": [_int, _vp, _vp, _vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
         "dgp_probe_stream_read": [_vp, _i64, _vp, _vp],
         "dgp_probe_mfma_peak": [_int, _int, _int, _vp, _vp, _vp],
@@ -109,7 +113,14 @@ def dtype_code(t: torch.Tensor) -> int:
         return BF16
     if t.dtype == torch.float8_e4m3fn:
         return FP8_E4M3
-    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float8_e4m3fn)")
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return FP4_E2M1
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16, float8_e4m3fn or float4_e2m1fn_x2)")
+
+
+def k_elements(t: torch.Tensor) -> int:
+    """Elements per row of a [rows][...] operand (fp4 stores two per byte)."""
+    return t.shape[1] * (2 if t.dtype == torch.float4_e2m1fn_x2 else 1)
 
 
 def _ptr(t):
@@ -145,7 +156,7 @@ def preshuffle_b(B: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
     if out is None:
         out = torch.empty_like(B)
     _dev(out, "out")
-    _check(lib().dgp_preshuffle_b(_ptr(B), _ptr(out), B.shape[0], B.shape[1], dtype_code(B),
+    _check(lib().dgp_preshuffle_b(_ptr(B), _ptr(out), B.shape[0], k_elements(B), dtype_code(B),
                                   _stream_handle(stream)))
     return out
 
@@ -155,7 +166,7 @@ def unshuffle_b(Bs: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
     if out is None:
         out = torch.empty_like(Bs)
     _dev(out, "out")
-    _check(lib().dgp_unshuffle_b(_ptr(Bs), _ptr(out), Bs.shape[0], Bs.shape[1], dtype_code(Bs),
+    _check(lib().dgp_unshuffle_b(_ptr(Bs), _ptr(out), Bs.shape[0], k_elements(Bs), dtype_code(Bs),
                                  _stream_handle(stream)))
     return out
 
@@ -167,6 +178,8 @@ def _scale_mode(A, sA, scale_mode):
         return scale_mode
     if dtype_code(A) == BF16:
         return SCALE_NONE
+    if dtype_code(A) == FP4_E2M1:
+        return SCALE_MX32
     if sA is not None and sA.dtype == torch.uint8:
         return SCALE_MX128
     return SCALE_TENSOR if sA is None or sA.numel() == 1 else SCALE_BLOCK128
@@ -177,7 +190,7 @@ def gemm_preshuffle(A: torch.Tensor, Bs: torch.Tensor, sA: torch.Tensor | None =
                     out: torch.Tensor | None = None, config=None, stream=None) -> torch.Tensor:
     """C = A * B^T (bf16 [M][N]) with Bs = preshuffle_b(B)."""
     _dev(A, "A"), _dev(Bs, "Bs")
-    M, K = A.shape
+    M, K = A.shape[0], k_elements(A)
     N = Bs.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
@@ -202,7 +215,7 @@ def gemm_preshuffle_splitk(A: torch.Tensor, Bs: torch.Tensor, split_k: int,
                            stream=None) -> torch.Tensor:
     """Two-pass split-K C = A * B^T; workspace (fp32) is allocated if not given."""
     _dev(A, "A"), _dev(Bs, "Bs")
-    M, K = A.shape
+    M, K = A.shape[0], k_elements(A)
     N = Bs.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
@@ -279,9 +292,10 @@ def probe_mfma_layout(which: int, a: torch.Tensor, b: torch.Tensor, stream=None)
 
 
 def probe_mfma_scaled(a: torch.Tensor, b: torch.Tensor, sa: torch.Tensor, sb: torch.Tensor,
-                      stream=None) -> torch.Tensor:
+                      which: int = 0, stream=None) -> torch.Tensor:
     out = torch.empty(64 * 4, dtype=torch.float32, device=a.device)
-    _check(lib().dgp_probe_mfma_scaled(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(out), _stream_handle(stream)))
+    _check(lib().dgp_probe_mfma_scaled(which, _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(out),
+                                       _stream_handle(stream)))
     return out.view(64, 4)
 
 

@@ -16,10 +16,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kNumXcd = 8;          // gfx950: 8 XCDs, workgroups dealt round-robin
 constexpr int kDtypeBf16 = 0;
 constexpr int kDtypeFp8 = 1;
+constexpr int kDtypeFp4 = 2;         // OCP E2M1, two per byte
 constexpr int kScaleNone = 0;
 constexpr int kScaleTensor = 1;
 constexpr int kScaleBlock = 2;
 constexpr int kScaleMx = 3;         // mxfp8: E8M0 byte per 128-K block per row of A / of B
+constexpr int kScaleMx32 = 4;       // mxfp4: E8M0 byte per 32-K block per row of A / of B
 constexpr int kOutBf16 = 0;         // direct epilogue: bf16 C
 constexpr int kOutPartial = 1;      // split-K pass 1: fp32 partials
 

@@ -60,7 +60,9 @@ dgp_status ok()
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int elem_bytes(int dtype) { return dtype == DGP_BF16 ? 2 : 1; }
+// Bytes of a row of K elements (fp4 packs two elements per byte).
+int64_t row_bytes(int dtype, int64_t K) { return dtype == DGP_BF16 ? 2 * K : dtype == DGP_FP4_E2M1 ? K / 2 : K; }
+bool known_dtype(int dtype) { return dtype == DGP_BF16 || dtype == DGP_FP8_E4M3 || dtype == DGP_FP4_E2M1; }
 
 // Per-row byte limit: keeps every in-tile offset of the kernels in 32 bits.
 constexpr int64_t kMaxRowBytes = int64_t(1) << 23;
@@ -136,6 +138,8 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
+    if (dtype == DGP_FP4_E2M1)   // mxfp4: the K-split decode kernel only
+        return find_spec(Query{kStream, dtype, scale, out, 16, 16});
     if (scale == DGP_SCALE_BLOCK128 || scale == DGP_SCALE_MX128 || M <= 32) {
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
@@ -238,16 +242,18 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
 
 dgp_status validate(const GemmCall &c, Plan *plan)
 {
-    if (c.dtype != DGP_BF16 && c.dtype != DGP_FP8_E4M3)
-        return fail(DGP_ERR_DTYPE, "dtype %d is neither DGP_BF16 nor DGP_FP8_E4M3", c.dtype);
+    if (!known_dtype(c.dtype))
+        return fail(DGP_ERR_DTYPE, "dtype %d is not DGP_BF16, DGP_FP8_E4M3 or DGP_FP4_E2M1", c.dtype);
     if (c.M < 0 || c.N < 0 || c.K < 0)
         return fail(DGP_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld", (long long)c.M, (long long)c.N,
                     (long long)c.K);
-    if (c.scale < DGP_SCALE_NONE || c.scale > DGP_SCALE_MX128)
+    if (c.scale < DGP_SCALE_NONE || c.scale > DGP_SCALE_MX32)
         return fail(DGP_ERR_SCALE_MODE, "unknown scale mode %d", c.scale);
+    if ((c.dtype == DGP_FP4_E2M1) != (c.scale == DGP_SCALE_MX32))
+        return fail(DGP_ERR_SCALE_MODE, "DGP_FP4_E2M1 takes DGP_SCALE_MX32, and only it");
     if (c.dtype == DGP_BF16 && c.scale != DGP_SCALE_NONE)
         return fail(DGP_ERR_SCALE_MODE, "bf16 takes DGP_SCALE_NONE");
-    if (c.dtype == DGP_FP8_E4M3 && c.scale == DGP_SCALE_NONE)
+    if (c.dtype == DGP_FP8_E4M3 && (c.scale == DGP_SCALE_NONE || c.scale == DGP_SCALE_MX32))
         return fail(DGP_ERR_SCALE_MODE, "fp8 takes DGP_SCALE_TENSOR, DGP_SCALE_BLOCK128 or DGP_SCALE_MX128");
     if (c.split_k < 1)
         return fail(DGP_ERR_SPLITK, "split_k %d < 1", c.split_k);
@@ -262,9 +268,11 @@ dgp_status validate(const GemmCall &c, Plan *plan)
     }
     if (c.N % 16 != 0)
         return fail(DGP_ERR_SHAPE, "N=%lld is not a multiple of 16 (preshuffle block rows)", (long long)c.N);
-    const int64_t Kb = c.K * elem_bytes(c.dtype);
+    if (c.dtype == DGP_FP4_E2M1 && c.K % 2 != 0)
+        return fail(DGP_ERR_SHAPE, "fp4 K=%lld is odd", (long long)c.K);
+    const int64_t Kb = row_bytes(c.dtype, c.K);
     if (Kb % 128 != 0)
-        return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld is not a multiple of 128", (long long)Kb);
+        return fail(DGP_ERR_SHAPE, "row bytes %lld (K=%lld) are not a multiple of 128", (long long)Kb, (long long)c.K);
     if (Kb > kMaxRowBytes)
         return fail(DGP_ERR_SHAPE, "K*element_bytes=%lld exceeds %lld", (long long)Kb, (long long)kMaxRowBytes);
     if (c.M > INT32_MAX / 2 || c.N > INT32_MAX / 2)
@@ -343,7 +351,7 @@ dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
     a.M = (int)c.M;
     a.N = (int)c.N;
     a.K = (int)c.K;
-    a.Kb = (int)(c.K * elem_bytes(c.dtype));
+    a.Kb = (int)row_bytes(c.dtype, c.K);
     a.Ks = a.Kb / c.split_k;
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
@@ -360,11 +368,13 @@ dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
 
 dgp_status shuffle(const void *src, void *dst, int64_t N, int64_t K, int dtype, void *stream, bool inverse)
 {
-    if (dtype != DGP_BF16 && dtype != DGP_FP8_E4M3)
-        return fail(DGP_ERR_DTYPE, "dtype %d is neither DGP_BF16 nor DGP_FP8_E4M3", dtype);
+    if (!known_dtype(dtype))
+        return fail(DGP_ERR_DTYPE, "dtype %d is not DGP_BF16, DGP_FP8_E4M3 or DGP_FP4_E2M1", dtype);
     if (N < 0 || K < 0)
         return fail(DGP_ERR_SHAPE, "negative size N=%lld K=%lld", (long long)N, (long long)K);
-    const int64_t Kb = K * elem_bytes(dtype);
+    if (dtype == DGP_FP4_E2M1 && K % 2 != 0)
+        return fail(DGP_ERR_SHAPE, "fp4 K=%lld is odd", (long long)K);
+    const int64_t Kb = row_bytes(dtype, K);
     if (N % 16 != 0)
         return fail(DGP_ERR_SHAPE, "N=%lld is not a multiple of 16", (long long)N);
     if (Kb % 64 != 0)
@@ -540,9 +550,11 @@ dgp_status dgp_probe_mfma_layout(int which, const void *a, const void *b, float 
     return hip_status(launch_probe_mfma(which, a, b, out, (hipStream_t)stream), "probe launch");
 }
 
-dgp_status dgp_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
-                                 void *stream)
+dgp_status dgp_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
+                                 float *out, void *stream)
 {
+    if (which != 0 && which != 1)
+        return fail(DGP_ERR_CONFIG, "which must be 0 or 1");
     if (!a || !b || !sa || !sb || !out)
         return fail(DGP_ERR_NULL, "NULL buffer");
     if (!aligned16(a) || !aligned16(b) || !aligned16(out))
@@ -550,7 +562,7 @@ dgp_status dgp_probe_mfma_scaled(const void *a, const void *b, const void *sa, c
     dgp_status st = check_device_arch();
     if (st != DGP_OK)
         return st;
-    return hip_status(launch_probe_mfma_scaled(a, b, sa, sb, out, (hipStream_t)stream), "probe launch");
+    return hip_status(launch_probe_mfma_scaled(which, a, b, sa, sb, out, (hipStream_t)stream), "probe launch");
 }
 
 dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, void *stream)

@@ -58,6 +58,17 @@ __device__ inline f32x4 mfma_mx(const i32x8 &b, const i32x8 &a, const f32x4 &c, 
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea);
 }
 
+// Hardware-scaled E2M1 MFMA (mxfp4): 16 bytes = 32 values per lane, lane l
+// holding K [32g, 32g+32) (g = l/16) of its row -- exactly one 32-element
+// microscaling block -- whose E8M0 scales are eb (B fragment, first operand)
+// and ea (A fragment, second operand).
+__device__ inline f32x4 mfma_mx4(const i32x4 &b, const i32x4 &a, const f32x4 &c, int eb, int ea)
+{
+    const i32x8 b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+    const i32x8 a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, c, 4, 4, 0, eb, 0, ea);
+}
+
 __device__ inline i32x8 cat(const i32x4 &lo, const i32x4 &hi)
 {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -75,11 +86,16 @@ struct Op<kDtypeFp8> {
     using Frag = i32x8;
     static constexpr int kBlocks = 2;   // 128 K-bytes
 };
+template <>
+struct Op<kDtypeFp4> {
+    using Frag = i32x4;
+    static constexpr int kBlocks = 1;   // 64 K-bytes = 128 elements
+};
 
 template <int DT>
 __device__ inline typename Op<DT>::Frag lds_frag(const uint8_t *p)
 {
-    if constexpr (DT == kDtypeBf16) {
+    if constexpr (Op<DT>::kBlocks == 1) {
         return *reinterpret_cast<const i32x4 *>(p);
     } else {
         return cat(*reinterpret_cast<const i32x4 *>(p), *reinterpret_cast<const i32x4 *>(p + 1024));

@@ -247,7 +247,9 @@ gemm_ksplit_kernel(const GemmArgs p)
     const int per = nsteps / NW, extra = nsteps % NW;
     const int s0 = wave * per + (wave < extra ? wave : extra);
     const int s1 = s0 + per + (wave < extra ? 1 : 0);
-    const int kblocks_row = p.K / 128;   // blockscale: scale columns per row
+    // Scale columns per row: one per 128-K block (blockscale, mxfp8), one per
+    // 32-K block (mxfp4).
+    const int kblocks_row = SCALE == kScaleMx32 ? p.K / 32 : p.K / 128;
 
     const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
     const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
@@ -257,10 +259,10 @@ gemm_ksplit_kernel(const GemmArgs p)
     const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
     const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
     // mxfp8: this lane's A row and B column E8M0 rows (A rows >= M: none).
-    const uint8_t *xa_row = (SCALE == kScaleMx && m < p.M)
-                                ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
-    const uint8_t *xb_row = SCALE == kScaleMx
-                                ? static_cast<const uint8_t *>(p.sB) + (int64_t)(strip * 16 + (lane & 15)) * kblocks_row
+    constexpr bool kMx = SCALE == kScaleMx || SCALE == kScaleMx32;
+    const uint8_t *xa_row = (kMx && m < p.M) ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row
+                                             : nullptr;
+    const uint8_t *xb_row = kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)(strip * 16 + (lane & 15)) * kblocks_row
                                 : nullptr;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -287,7 +289,7 @@ gemm_ksplit_kernel(const GemmArgs p)
             const int st = st0 + d;
             if (st < s1) {
                 Frag a, b;
-                if constexpr (DT == kDtypeBf16) {
+                if constexpr (kStepCh == 1) {
                     a = areg[d][0];
                     b = breg[d][0];
                 } else {
@@ -306,6 +308,10 @@ gemm_ksplit_kernel(const GemmArgs p)
                 } else if constexpr (SCALE == kScaleMx) {
                     const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
                     acc = mfma_mx(b, a, acc, xb_row[kb], xa_row ? xa_row[kb] : 127);
+                } else if constexpr (SCALE == kScaleMx32) {
+                    // this lane's 16 bytes are one 32-element block: 16 bytes per block
+                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 16u) + (lane >> 4);
+                    acc = mfma_mx4(b, a, acc, xb_row[kb], xa_row ? xa_row[kb] : 127);
                 } else {
                     acc = mfma_op(b, a, acc);
                 }
@@ -384,6 +390,7 @@ static const KernelSpec kStreamKernels[] = {
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32),
 };
 
 const KernelSpec *stream_kernels(int *count)

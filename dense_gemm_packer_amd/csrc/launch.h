@@ -63,8 +63,8 @@ hipError_t launch_splitk_reduce(const float *ws, void *C, int64_t M, int64_t N, 
 // Probes (probe.hip).
 hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s);
 hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s);
-hipError_t launch_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
-                                    hipStream_t s);
+hipError_t launch_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
+                                    float *out, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
 hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void *ops, uint32_t *sink,

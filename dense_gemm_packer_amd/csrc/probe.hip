@@ -27,17 +27,24 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(int which, const uint8_t
     *reinterpret_cast<f32x4 *>(out + l * 4) = acc;
 }
 
-// One hardware-scaled e4m3 MFMA: lane l supplies E8M0 scale byte sa[l] for
-// its A fragment (src1 here, as in the GEMM) and sb[l] for its B fragment
-// (src0), each in byte 0 of a 32-bit operand (op_sel 0).
+// One hardware-scaled MFMA: lane l supplies E8M0 scale byte sa[l] for its A
+// fragment (src1 here, as in the GEMM) and sb[l] for its B fragment (src0),
+// each in byte 0 of a 32-bit operand (op_sel 0).  FMT 0: e4m3 operands, 32
+// bytes per lane; FMT 4: e2m1 operands, the first 16 bytes of each lane's
+// 32-byte slot (32 fp4 values), the upper half unused.
+template <int FMT>
 __global__ __launch_bounds__(64) void probe_mfma_scaled_kernel(const uint8_t *a, const uint8_t *b,
                                                                const uint8_t *sa, const uint8_t *sb, float *out)
 {
     const int l = threadIdx.x;
-    const i32x8 x = *reinterpret_cast<const i32x8 *>(a + l * 32);
-    const i32x8 y = *reinterpret_cast<const i32x8 *>(b + l * 32);
+    i32x8 x = *reinterpret_cast<const i32x8 *>(a + l * 32);
+    i32x8 y = *reinterpret_cast<const i32x8 *>(b + l * 32);
+    if constexpr (FMT == 4) {
+        x.s4 = x.s5 = x.s6 = x.s7 = 0;
+        y.s4 = y.s5 = y.s6 = y.s7 = 0;
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(y, x, acc, 0, 0, 0, (int)sb[l], 0, (int)sa[l]);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(y, x, acc, FMT, FMT, 0, (int)sb[l], 0, (int)sa[l]);
     *reinterpret_cast<f32x4 *>(out + l * 4) = acc;
 }
 
@@ -147,11 +154,15 @@ hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out
     return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
-                                    hipStream_t s)
+hipError_t launch_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
+                                    float *out, hipStream_t s)
 {
-    probe_mfma_scaled_kernel<<<1, 64, 0, s>>>((const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sa,
-                                              (const uint8_t *)sb, out);
+    if (which == 0)
+        probe_mfma_scaled_kernel<0><<<1, 64, 0, s>>>((const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sa,
+                                                     (const uint8_t *)sb, out);
+    else
+        probe_mfma_scaled_kernel<4><<<1, 64, 0, s>>>((const uint8_t *)a, (const uint8_t *)b, (const uint8_t *)sa,
+                                                     (const uint8_t *)sb, out);
     return hipGetLastError();
 }
 

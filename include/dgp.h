@@ -55,7 +55,9 @@ typedef enum dgp_status {
     DGP_ERR_HIP = 10         /* a HIP runtime call or kernel launch failed       */
 } dgp_status;
 
-typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1 } dgp_dtype;
+/* Element types.  K always counts elements; a row of DGP_FP4_E2M1 (OCP E2M1,
+ * two per byte, element 2j in the low nibble of byte j) is K/2 bytes. */
+typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1, DGP_FP4_E2M1 = 2 } dgp_dtype;
 
 /* DGP_SCALE_NONE: bf16 only; sA, sB unused.  DGP_SCALE_TENSOR: fp8 only; sA,
  * sB each point to one fp32 and C = bf16(acc * (sA*sB)).  DGP_SCALE_BLOCK128:
@@ -68,12 +70,16 @@ typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1 } dgp_dtype;
  * 2^(e-127) (255: NaN) for one row of A or one row of B (= one column of C)
  * over one 128-wide K block; the matrix-core instruction applies them to each
  * block's products ([P3] "What's included": mxfp8 with 128-element blocks on
- * the hardware-scaled MFMA).  fp32 scales must be 4-byte aligned. */
+ * the hardware-scaled MFMA).  DGP_SCALE_MX32 (mxfp4): the only mode of
+ * DGP_FP4_E2M1, and only for it; as MX128 but one E8M0 byte per 32-element
+ * block, sA [M][K/32], sB [N][K/32] ([P3] "What's included": mxfp4, 4-bit
+ * packed with 32-element E8M0 blocks).  fp32 scales must be 4-byte aligned. */
 typedef enum dgp_scale_mode {
     DGP_SCALE_NONE = 0,
     DGP_SCALE_TENSOR = 1,
     DGP_SCALE_BLOCK128 = 2,
-    DGP_SCALE_MX128 = 3
+    DGP_SCALE_MX128 = 3,
+    DGP_SCALE_MX32 = 4
 } dgp_scale_mode;
 
 /* Optional tile configuration.  Pass NULL to use the built-in per-shape table.
@@ -156,8 +162,8 @@ dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dt
  * "Performance": bf16 in, bf16 out; [P3] "What's included": direct-output
  * epilogue for every scale mode).
  *
- * Requires M, N, K >= 0; N % 16 == 0; (K*element_bytes) % 128 == 0 (bf16:
- * K % 64, fp8: K % 128 -- the fp8 matrix-core step is 128 deep); blockscale
+ * Requires M, N, K >= 0; N % 16 == 0; row bytes % 128 == 0 (bf16: K % 64,
+ * fp8: K % 128 -- the fp8 matrix-core step is 128 deep, fp4: K % 256); blockscale
  * also N % 128 == 0 and K % 128 == 0 (rejected, never rounded up: the review
  * on [P3] flags the silent ceil-division), mxfp8 K % 128 == 0; A, Bs, C
  * 16-byte aligned.  sA, sB: device pointers to the scales of `scale_mode`.

@@ -70,15 +70,17 @@ dgp_status dgp_select_kernel(int64_t M, int64_t N, int64_t K, int dtype, int sca
 dgp_status dgp_probe_mfma_layout(int which, const void *a, const void *b, float *out, void *stream);
 
 /*
- * dgp_probe_mfma_scaled -- one hardware-scaled e4m3 matrix-core instruction
+ * dgp_probe_mfma_scaled -- one hardware-scaled matrix-core instruction
  * (v_mfma_scale_f32_16x16x128_f8f6f4) with per-lane E8M0 scales, operands in
  * the order the GEMM uses: the B fragment is the instruction's first operand
  * (scale sb[l]) and the A fragment its second (scale sa[l]).
+ * which = 0: e4m3 operands, 32 bytes per lane; which = 1: e2m1 operands, 16
+ * bytes (32 values) per lane taken from the first half of its 32-byte slot.
  * a, b: device buffers of 64 lanes x 32 bytes (lane-major); sa, sb: 64 bytes
  * each; out: 64 x 4 fp32 (lane-major accumulator registers).
  */
-dgp_status dgp_probe_mfma_scaled(const void *a, const void *b, const void *sa, const void *sb, float *out,
-                                 void *stream);
+dgp_status dgp_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
+                                 float *out, void *stream);
 
 /*
  * dgp_probe_lds_dma -- one wave copies 64 x 16 bytes from src (lane l reads

@@ -11,9 +11,10 @@ DEV = "cuda:0"
 
 
 def dev_codes(codes: np.ndarray, dtype: str) -> torch.Tensor:
-    """bf16 bit patterns (uint16) or e4m3 codes (uint8) -> device tensor."""
+    """bf16 bit patterns (uint16), e4m3 codes (uint8) or packed e2m1 pairs
+    (uint8, [rows][K/2]) -> device tensor of the matching torch type."""
     t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
-    t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn)
+    t = t.view({"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "fp4": torch.float4_e2m1fn_x2}[dtype])
     return t.to(DEV)
 
 
@@ -27,7 +28,7 @@ def dev_scales(x, mode: str) -> torch.Tensor | None:
     """Scales to the device: E8M0 bytes for mx128, fp32 otherwise."""
     if x is None:
         return None
-    if mode == "mx128":
+    if mode in ("mx128", "mx32"):
         return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.uint8))).to(DEV)
     return dev_f32(x)
 
@@ -41,17 +42,17 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def odt(dtype: str) -> int:
-    return oracle.BF16 if dtype == "bf16" else oracle.FP8_E4M3
+    return {"bf16": oracle.BF16, "fp8": oracle.FP8_E4M3, "fp4": oracle.FP4_E2M1}[dtype]
 
 
 def omode(mode: str) -> int:
     return {"none": oracle.SCALE_NONE, "tensor": oracle.SCALE_TENSOR, "block128": oracle.SCALE_BLOCK128,
-            "mx128": oracle.SCALE_MX128}[mode]
+            "mx128": oracle.SCALE_MX128, "mx32": oracle.SCALE_MX32}[mode]
 
 
 def dmode(mode: str) -> int:
     return {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128,
-            "mx128": dgp.SCALE_MX128}[mode]
+            "mx128": dgp.SCALE_MX128, "mx32": dgp.SCALE_MX32}[mode]
 
 
 def run_gpu(A, B, dtype, mode, sA=None, sB=None, split_k=1, config=None, Bs_dev=None):

@@ -88,13 +88,50 @@ def test_mfma_scaled_e8m0_semantics(per_group):
     to8 = lambda v: torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).contiguous().to(DEV)
     u8 = lambda v: torch.from_numpy(v).to(DEV)
     # the probe passes its `b` buffer as the first operand and `a` as the second
-    out = dgp.probe_mfma_scaled(to8(yb), to8(xa), u8(sa), u8(sb)).cpu().numpy()
+    out = dgp.probe_mfma_scaled(to8(yb), to8(xa), u8(sa), u8(sb), which=0).cpu().numpy()
     D = np.zeros((16, 16))
     for q in range(4):
         ks = groups[q]
         sub = X[:, ks].astype(np.float64) @ Y[ks, :].astype(np.float64)
         D += sub * np.exp2(sb[16 * q:16 * q + 16].astype(np.float64) - 127)[:, None] \
                  * np.exp2(sa[16 * q:16 * q + 16].astype(np.float64) - 127)[None, :]
+    want = np.array([[D[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)], np.float32)
+    assert np.array_equal(out, want)
+
+
+def _pack_e2m1(vals):
+    """values on the E2M1 grid -> packed bytes, even element in the low nibble."""
+    import synth
+    return synth.pack_e2m1(synth.to_e2m1_codes(np.asarray(vals, np.float32)))
+
+
+def test_mfma_scaled_e2m1_semantics():
+    """Hardware-scaled MFMA on E2M1 operands (cbsz = blgp = 4) with the
+    library's fp4 operand assembly: lane l holds the 16 bytes = 32 values of
+    K [32g, 32g+32) (g = l//16) of its row -- in the preshuffled layout, a
+    lane's 16-byte read of a 64-byte chunk.  Each lane's block is then
+    exactly one 32-element microscaling block, and lane 16q+i's scale byte
+    scales block q of row i (first operand) / column i (second operand)."""
+    g = np.random.Generator(np.random.PCG64(6))
+    X = g.integers(-4, 5, size=(16, 128)).astype(np.float32)   # first operand
+    Y = g.integers(-4, 5, size=(128, 16)).astype(np.float32)   # second operand
+    sb = g.integers(125, 130, size=64).astype(np.uint8)
+    sa = g.integers(125, 130, size=64).astype(np.uint8)
+    first = np.zeros((64, 32), np.uint8)
+    second = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        q, i = l // 16, l % 16
+        first[l, :16] = _pack_e2m1(X[i, 32 * q:32 * q + 32])
+        second[l, :16] = _pack_e2m1(Y[32 * q:32 * q + 32, i])
+    u8 = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    # the probe passes its `b` buffer as the first operand and `a` as the second
+    out = dgp.probe_mfma_scaled(u8(second), u8(first), u8(sa), u8(sb), which=1).cpu().numpy()
+    D = np.zeros((16, 16))
+    for q in range(4):
+        ks = slice(32 * q, 32 * q + 32)
+        D += (X[:, ks].astype(np.float64) @ Y[ks, :].astype(np.float64)) \
+            * np.exp2(sb[16 * q:16 * q + 16].astype(np.float64) - 127)[:, None] \
+            * np.exp2(sa[16 * q:16 * q + 16].astype(np.float64) - 127)[None, :]
     want = np.array([[D[4 * (l // 16) + r, l % 16] for r in range(4)] for l in range(64)], np.float32)
     assert np.array_equal(out, want)
 

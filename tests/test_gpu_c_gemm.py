@@ -21,6 +21,10 @@ TILED = [(256, 256, 1, 8), (256, 256, 2, 8), (128, 256, 1, 8), (128, 128, 2, 4)]
 
 
 def rand_inputs(dtype, mode, M, N, K, seed):
+    if dtype == "fp4":
+        A, sA = synth.fp4_mx32(M, K, seed, seed + 2)
+        B, sB = synth.fp4_mx32(N, K, seed + 1, seed + 3)
+        return A, B, sA, sB
     if dtype == "bf16":
         return synth.bf16_uniform((M, K), seed), synth.bf16_uniform((N, K), seed + 1), None, None
     if mode == "tensor":
@@ -46,6 +50,9 @@ def exact_inputs(dtype, mode, M, N, K, seed):
     if mode == "mx128":
         return (A, B, synth.exact_e8m0_scales((M, K // 128), seed + 2),
                 synth.exact_e8m0_scales((N, K // 128), seed + 3))
+    if mode == "mx32":
+        return (A, B, synth.exact_e8m0_scales((M, K // 32), seed + 2),
+                synth.exact_e8m0_scales((N, K // 32), seed + 3))
     return (A, B, synth.exact_block_scales((M, K // 128), seed + 2),
             synth.exact_block_scales((N // 128, K // 128), seed + 3))
 
@@ -69,6 +76,10 @@ CASES = [  # dtype, mode, M, N, K
     ("fp8", "mx128", 1, 2048, 896),
     ("fp8", "mx128", 37, 144, 768),
     ("fp8", "mx128", 300, 272, 512),
+    ("fp4", "mx32", 16, 256, 1024),
+    ("fp4", "mx32", 1, 2048, 768),
+    ("fp4", "mx32", 37, 144, 512),
+    ("fp4", "mx32", 300, 272, 256),
 ]
 
 
@@ -92,15 +103,15 @@ def test_every_compiled_kernel():
     """Each kernel of the compiled table, selected exactly through its config,
     on inputs ragged in M and N: exact integers bit-exact, random data within
     tolerance.  Split-output kernels run with split_k = 2."""
-    names = {0: "none", 1: "tensor", 2: "block128", 3: "mx128"}
+    names = {0: "none", 1: "tensor", 2: "block128", 3: "mx128", 4: "mx32"}
     for cfg, dt, sm, split_out in dgp.kernels():
-        dtype = "bf16" if dt == dgp.BF16 else "fp8"
+        dtype = {dgp.BF16: "bf16", dgp.FP8_E4M3: "fp8", dgp.FP4_E2M1: "fp4"}[dt]
         mode = names[sm]
         if cfg.tile_m == 16:
             M, N = 37, 384
         else:
             M, N = 2 * cfg.tile_m + 44, 2 * cfg.tile_n + 128
-        K = 1024 if dtype == "fp8" else 512
+        K = 1024 if dtype in ("fp8", "fp4") else 512
         split = 2 if split_out else 1
         what = f"{dtype} {mode} tile {cfg.tile_m}x{cfg.tile_n}x{cfg.tile_k} wm{cfg.waves_m} d{cfg.prefetch} s{split}"
         A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 5)
@@ -242,6 +253,43 @@ def test_schedules_ragged_splitk_and_remap(dtype, sched):
     got = run_gpu(A, B, dtype, mode, sA, sB, config=dgp.Config(256, 256, 128, 1, 8, 0, 0, wm, pf, sched))
     c32, _ = run_oracle(A, B, dtype, mode, sA, sB)
     assert_close(got, c32)
+
+
+@pytest.mark.parametrize("M", [1, 16, 20])
+@pytest.mark.parametrize("split_k", [1, 2, 4, 7])
+def test_mxfp4_decode(M, split_k):
+    """mxfp4 through the K-split kernel: exact integers bit-exact, random
+    microscaled data within tolerance, at the decode K = 7168; split 7 gives
+    8 steps of 64 bytes per split, split 4 14 (uneven over 8 waves)."""
+    N, K = 384, 7168
+    A, B, sA, sB = exact_inputs("fp4", "mx32", M, N, K, 51)
+    got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k, config=dgp.Config(16, 16, 0, 0, 1, 0, 0))
+    _, c16 = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
+    assert np.array_equal(got, c16)
+    A, B, sA, sB = rand_inputs("fp4", "mx32", M, N, K, 52)
+    got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
+    c32, _ = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
+    assert_close(got, c32)
+
+
+def test_mxfp4_scale_indexing_and_packer():
+    """Doubling one column's 32-block B scales doubles exactly that column; the
+    packer round-trips fp4 weights bit-exactly (bytes are bytes)."""
+    M, N, K = 3, 64, 512
+    A, B, eA, eB = exact_inputs("fp4", "mx32", M, N, K, 61)
+    eA[:] = 127
+    eB[:] = 127
+    base = run_gpu(A, B, "fp4", "mx32", eA, eB)
+    eB2 = eB.copy()
+    eB2[21, :] = 128
+    got = run_gpu(A, B, "fp4", "mx32", eA, eB2)
+    f = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f(got)[:, 21], 2 * f(base)[:, 21])
+    assert np.array_equal(np.delete(got, 21, axis=1), np.delete(base, 21, axis=1))
+    Bd = dev_codes(B, "fp4")
+    Bs = dgp.preshuffle_b(Bd)
+    assert np.array_equal(Bs.view(torch.uint8).cpu().numpy(), oracle.preshuffle_b(B))
+    assert torch.equal(dgp.unshuffle_b(Bs).view(torch.uint8), Bd.view(torch.uint8))
 
 
 @pytest.mark.parametrize("tile_n", [64, 16])

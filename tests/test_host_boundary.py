@@ -14,8 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INCLUDE = os.path.join(ROOT, "include")
 
 OK, NULL, SHAPE, ALIGN, DTYPE, SCALE, SPLITK, WS, CONFIG, ARCH, HIP = range(11)
-BF16, FP8 = 0, 1
-NONE, TENSOR, BLOCK, MX = 0, 1, 2, 3
+BF16, FP8, FP4 = 0, 1, 2
+NONE, TENSOR, BLOCK, MX, MX32 = 0, 1, 2, 3, 4
 P = 0x10000          # aligned fake device address (never dereferenced)
 
 
@@ -92,6 +92,10 @@ def splitk(L, split, ws=P, ws_bytes=1 << 30, **kw):
     (dict(scale=BLOCK, N=64), SHAPE),                     # blockscale N % 128
     (dict(dtype=BF16, scale=MX, K=64), SCALE),            # mxfp8 is fp8 only
     (dict(scale=MX, sA=0), NULL),                          # E8M0 bytes need pointers too
+    (dict(dtype=FP4, scale=MX), SCALE),                    # fp4 takes only its 32-block scales
+    (dict(dtype=FP8, scale=MX32), SCALE),                  # and they only fp4
+    (dict(dtype=FP4, scale=MX32, K=128), SHAPE),           # fp4 rows of 64 bytes
+    (dict(dtype=FP4, scale=MX32, K=255), SHAPE),           # odd K
     (dict(C=0), NULL), (dict(A=0), NULL), (dict(Bs=0), NULL),
     (dict(sA=0), NULL), (dict(sB=0), NULL),
     (dict(A=P + 8), ALIGN), (dict(Bs=P + 4), ALIGN), (dict(C=P + 2), ALIGN), (dict(sA=P + 1), ALIGN),
@@ -200,7 +204,7 @@ def test_kernel_table(dgp, L):
                cfg.preload_dsrd, cfg.schedule, dt, sm, split_out)
         assert key not in seen
         seen.add(key)
-        assert (dt, sm) in ((0, 0), (1, 1), (1, 2), (1, 3))
+        assert (dt, sm) in ((0, 0), (1, 1), (1, 2), (1, 3), (2, 4))
         if cfg.tile_m > 16:
             # the A-tile granularity rule: whole 16-byte loads per thread
             assert (cfg.tile_m * cfg.tile_k) % 1024 == 0 and cfg.prefetch >= 1
