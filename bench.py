@@ -320,7 +320,7 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                 sAt = None if base["sA"] is None else torch.from_numpy(np.ascontiguousarray(
                     base["sA"][:m_] if mode != "tensor" else base["sA"])).to(dev)
                 best = None
-                for split in (1, 2, 4, 8):
+                for split in synth.WORKLOADS[name]["splits"]:
                     Cs = [torch.empty((m_, n_), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
                     wsb = dgp.splitk_workspace_bytes(m_, n_, split)
                     wss = [torch.empty(max(wsb // 4, 4), dtype=torch.float32, device=dev) for _ in range(copies)]

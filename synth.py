@@ -46,7 +46,8 @@ WORKLOADS = {
     "fp8_mx128": dict(cfg=CFG_FP8_MX128, dtype="fp8", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
     "bf16_decode": dict(cfg=CFG_BF16_DECODE, dtype="bf16", Ms=(1, 16), Ns=(2048, 16384), K=7168,
                         splits=(1, 2, 4, 8)),
-    "fp4_mx32": dict(cfg=CFG_FP4_MX32, dtype="fp4", M=16, N=16384, K=7168, splits=(1, 2, 4, 8)),
+    # fp4 rows of K=7168 are 3584 bytes: split ranges must stay whole 128-byte multiples
+    "fp4_mx32": dict(cfg=CFG_FP4_MX32, dtype="fp4", M=16, N=16384, K=7168, splits=(1, 2, 4, 7)),
 }
 
 
