@@ -270,7 +270,7 @@ def select_kernel(M: int, N: int, K: int, dtype: int, scale_mode: int, split_k: 
 def describe_kernel(index: int) -> str:
     """One-line description of compiled kernel `index`."""
     cfg, dt, sm, so = kernels()[index]
-    dts = "bf16" if dt == BF16 else "fp8"
+    dts = {BF16: "bf16", FP8_E4M3: "fp8", FP4_E2M1: "fp4"}[dt]
     if cfg.tile_m == 16 and cfg.tile_n == 16:
         return (f"gemm_ksplit_kernel<{dts}, 16x16 tile, K split over {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")

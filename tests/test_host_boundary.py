@@ -287,3 +287,13 @@ def test_binding_fails_loudly_without_the_library(dgp, monkeypatch, tmp_path):
     monkeypatch.setattr(dgp, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         dgp.lib()
+
+
+def test_tune_spec_parsing(dgp):
+    from dense_gemm_packer_amd import tune
+    assert tune.parse("bf16:4096x4096x8192") == ("bf16", dgp.BF16, dgp.SCALE_NONE, 4096, 4096, 8192, 1)
+    assert tune.parse("mx4:16x16384x7168:7") == ("mx4", dgp.FP4_E2M1, dgp.SCALE_MX32, 16, 16384, 7168, 7)
+    assert tune.parse("fp8b:16x256x1024")[2] == dgp.SCALE_BLOCK128
+    for spec in tune.DEFAULT_SHAPES:
+        kind, dt, sm, M, N, K, split = tune.parse(spec)
+        assert dgp.select_kernel(M, N, K, dt, sm, split) >= 0     # every default shape is valid
