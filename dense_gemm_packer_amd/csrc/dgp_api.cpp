@@ -138,9 +138,7 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    if (dtype == DGP_FP4_E2M1)   // mxfp4: the K-split decode kernel only
-        return find_spec(Query{kStream, dtype, scale, out, 16, 16});
-    if (scale == DGP_SCALE_BLOCK128 || scale == DGP_SCALE_MX128 || M <= 32) {
+    if (scale == DGP_SCALE_BLOCK128 || scale >= DGP_SCALE_MX128 || M <= 32) {
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
         // waves spreads the stream wider (measured faster up to that point).

@@ -14,8 +14,21 @@ namespace dgp {
 
 // =============================================================== stream
 
-// Largest K range (bytes) of the 16 A rows held in LDS at once.
+// Largest K range (bytes) of the 16 A rows held in LDS at once.  mxfp4
+// also stages the panel's E8M0 scales in LDS, so its panel is smaller.
 constexpr int kStreamPanelMax = 8192;
+constexpr int kStreamPanelMax4 = 4096;
+constexpr int stream_panel_max(int dt) { return dt == kDtypeFp4 ? kStreamPanelMax4 : kStreamPanelMax; }
+// mxfp4 scale staging: a panel of S MFMA steps keeps, per A row and per
+// column of the workgroup, its S scale dwords (one dword = the four 32-element
+// blocks of one 64-byte step) plus one dword of padding, so the 16 rows a
+// step reads fall in different LDS banks.
+// Each region (A rows, then columns) is rounded up to whole 64-dword copies.
+constexpr int stream_mx32_region_dwords(int rows, int nsteps) { return (rows * (nsteps + 1) + 63) / 64 * 64; }
+constexpr size_t stream_mx32_scale_bytes(int cols, int panel)
+{
+    return (size_t)4 * (stream_mx32_region_dwords(16, panel / 64) + stream_mx32_region_dwords(cols, panel / 64));
+}
 
 template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
@@ -31,6 +44,10 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     // mxfp8: E8M0 bytes of the panel, per A row and per column of the workgroup.
     __shared__ uint8_t lds_xa[SCALE == kScaleMx ? 16 : 1][kScaleCols];
     __shared__ uint8_t lds_xb[SCALE == kScaleMx ? NW * SPW * 16 : 1][kScaleCols];
+    // mxfp4: scale dwords after the A panel, a region of the 16 A rows m0..
+    // then one of the workgroup's columns (row stride nsteps + 1 dwords).
+    constexpr int kCols = NW * SPW * 16;
+    uint32_t *lds_x4 = reinterpret_cast<uint32_t *>(lds_a + 16 * panel);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -43,12 +60,21 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     const uint32_t Kb = (uint32_t)p.Kb;
     const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
     const int nsteps = panel / kStepBytes;
-    const int kblocks_row = p.K / 128;   // blockscale: scale columns per row
+    // Scale columns per row: one per 128-K block (blockscale, mxfp8), one per
+    // 32-K block (mxfp4).
+    const int kblocks_row = SCALE == kScaleMx32 ? p.K / 32 : p.K / 128;
 
     const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
     const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
     const auto rB = make_rsrc(p.Bs + (int64_t)strip_w * 16 * Kb,
                               clamp_bytes((int64_t)(p.N / 16 - strip_w) * 16 * Kb));
+    // mxfp4 scales of rows m0.. and of the workgroup's columns (unused otherwise)
+    constexpr bool kX4 = SCALE == kScaleMx32;
+    const auto rXa = make_rsrc(kX4 ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblocks_row : nullptr,
+                               kX4 ? clamp_bytes((int64_t)(p.M - m0) * kblocks_row) : 0);
+    const auto rXb = make_rsrc(kX4 ? static_cast<const uint8_t *>(p.sB) + (int64_t)strip_wg * 16 * kblocks_row
+                                   : nullptr,
+                               kX4 ? clamp_bytes((int64_t)(p.N - strip_wg * 16) * kblocks_row) : 0);
     uint32_t b_voff[SPW];
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp)
@@ -126,6 +152,30 @@ gemm_stream_kernel(const GemmArgs p, int panel)
             }
         }
 
+        // mxfp4: this panel's scale dwords -> LDS with the async dword copy
+        // (lane l of a copy lands at its destination + 4l).  Slot e of a
+        // region is (row e / (nsteps+1), step e % (nsteps+1)); the padding
+        // slot repeats the row's last step.  The dword at E8M0 byte
+        // kb0 + 4*step of a row holds the scales of that step's four
+        // 32-element blocks.  Rows >= M and columns >= N read as 0 (2^-127,
+        // finite), which only ever multiplies zero data.
+        if constexpr (SCALE == kScaleMx32) {
+            const uint32_t kb0 = pk / 16u;
+            const int stride = nsteps + 1;
+            auto stage = [&](const auto &rs, uint32_t *dst, int rows) {
+                for (int j = wave; j * 64 < rows * stride; j += NW) {
+                    const int e = j * 64 + lane;
+                    const int r = e / stride < rows ? e / stride : rows - 1;
+                    const int st = e % stride < nsteps ? e % stride : nsteps - 1;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs, (__attribute__((address_space(3))) void *)(dst + j * 64), 4,
+                        (uint32_t)r * (uint32_t)kblocks_row + kb0 + 4u * (uint32_t)st, 0, 0, 0);
+                }
+            };
+            stage(rXa, lds_x4, 16);
+            stage(rXb, lds_x4 + stream_mx32_region_dwords(16, nsteps), kCols);
+        }
+
         // A rows m0..m0+15 of this panel -> LDS, one 1 KiB operand block per
         // 64-byte K chunk (blocks dealt round-robin to the waves).
         for (int c = wave; c < panel / 64; c += NW)
@@ -174,7 +224,7 @@ gemm_stream_kernel(const GemmArgs p, int panel)
 #pragma unroll
                     for (int sp = 0; sp < SPW; ++sp) {
                         Frag b;
-                        if constexpr (DT == kDtypeBf16)
+                        if constexpr (kStepCh == 1)
                             b = breg[d][sp][0];
                         else
                             b = cat(breg[d][sp][0], breg[d][sp][1]);
@@ -190,6 +240,15 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                         } else if constexpr (SCALE == kScaleMx) {
                             acc[sp] = mfma_mx(b, a, acc[sp], lds_xb[(wave * SPW + sp) * 16 + (lane & 15)][st],
                                               lds_xa[lane & 15][st]);
+                        } else if constexpr (SCALE == kScaleMx32) {
+                            // lane 16g+i: block g of the step, A row i / column i
+                            const uint8_t *xa4 = reinterpret_cast<const uint8_t *>(lds_x4);
+                            const uint8_t *xb4 = reinterpret_cast<const uint8_t *>(
+                                lds_x4 + stream_mx32_region_dwords(16, nsteps));
+                            const int ea = xa4[((lane & 15) * (nsteps + 1) + st) * 4 + (lane >> 4)];
+                            const int eb = xb4[(((wave * SPW + sp) * 16 + (lane & 15)) * (nsteps + 1) + st) * 4 +
+                                               (lane >> 4)];
+                            acc[sp] = mfma_mx4(b, a, acc[sp], eb, ea);
                         } else {
                             acc[sp] = mfma_op(b, a, acc[sp]);
                         }
@@ -342,20 +401,24 @@ template <int DT, int NW, int SPW, int DEPTH, int SCALE, int OUT>
 void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
     constexpr int kStepBytes = 64 * Op<DT>::kBlocks;
+    constexpr int kMax = stream_panel_max(DT);
     // Panel: the whole K range of a split if its 16 rows fit, else the
-    // largest step multiple <= kStreamPanelMax that divides it (the host
-    // layer only accepts K ranges for which one exists).
+    // largest step multiple <= kMax that divides it (K ranges are whole
+    // multiples of 128 bytes, so one exists).
     int panel = a.Ks;
-    if (panel > kStreamPanelMax) {
-        panel = kStreamPanelMax - kStreamPanelMax % kStepBytes;
+    if (panel > kMax) {
+        panel = kMax - kMax % kStepBytes;
         while (panel > kStepBytes && a.Ks % panel != 0)
             panel -= kStepBytes;
     }
-    const size_t lds = (size_t)16 * panel;
+    auto lds_bytes = [](int pnl) {
+        return (size_t)16 * pnl + (SCALE == kScaleMx32 ? stream_mx32_scale_bytes(NW * SPW * 16, pnl) : 0);
+    };
+    const size_t lds = lds_bytes(panel);
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void *)gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 16 * kStreamPanelMax);
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes(kMax));
         attr_set = true;
     }
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
@@ -372,7 +435,7 @@ void launch_ksplit(const GemmArgs &a, dim3 grid, hipStream_t s)
 #define DGP_KSPLIT_BOTH_OUT(DT, NW, DEPTH, SC)                                                \
     DGP_KSPLIT(DT, NW, DEPTH, SC, kOutBf16), DGP_KSPLIT(DT, NW, DEPTH, SC, kOutPartial)
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
-    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, kStreamPanelMax, NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
+    {kStream, DT, SC, OUT, 16, 16 * NW * SPW, stream_panel_max(DT), NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
      &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
 
 #define DGP_STREAM_BOTH_OUT(DT, NW, SPW, DEPTH, SC)                                           \
@@ -385,6 +448,7 @@ static const KernelSpec kStreamKernels[] = {
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 2, 8, kScaleTensor),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleMx),
+    DGP_STREAM_BOTH_OUT(kDtypeFp4, 4, 1, 8, kScaleMx32),
     // one strip per workgroup, K split over the waves: waves, ring depth
     DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),

@@ -142,7 +142,7 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
 
 @pytest.mark.parametrize("tile_n", [64, 16])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
-                                        ("fp8", "mx128")])
+                                        ("fp8", "mx128"), ("fp4", "mx32")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
 def test_stream_splitk(dtype, mode, M, split_k, tile_n):
@@ -179,12 +179,15 @@ def test_ksplit_uneven_and_empty_slices(dtype, mode):
         assert np.array_equal(got, c16), (steps, split)
 
 
-def test_stream_multi_panel():
-    """K range larger than one LDS panel of A (several panels per split)."""
-    M, N, K = 16, 256, 24576
-    A, B, sA, sB = exact_inputs("fp8", "tensor", M, N, K, 9)
-    got = run_gpu(A, B, "fp8", "tensor", sA, sB, split_k=1, config=dgp.Config(16, 64, 0, 0, 1, 0, 0))
-    _, c16 = run_oracle(A, B, "fp8", "tensor", sA, sB)
+@pytest.mark.parametrize("dtype,mode", [("fp8", "tensor"), ("fp4", "mx32")])
+@pytest.mark.parametrize("split_k", [1, 2])
+def test_stream_multi_panel(dtype, mode, split_k):
+    """K range larger than one LDS panel of A (several panels per split; the
+    fp4 panel, which also stages its scales, is 4096 bytes = 8192 values)."""
+    M, N, K = 20, 272, 24576 if dtype == "fp8" else 40960
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 9)
+    got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=dgp.Config(16, 64, 0, 0, 1, 0, 0))
+    _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
     assert np.array_equal(got, c16)
 
 
@@ -258,34 +261,52 @@ def test_schedules_ragged_splitk_and_remap(dtype, sched):
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 7])
 def test_mxfp4_decode(M, split_k):
-    """mxfp4 through the K-split kernel: exact integers bit-exact, random
-    microscaled data within tolerance, at the decode K = 7168; split 7 gives
-    8 steps of 64 bytes per split, split 4 14 (uneven over 8 waves)."""
+    """mxfp4 through the K-split and the streaming kernel: exact integers
+    bit-exact, random microscaled data within tolerance, at the decode
+    K = 7168; split 7 gives 8 steps of 64 bytes per split, split 4 14
+    (uneven over the K-split kernel's 8 waves)."""
     N, K = 384, 7168
     A, B, sA, sB = exact_inputs("fp4", "mx32", M, N, K, 51)
-    got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k, config=dgp.Config(16, 16, 0, 0, 1, 0, 0))
     _, c16 = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
-    assert np.array_equal(got, c16)
+    for tile_n in (16, 64):
+        got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k, config=dgp.Config(16, tile_n, 0, 0, 1, 0, 0))
+        assert np.array_equal(got, c16), tile_n
     A, B, sA, sB = rand_inputs("fp4", "mx32", M, N, K, 52)
-    got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
     c32, _ = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
-    assert_close(got, c32)
+    for cfg in (None, dgp.Config(16, 64, 0, 0, 1, 0, 0)):
+        got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k, config=cfg)
+        assert_close(got, c32)
 
 
-def test_mxfp4_scale_indexing_and_packer():
-    """Doubling one column's 32-block B scales doubles exactly that column; the
-    packer round-trips fp4 weights bit-exactly (bytes are bytes)."""
+@pytest.mark.parametrize("tile_n", [64, 16])
+def test_mxfp4_scale_indexing_and_packer(tile_n):
+    """Doubling one column's 32-block B scales doubles exactly that column,
+    doubling one A row's doubles exactly that row, and raising one 32-block
+    scale of one column changes only that column; the packer round-trips fp4
+    weights bit-exactly (bytes are bytes)."""
     M, N, K = 3, 64, 512
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
     A, B, eA, eB = exact_inputs("fp4", "mx32", M, N, K, 61)
     eA[:] = 127
     eB[:] = 127
-    base = run_gpu(A, B, "fp4", "mx32", eA, eB)
+    base = run_gpu(A, B, "fp4", "mx32", eA, eB, config=cfg)
+    f = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
     eB2 = eB.copy()
     eB2[21, :] = 128
-    got = run_gpu(A, B, "fp4", "mx32", eA, eB2)
-    f = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    got = run_gpu(A, B, "fp4", "mx32", eA, eB2, config=cfg)
     assert np.array_equal(f(got)[:, 21], 2 * f(base)[:, 21])
     assert np.array_equal(np.delete(got, 21, axis=1), np.delete(base, 21, axis=1))
+    eA2 = eA.copy()
+    eA2[1, :] = 128
+    got = run_gpu(A, B, "fp4", "mx32", eA2, eB, config=cfg)
+    assert np.array_equal(f(got)[1], 2 * f(base)[1])
+    assert np.array_equal(got[[0, 2]], base[[0, 2]])
+    eB3 = eB.copy()
+    eB3[37, 5] = 130
+    got = run_gpu(A, B, "fp4", "mx32", eA, eB3, config=cfg)
+    _, c16 = run_oracle(A, B, "fp4", "mx32", eA, eB3)
+    assert np.array_equal(got, c16)
+    assert np.array_equal(np.delete(got, 37, axis=1), np.delete(base, 37, axis=1))
     Bd = dev_codes(B, "fp4")
     Bs = dgp.preshuffle_b(Bd)
     assert np.array_equal(Bs.view(torch.uint8).cpu().numpy(), oracle.preshuffle_b(B))
