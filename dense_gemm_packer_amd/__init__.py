@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
         "dgp_probe_mfma_scaled": [_int, _vp, _vp, _vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
-        "dgp_probe_stream_read": [_vp, _i64, _vp, _vp],
+        "dgp_probe_stream_read": [_vp, _i64, _int, _vp, _vp],
         "dgp_probe_mfma_peak": [_int, _int, _int, _vp, _vp, _vp],
     }
     for name, args in sigs.items():
@@ -310,9 +310,15 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     _check(lib().dgp_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream_handle(stream)))
 
 
-def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    nbytes = src.numel() * src.element_size()
-    _check(lib().dgp_probe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream_handle(stream)))
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 1024, nbytes: int | None = None,
+                      stream=None) -> None:
+    """Read the first `nbytes` (default: all) bytes of src with `blocks`
+    workgroups, each streaming one contiguous span."""
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else nbytes
+    if nbytes > total:
+        raise ValueError(f"nbytes {nbytes} exceeds the buffer ({total} bytes)")
+    _check(lib().dgp_probe_stream_read(_ptr(src), nbytes, blocks, _ptr(sink), _stream_handle(stream)))
 
 
 # FLOP per matrix-core instruction of dgp_probe_mfma_peak (which = 0, 1), and

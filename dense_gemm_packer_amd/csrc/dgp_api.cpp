@@ -142,7 +142,10 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
         // waves spreads the stream wider (measured faster up to that point).
-        if (N * split_k < 128 * 64)
+        // A single bf16 row also streams faster through the K-split tile at
+        // any N: its 8 waves per workgroup keep more of the weight in flight,
+        // and re-reading one A row per strip costs little.
+        if (N * split_k < 128 * 64 || (dtype == DGP_BF16 && M == 1 && split_k == 1))
             return find_spec(Query{kStream, dtype, scale, out, 16, 16});
         return find_spec(Query{kStream, dtype, scale, out, 16, 64});
     }
@@ -591,10 +594,12 @@ dgp_status dgp_probe_copy(const void *src, void *dst, int64_t bytes, void *strea
     return hip_status(launch_probe_copy(src, dst, bytes, (hipStream_t)stream), "probe launch");
 }
 
-dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, int blocks, uint32_t *sink, void *stream)
 {
-    if (bytes < 0 || bytes % 4096 != 0)
-        return fail(DGP_ERR_SHAPE, "bytes must be a non-negative multiple of 4096");
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(DGP_ERR_SHAPE, "bytes must be a non-negative multiple of 16");
+    if (blocks < 1 || blocks > 65536)
+        return fail(DGP_ERR_SHAPE, "blocks must be in [1, 65536] (got %d)", blocks);
     if (bytes == 0)
         return ok();
     if (!src || !sink)
@@ -604,7 +609,7 @@ dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink,
     dgp_status st = check_device_arch();
     if (st != DGP_OK)
         return st;
-    return hip_status(launch_probe_stream_read(src, bytes, sink, (hipStream_t)stream), "probe launch");
+    return hip_status(launch_probe_stream_read(src, bytes, blocks, sink, (hipStream_t)stream), "probe launch");
 }
 
 dgp_status dgp_probe_mfma_peak(int which, int rounds, int blocks, const void *operands, uint32_t *sink,

@@ -66,7 +66,7 @@ hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst,
 hipError_t launch_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
                                     float *out, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
-hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_stream_read(const void *src, int64_t bytes, int blocks, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void *ops, uint32_t *sink,
                                   hipStream_t s);
 

@@ -70,18 +70,22 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const i32x4 *__restrict
 
 constexpr int kStreamThreads = 512;
 constexpr int kStreamUnroll = 8;   // 16-byte loads in flight per thread
+constexpr int64_t kStreamRound = (int64_t)kStreamThreads * 16 * kStreamUnroll;   // 64 KiB
 
-// Streaming read: round i of workgroup b covers the 64 KiB chunk i*grid + b;
-// thread t reads bytes chunk + u*8192 + 16*t for u < 8 (8 loads in flight per
-// thread, 64 KiB per workgroup), non-temporal.
+// Streaming read: workgroup b reads bytes [b*span, min((b+1)*span, bytes))
+// front to back in rounds of 64 KiB; in a round thread t reads 16 bytes at
+// u*8192 + 16*t for u < 8 (8 loads in flight per thread), non-temporal.  The
+// last round of a span is clamped by the buffer resource, so any span that
+// is a multiple of 16 bytes is read exactly.
 __global__ __launch_bounds__(kStreamThreads) void probe_stream_read_kernel(const uint8_t *__restrict__ src,
-                                                                           int64_t bytes, uint32_t *__restrict__ sink)
+                                                                           int64_t bytes, int64_t span,
+                                                                           uint32_t *__restrict__ sink)
 {
-    constexpr int64_t kChunk = (int64_t)kStreamThreads * 16 * kStreamUnroll;
-    const int64_t chunks = bytes / kChunk;
+    const int64_t b0 = (int64_t)blockIdx.x * span;
+    const int64_t b1 = b0 + span < bytes ? b0 + span : bytes;
     i32x4 x = {0, 0, 0, 0};
-    for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
-        const auto r = make_rsrc(src + c * kChunk, (uint32_t)kChunk);
+    for (int64_t off = b0; off < b1; off += kStreamRound) {
+        const auto r = make_rsrc(src + off, (uint32_t)(b1 - off < kStreamRound ? b1 - off : kStreamRound));
         i32x4 v[kStreamUnroll];
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u)
@@ -194,14 +198,14 @@ hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void 
     return hipGetLastError();
 }
 
-hipError_t launch_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s)
+hipError_t launch_probe_stream_read(const void *src, int64_t bytes, int blocks, uint32_t *sink, hipStream_t s)
 {
-    // Whole 64 KiB chunks are read; the tail (bytes % 64 KiB) is not.
-    const int64_t chunks = bytes / ((int64_t)kStreamThreads * 16 * kStreamUnroll);
-    if (chunks == 0)
-        return hipSuccess;
-    const int64_t blocks = chunks < 1024 ? chunks : 1024;
-    probe_stream_read_kernel<<<(unsigned)blocks, kStreamThreads, 0, s>>>((const uint8_t *)src, bytes, sink);
+    // Equal spans of whole 16-byte units; the last workgroups may get less
+    // (or nothing, when the rounded span already covers the range).
+    const int64_t units = bytes / 16;
+    const int64_t span = (units + blocks - 1) / blocks * 16;
+    const int64_t used = (bytes + span - 1) / span;
+    probe_stream_read_kernel<<<(unsigned)used, kStreamThreads, 0, s>>>((const uint8_t *)src, bytes, span, sink);
     return hipGetLastError();
 }
 

@@ -99,13 +99,15 @@ dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, vo
 dgp_status dgp_probe_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
 /*
- * dgp_probe_stream_read -- read `bytes` bytes (bytes % 4096 == 0; whole 64 KiB
- * chunks are read, a shorter tail is not) with 16-byte non-temporal loads,
- * 8 in flight per thread, 1024 workgroups of 512 threads, and write one
- * 32-bit xor-fold per workgroup to `sink` (>= 4096 uint32, normally left
- * untouched).  Measures the attainable HBM read rate.
+ * dgp_probe_stream_read -- read `bytes` bytes (bytes % 16 == 0) with
+ * `blocks` workgroups of 512 threads (1 <= blocks <= 65536), workgroup b
+ * reading one contiguous span of about bytes/blocks front to back with
+ * 16-byte non-temporal loads, 8 in flight per thread, and write one 32-bit
+ * xor-fold per workgroup to `sink` (>= 4096 uint32, normally left untouched).
+ * Measures the attainable HBM read rate for a range of that size (time it
+ * for a few values of `blocks` and keep the best).
  */
-dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, int blocks, uint32_t *sink, void *stream);
 
 /*
  * dgp_probe_mfma_peak -- sustained matrix-core rate on given operands.

@@ -165,7 +165,11 @@ def test_probe_validation(L):
     assert L.dgp_probe_mfma_layout(0, 0, P, P, None) == NULL
     assert L.dgp_probe_copy(P, P, 17, None) == SHAPE
     assert L.dgp_probe_copy(P, P, 0, None) == OK
-    assert L.dgp_probe_stream_read(P, 4095, P, None) == SHAPE
+    assert L.dgp_probe_stream_read(P, 4088, 512, P, None) == SHAPE     # not whole 16-byte units
+    assert L.dgp_probe_stream_read(P, 4096, 0, P, None) == SHAPE
+    assert L.dgp_probe_stream_read(P, 4096, 65537, P, None) == SHAPE
+    assert L.dgp_probe_stream_read(0, 4096, 512, P, None) == NULL
+    assert L.dgp_probe_stream_read(P, 0, 512, P, None) == OK
     assert L.dgp_probe_mfma_peak(2, 1, 1, P, P, None) == CONFIG
     assert L.dgp_probe_mfma_peak(0, 0, 1, P, P, None) == SHAPE
     assert L.dgp_probe_mfma_peak(1, 1, 0, P, P, None) == SHAPE
@@ -239,6 +243,13 @@ def test_default_selection(dgp):
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 64
     assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)][0].tile_m == 16
+    # a single bf16 row: the K-split tile at any N; fp8 keeps the 64-column tile
+    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
+    assert dgp.kernels()[dgp.select_kernel(2, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 64
+    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.FP8_E4M3, dgp.SCALE_TENSOR)][0].tile_n == 64
+    # mxfp4 follows the same rule as the other decode modes
+    assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 64
+    assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 16
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
