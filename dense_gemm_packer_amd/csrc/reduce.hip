@@ -2,7 +2,8 @@
 // partials ws[s][M][N], summed in fp32 in split order and rounded to bf16
 // once (aiter PR #5148, file table: an fp32 split-K reduction kernel that
 // downcasts once at the final store).  Each thread owns four consecutive
-// outputs: S 16-byte loads, one 8-byte store.  HBM-bound:
+// outputs: S 16-byte loads, issued up to 8 at a time so their latencies
+// overlap, added in split order; one 8-byte store.  HBM-bound:
 // S*M*N*4 + M*N*2 bytes.  Also a zero fill for K = 0 (C = A*B^T = 0).
 #include "common.h"
 #include "launch.h"
@@ -19,14 +20,30 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const flo
     const int64_t g = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
     if (g >= groups)
         return;
+    constexpr int kBatch = 8;
     const float *p = ws + g * 4;
-    f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-    for (int s = 1; s < splits; ++s) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + (int64_t)s * mn));
-        t.x = __fadd_rn(t.x, v.x);
-        t.y = __fadd_rn(t.y, v.y);
-        t.z = __fadd_rn(t.z, v.z);
-        t.w = __fadd_rn(t.w, v.w);
+    // The sum starts from partial 0 itself (not 0 + P_0, which would turn a
+    // -0 partial into +0).
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < splits)
+                v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + (int64_t)(s0 + u) * mn));
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (s0 + u >= splits)
+                break;
+            if (s0 + u == 0) {
+                t = v[0];
+            } else {
+                t.x = __fadd_rn(t.x, v[u].x);
+                t.y = __fadd_rn(t.y, v[u].y);
+                t.z = __fadd_rn(t.z, v[u].z);
+                t.w = __fadd_rn(t.w, v[u].w);
+            }
+        }
     }
     u32x2 out;
     out.x = pack_bf16x2(t.x, t.y);
