@@ -66,11 +66,15 @@ def read_traffic():
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The chip's clocks settle after some 30 ms of load, so the default
+    # warm-up (~40 ms of GEMMs) is long enough for the timed steps to run at
+    # the clock the kernel sustains.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of C in the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of C in the CPU oracle sample (default: all of them)")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and a few GEMM launches (for counter runs)")
     args = ap.parse_args()
