@@ -209,6 +209,52 @@ def test_one_hot_rows_bit_exact(dtype):
         assert np.array_equal(got, B[:, ks].T)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_longest_rows_one_hot(dtype):
+    """The longest rows the library accepts (K * element bytes = 8 MiB): A
+    rows one-hot at distinct k near the end of K reach the largest buffer
+    offsets of the tiled, streaming, K-split and split-K paths.  One-hot rows
+    turn the long contraction into a single product per output, so the
+    oracle computes the expected C from the extracted B columns alone."""
+    eb = 2 if dtype == "bf16" else 1
+    K = (8 << 20) // eb
+    M, N = 272, 272
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    if dtype == "bf16":
+        B = (torch.rand((N, K), generator=gen, device=DEV, dtype=torch.float32) - 0.5).to(torch.bfloat16)
+        one = 0x3F80
+    else:
+        codes = torch.randint(0, 256, (N, K), generator=gen, device=DEV, dtype=torch.int32)
+        codes = torch.where((codes & 0x7F) == 0x7F, torch.zeros_like(codes), codes)   # no NaN codes
+        B = codes.to(torch.uint8).view(torch.float8_e4m3fn)
+        del codes
+        one = 0x38
+    ks = K - 1 - 13 * np.arange(M)
+    A = torch.zeros((M, K), dtype=B.dtype, device=DEV)
+    A.view(torch.int16 if dtype == "bf16" else torch.uint8)[torch.arange(M, device=DEV),
+                                                             torch.from_numpy(ks).to(DEV)] = one
+    Bs = dgp.preshuffle_b(B)
+    # expected: the oracle on A' = [I 0] and B' = the picked columns, padded to 384
+    cols = B.view(torch.int16 if dtype == "bf16" else torch.uint8)[:, torch.from_numpy(ks).to(DEV)].cpu().numpy()
+    del B
+    Kp = 384
+    Ap = np.zeros((M, Kp), dtype=np.uint16 if dtype == "bf16" else np.uint8)
+    Ap[np.arange(M), np.arange(M)] = one
+    Bp = np.zeros((N, Kp), dtype=Ap.dtype)
+    Bp[:, :M] = cols.view(Ap.dtype)
+    mode = "none" if dtype == "bf16" else "tensor"
+    s1 = None if dtype == "bf16" else np.array([1.0], np.float32)
+    _, want = run_oracle(Ap, Bp, dtype, mode, s1, s1)
+    sd = None if dtype == "bf16" else torch.ones(1, device=DEV)
+    runs = [(M, None, 1), (M, dgp.Config(128, 128, 128, 1, 4, 0, 4, 2, 2), 2),
+            (20, dgp.Config(16, 64, 0, 0, 1, 0, 0), 1), (20, dgp.Config(16, 64, 0, 0, 1, 0, 0), 2),
+            (20, dgp.Config(16, 16, 0, 0, 1, 0, 0), 1), (1, None, 4)]
+    for rows, cfg, split in runs:
+        C = dgp.gemm_preshuffle_splitk(A[:rows], Bs, split, sd, sd, config=cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(C), want[:rows]), (rows, cfg, split)
+
+
 def test_identity_b_returns_a():
     M, K = 300, 512
     A = synth.bf16_uniform((M, K), 3)

@@ -1,0 +1,63 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times: the library's built-in kernel selection and every split
+count it reports, on the benchmark's own seeded inputs.  The oracle computes
+sampled rows of C one by one (all N columns of each); random data must be
+within 1e-2 * max|C_ref| of the oracle's fp32 value at the same split count."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_packer_amd as dgp
+import synth
+from gpu_common import DEV, assert_close, dev_codes, dev_scales, dmode, host_bits, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _scales(w, rows):
+    """The workload's scales for its first `rows` rows of A (per-tensor: as is)."""
+    if w["sA"] is None:
+        return None, None
+    sA = w["sA"] if w["scale_mode"] == "tensor" else w["sA"][:rows]
+    return sA, w["sB"]
+
+
+@pytest.mark.parametrize("name", ["bf16_large", "fp8_large"])
+def test_large_workload_sampled_rows(name):
+    """4096 x 4096 x 8192: rows on both sides of every 256-row tile boundary
+    the sample crosses, plus evenly spaced rows."""
+    w = synth.workload_inputs(name)
+    dt, mode, M = w["dtype"], w["scale_mode"], w["M"]
+    A = dev_codes(w["A"], dt)
+    Bs = dgp.preshuffle_b(dev_codes(w["B"], dt))
+    sA, sB = _scales(w, M)
+    C = dgp.gemm_preshuffle(A, Bs, dev_scales(sA, mode), dev_scales(sB, mode), dmode(mode))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.linspace(0, M - 1, 24).astype(np.int64),
+                                     np.array([255, 256, 2047, 2048, M - 1])]))
+    c32, _ = run_oracle(w["A"], w["B"], dt, mode, w["sA"], w["sB"], rows=rows)
+    assert_close(host_bits(C)[rows], c32, what=name)
+
+
+DECODE = [("fp8_decode", 2048), ("fp8_decode", 16384), ("bf16_decode", 2048), ("bf16_decode", 16384),
+          ("fp4_mx32", 2048), ("fp4_mx32", 16384), ("fp8_blockscale", 16384), ("fp8_mx128", 16384)]
+
+
+@pytest.mark.parametrize("name,N", DECODE)
+def test_decode_workload_every_split(name, N):
+    """Decode sizes (K = 7168): M = 1 and 16 where the benchmark times both,
+    every split count of the workload, rows 0, 5 and 15 of C."""
+    w = synth.workload_inputs(name, M=16, N=N)
+    dt, mode = w["dtype"], w["scale_mode"]
+    Bs = dgp.preshuffle_b(dev_codes(w["B"], dt))
+    Ms = (1, 16) if name in ("fp8_decode", "bf16_decode", "fp4_mx32") else (16,)
+    for M in Ms:
+        A = dev_codes(w["A"][:M], dt)
+        sA, sB = _scales(w, M)
+        dA, dB = dev_scales(sA, mode), dev_scales(sB, mode)
+        rows = np.array([0]) if M == 1 else np.array([0, 5, 15])
+        for split in synth.WORKLOADS[name]["splits"]:
+            C = dgp.gemm_preshuffle_splitk(A, Bs, split, dA, dB, dmode(mode))
+            torch.cuda.synchronize()
+            c32, _ = run_oracle(w["A"][:M], w["B"], dt, mode, sA, sB, split_k=split, rows=rows)
+            assert_close(host_bits(C)[rows], c32, what=f"{name} M={M} N={N} split={split}")
