@@ -415,11 +415,16 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
         return (size_t)16 * pnl + (SCALE == kScaleMx32 ? stream_mx32_scale_bytes(NW * SPW * 16, pnl) : 0);
     };
     const size_t lds = lds_bytes(panel);
-    static bool attr_set = false;
-    if (!attr_set) {
+    // The LDS allowance is a per-device attribute of the kernel: set it once
+    // on each device this launcher runs on (a failure surfaces at the launch).
+    static bool attr_set[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
         (void)hipFuncSetAttribute((const void *)gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes(kMax));
-        attr_set = true;
+        if (dev >= 0 && dev < 64)
+            attr_set[dev] = true;
     }
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
 }
