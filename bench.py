@@ -169,7 +169,8 @@ def main():
 
     secondary = {}
     if not args.no_secondary:
-        secondary = run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs, A, C, M, N, K)
+        secondary = run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs, A, C, M, N, K,
+                                  cpu_threads=None if args.no_cpu else threads)
         wall = secondary["mfma_wall_bf16"]["workload_data"]
         roofline["measured_wall"] = wall
         roofline["frac_measured_wall"] = round(achieved / wall, 4)
@@ -222,7 +223,28 @@ def graph_time_us(torch, fn, iters):
     return e0.elapsed_time(e1) * 1e3 / (reps * iters)
 
 
-def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C_bf16, M, N, K):
+def oracle_leg(np, w, rows, c_gpu_rows, threads, flop=None, nbytes=None):
+    """Time the CPU oracle on rows `rows` of workload inputs `w` (all N
+    columns) and check the GPU's bf16 rows against it."""
+    import oracle
+    dt = {"bf16": oracle.BF16, "fp8": oracle.FP8_E4M3, "fp4": oracle.FP4_E2M1}[w["dtype"]]
+    sm = {"none": oracle.SCALE_NONE, "tensor": oracle.SCALE_TENSOR, "block128": oracle.SCALE_BLOCK128,
+          "mx128": oracle.SCALE_MX128, "mx32": oracle.SCALE_MX32}[w["scale_mode"]]
+    t = time.perf_counter()
+    c32, _ = oracle.gemm(w["A"], w["B"], dt, sm, w["sA"], w["sB"], rows=rows, nthreads=threads)
+    sec = time.perf_counter() - t
+    g = (c_gpu_rows.astype(np.uint32) << 16).view(np.float32)
+    leg = {"s": round(sec, 3), "threads": threads, "rows": int(len(rows)),
+           "gpu_vs_oracle_rel_err": float(f"{np.max(np.abs(g - c32)) / np.max(np.abs(c32)):.3e}")}
+    if flop is not None:
+        leg["TFLOP/s"] = round(flop / sec / 1e12, 6)
+    if nbytes is not None:
+        leg["GB/s"] = round(nbytes / sec / 1e9, 3)
+    return leg
+
+
+def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C_bf16, M, N, K,
+                  cpu_threads=None):
     out = {}
     # Packer on the headline weight: read + write 2*N*K*2 bytes.
     B_raw = dgp.unshuffle_b(Bs_bf16)
@@ -296,6 +318,11 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                                       "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4)}
     out["fp8_gemm_4096x4096x8192"]["kernel"] = dgp.describe_kernel(
         dgp.select_kernel(4096, 4096, 8192, dgp.FP8_E4M3, dgp.SCALE_TENSOR))
+    if cpu_threads:
+        rows = np.linspace(0, 4095, 512).astype(np.int64)
+        out["fp8_gemm_4096x4096x8192"]["cpu_oracle"] = oracle_leg(
+            np, w, rows, C8.view(torch.int16).cpu().numpy().view(np.uint16)[rows], cpu_threads,
+            flop=2.0 * len(rows) * 4096 * 8192)
 
     # Context only: the vendor library (hipBLASLt through torch) on the same
     # shapes and bytes, in the same process, with B in its own row-major
@@ -362,6 +389,12 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                                 "frac_measured_wall": round(gbs / size_walls[nbytes], 4)}
                     if best is None or gbs > best[1]:
                         best = (split, gbs, nbytes)
+                    if cpu_threads and split == 1 and m_ == max(Ms) and n_ == max(Ns):
+                        wm = dict(base, A=base["A"][:m_], sA=None if base["sA"] is None else
+                                  (base["sA"] if mode == "tensor" else base["sA"][:m_]))
+                        dec[key]["cpu_oracle"] = oracle_leg(
+                            np, wm, np.arange(m_), Cs[0].view(torch.int16).cpu().numpy().view(np.uint16),
+                            cpu_threads, nbytes=nbytes)
                     del Cs, wss
                 dec[f"best {mode} M={m_} N={n_}"] = {"split": best[0], "GB/s": round(best[1], 1),
                                                      "frac_hbm": round(best[1] / PEAK_HBM_GBS, 4),
