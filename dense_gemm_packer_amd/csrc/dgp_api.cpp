@@ -147,6 +147,10 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         // and re-reading one A row per strip costs little.
         if (N * split_k < 128 * 64 || (dtype == DGP_BF16 && M == 1 && split_k == 1))
             return find_spec(Query{kStream, dtype, scale, out, 16, 16});
+        // Up to one 64-column workgroup per CU (256): the 32-column tile's
+        // twice as many workgroups stream faster (measured 3-15 %).
+        if (N * split_k < 256 * 64)
+            return find_spec(Query{kStream, dtype, scale, out, 16, 32});
         return find_spec(Query{kStream, dtype, scale, out, 16, 64});
     }
     const KernelSpec *k = nullptr;

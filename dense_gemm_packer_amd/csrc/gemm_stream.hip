@@ -454,6 +454,12 @@ static const KernelSpec kStreamKernels[] = {
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleBlock),
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 4, 1, 8, kScaleMx),
     DGP_STREAM_BOTH_OUT(kDtypeFp4, 4, 1, 8, kScaleMx32),
+    // 16 x 32 tiles: twice the workgroups where the 64-column grid is short
+    DGP_STREAM_BOTH_OUT(kDtypeBf16, 2, 1, 16, kScaleNone),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 1, 8, kScaleTensor),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 1, 8, kScaleBlock),
+    DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 1, 8, kScaleMx),
+    DGP_STREAM_BOTH_OUT(kDtypeFp4, 2, 1, 8, kScaleMx32),
     // one strip per workgroup, K split over the waves: waves, ring depth
     DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),

@@ -140,13 +140,13 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
-@pytest.mark.parametrize("tile_n", [64, 16])
+@pytest.mark.parametrize("tile_n", [64, 32, 16])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128"), ("fp4", "mx32")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
 def test_stream_splitk(dtype, mode, M, split_k, tile_n):
-    """Decode kernels: the 16x64 streaming tile and the 16x16 K-split tile."""
+    """Decode kernels: the 16x64 and 16x32 streaming tiles and the 16x16 K-split tile."""
     N, K = 384, 2048
     cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
     A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 3)
@@ -314,7 +314,7 @@ def test_mxfp4_decode(M, split_k):
     N, K = 384, 7168
     A, B, sA, sB = exact_inputs("fp4", "mx32", M, N, K, 51)
     _, c16 = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split_k)
-    for tile_n in (16, 64):
+    for tile_n in (16, 32, 64):
         got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split_k, config=dgp.Config(16, tile_n, 0, 0, 1, 0, 0))
         assert np.array_equal(got, c16), tile_n
     A, B, sA, sB = rand_inputs("fp4", "mx32", M, N, K, 52)
@@ -324,7 +324,7 @@ def test_mxfp4_decode(M, split_k):
         assert_close(got, c32)
 
 
-@pytest.mark.parametrize("tile_n", [64, 16])
+@pytest.mark.parametrize("tile_n", [64, 32, 16])
 def test_mxfp4_scale_indexing_and_packer(tile_n):
     """Doubling one column's 32-block B scales doubles exactly that column,
     doubling one A row's doubles exactly that row, and raising one 32-block
@@ -359,7 +359,7 @@ def test_mxfp4_scale_indexing_and_packer(tile_n):
     assert torch.equal(dgp.unshuffle_b(Bs).view(torch.uint8), Bd.view(torch.uint8))
 
 
-@pytest.mark.parametrize("tile_n", [64, 16])
+@pytest.mark.parametrize("tile_n", [64, 32, 16])
 def test_mx128_scale_indexing(tile_n):
     """mxfp8 scales reach the right operands: doubling one column's B scale
     row doubles exactly that column of C, and a NaN A scale poisons exactly

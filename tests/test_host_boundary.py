@@ -241,7 +241,9 @@ def test_default_selection(dgp):
         # narrow weights: one strip per workgroup, K split over its waves
         assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 1)][0].tile_n == 16
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
-        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 64
+        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 32
+        assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == 32
+        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 8)][0].tile_n == 64
     assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)][0].tile_m == 16
     # a single bf16 row: the K-split tile at any N; fp8 keeps the 64-column tile
     assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
