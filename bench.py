@@ -32,31 +32,34 @@ METRIC = "TFLOP/s (large M) and GB/s (decode M≤16) at 1 GPU; % of MFMA / HBM r
 PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_4096x4096x8192_traffic.md")
 KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_tiled.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
                   "dense_gemm_packer_amd/csrc/common.h"]
+DECODE_PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_decode_16x16384x7168_traffic.md")
+DECODE_KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_stream.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
+                         "dense_gemm_packer_amd/csrc/common.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, or None if
+def read_traffic(path=PROFILE_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None if
     missing or taken on a different version of the kernel source."""
     try:
         kv = {}
-        with open(PROFILE_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip().strip("-* `")] = v.strip().strip("`")
-        if kv.get("source_sha256") != kernel_source_sha():
+        if kv.get("source_sha256") != kernel_source_sha(sources):
             return None
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -77,6 +80,9 @@ def main():
                     help="rows of C in the CPU oracle sample (default: all of them)")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and a few GEMM launches (for counter runs)")
+    ap.add_argument("--profile-decode-traffic", action="store_true",
+                    help="run only a 256 MiB probe copy and three fp8 decode launches "
+                         "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -97,6 +103,23 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
         return t.view({"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
                        "fp4": torch.float4_e2m1fn_x2}[dtype]).to(dev)
+
+    if args.profile_decode_traffic:
+        wd = synth.workload_inputs("fp8_decode", M=16, N=16384)
+        Ad = to_dev(wd["A"], "fp8")
+        Bd = [dgp.preshuffle_b(to_dev(wd["B"], "fp8")) for _ in range(3)]
+        sAd = torch.from_numpy(wd["sA"]).to(dev)
+        sBd = torch.from_numpy(wd["sB"]).to(dev)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dgp.probe_copy(src, dst)
+        for b in Bd:
+            dgp.gemm_preshuffle(Ad, b, sAd, sBd)
+        torch.cuda.synchronize()
+        log("profile-decode-traffic: 3 x probe copy of 256 MiB, 3 x fp8 decode 16x16384x7168 on distinct weights")
+        return 0
 
     # ------------------------------------------------------------ headline
     w = synth.workload_inputs("bf16_large")
@@ -387,6 +410,10 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                     dec[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                                 "read_wall_same_bytes_GB/s": round(size_walls[nbytes], 1),
                                 "frac_measured_wall": round(gbs / size_walls[nbytes], 4)}
+                    if mode == "tensor" and m_ == 16 and n_ == 16384 and split == 1:
+                        # HBM bytes per launch from the committed counter runs (null if stale)
+                        dec[key]["traffic"] = read_traffic(DECODE_PROFILE_FILE, DECODE_KERNEL_SOURCES)
+                        dec[key]["algorithmic_bytes"] = nbytes
                     if best is None or gbs > best[1]:
                         best = (split, gbs, nbytes)
                     if cpu_threads and split == 1 and m_ == max(Ms) and n_ == max(Ns):
