@@ -141,7 +141,7 @@ def sweep(spec: str, iters: int, dev="cuda:0") -> dict:
             for idx, us in best.items()]
     rows.sort(key=lambda r: r["us"])
     chosen = select_kernel(M, N, K, dt, sm, split)
-    ratio = (best[chosen] / rows[0]["us"]) if rows and chosen in best else None
+    ratio = (best[chosen] / min(best.values())) if rows and chosen in best else None
     return {"shape": spec, "M": M, "N": N, "K": K, "split_k": split, "cold": copies > 1,
             "builtin_choice": describe_kernel(chosen),
             "builtin_time_over_fastest": None if ratio is None else round(ratio, 3),
