@@ -1,12 +1,16 @@
-// Decode-sized-M GEMM kernel for C = A * B^T with B preshuffled
-// (include/dgp.h) and its table entries.  Operand layout and epilogue:
+// Decode-sized-M GEMM kernels for C = A * B^T with B preshuffled
+// (include/dgp.h) and their table entries.  Operand layout and epilogue:
 // gemm_common.h.
 //
 // gemm_stream_kernel -- decode-sized M (aiter PR #5148, "Summary": split-K
-//    preshuffle GEMM for small M).  A workgroup owns 16 rows of C and a few
-//    16-column strips; the A rows of its K range sit in LDS and each wave
-//    streams its strips of B through a deep ring of in-flight 16-byte loads.
-//    It also carries the FP8 blockscale mode for any M.
+//    preshuffle GEMM for small M).  A workgroup owns 16 rows of C and 2 or 4
+//    16-column strips (a 16x32 or 16x64 tile); the A rows of its K range sit
+//    in LDS and each wave streams its strips of B through a deep ring of
+//    in-flight 16-byte loads.  It also carries the FP8 blockscale mode for any
+//    M and the microscaling modes (mxfp8, mxfp4), whose E8M0 scales are staged
+//    in LDS per panel.
+// gemm_ksplit_kernel -- decode-sized M over few columns: one strip per
+//    workgroup, its K range split over the waves, partials added in LDS.
 
 #include "gemm_common.h"
 
