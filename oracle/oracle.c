@@ -29,7 +29,7 @@
  *    #1008 and aiter PR #5148 but never written out; this file fixes one
  *    concrete byte permutation (oracle_preshuffle_b) and its inverse.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - fp8 is OCP e4m3fn: bias 7, no infinities, S.1111.111 is NaN, max 448.
  *  - fp32 -> bf16 rounds to nearest, ties to even; NaN stays a quiet NaN.
  *  - per-tensor scaling multiplies the fp32 sum by (sA*sB), the product of the
