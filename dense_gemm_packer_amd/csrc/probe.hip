@@ -1,6 +1,6 @@
 // Probe kernels: check the hardware facts the GEMM relies on (matrix-core
 // register layouts, where the async global->LDS copy puts each lane's bytes)
-// and measure the walls the GEMM is judged against (a plain copy of known
+// and measure the walls the GEMM is compared with (a plain copy of known
 // traffic for counter calibration, a streaming read for the HBM wall, a
 // register-only matrix-core loop for the sustained MFMA rate).
 #include <type_traits>
