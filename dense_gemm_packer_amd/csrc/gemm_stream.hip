@@ -72,8 +72,8 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
     const auto rB = make_rsrc(p.Bs + (int64_t)strip_w * 16 * Kb,
                               clamp_bytes((int64_t)(p.N / 16 - strip_w) * 16 * Kb));
-    // mxfp4 scales of rows m0.. and of the workgroup's columns (unused otherwise)
-    constexpr bool kX4 = SCALE == kScaleMx32;
+    // E8M0 scales (mxfp8, mxfp4) of rows m0.. and of the workgroup's columns
+    constexpr bool kX4 = SCALE == kScaleMx32 || SCALE == kScaleMx;
     const auto rXa = make_rsrc(kX4 ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblocks_row : nullptr,
                                kX4 ? clamp_bytes((int64_t)(p.M - m0) * kblocks_row) : 0);
     const auto rXb = make_rsrc(kX4 ? static_cast<const uint8_t *>(p.sB) + (int64_t)strip_wg * 16 * kblocks_row
@@ -134,25 +134,23 @@ gemm_stream_kernel(const GemmArgs p, int panel)
             }
         }
 
-        // mxfp8: this panel's E8M0 bytes into registers (rows >= M and columns
-        // >= N get 127 = 1.0; their data is zero).
-        constexpr int kXaPer = SCALE == kScaleMx ? (16 * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
-        constexpr int kXbPer = SCALE == kScaleMx ? (NW * SPW * 16 * kScaleCols + NW * 64 - 1) / (NW * 64) : 1;
-        uint32_t xa_v[kXaPer], xb_v[kXbPer];
+        // mxfp8: this panel's E8M0 bytes into registers, one staged row per
+        // wave at a time and one K block per lane: rows 0..15 are A rows m0..,
+        // rows 16.. the workgroup's columns.  Bytes past M or N read as 0 (a
+        // finite 2^-127 that only ever scales zero data).
+        constexpr int kXRows = 16 + NW * SPW * 16;
+        constexpr int kXPer = SCALE == kScaleMx ? (kXRows + NW - 1) / NW : 1;
+        uint32_t x_v[kXPer];
         if constexpr (SCALE == kScaleMx) {
-            const uint8_t *xa = static_cast<const uint8_t *>(p.sA), *xb = static_cast<const uint8_t *>(p.sB);
+            const uint32_t xoff = pk / 128u + (uint32_t)lane;
 #pragma unroll
-            for (int u = 0; u < kXaPer; ++u) {
-                const int i = threadIdx.x + u * NW * 64;
-                const int r = i / cols, c = i % cols;
-                xa_v[u] = (i < 16 * cols && m0 + r < p.M) ? xa[(int64_t)(m0 + r) * kblocks_row + kb0 + c] : 127u;
-            }
-#pragma unroll
-            for (int u = 0; u < kXbPer; ++u) {
-                const int i = threadIdx.x + u * NW * 64;
-                const int col = i / cols, c = i % cols;
-                const int n = strip_wg * 16 + col;
-                xb_v[u] = (i < NW * SPW * 16 * cols && n < p.N) ? xb[(int64_t)n * kblocks_row + kb0 + c] : 127u;
+            for (int u = 0; u < kXPer; ++u) {
+                const int r = wave + u * NW;
+                x_v[u] = 0u;
+                if (r < 16)
+                    x_v[u] = __builtin_amdgcn_raw_buffer_load_b8(rXa, (uint32_t)r * kblocks_row + xoff, 0, 0);
+                else if (r < kXRows)
+                    x_v[u] = __builtin_amdgcn_raw_buffer_load_b8(rXb, (uint32_t)(r - 16) * kblocks_row + xoff, 0, 0);
             }
         }
 
@@ -205,16 +203,14 @@ gemm_stream_kernel(const GemmArgs p, int panel)
         }
         if constexpr (SCALE == kScaleMx) {
 #pragma unroll
-            for (int u = 0; u < kXaPer; ++u) {
-                const int i = threadIdx.x + u * NW * 64;
-                if (i < 16 * cols)
-                    lds_xa[i / cols][i % cols] = (uint8_t)xa_v[u];
-            }
-#pragma unroll
-            for (int u = 0; u < kXbPer; ++u) {
-                const int i = threadIdx.x + u * NW * 64;
-                if (i < NW * SPW * 16 * cols)
-                    lds_xb[i / cols][i % cols] = (uint8_t)xb_v[u];
+            for (int u = 0; u < kXPer; ++u) {
+                const int r = wave + u * NW;
+                if (lane < cols) {
+                    if (r < 16)
+                        lds_xa[r][lane] = (uint8_t)x_v[u];
+                    else if (r < kXRows)
+                        lds_xb[r - 16][lane] = (uint8_t)x_v[u];
+                }
             }
         }
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DEPTH * SPW * kStepCh) : "memory");
