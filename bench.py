@@ -367,6 +367,29 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["vendor_library_same_process"] = vend
     del A8, Bs8, C8
 
+    # fp8 blockscale and mxfp8 GEMMs at the same size: the tiled kernel with
+    # each k-tile's scales staged in LDS beside the A tile.
+    for name, mode, smode in (("fp8_blockscale", "block128", dgp.SCALE_BLOCK128),
+                              ("fp8_mx128", "mx128", dgp.SCALE_MX128)):
+        w = synth.workload_inputs(name, M=4096, N=4096, K=8192)
+        A8 = to_dev(w["A"], "fp8")
+        Bs8 = dgp.preshuffle_b(to_dev(w["B"], "fp8"))
+        sA = torch.from_numpy(w["sA"]).to(dev)
+        sB = torch.from_numpy(w["sB"]).to(dev)
+        C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+        us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, smode, out=C8), 10)
+        tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
+        key = f"fp8_{mode}_gemm_4096x4096x8192"
+        out[key] = {"us": round(us, 1), "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                    "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4),
+                    "kernel": dgp.describe_kernel(dgp.select_kernel(4096, 4096, 8192, dgp.FP8_E4M3, smode))}
+        if cpu_threads:
+            rows = np.linspace(0, 4095, 64).astype(np.int64)
+            out[key]["cpu_oracle"] = oracle_leg(
+                np, w, rows, C8.view(torch.int16).cpu().numpy().view(np.uint16)[rows], cpu_threads,
+                flop=2.0 * len(rows) * 4096 * 8192)
+        del A8, Bs8, C8, sA, sB
+
     # Decode-sized M, cold cache: fp8 per-tensor, blockscale, mxfp8, mxfp4, and bf16.
     dec = {}
     for mode in ("tensor", "block128", "mx128", "mx32", "bf16"):

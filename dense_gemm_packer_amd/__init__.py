@@ -54,7 +54,7 @@ class Config(ctypes.Structure):
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
            "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
-           "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_copy",
+           "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_lds_dma_narrow", "dgp_probe_copy",
            "dgp_probe_stream_read", "dgp_probe_mfma_peak")
 
 _lib = None
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "dgp_select_kernel": [_i64, _i64, _i64, _int, _int, _int, ctypes.POINTER(Config), ctypes.POINTER(_int)],
         "dgp_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_lds_dma": [_vp, _vp, _vp, _vp],
+        "dgp_probe_lds_dma_narrow": [_int, _vp, _vp, _vp, _vp],
         "dgp_probe_mfma_scaled": [_int, _vp, _vp, _vp, _vp, _vp, _vp],
         "dgp_probe_copy": [_vp, _vp, _i64, _vp],
         "dgp_probe_stream_read": [_vp, _i64, _int, _vp, _vp],
@@ -302,6 +303,12 @@ def probe_mfma_scaled(a: torch.Tensor, b: torch.Tensor, sa: torch.Tensor, sb: to
 def probe_lds_dma(src: torch.Tensor, perm: torch.Tensor, stream=None) -> torch.Tensor:
     dst = torch.empty(1024, dtype=torch.uint8, device=src.device)
     _check(lib().dgp_probe_lds_dma(_ptr(src), _ptr(perm), _ptr(dst), _stream_handle(stream)))
+    return dst
+
+
+def probe_lds_dma_narrow(width: int, src: torch.Tensor, perm: torch.Tensor, stream=None) -> torch.Tensor:
+    dst = torch.empty(1024, dtype=torch.uint8, device=src.device)
+    _check(lib().dgp_probe_lds_dma_narrow(width, _ptr(src), _ptr(perm), _ptr(dst), _stream_handle(stream)))
     return dst
 
 

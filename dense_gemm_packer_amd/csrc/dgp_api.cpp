@@ -138,7 +138,10 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    if (scale == DGP_SCALE_BLOCK128 || scale >= DGP_SCALE_MX128 || M <= 32) {
+    // Decode-sized M streams the weight through the 16-row tiles; so does
+    // mxfp4 at any M (its 32-K scale blocks have no tiled kernel).  Larger M
+    // takes the tiled kernels, blockscale and mxfp8 included.
+    if (scale == DGP_SCALE_MX32 || M <= 32) {
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
         // waves spreads the stream wider (measured faster up to that point).
@@ -156,7 +159,8 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     const KernelSpec *k = nullptr;
     if (M >= 1024 && N >= 1024) {
         Query q{kTiled, dtype, scale, out, 256, 256};
-        q.kt = 128, q.wm = 1, q.depth = 2, q.pv = 0, q.pd = 8;
+        q.kt = 128, q.wm = 1, q.depth = 2, q.pv = 0;
+        q.pd = (scale == DGP_SCALE_BLOCK128 || scale == DGP_SCALE_MX128) ? 4 : 8;
         k = find_spec(q);
     }
     if (!k || !spec_fits(*k, Ks)) {
@@ -580,6 +584,20 @@ dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, vo
     if (st != DGP_OK)
         return st;
     return hip_status(launch_probe_lds_dma(src, perm, dst, (hipStream_t)stream), "probe launch");
+}
+
+dgp_status dgp_probe_lds_dma_narrow(int width, const void *src, const int32_t *perm, void *dst, void *stream)
+{
+    if (width != 1 && width != 2 && width != 4)
+        return fail(DGP_ERR_CONFIG, "width must be 1, 2 or 4 (got %d)", width);
+    if (!src || !perm || !dst)
+        return fail(DGP_ERR_NULL, "NULL buffer");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(DGP_ERR_ALIGN, "buffers must be 16-byte aligned");
+    dgp_status st = check_device_arch();
+    if (st != DGP_OK)
+        return st;
+    return hip_status(launch_probe_lds_dma_narrow(width, src, perm, dst, (hipStream_t)stream), "probe launch");
 }
 
 dgp_status dgp_probe_copy(const void *src, void *dst, int64_t bytes, void *stream)

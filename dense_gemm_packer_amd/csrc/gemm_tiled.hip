@@ -13,6 +13,11 @@
 //    A fragments are read from LDS per MFMA k-step, interleaved with the
 //    MFMAs that consume them (the per-k-step reads restored on FlyDSL PR #974,
 //    follow-up commit item 2).
+//    fp8 blockscale (fp32 scales per 128-K block, aiter PR #5148) and mxfp8
+//    (E8M0 bytes per 128-K block, the hardware-scaled MFMA) take one k-tile
+//    per K block: the tile's scales ride in a small area after each A buffer,
+//    copied with the same async load as A (one instruction per wave per
+//    k-tile), so the wait and barrier that certify A certify them too.
 
 #include "gemm_common.h"
 
@@ -28,11 +33,26 @@ gemm_tiled_kernel(const GemmArgs p)
 {
     using S = TiledShape<DT, TM, TN, WM, WN, KT>;
     using Frag = typename Op<DT>::Frag;
-    static_assert(DEPTH >= 1 && (DEPTH + 1) * TM * KT <= 160 * 1024, "A ring must fit in LDS");
+    // Per-k-tile scales staged in LDS: fp32 (blockscale) or E8M0 bytes (mxfp8).
+    // The scale area after an A buffer holds TM + TN dwords: dword d < TM is
+    // A row (d % (TM/16))*16 + d / (TM/16) of the tile, dword TM + d is B
+    // column (d % (TN/16))*16 + d / (TN/16); so a lane's scales for its row
+    // tiles (column strips) are consecutive dwords.  An E8M0 byte lands in
+    // the low byte of its dword (the narrow async load writes lane l at dword
+    // l), which is the byte the scaled MFMA reads.
+    constexpr bool kXS = SCALE == kScaleBlock || SCALE == kScaleMx;
+    constexpr int kES = SCALE == kScaleBlock ? 4 : 1;          // bytes per scale
+    constexpr int kXDwords = kXS ? TM + TN : 0;
+    constexpr int kXDma = kXDwords / (64 * S::kWaves);        // scale copies per wave per k-tile
+    static_assert(!kXS || (DT == kDtypeFp8 && KT == 128 && kXDwords % (64 * S::kWaves) == 0 &&
+                           TM % 64 == 0 && S::kMT % 4 == 0 && (S::kNT == 2 || S::kNT == 4)),
+                  "staged scales: fp8, one 128-K block per k-tile, whole copies per wave");
+    constexpr int kStageBytes = S::kBufBytes + kXDwords * 4;
+    static_assert(DEPTH >= 1 && (DEPTH + 1) * kStageBytes <= 160 * 1024, "A ring must fit in LDS");
     // Prefetch distance DEPTH k-tiles: a ring of DEPTH+1 A buffers in LDS and
     // DEPTH sets of B registers.
     constexpr int kRing = DEPTH + 1;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * S::kBufBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kStageBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -72,6 +92,36 @@ gemm_tiled_kernel(const GemmArgs p)
     if constexpr (SCALE == kScaleTensor)
         scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
 
+    // Scale copies: instruction j of this wave fills dwords 64g .. 64g+63 of
+    // the scale area (g = j*waves + wave); lane l supplies dword 64g + l.
+    // Rows >= M and (blockscale) column blocks past N load as zero.
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t x_rsrc[kXDma > 0 ? kXDma : 1];
+    [[maybe_unused]] uint32_t x_voff[kXDma > 0 ? kXDma : 1];
+    if constexpr (kXS) {
+        const uint32_t kblk = Kb / 128u;   // 128-K blocks per row (fp8: one byte per element)
+        const auto rXA = make_rsrc((const uint8_t *)p.sA + (int64_t)m0 * kblk * kES,
+                                   clamp_bytes((int64_t)(p.M - m0) * kblk * kES));
+        const int64_t bcol0 = SCALE == kScaleBlock ? n0 / 128 : n0;   // first sB row of the tile
+        const int64_t brows = SCALE == kScaleBlock ? p.N / 128 : p.N;
+        const auto rXB = make_rsrc((const uint8_t *)p.sB + bcol0 * kblk * kES,
+                                   clamp_bytes((brows - bcol0) * kblk * kES));
+#pragma unroll
+        for (int j = 0; j < kXDma; ++j) {
+            const int g = j * S::kWaves + wave;
+            if (g * 64 < TM) {
+                const int d = g * 64 + lane;
+                const int row = (d % (TM / 16)) * 16 + d / (TM / 16);
+                x_rsrc[j] = rXA;
+                x_voff[j] = (uint32_t)row * kblk * kES;
+            } else {
+                const int d = g * 64 - TM + lane;
+                const int col = (d % (TN / 16)) * 16 + d / (TN / 16);
+                x_rsrc[j] = rXB;
+                x_voff[j] = (uint32_t)(SCALE == kScaleBlock ? col / 128 : col) * kblk * kES;
+            }
+        }
+    }
+
     f32x4 acc[S::kMT][S::kNT];
 #pragma unroll
     for (int i = 0; i < S::kMT; ++i)
@@ -95,6 +145,17 @@ gemm_tiled_kernel(const GemmArgs p)
 #pragma unroll
         for (int j = 0; j < S::kDmaPerWave; ++j)
             lds_dma16(rA, lds + buf_off + (j * S::kWaves + wave) * 1024, dma_voff[j], koff);
+        if constexpr (kXS) {
+#pragma unroll
+            for (int j = 0; j < kXDma; ++j) {
+                auto *d = (__attribute__((address_space(3))) void *)(lds + buf_off + S::kBufBytes +
+                                                                     (j * S::kWaves + wave) * 256);
+                if constexpr (kES == 4)   // the size operand must be a literal
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 4, x_voff[j], (koff / 128u) * 4u, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 1, x_voff[j], koff / 128u, 0, 0);
+            }
+        }
     };
     auto kofs = [&](int t) {   // first K byte of tile t, clamped to the last tile
         return kbase + (uint32_t)(t < ntiles ? t : ntiles - 1) * KT;
@@ -105,7 +166,7 @@ gemm_tiled_kernel(const GemmArgs p)
     // counters agree on the loop-entry and back-edge paths.
     auto prologue_tile = [&](auto setc) {
         constexpr int D = decltype(setc)::value;
-        dma_a((uint32_t)D * S::kBufBytes, kofs(D));
+        dma_a((uint32_t)D * kStageBytes, kofs(D));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ch = 0; ch < S::kCH; ++ch) {
@@ -122,13 +183,14 @@ gemm_tiled_kernel(const GemmArgs p)
         prologue_tile(std::integral_constant<int, (DEPTH > 3 ? 3 : 0)>{});
     static_assert(DEPTH <= 4, "prologue and loop unrolled for DEPTH <= 4");
 
-    // Loads issued after the A copy of tile t, when step t begins: the B
-    // loads of tile t, then DEPTH-1 more tiles of A copies and B loads.
-    constexpr int kAfter = S::kBLoads + (DEPTH - 1) * (S::kDmaPerWave + S::kBLoads);
+    // Loads issued after the A (and scale) copy of tile t, when step t
+    // begins: the B loads of tile t, then DEPTH-1 more tiles of A copies,
+    // scale copies and B loads.
+    constexpr int kAfter = S::kBLoads + (DEPTH - 1) * (S::kDmaPerWave + kXDma + S::kBLoads);
     static_assert(kAfter <= 63, "vmcnt field is 6 bits");
 
     uint32_t cur = 0;                                   // LDS offset of tile t
-    uint32_t nxt = (uint32_t)DEPTH * S::kBufBytes;      // LDS offset of tile t+DEPTH
+    uint32_t nxt = (uint32_t)DEPTH * kStageBytes;       // LDS offset of tile t+DEPTH
     auto step = [&](auto setc, int t) {
         // This wave's A copy of tile t has landed once at most kAfter loads are
         // outstanding, and every earlier LDS read has completed; the barrier
@@ -138,6 +200,28 @@ gemm_tiled_kernel(const GemmArgs p)
         const uint32_t knext = kofs(t + DEPTH);
         dma_a(nxt, knext);
 
+        // This tile's scales: the lane's row tiles (A) and column strips (B).
+        [[maybe_unused]] i32x4 xa[kXS ? S::kMT / 4 : 1];
+        [[maybe_unused]] int xb[kXS ? S::kNT : 1];
+        if constexpr (kXS) {
+            const uint8_t *xs = lds + cur + S::kBufBytes;
+            const int rit = lane & 15;
+#pragma unroll
+            for (int q = 0; q < S::kMT / 4; ++q)
+                xa[q] = *reinterpret_cast<const i32x4 *>(xs + (rit * (TM / 16) + wm * S::kMT) * 4 + 16 * q);
+            const uint8_t *xbp = xs + TM * 4 + (rit * (TN / 16) + wn * S::kNT) * 4;
+            if constexpr (S::kNT == 2) {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(xbp);
+                xb[0] = (int)v.x;
+                xb[1] = (int)v.y;
+            } else {
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(xbp);
+#pragma unroll
+                for (int nt = 0; nt < S::kNT; ++nt)
+                    xb[nt] = v[nt];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
         constexpr int SET = decltype(setc)::value;
         // A fragments in MFMA order: fragment f = (step f / kMT, row tile f % kMT).
@@ -145,6 +229,24 @@ gemm_tiled_kernel(const GemmArgs p)
         auto frag_at = [&](int f) {
             return lds_frag<DT>(abase + ((f % S::kMT) * S::kCH + (f / S::kMT) * S::kStepCh) * 1024);
         };
+        // Blockscale: the partials of fragment f are scaled and added after
+        // the MFMAs of fragment f+1 are issued, so the VALU work never waits
+        // on the MFMA that produced its operand.  All columns of a wave lie
+        // in one 128-column block (its 16*kNT columns divide 128), so sB is
+        // one value per wave and k-tile and sA * sB is formed once per row
+        // tile.
+        [[maybe_unused]] f32x4 part[2][S::kNT];
+        [[maybe_unused]] auto rescale = [&](int mt, const f32x4 *pp) {
+            const float sc = __fmul_rn(__int_as_float(xa[mt / 4][mt % 4]), __int_as_float(xb[0]));
+#pragma unroll
+            for (int nt = 0; nt < S::kNT; ++nt) {
+                acc[mt][nt].x = __fadd_rn(acc[mt][nt].x, __fmul_rn(pp[nt].x, sc));
+                acc[mt][nt].y = __fadd_rn(acc[mt][nt].y, __fmul_rn(pp[nt].y, sc));
+                acc[mt][nt].z = __fadd_rn(acc[mt][nt].z, __fmul_rn(pp[nt].z, sc));
+                acc[mt][nt].w = __fadd_rn(acc[mt][nt].w, __fmul_rn(pp[nt].w, sc));
+            }
+        };
+        static_assert(SCALE != kScaleBlock || 128 % (16 * S::kNT) == 0, "a wave's columns in one block");
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
             const int st = f / S::kMT, mt = f % S::kMT;
@@ -156,14 +258,27 @@ gemm_tiled_kernel(const GemmArgs p)
                     b = breg[SET][nt][st];
                 else
                     b = cat(breg[SET][nt][2 * st], breg[SET][nt][2 * st + 1]);
-                acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
+                if constexpr (SCALE == kScaleMx) {
+                    acc[mt][nt] = mfma_mx(b, a, acc[mt][nt], xb[nt], xa[mt / 4][mt % 4]);
+                } else if constexpr (SCALE == kScaleBlock) {
+                    // One MFMA is one 128-wide K block: its fp32 partial is
+                    // scaled by sA * sB and added (below, one fragment later).
+                    part[f & 1][nt] = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
+                } else {
+                    acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
+                }
             }
+            if constexpr (SCALE == kScaleBlock)
+                if (f > 0)
+                    rescale((f - 1) % S::kMT, part[(f - 1) & 1]);
             if (mt == S::kMT - 1) {
 #pragma unroll
                 for (int cc = 0; cc < S::kStepCh; ++cc)
                     load_b(setc, st * S::kStepCh + cc, knext);
             }
         }
+        if constexpr (SCALE == kScaleBlock)
+            rescale((kFr - 1) % S::kMT, part[(kFr - 1) & 1]);
         if constexpr (PD > 0) {
             // Software-pipeline the A fragments: the LDS reads of PD fragments
             // first, then for every fragment its MFMAs followed by the reads of
@@ -185,12 +300,15 @@ gemm_tiled_kernel(const GemmArgs p)
                 } else {
                     __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
                 }
+                // blockscale: the previous fragment's scaling (1 + 8 VALU ops per column strip pair)
+                if constexpr (SCALE == kScaleBlock)
+                    __builtin_amdgcn_sched_group_barrier(0x002, 1 + 4 * S::kNT, 0);
                 if (f + kRA < kFr)
                     __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
             }
         }
-        cur = cur + S::kBufBytes == kRing * S::kBufBytes ? 0 : cur + S::kBufBytes;
-        nxt = nxt + S::kBufBytes == kRing * S::kBufBytes ? 0 : nxt + S::kBufBytes;
+        cur = cur + kStageBytes == kRing * kStageBytes ? 0 : cur + kStageBytes;
+        nxt = nxt + kStageBytes == kRing * kStageBytes ? 0 : nxt + kStageBytes;
     };
 
     // Main loop, unrolled by DEPTH so that the B register set of every step is
@@ -463,6 +581,13 @@ static const KernelSpec kTiledKernels[] = {
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 2, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 256, 1, 4, 128, 2, kScaleTensor, 0, 8),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleTensor, 0, 4),
+    // large tiles, fp8 blockscale and mxfp8 (scales staged per k-tile)
+    // (LDS read-ahead 4 fragments: the staged scales leave no registers for
+    // 8; measured equal to 2 and 6)
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleBlock, 0, 4),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleBlock, 0, 4),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleMx, 0, 4),
+    DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleMx, 0, 4),
 };
 
 const KernelSpec *tiled_kernels(int *count)

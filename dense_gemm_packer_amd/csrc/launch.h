@@ -63,6 +63,7 @@ hipError_t launch_splitk_reduce(const float *ws, void *C, int64_t M, int64_t N, 
 // Probes (probe.hip).
 hipError_t launch_probe_mfma(int which, const void *a, const void *b, float *out, hipStream_t s);
 hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s);
+hipError_t launch_probe_lds_dma_narrow(int width, const void *src, const int32_t *perm, void *dst, hipStream_t s);
 hipError_t launch_probe_mfma_scaled(int which, const void *a, const void *b, const void *sa, const void *sb,
                                     float *out, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);

@@ -62,6 +62,31 @@ __global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint8_t *src, c
     *reinterpret_cast<i32x4 *>(dst + l * 16) = *reinterpret_cast<const i32x4 *>(lds + l * 16);
 }
 
+// The narrow forms of the same load (W = 1, 2 or 4 bytes per lane): LDS is
+// filled with 0xFF first, so the dump shows both where each lane's bytes land
+// and which LDS bytes the load leaves alone.
+template <int W>
+__global__ __launch_bounds__(64) void probe_lds_dma_narrow_kernel(const uint8_t *src, const int32_t *perm,
+                                                                  uint8_t *dst)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[1024];
+    const int l = threadIdx.x;
+    *reinterpret_cast<i32x4 *>(lds + l * 16) = i32x4{-1, -1, -1, -1};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const auto r = make_rsrc(src, 64 * W);
+    const int q = perm[l];
+    const uint32_t off = (uint32_t)((q >= 0 && q < 64) ? q : 0) * W;
+    auto *d = (__attribute__((address_space(3))) void *)lds;
+    if constexpr (W == 1)   // the size operand must be a literal
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 1, off, 0, 0, 0);
+    else if constexpr (W == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 2, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, off, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    *reinterpret_cast<i32x4 *>(dst + l * 16) = *reinterpret_cast<const i32x4 *>(lds + l * 16);
+}
+
 __global__ __launch_bounds__(256) void probe_copy_kernel(const i32x4 *__restrict__ src, i32x4 *__restrict__ dst, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -173,6 +198,19 @@ hipError_t launch_probe_mfma_scaled(int which, const void *a, const void *b, con
 hipError_t launch_probe_lds_dma(const void *src, const int32_t *perm, void *dst, hipStream_t s)
 {
     probe_lds_dma_kernel<<<1, 64, 0, s>>>((const uint8_t *)src, perm, (uint8_t *)dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_lds_dma_narrow(int width, const void *src, const int32_t *perm, void *dst, hipStream_t s)
+{
+    const auto *in = (const uint8_t *)src;
+    auto *out = (uint8_t *)dst;
+    if (width == 1)
+        probe_lds_dma_narrow_kernel<1><<<1, 64, 0, s>>>(in, perm, out);
+    else if (width == 2)
+        probe_lds_dma_narrow_kernel<2><<<1, 64, 0, s>>>(in, perm, out);
+    else
+        probe_lds_dma_narrow_kernel<4><<<1, 64, 0, s>>>(in, perm, out);
     return hipGetLastError();
 }
 

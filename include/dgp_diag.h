@@ -92,6 +92,17 @@ dgp_status dgp_probe_mfma_scaled(int which, const void *a, const void *b, const 
 dgp_status dgp_probe_lds_dma(const void *src, const int32_t *perm, void *dst, void *stream);
 
 /*
+ * dgp_probe_lds_dma_narrow -- the same async global->LDS load at 1, 2 or 4
+ * bytes per lane (the width the GEMM uses to stage per-k-tile scales): LDS
+ * bytes 0..1023 are set to 0xFF, lane l loads `width` bytes at
+ * src + perm[l]*width, and LDS bytes 0..1023 are copied to dst, showing where
+ * each lane's bytes landed and which bytes stayed 0xFF.
+ * width: 1, 2 or 4 (else DGP_ERR_CONFIG); src: >= 64*width bytes, 16-byte
+ * aligned; perm: 64 int32 in [0, 64); dst: 1024 bytes, 16-byte aligned.
+ */
+dgp_status dgp_probe_lds_dma_narrow(int width, const void *src, const int32_t *perm, void *dst, void *stream);
+
+/*
  * dgp_probe_copy -- plain 16-byte-per-thread device copy of `bytes` bytes
  * (bytes % 16 == 0).  The reference kernel of known traffic used to calibrate
  * hardware byte counters.

@@ -145,6 +145,23 @@ def test_lds_dma_destination_is_linear_per_lane():
     assert np.array_equal(out, want)
 
 
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_lds_dma_narrow_lands_one_dword_per_lane(width):
+    # The per-k-tile scale staging of the tiled GEMM relies on this: a load of
+    # 1, 2 or 4 bytes per lane writes lane l's value, zero-extended, as LDS
+    # dword l, and nothing beyond the first 256 bytes is touched.
+    g = np.random.Generator(np.random.PCG64(4 + width))
+    src = g.integers(0, 256, size=1024, dtype=np.uint8)
+    perm = g.permutation(64).astype(np.int32)
+    out = dgp.probe_lds_dma_narrow(width, torch.from_numpy(src).to(DEV),
+                                   torch.from_numpy(perm).to(DEV)).cpu().numpy()
+    got = out[:256].reshape(64, 4)
+    want = np.stack([src[width * p:width * p + width] for p in perm])
+    assert np.array_equal(got[:, :width], want)
+    assert np.all(got[:, width:] == 0)
+    assert np.all(out[256:] == 0xFF)
+
+
 def test_probe_copy_copies():
     x = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=DEV)
     y = torch.empty_like(x)

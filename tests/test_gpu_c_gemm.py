@@ -72,10 +72,13 @@ CASES = [  # dtype, mode, M, N, K
     ("fp8", "block128", 16, 256, 1024),
     ("fp8", "block128", 1, 384, 512),
     ("fp8", "block128", 33, 128, 768),
+    ("fp8", "block128", 300, 384, 640),
+    ("fp8", "block128", 1030, 1152, 1280),
     ("fp8", "mx128", 16, 256, 1024),
     ("fp8", "mx128", 1, 2048, 896),
     ("fp8", "mx128", 37, 144, 768),
     ("fp8", "mx128", 300, 272, 512),
+    ("fp8", "mx128", 1030, 1040, 1280),
     ("fp4", "mx32", 16, 256, 1024),
     ("fp4", "mx32", 1, 2048, 768),
     ("fp4", "mx32", 37, 144, 512),
@@ -124,17 +127,21 @@ def test_every_compiled_kernel():
         assert_close(got, c32, what=what)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype):
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
+                                        ("fp8", "mx128")])
+def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):
     """ntiles % depth != 0 exercises the steps after the unrolled main loop
     (1, 2, 3, 5, 7 k-tiles of 128 bytes)."""
     eb = 2 if dtype == "bf16" else 1
-    mode = "none" if dtype == "bf16" else "tensor"
     dcode = dgp.BF16 if dtype == "bf16" else dgp.FP8_E4M3
+    scode = {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128,
+             "mx128": dgp.SCALE_MX128}[mode]
     for tiles in (1, 2, 3, 5, 7):
         k = tiles * 128 // eb
-        for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dcode and not so]:
-            A, B, sA, sB = exact_inputs(dtype, mode, 300, 528, k, 13)
+        for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dcode and sm == scode
+                    and not so]:
+            N = 640 if mode == "block128" else 528   # blockscale: whole 128-column blocks
+            A, B, sA, sB = exact_inputs(dtype, mode, 300, N, k, 13)
             got = run_gpu(A, B, dtype, mode, sA, sB, config=cfg)
             _, c16 = run_oracle(A, B, dtype, mode, sA, sB)
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)

@@ -177,6 +177,10 @@ def test_probe_validation(L):
     assert L.dgp_probe_mfma_peak(0, 1, 1, 0, P, None) == NULL
     assert L.dgp_probe_mfma_peak(0, 1, 1, P, 0, None) == NULL
     assert L.dgp_probe_mfma_peak(0, 1, 1, P + 8, P, None) == ALIGN
+    assert L.dgp_probe_lds_dma_narrow(3, P, P, P, None) == CONFIG
+    assert L.dgp_probe_lds_dma_narrow(16, P, P, P, None) == CONFIG
+    assert L.dgp_probe_lds_dma_narrow(1, 0, P, P, None) == NULL
+    assert L.dgp_probe_lds_dma_narrow(4, P, P, P + 4, None) == ALIGN
 
 
 @pytest.mark.parametrize("remap,group_m", [(0, 1), (1, 1), (1, 4), (1, 8)])
@@ -232,8 +236,8 @@ def test_every_kernel_is_selected_by_its_reported_config(dgp):
 
 
 def test_default_selection(dgp):
-    # Headline shapes take a 256x256 tile, decode-sized M and blockscale the
-    # 16-row streaming kernel; empty calls launch nothing.
+    # Headline shapes take a 256x256 tile, decode-sized M and mxfp4 the
+    # 16-row streaming kernels; empty calls launch nothing.
     for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
         cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
         assert (cfg.tile_m, cfg.tile_n) == (256, 256)
@@ -244,7 +248,15 @@ def test_default_selection(dgp):
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 32
         assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == 32
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 8)][0].tile_n == 64
-    assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)][0].tile_m == 16
+    # blockscale and mxfp8: the tiled kernels above decode-sized M, the
+    # streaming tiles at it; mxfp4 streams at any M
+    for sm in (dgp.SCALE_BLOCK128, dgp.SCALE_MX128):
+        i = dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, sm)
+        assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][0].tile_n, dgp.kernels()[i][2]) == (256, 256, sm)
+        i = dgp.select_kernel(300, 1024, 7168, dgp.FP8_E4M3, sm, 2)
+        assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][3]) == (128, True)
+        assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dgp.FP8_E4M3, sm)][0].tile_m == 16
+    assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_m == 16
     # a single bf16 row: the K-split tile at any N; fp8 keeps the 64-column tile
     assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
     assert dgp.kernels()[dgp.select_kernel(2, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 64
