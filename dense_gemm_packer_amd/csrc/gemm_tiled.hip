@@ -191,6 +191,87 @@ gemm_tiled_kernel(const GemmArgs p)
 
     uint32_t cur = 0;                                   // LDS offset of tile t
     uint32_t nxt = (uint32_t)DEPTH * kStageBytes;       // LDS offset of tile t+DEPTH
+    // Blockscale k-tile (one 128-K scale block per k-tile).  Each fragment's
+    // MFMAs start from a zero accumulator; the fp32 partial is multiplied by
+    // sA[row][kb] * sB[col / 128][kb] and added to the running sum.  The order
+    // is fixed by scheduling fences, one fragment at a time: issue the LDS
+    // reads (A fragment and the row's A scale) of fragment f + PD, issue the
+    // MFMAs of fragment f, then scale and add the partials of fragment f - 1,
+    // whose MFMAs completed while those of f were issued (the scaling of
+    // each column strip follows the MFMA of the same strip of fragment f).
+    // So the LDS reads have PD fragments of work to land in and the VALU work
+    // never waits on the MFMA that produced its operand.  All columns of a
+    // wave lie in one 128-column block (its 16 * kNT columns divide 128), so
+    // sB is one value per wave and k-tile.
+    [[maybe_unused]] auto block_step = [&](auto setc, uint32_t knext) {
+        if constexpr (SCALE == kScaleBlock) {
+        constexpr int SET = decltype(setc)::value;
+        static_assert(DT == kDtypeFp8 && S::kSteps == 1 && PD >= 1, "blockscale: one fp8 MFMA step per k-tile");
+        static_assert(128 % (16 * S::kNT) == 0, "a wave's columns in one block");
+        constexpr int kFr = S::kMT;
+        constexpr int kRA = PD < kFr ? PD : kFr;
+        constexpr int kR = kRA + 1;                        // fragment ring slots
+        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+        const uint8_t *xs = lds + cur + S::kBufBytes;
+        const uint8_t *xap = xs + ((lane & 15) * (TM / 16) + wm * S::kMT) * 4;
+        const float sb = *reinterpret_cast<const float *>(xs + TM * 4 + ((lane & 15) * (TN / 16) + wn * S::kNT) * 4);
+        Frag ring[kR];
+        float ra[kR];
+        auto fetch = [&](int f) {
+            ring[f % kR] = lds_frag<DT>(abase + f * S::kCH * 1024);
+            ra[f % kR] = *reinterpret_cast<const float *>(xap + 4 * f);
+        };
+        __builtin_amdgcn_sched_barrier(0);   // sB first: the first product needs it
+#pragma unroll
+        for (int f = 0; f < kRA; ++f) {
+            fetch(f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x4 part[2][S::kNT];
+        float sc[2];
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+            if (f + kRA < kFr)
+                fetch(f + kRA);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int nt = 0; nt < S::kNT; ++nt) {
+                part[f & 1][nt] = mfma_op(cat(breg[SET][nt][0], breg[SET][nt][1]), ring[f % kR],
+                                          f32x4{0.f, 0.f, 0.f, 0.f});
+                if (nt == 0)
+                    sc[f & 1] = __fmul_rn(ra[f % kR], sb);
+                if (f == kFr - 1 && nt == S::kNT - 1) {
+#pragma unroll
+                    for (int cc = 0; cc < S::kStepCh; ++cc)
+                        load_b(setc, cc, knext);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (f > 0) {
+                    f32x4 &a = acc[f - 1][nt];
+                    const f32x4 &q = part[(f - 1) & 1][nt];
+                    const float c = sc[(f - 1) & 1];
+                    a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
+                    a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
+                    a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
+                    a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < S::kNT; ++nt) {
+            f32x4 &a = acc[kFr - 1][nt];
+            const f32x4 &q = part[(kFr - 1) & 1][nt];
+            const float c = sc[(kFr - 1) & 1];
+            a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
+            a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
+            a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
+            a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+        }
+        }
+    };
+
     auto step = [&](auto setc, int t) {
         // This wave's A copy of tile t has landed once at most kAfter loads are
         // outstanding, and every earlier LDS read has completed; the barrier
@@ -200,7 +281,11 @@ gemm_tiled_kernel(const GemmArgs p)
         const uint32_t knext = kofs(t + DEPTH);
         dma_a(nxt, knext);
 
-        // This tile's scales: the lane's row tiles (A) and column strips (B).
+        constexpr int SET = decltype(setc)::value;
+        if constexpr (SCALE == kScaleBlock) {
+            block_step(setc, knext);
+        } else {
+        // mxfp8: this tile's E8M0 scales, the lane's row tiles (A) and column strips (B).
         [[maybe_unused]] i32x4 xa[kXS ? S::kMT / 4 : 1];
         [[maybe_unused]] int xb[kXS ? S::kNT : 1];
         if constexpr (kXS) {
@@ -223,30 +308,11 @@ gemm_tiled_kernel(const GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
         }
         const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
-        constexpr int SET = decltype(setc)::value;
         // A fragments in MFMA order: fragment f = (step f / kMT, row tile f % kMT).
         constexpr int kFr = S::kSteps * S::kMT;
         auto frag_at = [&](int f) {
             return lds_frag<DT>(abase + ((f % S::kMT) * S::kCH + (f / S::kMT) * S::kStepCh) * 1024);
         };
-        // Blockscale: the partials of fragment f are scaled and added after
-        // the MFMAs of fragment f+1 are issued, so the VALU work never waits
-        // on the MFMA that produced its operand.  All columns of a wave lie
-        // in one 128-column block (its 16*kNT columns divide 128), so sB is
-        // one value per wave and k-tile and sA * sB is formed once per row
-        // tile.
-        [[maybe_unused]] f32x4 part[2][S::kNT];
-        [[maybe_unused]] auto rescale = [&](int mt, const f32x4 *pp) {
-            const float sc = __fmul_rn(__int_as_float(xa[mt / 4][mt % 4]), __int_as_float(xb[0]));
-#pragma unroll
-            for (int nt = 0; nt < S::kNT; ++nt) {
-                acc[mt][nt].x = __fadd_rn(acc[mt][nt].x, __fmul_rn(pp[nt].x, sc));
-                acc[mt][nt].y = __fadd_rn(acc[mt][nt].y, __fmul_rn(pp[nt].y, sc));
-                acc[mt][nt].z = __fadd_rn(acc[mt][nt].z, __fmul_rn(pp[nt].z, sc));
-                acc[mt][nt].w = __fadd_rn(acc[mt][nt].w, __fmul_rn(pp[nt].w, sc));
-            }
-        };
-        static_assert(SCALE != kScaleBlock || 128 % (16 * S::kNT) == 0, "a wave's columns in one block");
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
             const int st = f / S::kMT, mt = f % S::kMT;
@@ -260,25 +326,16 @@ gemm_tiled_kernel(const GemmArgs p)
                     b = cat(breg[SET][nt][2 * st], breg[SET][nt][2 * st + 1]);
                 if constexpr (SCALE == kScaleMx) {
                     acc[mt][nt] = mfma_mx(b, a, acc[mt][nt], xb[nt], xa[mt / 4][mt % 4]);
-                } else if constexpr (SCALE == kScaleBlock) {
-                    // One MFMA is one 128-wide K block: its fp32 partial is
-                    // scaled by sA * sB and added (below, one fragment later).
-                    part[f & 1][nt] = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
                 } else {
                     acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
                 }
             }
-            if constexpr (SCALE == kScaleBlock)
-                if (f > 0)
-                    rescale((f - 1) % S::kMT, part[(f - 1) & 1]);
             if (mt == S::kMT - 1) {
 #pragma unroll
                 for (int cc = 0; cc < S::kStepCh; ++cc)
                     load_b(setc, st * S::kStepCh + cc, knext);
             }
         }
-        if constexpr (SCALE == kScaleBlock)
-            rescale((kFr - 1) % S::kMT, part[(kFr - 1) & 1]);
         if constexpr (PD > 0) {
             // Software-pipeline the A fragments: the LDS reads of PD fragments
             // first, then for every fragment its MFMAs followed by the reads of
@@ -300,12 +357,10 @@ gemm_tiled_kernel(const GemmArgs p)
                 } else {
                     __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
                 }
-                // blockscale: the previous fragment's scaling (1 + 8 VALU ops per column strip pair)
-                if constexpr (SCALE == kScaleBlock)
-                    __builtin_amdgcn_sched_group_barrier(0x002, 1 + 4 * S::kNT, 0);
                 if (f + kRA < kFr)
                     __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
             }
+        }
         }
         cur = cur + kStageBytes == kRing * kStageBytes ? 0 : cur + kStageBytes;
         nxt = nxt + kStageBytes == kRing * kStageBytes ? 0 : nxt + kStageBytes;
