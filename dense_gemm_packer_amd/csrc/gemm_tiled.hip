@@ -88,10 +88,6 @@ gemm_tiled_kernel(const GemmArgs p)
     for (int nt = 0; nt < S::kNT; ++nt)
         b_voff[nt] = (uint32_t)nt * 16u * Kb + (uint32_t)lane * 16u;
 
-    float scale = 1.0f;
-    if constexpr (SCALE == kScaleTensor)
-        scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
-
     // Scale copies: instruction j of this wave fills dwords 64g .. 64g+63 of
     // the scale area (g = j*waves + wave); lane l supplies dword 64g + l.
     // Rows >= M and (blockscale) column blocks past N load as zero.
@@ -389,7 +385,13 @@ gemm_tiled_kernel(const GemmArgs p)
             step(std::integral_constant<int, (DEPTH > 3 ? 2 : 0)>{}, t++);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue: scale once, round once.
+    // Epilogue: scale once, round once.  The per-tensor scales are loaded
+    // here, not before the loop: a scalar load still in flight at the loop
+    // would make the compiler wait for every LDS read (lgkmcnt(0)) before the
+    // first MFMA of each unrolled loop body.
+    float scale = 1.0f;
+    if constexpr (SCALE == kScaleTensor)
+        scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
 #pragma unroll
     for (int mt = 0; mt < S::kMT; ++mt) {
         const int m = m0 + (wm * S::kMT + mt) * 16 + (lane & 15);
