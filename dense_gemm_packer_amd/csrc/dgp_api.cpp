@@ -148,6 +148,12 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         // A single bf16 row also streams faster through the K-split tile at
         // any N: its 8 waves per workgroup keep more of the weight in flight,
         // and re-reading one A row per strip costs little.
+        // Fewer strips x splits than CUs (256): half a strip per workgroup
+        // doubles the workgroups with no second pass (measured equal at M = 1
+        // and 2-10 % faster at M = 16, N = 2048; at 256 strips and more, the
+        // whole strip is faster).
+        if (N * split_k < 256 * 16)
+            return find_spec(Query{kStream, dtype, scale, out, 16, 8});
         if (N * split_k < 128 * 64 || (dtype == DGP_BF16 && M == 1 && split_k == 1))
             return find_spec(Query{kStream, dtype, scale, out, 16, 16});
         // Up to one 64-column workgroup per CU (256): the 32-column tile's

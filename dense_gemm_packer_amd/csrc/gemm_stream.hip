@@ -283,10 +283,18 @@ gemm_stream_kernel(const GemmArgs p, int panel)
 // a fixed order, so results are reproducible -- and wave 0 runs the epilogue.
 // Blockscale: one fp8 MFMA step is exactly one 128-wide K block, scaled as in
 // gemm_stream_kernel with the scales read straight from global memory.
-template <int DT, int NW, int DEPTH, int SCALE, int OUT>
+// TN = 8 (half strips): two workgroups share a strip, each owning 8 of its 16
+// columns, so a narrow weight fills twice as many CUs with no second pass.
+// Lanes whose B row (lane % 16) belongs to the other half load at an offset
+// past the strip's buffer range, which returns zeros without a memory
+// access: each workgroup reads only its half of every 1 KiB block (8 rows x
+// 4 contiguous 128-byte pieces), and its MFMAs compute zeros for the other
+// half's columns, which it does not store.
+template <int DT, int NW, int DEPTH, int SCALE, int OUT, int TN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 gemm_ksplit_kernel(const GemmArgs p)
 {
+    static_assert(TN == 16 || TN == 8, "a whole strip or half of one");
     using Frag = typename Op<DT>::Frag;
     constexpr int kStepCh = Op<DT>::kBlocks;
     constexpr int kStepBytes = 64 * kStepCh;
@@ -297,7 +305,8 @@ gemm_ksplit_kernel(const GemmArgs p)
 
     const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
     const int m0 = (int)tc.tm * 16;
-    const int strip = (int)tc.tn;
+    const int strip = TN == 16 ? (int)tc.tn : (int)tc.tn >> 1;
+    const int half = TN == 16 ? 0 : (int)tc.tn & 1;
     const int split = (int)tc.s;
     const uint32_t Kb = (uint32_t)p.Kb;
     const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
@@ -312,8 +321,14 @@ gemm_ksplit_kernel(const GemmArgs p)
 
     const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
     const uint32_t a_voff = (uint32_t)(lane & 15) * Kb + (uint32_t)(lane >> 4) * 16u;
-    const auto rB = make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip) * 16 * Kb));
-    const uint32_t b_voff = (uint32_t)lane * 16u;
+    // Half strips: the resource covers exactly the strip (16 rows, at most
+    // 128 MiB), and the other half's lanes start at 2^31, so every offset
+    // they form stays past the range and below 2^32.
+    const auto rB = TN == 16
+        ? make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip) * 16 * Kb))
+        : make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, strip < p.N / 16 ? 16u * Kb : 0u);
+    const bool row_on = TN == 16 || ((lane & 15) >> 3) == half;
+    const uint32_t b_voff = (uint32_t)lane * 16u + (row_on ? 0u : 0x80000000u);
     const int m = m0 + (lane & 15);
     const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
     const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
@@ -392,7 +407,9 @@ gemm_ksplit_kernel(const GemmArgs p)
         }
         if constexpr (SCALE == kScaleTensor)
             v = v * (static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0]);
-        store_tile<OUT>(p, split, m, strip * 16 + (lane >> 4) * 4, v);
+        // lane l holds columns 4*(l/16) .. +3 of the strip
+        if (TN == 16 || ((lane >> 4) >> 1) == half)
+            store_tile<OUT>(p, split, m, strip * 16 + (lane >> 4) * 4, v);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -429,16 +446,16 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
 }
 
-template <int DT, int NW, int DEPTH, int SCALE, int OUT>
+template <int DT, int NW, int DEPTH, int SCALE, int OUT, int TN>
 void launch_ksplit(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    gemm_ksplit_kernel<DT, NW, DEPTH, SCALE, OUT><<<grid, NW * 64, 0, s>>>(a);
+    gemm_ksplit_kernel<DT, NW, DEPTH, SCALE, OUT, TN><<<grid, NW * 64, 0, s>>>(a);
 }
 
-#define DGP_KSPLIT(DT, NW, DEPTH, SC, OUT)                                                    \
-    {kStream, DT, SC, OUT, 16, 16, 0, NW, 1, DEPTH, 0, 0, DEPTH, 0, &launch_ksplit<DT, NW, DEPTH, SC, OUT>}
-#define DGP_KSPLIT_BOTH_OUT(DT, NW, DEPTH, SC)                                                \
-    DGP_KSPLIT(DT, NW, DEPTH, SC, kOutBf16), DGP_KSPLIT(DT, NW, DEPTH, SC, kOutPartial)
+#define DGP_KSPLIT(DT, NW, DEPTH, SC, OUT, TN)                                                \
+    {kStream, DT, SC, OUT, 16, TN, 0, NW, 1, DEPTH, 0, 0, DEPTH, 0, &launch_ksplit<DT, NW, DEPTH, SC, OUT, TN>}
+#define DGP_KSPLIT_BOTH_OUT(DT, NW, DEPTH, SC, TN)                                            \
+    DGP_KSPLIT(DT, NW, DEPTH, SC, kOutBf16, TN), DGP_KSPLIT(DT, NW, DEPTH, SC, kOutPartial, TN)
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
     {kStream, DT, SC, OUT, 16, 16 * NW * SPW, stream_panel_max(DT), NW, SPW, DEPTH, 0, 0, DEPTH, 0, \
      &launch_stream<DT, NW, SPW, DEPTH, SC, OUT>}
@@ -461,11 +478,17 @@ static const KernelSpec kStreamKernels[] = {
     DGP_STREAM_BOTH_OUT(kDtypeFp8, 2, 1, 8, kScaleMx),
     DGP_STREAM_BOTH_OUT(kDtypeFp4, 2, 1, 8, kScaleMx32),
     // one strip per workgroup, K split over the waves: waves, ring depth
-    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone),
-    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor),
-    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock),
-    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx),
-    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone, 16),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor, 16),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 16),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 16),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 16),
+    // half a strip per workgroup (16 x 8 tiles)
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone, 8),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor, 8),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 8),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 8),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 8),
 };
 
 const KernelSpec *stream_kernels(int *count)

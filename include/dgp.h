@@ -85,7 +85,10 @@ typedef enum dgp_scale_mode {
 /* Optional tile configuration.  Pass NULL to use the built-in per-shape table.
  *   tile_m, tile_n : output tile of one workgroup (must name a compiled tile:
  *                    256x256, 128x256, 128x128 for bf16 and per-tensor fp8;
- *                    16x64, 16x32 streaming and 16x16 K-split for every mode)
+ *                    256x256 and 128x128 for fp8 blockscale and mxfp8;
+ *                    16x64, 16x32 streaming, 16x16 K-split and 16x8 K-split
+ *                    over half a strip (two workgroups per 16-column strip)
+ *                    for every mode)
  *   tile_k         : K bytes staged per main-loop step (128 or 256)
  *   xcd_remap      : 1 = map workgroup ids so neighbouring tiles share an XCD's
  *                    L2 (output is bit-identical either way), 0 = plain raster
@@ -101,8 +104,9 @@ typedef enum dgp_scale_mode {
  *   waves_m        : tiled kernels: waves along M inside the workgroup; the
  *                    16-row streaming kernel (tile_m = 16, tile_n 32 or 64):
  *                    waves per workgroup, each owning tile_n / (16 * waves)
- *                    strips; the K-split kernel (16x16): waves sharing the
- *                    strip's K range (0 = any compiled layout for this tile).
+ *                    strips; the K-split kernel (16x16, 16x8): waves sharing
+ *                    the strip's K range (0 = any compiled layout for this
+ *                    tile).
  *   prefetch       : tiled kernels: k-tiles loaded ahead of the one being
  *                    multiplied; streaming kernel: MFMA steps of loads in
  *                    flight per wave (0 = any compiled depth for this tile).

@@ -12,7 +12,7 @@ import torch
 import dense_gemm_packer_amd as dgp
 import oracle
 import synth
-from gpu_common import (DEV, assert_close, dev_codes, dev_f32, dmode, host_bits, run_gpu,
+from gpu_common import (DEV, assert_close, dev_codes, dev_f32, dev_scales, dmode, host_bits, run_gpu,
                         run_oracle)
 
 pytestmark = pytest.mark.gpu
@@ -147,13 +147,14 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
-@pytest.mark.parametrize("tile_n", [64, 32, 16])
+@pytest.mark.parametrize("tile_n", [64, 32, 16, 8])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128"), ("fp4", "mx32")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
 def test_stream_splitk(dtype, mode, M, split_k, tile_n):
-    """Decode kernels: the 16x64 and 16x32 streaming tiles and the 16x16 K-split tile."""
+    """Decode kernels: the 16x64 and 16x32 streaming tiles, the 16x16 K-split
+    tile and its half-strip form (16x8)."""
     N, K = 384, 2048
     cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
     A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 3)
@@ -166,13 +167,15 @@ def test_stream_splitk(dtype, mode, M, split_k, tile_n):
     assert_close(got, c32)
 
 
+@pytest.mark.parametrize("tile_n", [16, 8])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128")])
-def test_ksplit_uneven_and_empty_slices(dtype, mode):
-    """K-split kernel: step counts not divisible by the 8 waves and fewer
-    steps than waves (some waves own no K), with splits.  (bf16 steps are 64
-    bytes and K rows must be whole 128 bytes, so its counts are even.)"""
-    cfg = dgp.Config(16, 16, 0, 0, 1, 0, 0)
+def test_ksplit_uneven_and_empty_slices(dtype, mode, tile_n):
+    """K-split kernel (whole and half strips): step counts not divisible by
+    the 8 waves and fewer steps than waves (some waves own no K), with splits.
+    (bf16 steps are 64 bytes and K rows must be whole 128 bytes, so its
+    counts are even.)"""
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
     step = 32 if dtype == "bf16" else 128    # K elements per MFMA step
     cases = (((18, 1), (26, 1), (2, 1), (6, 1), (36, 2), (20, 2)) if dtype == "bf16" else
              ((9, 1), (13, 1), (1, 1), (3, 1), (5, 1), (18, 2), (10, 2)))
@@ -184,6 +187,25 @@ def test_ksplit_uneven_and_empty_slices(dtype, mode):
         got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
         _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
         assert np.array_equal(got, c16), (steps, split)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
+                                        ("fp8", "mx128"), ("fp4", "mx32")])
+@pytest.mark.parametrize("M,split_k", [(1, 1), (16, 1), (20, 2)])
+def test_half_strip_writes_every_column(dtype, mode, M, split_k):
+    """Half-strip K-split tile: the two workgroups of a strip each store
+    only their 8 columns; together they cover C.  C starts as NaN, so a
+    column that neither stores stays NaN and fails the bit-exact check."""
+    N, K = 256, 1024
+    A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 17)
+    a = dev_codes(A, dtype)
+    Bs_dev = dgp.preshuffle_b(dev_codes(B, dtype))
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dgp.gemm_preshuffle_splitk(a, Bs_dev, split_k, dev_scales(sA, mode), dev_scales(sB, mode), dmode(mode),
+                               out=out, config=dgp.Config(16, 8, 0, 0, 1, 0, 0))
+    torch.cuda.synchronize()
+    _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+    assert np.array_equal(host_bits(out), c16)
 
 
 @pytest.mark.parametrize("dtype,mode", [("fp8", "tensor"), ("fp4", "mx32")])

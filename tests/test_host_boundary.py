@@ -242,8 +242,11 @@ def test_default_selection(dgp):
         cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
         assert (cfg.tile_m, cfg.tile_n) == (256, 256)
         assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dt, sm, 4)][0].tile_n == 64
-        # narrow weights: one strip per workgroup, K split over its waves
-        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 1)][0].tile_n == 16
+        # narrow weights: one strip per workgroup, K split over its waves;
+        # fewer strips x splits than CUs: half a strip per workgroup
+        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 1)][0].tile_n == 8
+        assert dgp.kernels()[dgp.select_kernel(16, 1024, 7168, dt, sm, 2)][0].tile_n == 8
+        assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dt, sm, 1)][0].tile_n == 16
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 32
         assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == 32
@@ -263,7 +266,8 @@ def test_default_selection(dgp):
     assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.FP8_E4M3, dgp.SCALE_TENSOR)][0].tile_n == 64
     # mxfp4 follows the same rule as the other decode modes
     assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 64
-    assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 16
+    assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 8
+    assert dgp.kernels()[dgp.select_kernel(1, 4096, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 16
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
