@@ -138,10 +138,9 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    // Decode-sized M streams the weight through the 16-row tiles; so does
-    // mxfp4 at any M (its 32-K scale blocks have no tiled kernel).  Larger M
-    // takes the tiled kernels, blockscale and mxfp8 included.
-    if (scale == DGP_SCALE_MX32 || M <= 32) {
+    // Decode-sized M streams the weight through the 16-row tiles.  Larger M
+    // takes the tiled kernels, every scale mode included.
+    if (M <= 32) {
         // Narrow weights: when the 64-column streaming tile would give fewer
         // than 128 workgroups, one strip per workgroup with K split over its
         // waves spreads the stream wider (measured faster up to that point).

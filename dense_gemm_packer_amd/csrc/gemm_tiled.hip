@@ -40,13 +40,19 @@ gemm_tiled_kernel(const GemmArgs p)
     // tiles (column strips) are consecutive dwords.  An E8M0 byte lands in
     // the low byte of its dword (the narrow async load writes lane l at dword
     // l), which is the byte the scaled MFMA reads.
-    constexpr bool kXS = SCALE == kScaleBlock || SCALE == kScaleMx;
-    constexpr int kES = SCALE == kScaleBlock ? 4 : 1;          // bytes per scale
-    constexpr int kXDwords = kXS ? TM + TN : 0;
+    // mxfp4: a 128-byte k-tile is 256 elements, 8 E8M0 bytes per row (one per
+    // 32-element block), copied as 2 dwords per row: dword 2r + j of the
+    // area is bytes 4j..4j+3 of tile row r, dword 2*TM + 2c + j the same for
+    // column c -- the byte order of the [rows][K/32] scale arrays.
+    constexpr bool kX4 = SCALE == kScaleMx32;
+    constexpr bool kXS = SCALE == kScaleBlock || SCALE == kScaleMx || kX4;
+    constexpr int kES = SCALE == kScaleMx ? 1 : 4;             // bytes per scale copy
+    constexpr int kXDwords = kX4 ? 2 * (TM + TN) : kXS ? TM + TN : 0;
     constexpr int kXDma = kXDwords / (64 * S::kWaves);        // scale copies per wave per k-tile
-    static_assert(!kXS || (DT == kDtypeFp8 && KT == 128 && kXDwords % (64 * S::kWaves) == 0 &&
-                           TM % 64 == 0 && S::kMT % 4 == 0 && (S::kNT == 2 || S::kNT == 4)),
-                  "staged scales: fp8, one 128-K block per k-tile, whole copies per wave");
+    static_assert(!kXS || (KT == 128 && kXDwords % (64 * S::kWaves) == 0 && TM % 64 == 0 &&
+                           (kX4 ? DT == kDtypeFp4 : DT == kDtypeFp8 && S::kMT % 4 == 0) &&
+                           (S::kNT == 2 || S::kNT == 4)),
+                  "staged scales: one 128-byte k-tile per scale stage, whole copies per wave");
     constexpr int kStageBytes = S::kBufBytes + kXDwords * 4;
     static_assert(DEPTH >= 1 && (DEPTH + 1) * kStageBytes <= 160 * 1024, "A ring must fit in LDS");
     // Prefetch distance DEPTH k-tiles: a ring of DEPTH+1 A buffers in LDS and
@@ -93,7 +99,21 @@ gemm_tiled_kernel(const GemmArgs p)
     // Rows >= M and (blockscale) column blocks past N load as zero.
     [[maybe_unused]] __amdgpu_buffer_rsrc_t x_rsrc[kXDma > 0 ? kXDma : 1];
     [[maybe_unused]] uint32_t x_voff[kXDma > 0 ? kXDma : 1];
-    if constexpr (kXS) {
+    if constexpr (kX4) {
+        const uint32_t rowb = Kb / 16u;    // E8M0 bytes per row: one per 32 elements = 16 bytes
+        const auto rXA = make_rsrc((const uint8_t *)p.sA + (int64_t)m0 * rowb,
+                                   clamp_bytes((int64_t)(p.M - m0) * rowb));
+        const auto rXB = make_rsrc((const uint8_t *)p.sB + (int64_t)n0 * rowb,
+                                   clamp_bytes((int64_t)(p.N - n0) * rowb));
+#pragma unroll
+        for (int j = 0; j < kXDma; ++j) {
+            const int g = j * S::kWaves + wave;
+            const bool on_a = g * 64 < 2 * TM;
+            const int d = (on_a ? g * 64 : g * 64 - 2 * TM) + lane;
+            x_rsrc[j] = on_a ? rXA : rXB;
+            x_voff[j] = (uint32_t)(d >> 1) * rowb + 4u * (uint32_t)(d & 1);
+        }
+    } else if constexpr (kXS) {
         const uint32_t kblk = Kb / 128u;   // 128-K blocks per row (fp8: one byte per element)
         const auto rXA = make_rsrc((const uint8_t *)p.sA + (int64_t)m0 * kblk * kES,
                                    clamp_bytes((int64_t)(p.M - m0) * kblk * kES));
@@ -146,7 +166,9 @@ gemm_tiled_kernel(const GemmArgs p)
             for (int j = 0; j < kXDma; ++j) {
                 auto *d = (__attribute__((address_space(3))) void *)(lds + buf_off + S::kBufBytes +
                                                                      (j * S::kWaves + wave) * 256);
-                if constexpr (kES == 4)   // the size operand must be a literal
+                if constexpr (kX4)   // the size operand must be a literal
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 4, x_voff[j], koff / 16u, 0, 0);
+                else if constexpr (kES == 4)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 4, x_voff[j], (koff / 128u) * 4u, 0, 0);
                 else
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 1, x_voff[j], koff / 128u, 0, 0);
@@ -268,6 +290,61 @@ gemm_tiled_kernel(const GemmArgs p)
         }
     };
 
+    // mxfp4 k-tile: two 128-element MFMA steps, 32 fragments (step-major,
+    // as in the other modes).  Lane l's 16-byte fragment is one 32-element
+    // block of its row, block 4*step + l/16 of the k-tile, whose E8M0 byte is
+    // byte l/16 of the row's scale dword for that step.  Same fenced order as
+    // the blockscale k-tile: LDS reads (fragment and scale dword) PD
+    // fragments ahead, then the fragment's MFMAs.
+    [[maybe_unused]] auto mx4_step = [&](auto setc, uint32_t knext) {
+        if constexpr (SCALE == kScaleMx32) {
+        constexpr int SET = decltype(setc)::value;
+        static_assert(DT == kDtypeFp4 && S::kStepCh == 1 && PD >= 1, "mxfp4: one 64-byte chunk per MFMA step");
+        constexpr int kFr = S::kSteps * S::kMT;
+        constexpr int kRA = PD < kFr ? PD : kFr;
+        constexpr int kR = kRA + 1;                        // fragment ring slots
+        const int rit = lane & 15;
+        const uint32_t sh = 8u * (uint32_t)(lane >> 4);
+        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+        const uint8_t *xs = lds + cur + S::kBufBytes;
+        const uint8_t *xap = xs + ((wm * S::kMT * 16 + rit) * 2) * 4;
+        const uint8_t *xbp = xs + 2 * TM * 4 + ((wn * S::kNT * 16 + rit) * 2) * 4;
+        int eb[S::kNT][S::kSteps];
+#pragma unroll
+        for (int nt = 0; nt < S::kNT; ++nt)
+#pragma unroll
+            for (int st = 0; st < S::kSteps; ++st)
+                eb[nt][st] = (int)((*reinterpret_cast<const uint32_t *>(xbp + (nt * 32 + st) * 4) >> sh) & 0xFFu);
+        Frag ring[kR];
+        uint32_t ra[kR];
+        auto fetch = [&](int f) {
+            const int st = f / S::kMT, mt = f % S::kMT;
+            ring[f % kR] = lds_frag<DT>(abase + (mt * S::kCH + st) * 1024);
+            ra[f % kR] = *reinterpret_cast<const uint32_t *>(xap + (mt * 32 + st) * 4);
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kRA; ++f) {
+            fetch(f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+            const int st = f / S::kMT, mt = f % S::kMT;
+            if (f + kRA < kFr)
+                fetch(f + kRA);
+            __builtin_amdgcn_sched_barrier(0);
+            const int ea = (int)((ra[f % kR] >> sh) & 0xFFu);
+#pragma unroll
+            for (int nt = 0; nt < S::kNT; ++nt)
+                acc[mt][nt] = mfma_mx4(breg[SET][nt][st], ring[f % kR], acc[mt][nt], eb[nt][st], ea);
+            if (mt == S::kMT - 1)
+                load_b(setc, st, knext);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+    };
+
     auto step = [&](auto setc, int t) {
         // This wave's A copy of tile t has landed once at most kAfter loads are
         // outstanding, and every earlier LDS read has completed; the barrier
@@ -280,6 +357,8 @@ gemm_tiled_kernel(const GemmArgs p)
         constexpr int SET = decltype(setc)::value;
         if constexpr (SCALE == kScaleBlock) {
             block_step(setc, knext);
+        } else if constexpr (SCALE == kScaleMx32) {
+            mx4_step(setc, knext);
         } else {
         // mxfp8: this tile's E8M0 scales, the lane's row tiles (A) and column strips (B).
         [[maybe_unused]] i32x4 xa[kXS ? S::kMT / 4 : 1];
@@ -645,6 +724,9 @@ static const KernelSpec kTiledKernels[] = {
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleBlock, 0, 4),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 256, 256, 1, 8, 128, 2, kScaleMx, 0, 4),
     DGP_TILED_BOTH_OUT(kDtypeFp8, 128, 128, 2, 2, 128, 2, kScaleMx, 0, 4),
+    // large tiles, mxfp4 (two 128-element steps and 8 scale bytes per row per k-tile)
+    DGP_TILED_BOTH_OUT(kDtypeFp4, 256, 256, 1, 8, 128, 2, kScaleMx32, 0, 8),
+    DGP_TILED_BOTH_OUT(kDtypeFp4, 128, 128, 2, 2, 128, 2, kScaleMx32, 0, 4),
 };
 
 const KernelSpec *tiled_kernels(int *count)

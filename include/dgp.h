@@ -85,7 +85,7 @@ typedef enum dgp_scale_mode {
 /* Optional tile configuration.  Pass NULL to use the built-in per-shape table.
  *   tile_m, tile_n : output tile of one workgroup (must name a compiled tile:
  *                    256x256, 128x256, 128x128 for bf16 and per-tensor fp8;
- *                    256x256 and 128x128 for fp8 blockscale and mxfp8;
+ *                    256x256 and 128x128 for fp8 blockscale, mxfp8 and mxfp4;
  *                    16x64, 16x32 streaming, 16x16 K-split and 16x8 K-split
  *                    over half a strip (two workgroups per 16-column strip)
  *                    for every mode)

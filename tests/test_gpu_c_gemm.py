@@ -83,6 +83,7 @@ CASES = [  # dtype, mode, M, N, K
     ("fp4", "mx32", 1, 2048, 768),
     ("fp4", "mx32", 37, 144, 512),
     ("fp4", "mx32", 300, 272, 256),
+    ("fp4", "mx32", 1030, 1040, 1280),
 ]
 
 
@@ -128,16 +129,16 @@ def test_every_compiled_kernel():
 
 
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
-                                        ("fp8", "mx128")])
+                                        ("fp8", "mx128"), ("fp4", "mx32")])
 def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):
     """ntiles % depth != 0 exercises the steps after the unrolled main loop
     (1, 2, 3, 5, 7 k-tiles of 128 bytes)."""
-    eb = 2 if dtype == "bf16" else 1
-    dcode = dgp.BF16 if dtype == "bf16" else dgp.FP8_E4M3
+    per_byte = {"bf16": 0.5, "fp8": 1, "fp4": 2}[dtype]   # elements per row byte
+    dcode = {"bf16": dgp.BF16, "fp8": dgp.FP8_E4M3, "fp4": dgp.FP4_E2M1}[dtype]
     scode = {"none": dgp.SCALE_NONE, "tensor": dgp.SCALE_TENSOR, "block128": dgp.SCALE_BLOCK128,
-             "mx128": dgp.SCALE_MX128}[mode]
+             "mx128": dgp.SCALE_MX128, "mx32": dgp.SCALE_MX32}[mode]
     for tiles in (1, 2, 3, 5, 7):
-        k = tiles * 128 // eb
+        k = int(tiles * 128 * per_byte)
         for cfg in [c for c, dt, sm, so in dgp.kernels() if c.tile_m > 16 and dt == dcode and sm == scode
                     and not so]:
             N = 640 if mode == "block128" else 528   # blockscale: whole 128-column blocks

@@ -251,15 +251,15 @@ def test_default_selection(dgp):
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 32
         assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == 32
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 8)][0].tile_n == 64
-    # blockscale and mxfp8: the tiled kernels above decode-sized M, the
-    # streaming tiles at it; mxfp4 streams at any M
-    for sm in (dgp.SCALE_BLOCK128, dgp.SCALE_MX128):
-        i = dgp.select_kernel(4096, 4096, 7168, dgp.FP8_E4M3, sm)
+    # blockscale, mxfp8 and mxfp4: the tiled kernels above decode-sized M,
+    # the streaming tiles at it
+    for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
+                   (dgp.FP4_E2M1, dgp.SCALE_MX32)):
+        i = dgp.select_kernel(4096, 4096, 7168, dt, sm)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][0].tile_n, dgp.kernels()[i][2]) == (256, 256, sm)
-        i = dgp.select_kernel(300, 1024, 7168, dgp.FP8_E4M3, sm, 2)
+        i = dgp.select_kernel(300, 1024, 7168, dt, sm, 2)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][3]) == (128, True)
-        assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dgp.FP8_E4M3, sm)][0].tile_m == 16
-    assert dgp.kernels()[dgp.select_kernel(4096, 4096, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_m == 16
+        assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dt, sm)][0].tile_m == 16
     # a single bf16 row: the K-split tile at any N; fp8 keeps the 64-column tile
     assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
     assert dgp.kernels()[dgp.select_kernel(2, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 64
