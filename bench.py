@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 (published)
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (published)
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 MALL_BYTES = 256 << 20         # Infinity Cache; cold-cache rotation exceeds 2x this
 METRIC = "TFLOP/s (large M) and GB/s (decode M≤16) at 1 GPU; % of MFMA / HBM roofline"
@@ -79,7 +80,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of C in the CPU oracle sample (default: all of them)")
     ap.add_argument("--profile-traffic", action="store_true",
-                    help="run only a 256 MiB probe copy and a few GEMM launches (for counter runs)")
+                    help="run only a 256 MiB probe copy and a few GEMM launches (for counter runs): "
+                         "3 with the default XCD remap, then 3 with the plain raster (remap off)")
+    ap.add_argument("--profile-splitk-traffic", action="store_true",
+                    help="run only a 256 MiB probe copy and three fp8 split-K decode calls "
+                         "(M=16, N=16384, K=7168, split 4: pass 1 writing fp32 partials, then the reduce)")
     ap.add_argument("--profile-decode-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and three fp8 decode launches "
                          "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
@@ -121,6 +126,25 @@ def main():
         log("profile-decode-traffic: 3 x probe copy of 256 MiB, 3 x fp8 decode 16x16384x7168 on distinct weights")
         return 0
 
+    if args.profile_splitk_traffic:
+        wd = synth.workload_inputs("fp8_decode", M=16, N=16384)
+        Ad = to_dev(wd["A"], "fp8")
+        Bd = [dgp.preshuffle_b(to_dev(wd["B"], "fp8")) for _ in range(3)]
+        sAd = torch.from_numpy(wd["sA"]).to(dev)
+        sBd = torch.from_numpy(wd["sB"]).to(dev)
+        ws = torch.empty(dgp.splitk_workspace_bytes(16, 16384, 4) // 4, dtype=torch.float32, device=dev)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dgp.probe_copy(src, dst)
+        for b in Bd:
+            dgp.gemm_preshuffle_splitk(Ad, b, 4, sAd, sBd, workspace=ws)
+        torch.cuda.synchronize()
+        log("profile-splitk-traffic: 3 x probe copy of 256 MiB, 3 x fp8 split-K (4) decode 16x16384x7168 "
+            "on distinct weights")
+        return 0
+
     # ------------------------------------------------------------ headline
     w = synth.workload_inputs("bf16_large")
     M, N, K = w["M"], w["N"], w["K"]
@@ -137,8 +161,12 @@ def main():
             dgp.probe_copy(src, dst)
         for _ in range(3):
             dgp.gemm_preshuffle(A, Bs, out=C)
+        plain = dgp.Config(tile_m=256, tile_n=256, tile_k=128, xcd_remap=0, group_m=1)
+        for _ in range(3):
+            dgp.gemm_preshuffle(A, Bs, out=C, config=plain)
         torch.cuda.synchronize()
-        log("profile-traffic: 3 x probe copy of 256 MiB, 3 x GEMM bf16 4096x4096x8192")
+        log("profile-traffic: 3 x probe copy of 256 MiB, 3 x GEMM bf16 4096x4096x8192, "
+            "3 x the same GEMM with the plain raster (XCD remap off)")
         return 0
 
     for _ in range(args.warmup):
@@ -370,19 +398,25 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     # fp8 blockscale and mxfp8 GEMMs at the same size: the tiled kernel with
     # each k-tile's scales staged in LDS beside the A tile.
     for name, mode, smode in (("fp8_blockscale", "block128", dgp.SCALE_BLOCK128),
-                              ("fp8_mx128", "mx128", dgp.SCALE_MX128)):
+                              ("fp8_mx128", "mx128", dgp.SCALE_MX128), ("fp4_mx32", "mx32", dgp.SCALE_MX32)):
         w = synth.workload_inputs(name, M=4096, N=4096, K=8192)
-        A8 = to_dev(w["A"], "fp8")
-        Bs8 = dgp.preshuffle_b(to_dev(w["B"], "fp8"))
+        edt = "fp4" if mode == "mx32" else "fp8"
+        A8 = to_dev(w["A"], edt)
+        Bs8 = dgp.preshuffle_b(to_dev(w["B"], edt))
         sA = torch.from_numpy(w["sA"]).to(dev)
         sB = torch.from_numpy(w["sB"]).to(dev)
         C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
         us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, smode, out=C8), 10)
         tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
-        key = f"fp8_{mode}_gemm_4096x4096x8192"
-        out[key] = {"us": round(us, 1), "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-                    "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4),
-                    "kernel": dgp.describe_kernel(dgp.select_kernel(4096, 4096, 8192, dgp.FP8_E4M3, smode))}
+        key = f"{edt}_{mode}_gemm_4096x4096x8192"
+        dcode = dgp.FP4_E2M1 if mode == "mx32" else dgp.FP8_E4M3
+        out[key] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+                    "kernel": dgp.describe_kernel(dgp.select_kernel(4096, 4096, 8192, dcode, smode))}
+        if mode == "mx32":   # fp4 dense matrix-core peak (published); no fp4 wall is probed
+            out[key]["frac_of_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
+        else:
+            out[key]["frac_of_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+            out[key]["frac_measured_wall"] = round(tf / out["mfma_wall_fp8"]["workload_data"], 4)
         if cpu_threads:
             rows = np.linspace(0, 4095, 64).astype(np.int64)
             out[key]["cpu_oracle"] = oracle_leg(

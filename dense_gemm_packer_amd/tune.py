@@ -37,7 +37,7 @@ LLC_BYTES = 256 << 20
 DEFAULT_SHAPES = ["bf16:4096x4096x8192", "fp8:4096x4096x8192",
                   "fp8:1x2048x7168", "fp8:16x2048x7168", "fp8:1x16384x7168", "fp8:16x16384x7168",
                   "fp8:16x2048x7168:4", "fp8:16x16384x7168:2",
-                  "fp8b:16x16384x7168", "mx8:16x16384x7168", "fp8b:4096x4096x8192", "mx8:4096x4096x8192",
+                  "fp8b:16x16384x7168", "mx8:16x16384x7168", "fp8b:4096x4096x8192", "mx8:4096x4096x8192", "mx4:4096x4096x8192",
                   "mx4:1x2048x7168", "mx4:1x16384x7168", "mx4:16x16384x7168", "mx4:16x2048x7168:4",
                   "bf16:1x2048x7168", "bf16:16x2048x7168", "bf16:1x16384x7168", "bf16:16x16384x7168"]
 MODES = {"bf16": (BF16, SCALE_NONE), "fp8": (FP8_E4M3, SCALE_TENSOR), "fp8b": (FP8_E4M3, SCALE_BLOCK128),
