@@ -22,11 +22,11 @@ def _scales(w, rows):
     return sA, w["sB"]
 
 
-@pytest.mark.parametrize("name", ["bf16_large", "fp8_large", "fp8_blockscale", "fp8_mx128"])
+@pytest.mark.parametrize("name", ["bf16_large", "fp8_large", "fp8_blockscale", "fp8_mx128", "fp4_mx32"])
 def test_large_workload_sampled_rows(name):
-    """4096 x 4096 x 8192 (blockscale and mxfp8 at the size of the fp8
-    GEMM): rows on both sides of every 256-row tile boundary the sample
-    crosses, plus evenly spaced rows."""
+    """4096 x 4096 x 8192 (blockscale, mxfp8 and mxfp4 at the size of the
+    fp8 GEMM, as the benchmark times them): rows on both sides of every
+    256-row tile boundary the sample crosses, plus evenly spaced rows."""
     w = synth.workload_inputs(name, M=4096, N=4096, K=8192)
     dt, mode, M = w["dtype"], w["scale_mode"], w["M"]
     A = dev_codes(w["A"], dt)
