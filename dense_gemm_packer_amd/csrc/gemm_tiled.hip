@@ -223,70 +223,71 @@ gemm_tiled_kernel(const GemmArgs p)
     // sB is one value per wave and k-tile.
     [[maybe_unused]] auto block_step = [&](auto setc, uint32_t knext) {
         if constexpr (SCALE == kScaleBlock) {
-        constexpr int SET = decltype(setc)::value;
-        static_assert(DT == kDtypeFp8 && S::kSteps == 1 && PD >= 1, "blockscale: one fp8 MFMA step per k-tile");
-        static_assert(128 % (16 * S::kNT) == 0, "a wave's columns in one block");
-        constexpr int kFr = S::kMT;
-        constexpr int kRA = PD < kFr ? PD : kFr;
-        constexpr int kR = kRA + 1;                        // fragment ring slots
-        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
-        const uint8_t *xs = lds + cur + S::kBufBytes;
-        const uint8_t *xap = xs + ((lane & 15) * (TM / 16) + wm * S::kMT) * 4;
-        const float sb = *reinterpret_cast<const float *>(xs + TM * 4 + ((lane & 15) * (TN / 16) + wn * S::kNT) * 4);
-        Frag ring[kR];
-        float ra[kR];
-        auto fetch = [&](int f) {
-            ring[f % kR] = lds_frag<DT>(abase + f * S::kCH * 1024);
-            ra[f % kR] = *reinterpret_cast<const float *>(xap + 4 * f);
-        };
-        __builtin_amdgcn_sched_barrier(0);   // sB first: the first product needs it
+            constexpr int SET = decltype(setc)::value;
+            static_assert(DT == kDtypeFp8 && S::kSteps == 1 && PD >= 1, "blockscale: one fp8 MFMA step per k-tile");
+            static_assert(128 % (16 * S::kNT) == 0, "a wave's columns in one block");
+            constexpr int kFr = S::kMT;
+            constexpr int kRA = PD < kFr ? PD : kFr;
+            constexpr int kR = kRA + 1;                        // fragment ring slots
+            const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+            const uint8_t *xs = lds + cur + S::kBufBytes;
+            const uint8_t *xap = xs + ((lane & 15) * (TM / 16) + wm * S::kMT) * 4;
+            const float sb =
+                *reinterpret_cast<const float *>(xs + TM * 4 + ((lane & 15) * (TN / 16) + wn * S::kNT) * 4);
+            Frag ring[kR];
+            float ra[kR];
+            auto fetch = [&](int f) {
+                ring[f % kR] = lds_frag<DT>(abase + f * S::kCH * 1024);
+                ra[f % kR] = *reinterpret_cast<const float *>(xap + 4 * f);
+            };
+            __builtin_amdgcn_sched_barrier(0);   // sB first: the first product needs it
 #pragma unroll
-        for (int f = 0; f < kRA; ++f) {
-            fetch(f);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        f32x4 part[2][S::kNT];
-        float sc[2];
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-            if (f + kRA < kFr)
-                fetch(f + kRA);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int nt = 0; nt < S::kNT; ++nt) {
-                part[f & 1][nt] = mfma_op(cat(breg[SET][nt][0], breg[SET][nt][1]), ring[f % kR],
-                                          f32x4{0.f, 0.f, 0.f, 0.f});
-                if (nt == 0)
-                    sc[f & 1] = __fmul_rn(ra[f % kR], sb);
-                if (f == kFr - 1 && nt == S::kNT - 1) {
-#pragma unroll
-                    for (int cc = 0; cc < S::kStepCh; ++cc)
-                        load_b(setc, cc, knext);
-                }
+            for (int f = 0; f < kRA; ++f) {
+                fetch(f);
                 __builtin_amdgcn_sched_barrier(0);
-                if (f > 0) {
-                    f32x4 &a = acc[f - 1][nt];
-                    const f32x4 &q = part[(f - 1) & 1][nt];
-                    const float c = sc[(f - 1) & 1];
-                    a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
-                    a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
-                    a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
-                    a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+            }
+            f32x4 part[2][S::kNT];
+            float sc[2];
+#pragma unroll
+            for (int f = 0; f < kFr; ++f) {
+                if (f + kRA < kFr)
+                    fetch(f + kRA);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 0; nt < S::kNT; ++nt) {
+                    part[f & 1][nt] = mfma_op(cat(breg[SET][nt][0], breg[SET][nt][1]), ring[f % kR],
+                                              f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (nt == 0)
+                        sc[f & 1] = __fmul_rn(ra[f % kR], sb);
+                    if (f == kFr - 1 && nt == S::kNT - 1) {
+#pragma unroll
+                        for (int cc = 0; cc < S::kStepCh; ++cc)
+                            load_b(setc, cc, knext);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (f > 0) {
+                        f32x4 &a = acc[f - 1][nt];
+                        const f32x4 &q = part[(f - 1) & 1][nt];
+                        const float c = sc[(f - 1) & 1];
+                        a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
+                        a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
+                        a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
+                        a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
-        for (int nt = 0; nt < S::kNT; ++nt) {
-            f32x4 &a = acc[kFr - 1][nt];
-            const f32x4 &q = part[(kFr - 1) & 1][nt];
-            const float c = sc[(kFr - 1) & 1];
-            a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
-            a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
-            a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
-            a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
-        }
+            for (int nt = 0; nt < S::kNT; ++nt) {
+                f32x4 &a = acc[kFr - 1][nt];
+                const f32x4 &q = part[(kFr - 1) & 1][nt];
+                const float c = sc[(kFr - 1) & 1];
+                a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
+                a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
+                a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
+                a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+            }
         }
     };
 
@@ -298,50 +299,50 @@ gemm_tiled_kernel(const GemmArgs p)
     // fragments ahead, then the fragment's MFMAs.
     [[maybe_unused]] auto mx4_step = [&](auto setc, uint32_t knext) {
         if constexpr (SCALE == kScaleMx32) {
-        constexpr int SET = decltype(setc)::value;
-        static_assert(DT == kDtypeFp4 && S::kStepCh == 1 && PD >= 1, "mxfp4: one 64-byte chunk per MFMA step");
-        constexpr int kFr = S::kSteps * S::kMT;
-        constexpr int kRA = PD < kFr ? PD : kFr;
-        constexpr int kR = kRA + 1;                        // fragment ring slots
-        const int rit = lane & 15;
-        const uint32_t sh = 8u * (uint32_t)(lane >> 4);
-        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
-        const uint8_t *xs = lds + cur + S::kBufBytes;
-        const uint8_t *xap = xs + ((wm * S::kMT * 16 + rit) * 2) * 4;
-        const uint8_t *xbp = xs + 2 * TM * 4 + ((wn * S::kNT * 16 + rit) * 2) * 4;
-        int eb[S::kNT][S::kSteps];
-#pragma unroll
-        for (int nt = 0; nt < S::kNT; ++nt)
-#pragma unroll
-            for (int st = 0; st < S::kSteps; ++st)
-                eb[nt][st] = (int)((*reinterpret_cast<const uint32_t *>(xbp + (nt * 32 + st) * 4) >> sh) & 0xFFu);
-        Frag ring[kR];
-        uint32_t ra[kR];
-        auto fetch = [&](int f) {
-            const int st = f / S::kMT, mt = f % S::kMT;
-            ring[f % kR] = lds_frag<DT>(abase + (mt * S::kCH + st) * 1024);
-            ra[f % kR] = *reinterpret_cast<const uint32_t *>(xap + (mt * 32 + st) * 4);
-        };
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int f = 0; f < kRA; ++f) {
-            fetch(f);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-            const int st = f / S::kMT, mt = f % S::kMT;
-            if (f + kRA < kFr)
-                fetch(f + kRA);
-            __builtin_amdgcn_sched_barrier(0);
-            const int ea = (int)((ra[f % kR] >> sh) & 0xFFu);
+            constexpr int SET = decltype(setc)::value;
+            static_assert(DT == kDtypeFp4 && S::kStepCh == 1 && PD >= 1, "mxfp4: one 64-byte chunk per MFMA step");
+            constexpr int kFr = S::kSteps * S::kMT;
+            constexpr int kRA = PD < kFr ? PD : kFr;
+            constexpr int kR = kRA + 1;                        // fragment ring slots
+            const int rit = lane & 15;
+            const uint32_t sh = 8u * (uint32_t)(lane >> 4);
+            const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+            const uint8_t *xs = lds + cur + S::kBufBytes;
+            const uint8_t *xap = xs + ((wm * S::kMT * 16 + rit) * 2) * 4;
+            const uint8_t *xbp = xs + 2 * TM * 4 + ((wn * S::kNT * 16 + rit) * 2) * 4;
+            int eb[S::kNT][S::kSteps];
 #pragma unroll
             for (int nt = 0; nt < S::kNT; ++nt)
-                acc[mt][nt] = mfma_mx4(breg[SET][nt][st], ring[f % kR], acc[mt][nt], eb[nt][st], ea);
-            if (mt == S::kMT - 1)
-                load_b(setc, st, knext);
+#pragma unroll
+                for (int st = 0; st < S::kSteps; ++st)
+                    eb[nt][st] = (int)((*reinterpret_cast<const uint32_t *>(xbp + (nt * 32 + st) * 4) >> sh) & 0xFFu);
+            Frag ring[kR];
+            uint32_t ra[kR];
+            auto fetch = [&](int f) {
+                const int st = f / S::kMT, mt = f % S::kMT;
+                ring[f % kR] = lds_frag<DT>(abase + (mt * S::kCH + st) * 1024);
+                ra[f % kR] = *reinterpret_cast<const uint32_t *>(xap + (mt * 32 + st) * 4);
+            };
             __builtin_amdgcn_sched_barrier(0);
-        }
+#pragma unroll
+            for (int f = 0; f < kRA; ++f) {
+                fetch(f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int f = 0; f < kFr; ++f) {
+                const int st = f / S::kMT, mt = f % S::kMT;
+                if (f + kRA < kFr)
+                    fetch(f + kRA);
+                __builtin_amdgcn_sched_barrier(0);
+                const int ea = (int)((ra[f % kR] >> sh) & 0xFFu);
+#pragma unroll
+                for (int nt = 0; nt < S::kNT; ++nt)
+                    acc[mt][nt] = mfma_mx4(breg[SET][nt][st], ring[f % kR], acc[mt][nt], eb[nt][st], ea);
+                if (mt == S::kMT - 1)
+                    load_b(setc, st, knext);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -360,82 +361,82 @@ gemm_tiled_kernel(const GemmArgs p)
         } else if constexpr (SCALE == kScaleMx32) {
             mx4_step(setc, knext);
         } else {
-        // mxfp8: this tile's E8M0 scales, the lane's row tiles (A) and column strips (B).
-        [[maybe_unused]] i32x4 xa[kXS ? S::kMT / 4 : 1];
-        [[maybe_unused]] int xb[kXS ? S::kNT : 1];
-        if constexpr (kXS) {
-            const uint8_t *xs = lds + cur + S::kBufBytes;
-            const int rit = lane & 15;
+            // mxfp8: this tile's E8M0 scales, the lane's row tiles (A) and column strips (B).
+            [[maybe_unused]] i32x4 xa[kXS ? S::kMT / 4 : 1];
+            [[maybe_unused]] int xb[kXS ? S::kNT : 1];
+            if constexpr (kXS) {
+                const uint8_t *xs = lds + cur + S::kBufBytes;
+                const int rit = lane & 15;
 #pragma unroll
-            for (int q = 0; q < S::kMT / 4; ++q)
-                xa[q] = *reinterpret_cast<const i32x4 *>(xs + (rit * (TM / 16) + wm * S::kMT) * 4 + 16 * q);
-            const uint8_t *xbp = xs + TM * 4 + (rit * (TN / 16) + wn * S::kNT) * 4;
-            if constexpr (S::kNT == 2) {
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(xbp);
-                xb[0] = (int)v.x;
-                xb[1] = (int)v.y;
-            } else {
-                const i32x4 v = *reinterpret_cast<const i32x4 *>(xbp);
-#pragma unroll
-                for (int nt = 0; nt < S::kNT; ++nt)
-                    xb[nt] = v[nt];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
-        // A fragments in MFMA order: fragment f = (step f / kMT, row tile f % kMT).
-        constexpr int kFr = S::kSteps * S::kMT;
-        auto frag_at = [&](int f) {
-            return lds_frag<DT>(abase + ((f % S::kMT) * S::kCH + (f / S::kMT) * S::kStepCh) * 1024);
-        };
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-            const int st = f / S::kMT, mt = f % S::kMT;
-            const Frag a = frag_at(f);
-#pragma unroll
-            for (int nt = 0; nt < S::kNT; ++nt) {
-                Frag b;
-                if constexpr (DT == kDtypeBf16)
-                    b = breg[SET][nt][st];
-                else
-                    b = cat(breg[SET][nt][2 * st], breg[SET][nt][2 * st + 1]);
-                if constexpr (SCALE == kScaleMx) {
-                    acc[mt][nt] = mfma_mx(b, a, acc[mt][nt], xb[nt], xa[mt / 4][mt % 4]);
+                for (int q = 0; q < S::kMT / 4; ++q)
+                    xa[q] = *reinterpret_cast<const i32x4 *>(xs + (rit * (TM / 16) + wm * S::kMT) * 4 + 16 * q);
+                const uint8_t *xbp = xs + TM * 4 + (rit * (TN / 16) + wn * S::kNT) * 4;
+                if constexpr (S::kNT == 2) {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(xbp);
+                    xb[0] = (int)v.x;
+                    xb[1] = (int)v.y;
                 } else {
-                    acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
-                }
-            }
-            if (mt == S::kMT - 1) {
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(xbp);
 #pragma unroll
-                for (int cc = 0; cc < S::kStepCh; ++cc)
-                    load_b(setc, st * S::kStepCh + cc, knext);
+                    for (int nt = 0; nt < S::kNT; ++nt)
+                        xb[nt] = v[nt];
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        if constexpr (PD > 0) {
-            // Software-pipeline the A fragments: the LDS reads of PD fragments
-            // first, then for every fragment its MFMAs followed by the reads of
-            // the fragment PD places ahead -- each read gets PD fragments'
-            // worth of MFMAs to land.  With PV > 0, one global load (B reload
-            // or A copy) is placed after every PV MFMAs.
-            constexpr int kRA = PD < kFr ? PD : kFr;
-            constexpr int kRd = S::kStepCh;   // LDS reads per fragment
-            __builtin_amdgcn_sched_group_barrier(0x100, kRA * kRd, 0);
+            const uint8_t *abase = lds + cur + (wm * S::kMT * S::kCH) * 1024 + lane * 16;
+            // A fragments in MFMA order: fragment f = (step f / kMT, row tile f % kMT).
+            constexpr int kFr = S::kSteps * S::kMT;
+            auto frag_at = [&](int f) {
+                return lds_frag<DT>(abase + ((f % S::kMT) * S::kCH + (f / S::kMT) * S::kStepCh) * 1024);
+            };
 #pragma unroll
             for (int f = 0; f < kFr; ++f) {
-                if constexpr (PV > 0) {
-                    static_assert(PV <= S::kNT && S::kNT % PV == 0, "PV must divide the MFMAs per fragment");
+                const int st = f / S::kMT, mt = f % S::kMT;
+                const Frag a = frag_at(f);
 #pragma unroll
-                    for (int m = 0; m < S::kNT / PV; ++m) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, PV, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                for (int nt = 0; nt < S::kNT; ++nt) {
+                    Frag b;
+                    if constexpr (DT == kDtypeBf16)
+                        b = breg[SET][nt][st];
+                    else
+                        b = cat(breg[SET][nt][2 * st], breg[SET][nt][2 * st + 1]);
+                    if constexpr (SCALE == kScaleMx) {
+                        acc[mt][nt] = mfma_mx(b, a, acc[mt][nt], xb[nt], xa[mt / 4][mt % 4]);
+                    } else {
+                        acc[mt][nt] = mfma_op(b, a, acc[mt][nt]);
                     }
-                } else {
-                    __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
                 }
-                if (f + kRA < kFr)
-                    __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+                if (mt == S::kMT - 1) {
+#pragma unroll
+                    for (int cc = 0; cc < S::kStepCh; ++cc)
+                        load_b(setc, st * S::kStepCh + cc, knext);
+                }
             }
-        }
+            if constexpr (PD > 0) {
+                // Software-pipeline the A fragments: the LDS reads of PD fragments
+                // first, then for every fragment its MFMAs followed by the reads of
+                // the fragment PD places ahead -- each read gets PD fragments'
+                // worth of MFMAs to land.  With PV > 0, one global load (B reload
+                // or A copy) is placed after every PV MFMAs.
+                constexpr int kRA = PD < kFr ? PD : kFr;
+                constexpr int kRd = S::kStepCh;   // LDS reads per fragment
+                __builtin_amdgcn_sched_group_barrier(0x100, kRA * kRd, 0);
+#pragma unroll
+                for (int f = 0; f < kFr; ++f) {
+                    if constexpr (PV > 0) {
+                        static_assert(PV <= S::kNT && S::kNT % PV == 0, "PV must divide the MFMAs per fragment");
+#pragma unroll
+                        for (int m = 0; m < S::kNT / PV; ++m) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, PV, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        }
+                    } else {
+                        __builtin_amdgcn_sched_group_barrier(0x008, S::kNT, 0);
+                    }
+                    if (f + kRA < kFr)
+                        __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+                }
+            }
         }
         cur = cur + kStageBytes == kRing * kStageBytes ? 0 : cur + kStageBytes;
         nxt = nxt + kStageBytes == kRing * kStageBytes ? 0 : nxt + kStageBytes;
