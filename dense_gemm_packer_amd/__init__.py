@@ -53,7 +53,7 @@ class Config(ctypes.Structure):
 # Every symbol include/dgp.h and include/dgp_diag.h declare.
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
            "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
-           "dgp_tile_of_workgroup", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
+           "dgp_tile_of_workgroup", "dgp_tile_map", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
            "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_lds_dma_narrow", "dgp_probe_copy",
            "dgp_probe_stream_read", "dgp_probe_mfma_peak")
 
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
                                        _sz, _vp, _vp],
         "dgp_check_arch": [ctypes.c_char_p],
         "dgp_tile_of_workgroup": [_i64, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_i64)],
+        "dgp_tile_map": [_i64, _i64, _i64, _int, _int, _vp, _i64],
         "dgp_kernel_count": [],
         "dgp_kernel_info": [_int, ctypes.POINTER(Config), ctypes.POINTER(_int), ctypes.POINTER(_int),
                             ctypes.POINTER(_int)],
@@ -246,6 +247,14 @@ def tile_of_workgroup(wg: int, tiles_m: int, tiles_n: int, splits: int, xcd_rema
     out = (ctypes.c_int64 * 3)()
     _check(lib().dgp_tile_of_workgroup(wg, tiles_m, tiles_n, splits, xcd_remap, group_m, out))
     return int(out[0]), int(out[1]), int(out[2])
+
+
+def tile_map(tiles_m: int, tiles_n: int, splits: int, xcd_remap: int, group_m: int):
+    """(tile_m, tile_n, split) of every workgroup of the grid: an int64 numpy array [W][3]."""
+    import numpy as np
+    out = np.empty((tiles_m * tiles_n * splits, 3), dtype=np.int64)
+    _check(lib().dgp_tile_map(tiles_m, tiles_n, splits, xcd_remap, group_m, out.ctypes.data, out.size))
+    return out
 
 
 def kernels():

@@ -499,6 +499,27 @@ dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, i
     return ok();
 }
 
+dgp_status dgp_tile_map(int64_t tiles_m, int64_t tiles_n, int64_t splits, int xcd_remap, int group_m,
+                        int64_t *out, int64_t out_len)
+{
+    if (!out)
+        return fail(DGP_ERR_NULL, "out is NULL");
+    if (tiles_m < 1 || tiles_n < 1 || splits < 1 || (xcd_remap != 0 && xcd_remap != 1) ||
+        tiles_m * tiles_n * splits > INT32_MAX)
+        return fail(DGP_ERR_SHAPE, "bad tile-map arguments");
+    const int64_t total = tiles_m * tiles_n * splits;
+    if (out_len < 3 * total)
+        return fail(DGP_ERR_SHAPE, "out holds %lld values, the grid needs %lld", (long long)out_len,
+                    (long long)(3 * total));
+    for (int64_t wg = 0; wg < total; ++wg) {
+        const TileCoord c = tile_of_workgroup<int64_t>(wg, tiles_m, tiles_n, splits, xcd_remap, group_m);
+        out[3 * wg] = c.tm;
+        out[3 * wg + 1] = c.tn;
+        out[3 * wg + 2] = c.s;
+    }
+    return ok();
+}
+
 int dgp_kernel_count(void)
 {
     int n = 0;

@@ -35,6 +35,18 @@ dgp_status dgp_tile_of_workgroup(int64_t wg, int64_t tiles_m, int64_t tiles_n, i
                                  int xcd_remap, int group_m, int64_t out[3]);
 
 /*
+ * dgp_tile_map -- the same map for every workgroup of the grid at once:
+ * out[3*wg .. 3*wg+2] = (tile_m index, tile_n index, split index) for
+ * wg = 0 .. tiles_m*tiles_n*splits - 1.  `out` is a caller-owned host array
+ * of out_len int64 values (at least 3 per workgroup).  Pure host code, so a
+ * test can check the map is a bijection over many grid sizes cheaply.
+ * Returns DGP_ERR_NULL for a NULL out, DGP_ERR_SHAPE for bad arguments or
+ * an out array that is too short.
+ */
+dgp_status dgp_tile_map(int64_t tiles_m, int64_t tiles_n, int64_t splits, int xcd_remap, int group_m,
+                        int64_t *out, int64_t out_len);
+
+/*
  * dgp_kernel_info -- describe compiled GEMM kernel number `index`
  * (0 <= index < dgp_kernel_count()).  Fills *cfg with the configuration that
  * selects exactly this kernel through dgp_gemm_preshuffle[_splitk] (xcd_remap

@@ -4,6 +4,7 @@ status before making any HIP call (only invalid calls are made here, so no
 device is touched).  Also: the workgroup -> tile map is a bijection, and the
 product path shares nothing with the oracle."""
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -192,6 +193,50 @@ def test_tile_map_is_a_bijection(dgp, remap, group_m):
                 seen = {dgp.tile_of_workgroup(w, tm, tn, sp, remap, group_m) for w in range(W)}
                 assert len(seen) == W
                 assert all(0 <= a < tm and 0 <= b < tn and 0 <= c < sp for a, b, c in seen)
+
+
+def _grid_shapes(W):
+    """A few ways to factor a grid of W workgroups as tiles_m x tiles_n x splits."""
+    def near_square(n):
+        d = max(x for x in range(1, math.isqrt(n) + 1) if n % x == 0)
+        return n // d, d
+    shapes = {(W, 1, 1), (1, W, 1), (*near_square(W), 1)}
+    if W % 2 == 0:
+        shapes.add((*near_square(W // 2), 2))
+    return shapes
+
+
+@pytest.mark.parametrize("remap,group_m", [(0, 1), (1, 1), (1, 4), (1, 8)])
+def test_tile_map_bijective_over_grid_sizes(dgp, remap, group_m):
+    """Every grid size W = 1..4096 and every 97th size up to 65536 (and 65536
+    itself), each factored several ways: the workgroup -> (tile_m, tile_n,
+    split) map of the library hits every tile of every split exactly once."""
+    import numpy as np
+    sizes = list(range(1, 4097)) + list(range(4097, 65536, 97)) + [65536]
+    for W in sizes:
+        for tm, tn, sp in _grid_shapes(W):
+            assert tm * tn * sp == W
+            c = dgp.tile_map(tm, tn, sp, remap, group_m)
+            assert c[:, 0].min() >= 0 and c[:, 0].max() < tm
+            assert c[:, 1].min() >= 0 and c[:, 1].max() < tn
+            assert c[:, 2].min() >= 0 and c[:, 2].max() < sp
+            lin = (c[:, 2] * tm + c[:, 0]) * tn + c[:, 1]
+            assert np.all(np.bincount(lin, minlength=W) == 1), (W, tm, tn, sp)
+
+
+def test_tile_map_agrees_with_the_single_workgroup_mirror(dgp):
+    for tm, tn, sp, remap, gm in ((7, 5, 3, 1, 4), (16, 16, 1, 1, 8), (3, 9, 2, 0, 1), (9, 33, 1, 1, 4)):
+        c = dgp.tile_map(tm, tn, sp, remap, gm)
+        for w in range(tm * tn * sp):
+            assert tuple(c[w]) == dgp.tile_of_workgroup(w, tm, tn, sp, remap, gm)
+
+
+def test_tile_map_rejects_short_output(dgp, L):
+    import numpy as np
+    out = np.zeros(3 * 11, dtype=np.int64)
+    assert L.dgp_tile_map(3, 4, 1, 1, 8, out.ctypes.data, out.size) == 2        # DGP_ERR_SHAPE
+    assert L.dgp_tile_map(3, 4, 1, 1, 8, None, 36) == 1                         # DGP_ERR_NULL
+    assert L.dgp_tile_map(3, 4, 1, 2, 8, out.ctypes.data, out.size) == 2        # remap flag not 0/1
 
 
 def test_tile_map_remap_groups_xcd_neighbours(dgp):
