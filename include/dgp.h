@@ -89,7 +89,9 @@ typedef enum dgp_scale_mode {
  *                    16x64, 16x32 streaming, 16x16 K-split and 16x8 K-split
  *                    over half a strip (two workgroups per 16-column strip)
  *                    for every mode)
- *   tile_k         : K bytes staged per main-loop step (128 or 256)
+ *   tile_k         : tiled kernels: K bytes staged per main-loop step (128,
+ *                    the k-tile of every compiled tiled kernel); ignored by
+ *                    the 16-row kernels
  *   xcd_remap      : 1 = map workgroup ids so neighbouring tiles share an XCD's
  *                    L2 (output is bit-identical either way), 0 = plain raster
  *   group_m        : tile rows per raster group when xcd_remap = 1 (>= 1)
