@@ -215,11 +215,9 @@ gemm_stream_kernel(const GemmArgs p, int panel)
         }
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DEPTH * SPW * kStepCh) : "memory");
 
-        for (int st0 = 0; st0 < nsteps; st0 += DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int st = st0 + d;
-                if (st < nsteps) {
+        // One MFMA step: consume ring slot d (step st).
+        auto consume = [&](int d, int st) {
+                {
                     const Frag a = lds_frag<DT>(lds_a + (st * kStepCh) * 1024 + lane * 16);
 #pragma unroll
                     for (int sp = 0; sp < SPW; ++sp) {
@@ -254,8 +252,26 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                         }
                     }
                 }
-                const int nx = st + DEPTH < nsteps ? st + DEPTH : nsteps - 1;
-                load_step(d, nx, pk);
+        };
+        // Main part: every load the ring issues is a real step.  Tail (the
+        // last 2*DEPTH-1 steps or fewer): loads only for steps that exist,
+        // so no wave ends waiting on repeats of its last step.
+        int st0 = 0;
+        for (; st0 + 2 * DEPTH <= nsteps; st0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                consume(d, st0 + d);
+                load_step(d, st0 + d + DEPTH, pk);
+            }
+        }
+        for (; st0 < nsteps; st0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int st = st0 + d;
+                if (st < nsteps)
+                    consume(d, st);
+                if (st + DEPTH < nsteps)
+                    load_step(d, st + DEPTH, pk);
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -351,12 +367,12 @@ gemm_ksplit_kernel(const GemmArgs p)
             breg[d][cc] = load16<kAuxNonTemporal>(rB, b_voff + k * 16u + cc * 1024u);
         }
     };
-    // Clamp target of the ring: the slice's last step, or for an empty slice
-    // (nsteps < NW) the split's last step -- loaded, never used.
-    const int last = (s1 > s0 ? s1 : nsteps) - 1;
+    // The ring loads only steps of this wave's slice (an empty slice, when
+    // nsteps < NW, loads nothing), so no wave waits on loads it never uses.
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-        load_step(d, s0 + d < s1 ? s0 + d : last);
+        if (s0 + d < s1)
+            load_step(d, s0 + d);
     for (int st0 = s0; st0 < s1; st0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
@@ -389,7 +405,8 @@ gemm_ksplit_kernel(const GemmArgs p)
                 } else {
                     acc = mfma_op(b, a, acc);
                 }
-                load_step(d, st + DEPTH < s1 ? st + DEPTH : last);
+                if (st + DEPTH < s1)
+                    load_step(d, st + DEPTH);
             }
         }
     }
