@@ -141,25 +141,37 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     // Decode-sized M streams the weight through the 16-row tiles.  Larger M
     // takes the tiled kernels, every scale mode included.
     if (M <= 32) {
-        // Narrow weights: when the 64-column streaming tile would give fewer
-        // than 128 workgroups, one strip per workgroup with K split over its
-        // waves spreads the stream wider (measured faster up to that point).
-        // A single bf16 row also streams faster through the K-split tile at
-        // any N: its 8 waves per workgroup keep more of the weight in flight,
-        // and re-reading one A row per strip costs little.
+        // Rules from cold-cache sweeps of the four 16-row tiles at K = 7168
+        // (every mode, M = 1 and 16, N 2048-16384, split 1-8).
+        const int64_t ns = N * split_k;   // strips x splits, in columns
+        const bool fp8t = dtype == DGP_FP8_E4M3 && scale == DGP_SCALE_TENSOR;
+        const auto tile = [&](int tn) { return find_spec(Query{kStream, dtype, scale, out, 16, tn}); };
         // Fewer strips x splits than CUs (256): half a strip per workgroup
-        // doubles the workgroups with no second pass (measured equal at M = 1
-        // and 2-10 % faster at M = 16, N = 2048; at 256 strips and more, the
-        // whole strip is faster).
-        if (N * split_k < 256 * 16)
-            return find_spec(Query{kStream, dtype, scale, out, 16, 8});
-        if (N * split_k < 128 * 64 || (dtype == DGP_BF16 && M == 1 && split_k == 1))
-            return find_spec(Query{kStream, dtype, scale, out, 16, 16});
-        // Up to one 64-column workgroup per CU (256): the 32-column tile's
-        // twice as many workgroups stream faster (measured 3-15 %).
-        if (N * split_k < 256 * 64)
-            return find_spec(Query{kStream, dtype, scale, out, 16, 32});
-        return find_spec(Query{kStream, dtype, scale, out, 16, 64});
+        // doubles the workgroups with no second pass.
+        if (ns < 256 * 16)
+            return tile(8);
+        if (M == 1) {
+            // A single row: one strip per workgroup with K split over its 8
+            // waves keeps the most of the weight in flight up to 1024
+            // strips x splits (10-36 % ahead of the streaming tiles), and
+            // at any width for fp8 per-tensor and bf16 without split-K; the
+            // scaled modes' streaming tile stages their scales once per
+            // workgroup and leads from there.
+            if (ns < 1024 * 16 || (split_k == 1 && (fp8t || dtype == DGP_BF16)))
+                return tile(16);
+            return tile(64);
+        }
+        // Up to 512 strips x splits: K split over the waves of one strip.
+        if (ns < 128 * 64)
+            return tile(16);
+        // Up to 1024: the K-split tile for fp8 per-tensor and mxfp8 (and
+        // blockscale at N <= 2048); the 16x32 streaming tile, with twice
+        // the workgroups of the 64-column one, for bf16, mxfp4 and wider
+        // blockscale weights.
+        if (ns < 256 * 64)
+            return (fp8t || scale == DGP_SCALE_MX128 || (scale == DGP_SCALE_BLOCK128 && N <= 2048)) ? tile(16)
+                                                                                                  : tile(32);
+        return tile(64);
     }
     const KernelSpec *k = nullptr;
     if (M >= 1024 && N >= 1024) {

@@ -293,9 +293,15 @@ def test_default_selection(dgp):
         assert dgp.kernels()[dgp.select_kernel(16, 1024, 7168, dt, sm, 2)][0].tile_n == 8
         assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dt, sm, 1)][0].tile_n == 16
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
-        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == 32
-        assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == 32
+        # 512-1023 strips x splits: K-split for fp8 per-tensor, 16x32 streaming for bf16
+        wide = 16 if dt == dgp.FP8_E4M3 else 32
+        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == wide
+        assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == wide
         assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 8)][0].tile_n == 64
+        # a single row: K-split up to 1024 strips x splits and at any width without split-K
+        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 4)][0].tile_n == 16
+        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm, 1)][0].tile_n == 16
+        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm, 2)][0].tile_n == 64
     # blockscale, mxfp8 and mxfp4: the tiled kernels above decode-sized M,
     # the streaming tiles at it
     for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
@@ -305,10 +311,21 @@ def test_default_selection(dgp):
         i = dgp.select_kernel(300, 1024, 7168, dt, sm, 2)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][3]) == (128, True)
         assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dt, sm)][0].tile_m == 16
-    # a single bf16 row: the K-split tile at any N; fp8 keeps the 64-column tile
+    # a single row at N = 16384: the K-split tile for bf16 and fp8 per-tensor,
+    # the 64-column streaming tile for the scaled modes and for two rows
     assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
     assert dgp.kernels()[dgp.select_kernel(2, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 64
-    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.FP8_E4M3, dgp.SCALE_TENSOR)][0].tile_n == 64
+    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.FP8_E4M3, dgp.SCALE_TENSOR)][0].tile_n == 16
+    for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
+                   (dgp.FP4_E2M1, dgp.SCALE_MX32)):
+        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm)][0].tile_n == 64
+        assert dgp.kernels()[dgp.select_kernel(1, 8192, 7168, dt, sm)][0].tile_n == 16
+    # 512-1023 strips x splits at M = 16: mxfp8 and narrow blockscale K-split,
+    # wider blockscale and mxfp4 the 16x32 streaming tile
+    assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_MX128, 2)][0].tile_n == 16
+    assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128, 4)][0].tile_n == 16
+    assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128, 2)][0].tile_n == 32
+    assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 32
     # mxfp4 follows the same rule as the other decode modes
     assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 64
     assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 8
