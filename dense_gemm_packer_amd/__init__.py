@@ -281,7 +281,8 @@ def describe_kernel(index: int) -> str:
     """One-line description of compiled kernel `index`."""
     cfg, dt, sm, so = kernels()[index]
     dts = {BF16: "bf16", FP8_E4M3: "fp8", FP4_E2M1: "fp4"}[dt]
-    if cfg.tile_m == 16 and cfg.tile_n in (8, 16):
+    # the K-split tiles run 8 waves per workgroup, the streaming tiles 2 or 4
+    if cfg.tile_m == 16 and (cfg.tile_n in (8, 16) or cfg.waves_m == 8):
         half = ", half a strip" if cfg.tile_n == 8 else ""
         return (f"gemm_ksplit_kernel<{dts}, 16x{cfg.tile_n} tile{half}, K split over {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")

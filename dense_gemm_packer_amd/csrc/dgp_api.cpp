@@ -141,37 +141,51 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     // Decode-sized M streams the weight through the 16-row tiles.  Larger M
     // takes the tiled kernels, every scale mode included.
     if (M <= 32) {
-        // Rules from cold-cache sweeps of the four 16-row tiles at K = 7168
-        // (every mode, M = 1 and 16, N 2048-16384, split 1-8).
-        const int64_t ns = N * split_k;   // strips x splits, in columns
+        // Rules from cold-cache sweeps of the 16-row tiles at K = 7168 (every
+        // mode; M = 1, 4 and 16; N 2048-16384; split 1-8).  u = strips x
+        // splits; ks(t) = the K-split tile t columns wide (8 waves), st(t) =
+        // the streaming tile.
+        const int64_t u = N / 16 * split_k;
         const bool fp8t = dtype == DGP_FP8_E4M3 && scale == DGP_SCALE_TENSOR;
-        const auto tile = [&](int tn) { return find_spec(Query{kStream, dtype, scale, out, 16, tn}); };
-        // Fewer strips x splits than CUs (256): half a strip per workgroup
-        // doubles the workgroups with no second pass.
-        if (ns < 256 * 16)
-            return tile(8);
-        if (M == 1) {
-            // A single row: one strip per workgroup with K split over its 8
-            // waves keeps the most of the weight in flight up to 1024
-            // strips x splits (10-36 % ahead of the streaming tiles), and
-            // at any width for fp8 per-tensor and bf16 without split-K; the
-            // scaled modes' streaming tile stages their scales once per
-            // workgroup and leads from there.
-            if (ns < 1024 * 16 || (split_k == 1 && (fp8t || dtype == DGP_BF16)))
-                return tile(16);
-            return tile(64);
+        const bool mx4 = scale == DGP_SCALE_MX32;
+        const auto ks = [&](int tn) {
+            Query q{kStream, dtype, scale, out, 16, tn};
+            q.wm = 8;
+            return find_spec(q);
+        };
+        const auto st = [&](int tn) {
+            Query q{kStream, dtype, scale, out, 16, tn};
+            q.wm = tn == 64 ? 4 : 2;
+            return find_spec(q);
+        };
+        // Fewer strips x splits than CUs: half a strip per workgroup doubles
+        // the workgroups with no second pass.
+        if (u < 256)
+            return ks(8);
+        if (M <= 4) {
+            // A few rows: A is cheap to re-read, so one strip per workgroup
+            // with K over 8 waves keeps the most of the weight in flight
+            // (10-36 % ahead of the streaming tiles); blockscale and mxfp8
+            // gain from 2 strips from 512 on; mxfp4's streaming tile, which
+            // stages its scales once per workgroup, leads from 1024.
+            if (mx4)
+                return u < 1024 ? ks(16) : st(64);
+            if (fp8t || dtype == DGP_BF16)
+                return (u < 1024 || split_k == 1) ? ks(16) : st(64);
+            if (u < 512)
+                return ks(16);
+            return (scale == DGP_SCALE_MX128 && u >= 1024) ? ks(64) : ks(32);
         }
-        // Up to 512 strips x splits: K split over the waves of one strip.
-        if (ns < 128 * 64)
-            return tile(16);
-        // Up to 1024: the K-split tile for fp8 per-tensor and mxfp8 (and
-        // blockscale at N <= 2048); the 16x32 streaming tile, with twice
-        // the workgroups of the 64-column one, for bf16, mxfp4 and wider
-        // blockscale weights.
-        if (ns < 256 * 64)
-            return (fp8t || scale == DGP_SCALE_MX128 || (scale == DGP_SCALE_BLOCK128 && N <= 2048)) ? tile(16)
-                                                                                                  : tile(32);
-        return tile(64);
+        // More rows: A is read once per workgroup, so wider K-split tiles
+        // (2 or 4 strips sharing each A fragment) lead from 512 strips x
+        // splits (6-18 %), except for mxfp4 past N = 2048.
+        if (u < 512)
+            return ks(16);
+        if (mx4)
+            return u < 1024 ? (N <= 2048 ? ks(32) : st(32)) : st(64);
+        if (u < 1024 || fp8t)
+            return ks(32);
+        return ks(64);
     }
     const KernelSpec *k = nullptr;
     if (M >= 1024 && N >= 1024) {

@@ -9,8 +9,8 @@
 //    in-flight 16-byte loads.  It also carries the FP8 blockscale mode for any
 //    M and the microscaling modes (mxfp8, mxfp4), whose E8M0 scales are staged
 //    in LDS per panel.
-// gemm_ksplit_kernel -- decode-sized M over few columns: one strip per
-//    workgroup, its K range split over the waves, partials added in LDS.
+// gemm_ksplit_kernel -- decode-sized M: a workgroup owns half a strip or 1,
+//    2 or 4 strips, its K range split over 8 waves, partials added in LDS.
 
 #include "gemm_common.h"
 
@@ -288,41 +288,48 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     }
 }
 
-// gemm_ksplit_kernel -- decode-sized M over few columns.  A workgroup owns a
-// 16-row x 16-column tile of C (one strip of Bs) and divides its K range into
-// NW contiguous slices of whole MFMA steps, one per wave, so a narrow weight
-// still spreads over many waves without a second pass: N = 2048 gives 128
-// workgroups of NW waves where the 64-column streaming tile gives 32.  Each
-// wave streams its slice of A and B straight into registers through a ring
-// of DEPTH MFMA steps of in-flight loads (A rows >= M and the B strip past N
-// load as zero), then the NW partial tiles are added in LDS in wave order --
-// a fixed order, so results are reproducible -- and wave 0 runs the epilogue.
-// Blockscale: one fp8 MFMA step is exactly one 128-wide K block, scaled as in
-// gemm_stream_kernel with the scales read straight from global memory.
-// TN = 8 (half strips): two workgroups share a strip, each owning 8 of its 16
-// columns, so a narrow weight fills twice as many CUs with no second pass.
-// Lanes whose B row (lane % 16) belongs to the other half load at an offset
-// past the strip's buffer range, which returns zeros without a memory
-// access: each workgroup reads only its half of every 1 KiB block (8 rows x
-// 4 contiguous 128-byte pieces), and its MFMAs compute zeros for the other
-// half's columns, which it does not store.
+// gemm_ksplit_kernel -- decode-sized M.  A workgroup owns a 16-row tile of C
+// TN columns wide -- one strip of Bs (TN = 16), SPW = TN/16 strips (TN = 32,
+// 64), or half a strip (TN = 8) -- and divides its K range into NW
+// contiguous slices of whole MFMA steps, one per wave, so a weight spreads
+// over many waves without a second pass: N = 2048 gives 128 workgroups of NW
+// waves with whole strips where the 64-column streaming tile gives 32.  Each
+// wave streams its slice of A and of its strips of B straight into
+// registers through a ring of DEPTH MFMA steps of in-flight loads (A rows
+// >= M and strips past N load as zero); each A fragment serves all SPW
+// strips, so wider tiles read A fewer times.  Then the NW partial tiles are
+// added in LDS in wave order -- a fixed order, so results are reproducible
+// and the same for every TN -- and wave sp runs the epilogue of strip sp.
+// Blockscale: one fp8 MFMA step is exactly one 128-wide K block, scaled as
+// in gemm_stream_kernel with the scales read straight from global memory
+// (the SPW strips of a tile lie in one 128-column block).
+// TN = 8 (half strips): two workgroups share a strip, each owning 8 of its
+// 16 columns, so a narrow weight fills twice as many CUs with no second
+// pass.  Lanes whose B row (lane % 16) belongs to the other half load at an
+// offset past the strip's buffer range, which returns zeros without a
+// memory access: each workgroup reads only its half of every 1 KiB block
+// (8 rows x 4 contiguous 128-byte pieces), and its MFMAs compute zeros for
+// the other half's columns, which it does not store.
 template <int DT, int NW, int DEPTH, int SCALE, int OUT, int TN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 gemm_ksplit_kernel(const GemmArgs p)
 {
-    static_assert(TN == 16 || TN == 8, "a whole strip or half of one");
+    static_assert(TN == 8 || TN == 16 || TN == 32 || TN == 64, "half a strip, or 1, 2 or 4 strips");
+    constexpr bool kHalf = TN == 8;
+    constexpr int SPW = kHalf ? 1 : TN / 16;
+    static_assert(SPW <= NW, "one wave per strip in the epilogue");
     using Frag = typename Op<DT>::Frag;
     constexpr int kStepCh = Op<DT>::kBlocks;
     constexpr int kStepBytes = 64 * kStepCh;
-    __shared__ f32x4 red[NW][64];
+    __shared__ f32x4 red[NW][SPW][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
     const int m0 = (int)tc.tm * 16;
-    const int strip = TN == 16 ? (int)tc.tn : (int)tc.tn >> 1;
-    const int half = TN == 16 ? 0 : (int)tc.tn & 1;
+    const int strip0 = kHalf ? (int)tc.tn >> 1 : (int)tc.tn * SPW;
+    const int half = kHalf ? (int)tc.tn & 1 : 0;
     const int split = (int)tc.s;
     const uint32_t Kb = (uint32_t)p.Kb;
     const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
@@ -340,32 +347,45 @@ gemm_ksplit_kernel(const GemmArgs p)
     // Half strips: the resource covers exactly the strip (16 rows, at most
     // 128 MiB), and the other half's lanes start at 2^31, so every offset
     // they form stays past the range and below 2^32.
-    const auto rB = TN == 16
-        ? make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip) * 16 * Kb))
-        : make_rsrc(p.Bs + (int64_t)strip * 16 * Kb, strip < p.N / 16 ? 16u * Kb : 0u);
-    const bool row_on = TN == 16 || ((lane & 15) >> 3) == half;
-    const uint32_t b_voff = (uint32_t)lane * 16u + (row_on ? 0u : 0x80000000u);
+    const auto rB = kHalf
+        ? make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb, strip0 < p.N / 16 ? 16u * Kb : 0u)
+        : make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
+    const bool row_on = !kHalf || ((lane & 15) >> 3) == half;
+    uint32_t b_voff[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        b_voff[sp] = (uint32_t)sp * 16u * Kb + (uint32_t)lane * 16u + (row_on ? 0u : 0x80000000u);
     const int m = m0 + (lane & 15);
     const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
-    const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip * 16 / 128) * kblocks_row : nullptr;
-    // mxfp8: this lane's A row and B column E8M0 rows (A rows >= M: none).
+    const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip0 * 16 / 128) * kblocks_row : nullptr;
+    static_assert(SCALE != kScaleBlock || 128 % (16 * SPW) == 0, "a tile's strips in one 128-column block");
+    // mxfp8 / mxfp4: this lane's A row and its B column in each strip (A rows >= M: none).
     constexpr bool kMx = SCALE == kScaleMx || SCALE == kScaleMx32;
     const uint8_t *xa_row = (kMx && m < p.M) ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row
                                              : nullptr;
-    const uint8_t *xb_row = kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)(strip * 16 + (lane & 15)) * kblocks_row
-                                : nullptr;
+    const uint8_t *xb_row[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        xb_row[sp] = kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)((strip0 + sp) * 16 + (lane & 15)) * kblocks_row
+                         : nullptr;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    i32x4 areg[DEPTH][kStepCh], breg[DEPTH][kStepCh];
+    f32x4 acc[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 areg[DEPTH][kStepCh], breg[DEPTH][SPW][kStepCh];
     // Step st of the split: K bytes kbase + st*kStepBytes; A chunk cc of it is
-    // one 16-row x 64-byte operand read, B chunk cc one 1 KiB block of the strip.
+    // one 16-row x 64-byte operand read, B chunk cc of strip sp one 1 KiB block.
     auto load_step = [&](int d, int st) {
         const uint32_t k = kbase + (uint32_t)st * kStepBytes;
 #pragma unroll
-        for (int cc = 0; cc < kStepCh; ++cc) {
+        for (int cc = 0; cc < kStepCh; ++cc)
             areg[d][cc] = load16<kAuxNone>(rA, a_voff + k + cc * 64u);
-            breg[d][cc] = load16<kAuxNonTemporal>(rB, b_voff + k * 16u + cc * 1024u);
-        }
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int cc = 0; cc < kStepCh; ++cc)
+                breg[d][sp][cc] = load16<kAuxNonTemporal>(rB, b_voff[sp] + k * 16u + cc * 1024u);
     };
     // The ring loads only steps of this wave's slice (an empty slice, when
     // nsteps < NW, loads nothing), so no wave waits on loads it never uses.
@@ -378,45 +398,60 @@ gemm_ksplit_kernel(const GemmArgs p)
         for (int d = 0; d < DEPTH; ++d) {
             const int st = st0 + d;
             if (st < s1) {
-                Frag a, b;
-                if constexpr (kStepCh == 1) {
+                Frag a;
+                if constexpr (kStepCh == 1)
                     a = areg[d][0];
-                    b = breg[d][0];
-                } else {
+                else
                     a = cat(areg[d][0], areg[d][1]);
-                    b = cat(breg[d][0], breg[d][1]);
-                }
+                [[maybe_unused]] float sc = 0.f;
+                [[maybe_unused]] int kb = 0, ea = 127;
                 if constexpr (SCALE == kScaleBlock) {
-                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
-                    const float sa = sa_row ? sa_row[kb] : 0.f;
-                    const float sc = __fmul_rn(sa, sb_row[kb]);
-                    const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
-                    acc.x = __fadd_rn(acc.x, __fmul_rn(part.x, sc));
-                    acc.y = __fadd_rn(acc.y, __fmul_rn(part.y, sc));
-                    acc.z = __fadd_rn(acc.z, __fmul_rn(part.z, sc));
-                    acc.w = __fadd_rn(acc.w, __fmul_rn(part.w, sc));
+                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
+                    sc = __fmul_rn(sa_row ? sa_row[kb] : 0.f, sb_row[kb]);
                 } else if constexpr (SCALE == kScaleMx) {
-                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
-                    acc = mfma_mx(b, a, acc, xb_row[kb], xa_row ? xa_row[kb] : 127);
+                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
+                    ea = xa_row ? xa_row[kb] : 127;
                 } else if constexpr (SCALE == kScaleMx32) {
                     // this lane's 16 bytes are one 32-element block: 16 bytes per block
-                    const int kb = (int)((kbase + (uint32_t)st * kStepBytes) / 16u) + (lane >> 4);
-                    acc = mfma_mx4(b, a, acc, xb_row[kb], xa_row ? xa_row[kb] : 127);
-                } else {
-                    acc = mfma_op(b, a, acc);
+                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 16u) + (lane >> 4);
+                    ea = xa_row ? xa_row[kb] : 127;
+                }
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    Frag b;
+                    if constexpr (kStepCh == 1)
+                        b = breg[d][sp][0];
+                    else
+                        b = cat(breg[d][sp][0], breg[d][sp][1]);
+                    if constexpr (SCALE == kScaleBlock) {
+                        const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
+                        acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, sc));
+                        acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, sc));
+                        acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, sc));
+                        acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, sc));
+                    } else if constexpr (SCALE == kScaleMx) {
+                        acc[sp] = mfma_mx(b, a, acc[sp], xb_row[sp][kb], ea);
+                    } else if constexpr (SCALE == kScaleMx32) {
+                        acc[sp] = mfma_mx4(b, a, acc[sp], xb_row[sp][kb], ea);
+                    } else {
+                        acc[sp] = mfma_op(b, a, acc[sp]);
+                    }
                 }
                 if (st + DEPTH < s1)
                     load_step(d, st + DEPTH);
             }
         }
     }
-    red[wave][lane] = acc;
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+        red[wave][sp][lane] = acc[sp];
     __syncthreads();
-    if (wave == 0) {
-        f32x4 v = red[0][lane];
+    if (wave < SPW) {
+        const int sp = wave;
+        f32x4 v = red[0][sp][lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) {
-            const f32x4 u = red[w][lane];
+            const f32x4 u = red[w][sp][lane];
             v.x = __fadd_rn(v.x, u.x);
             v.y = __fadd_rn(v.y, u.y);
             v.z = __fadd_rn(v.z, u.z);
@@ -425,8 +460,8 @@ gemm_ksplit_kernel(const GemmArgs p)
         if constexpr (SCALE == kScaleTensor)
             v = v * (static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0]);
         // lane l holds columns 4*(l/16) .. +3 of the strip
-        if (TN == 16 || ((lane >> 4) >> 1) == half)
-            store_tile<OUT>(p, split, m, strip * 16 + (lane >> 4) * 4, v);
+        if (!kHalf || ((lane >> 4) >> 1) == half)
+            store_tile<OUT>(p, split, m, (strip0 + sp) * 16 + (lane >> 4) * 4, v);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -470,7 +505,8 @@ void launch_ksplit(const GemmArgs &a, dim3 grid, hipStream_t s)
 }
 
 #define DGP_KSPLIT(DT, NW, DEPTH, SC, OUT, TN)                                                \
-    {kStream, DT, SC, OUT, 16, TN, 0, NW, 1, DEPTH, 0, 0, DEPTH, 0, &launch_ksplit<DT, NW, DEPTH, SC, OUT, TN>}
+    {kStream, DT, SC, OUT, 16, TN, 0, NW, (TN >= 16 ? TN / 16 : 1), DEPTH, 0, 0, DEPTH, 0,          \
+     &launch_ksplit<DT, NW, DEPTH, SC, OUT, TN>}
 #define DGP_KSPLIT_BOTH_OUT(DT, NW, DEPTH, SC, TN)                                            \
     DGP_KSPLIT(DT, NW, DEPTH, SC, kOutBf16, TN), DGP_KSPLIT(DT, NW, DEPTH, SC, kOutPartial, TN)
 #define DGP_STREAM(DT, NW, SPW, DEPTH, SC, OUT)                                               \
@@ -506,6 +542,18 @@ static const KernelSpec kStreamKernels[] = {
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 8),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 8),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 8),
+    // 2 and 4 strips per workgroup (16 x 32, 16 x 64 tiles; 8 waves, which
+    // tells them apart from the streaming tiles of the same size)
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone, 32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor, 32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 32),
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 8, 4, kScaleNone, 64),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleTensor, 64),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 64),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 64),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 64),
 };
 
 const KernelSpec *stream_kernels(int *count)

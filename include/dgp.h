@@ -86,9 +86,10 @@ typedef enum dgp_scale_mode {
  *   tile_m, tile_n : output tile of one workgroup (must name a compiled tile:
  *                    256x256, 128x256, 128x128 for bf16 and per-tensor fp8;
  *                    256x256 and 128x128 for fp8 blockscale, mxfp8 and mxfp4;
- *                    16x64, 16x32 streaming, 16x16 K-split and 16x8 K-split
- *                    over half a strip (two workgroups per 16-column strip)
- *                    for every mode)
+ *                    16x64 and 16x32 streaming (4 and 2 waves); K-split
+ *                    (8 waves) over 16x8 -- half a strip, two workgroups
+ *                    per 16-column strip -- 16x16, 16x32 and 16x64; every
+ *                    16-row tile for every mode)
  *   tile_k         : tiled kernels: K bytes staged per main-loop step (128,
  *                    the k-tile of every compiled tiled kernel); ignored by
  *                    the 16-row kernels
@@ -106,9 +107,10 @@ typedef enum dgp_scale_mode {
  *   waves_m        : tiled kernels: waves along M inside the workgroup; the
  *                    16-row streaming kernel (tile_m = 16, tile_n 32 or 64):
  *                    waves per workgroup, each owning tile_n / (16 * waves)
- *                    strips; the K-split kernel (16x16, 16x8): waves sharing
- *                    the strip's K range (0 = any compiled layout for this
- *                    tile).
+ *                    strips; the K-split kernel (8 waves): waves sharing
+ *                    the tile's K range, which also tells the 16x32 and
+ *                    16x64 K-split tiles from the streaming ones (0 = the
+ *                    first compiled kernel for this tile: the streaming one).
  *   prefetch       : tiled kernels: k-tiles loaded ahead of the one being
  *                    multiplied; streaming kernel: MFMA steps of loads in
  *                    flight per wave (0 = any compiled depth for this tile).

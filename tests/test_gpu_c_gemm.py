@@ -148,16 +148,17 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
-@pytest.mark.parametrize("tile_n", [64, 32, 16, 8])
+@pytest.mark.parametrize("tile_n,waves", [(64, 0), (32, 0), (16, 0), (8, 0), (32, 8), (64, 8)])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128"), ("fp4", "mx32")])
 @pytest.mark.parametrize("M", [1, 16, 20])
 @pytest.mark.parametrize("split_k", [1, 2, 4, 8])
-def test_stream_splitk(dtype, mode, M, split_k, tile_n):
+def test_stream_splitk(dtype, mode, M, split_k, tile_n, waves):
     """Decode kernels: the 16x64 and 16x32 streaming tiles, the 16x16 K-split
-    tile and its half-strip form (16x8)."""
+    tile, its half-strip form (16x8) and its 2- and 4-strip forms (16x32,
+    16x64 with 8 waves)."""
     N, K = 384, 2048
-    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0, waves)
     A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 3)
     got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split_k, config=cfg)
     _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
@@ -168,15 +169,15 @@ def test_stream_splitk(dtype, mode, M, split_k, tile_n):
     assert_close(got, c32)
 
 
-@pytest.mark.parametrize("tile_n", [16, 8])
+@pytest.mark.parametrize("tile_n", [16, 8, 32, 64])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128")])
 def test_ksplit_uneven_and_empty_slices(dtype, mode, tile_n):
-    """K-split kernel (whole and half strips): step counts not divisible by
-    the 8 waves and fewer steps than waves (some waves own no K), with splits.
-    (bf16 steps are 64 bytes and K rows must be whole 128 bytes, so its
-    counts are even.)"""
-    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0)
+    """K-split kernel (half, one, two and four strips): step counts not
+    divisible by the 8 waves and fewer steps than waves (some waves own no
+    K), with splits.  (bf16 steps are 64 bytes and K rows must be whole 128
+    bytes, so its counts are even.)"""
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0, 8)
     step = 32 if dtype == "bf16" else 128    # K elements per MFMA step
     cases = (((18, 1), (26, 1), (2, 1), (6, 1), (36, 2), (20, 2)) if dtype == "bf16" else
              ((9, 1), (13, 1), (1, 1), (3, 1), (5, 1), (18, 2), (10, 2)))

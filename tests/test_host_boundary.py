@@ -280,30 +280,21 @@ def test_every_kernel_is_selected_by_its_reported_config(dgp):
         assert dgp.describe_kernel(i)
 
 
+def _pick(dgp, M, N, split, dt, sm):
+    """The built-in choice as 'k<tile_n>' (K-split tiles, 8 waves) or 's<tile_n>' (streaming)."""
+    c = dgp.kernels()[dgp.select_kernel(M, N, 7168, dt, sm, split)][0]
+    if c.tile_m != 16:
+        return f"t{c.tile_m}x{c.tile_n}"
+    return ("k" if c.waves_m == 8 else "s") + str(c.tile_n)
+
+
 def test_default_selection(dgp):
-    # Headline shapes take a 256x256 tile, decode-sized M and mxfp4 the
-    # 16-row streaming kernels; empty calls launch nothing.
+    # Headline shapes take a 256x256 tile; empty calls launch nothing.
     for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
         cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
         assert (cfg.tile_m, cfg.tile_n) == (256, 256)
-        assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dt, sm, 4)][0].tile_n == 64
-        # narrow weights: one strip per workgroup, K split over its waves;
-        # fewer strips x splits than CUs: half a strip per workgroup
-        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 1)][0].tile_n == 8
-        assert dgp.kernels()[dgp.select_kernel(16, 1024, 7168, dt, sm, 2)][0].tile_n == 8
-        assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dt, sm, 1)][0].tile_n == 16
-        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 2)][0].tile_n == 16
-        # 512-1023 strips x splits: K-split for fp8 per-tensor, 16x32 streaming for bf16
-        wide = 16 if dt == dgp.FP8_E4M3 else 32
-        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 4)][0].tile_n == wide
-        assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dt, sm, 1)][0].tile_n == wide
-        assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dt, sm, 8)][0].tile_n == 64
-        # a single row: K-split up to 1024 strips x splits and at any width without split-K
-        assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dt, sm, 4)][0].tile_n == 16
-        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm, 1)][0].tile_n == 16
-        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm, 2)][0].tile_n == 64
     # blockscale, mxfp8 and mxfp4: the tiled kernels above decode-sized M,
-    # the streaming tiles at it
+    # the 16-row tiles at it
     for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
                    (dgp.FP4_E2M1, dgp.SCALE_MX32)):
         i = dgp.select_kernel(4096, 4096, 7168, dt, sm)
@@ -311,25 +302,28 @@ def test_default_selection(dgp):
         i = dgp.select_kernel(300, 1024, 7168, dt, sm, 2)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][3]) == (128, True)
         assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dt, sm)][0].tile_m == 16
-    # a single row at N = 16384: the K-split tile for bf16 and fp8 per-tensor,
-    # the 64-column streaming tile for the scaled modes and for two rows
-    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 16
-    assert dgp.kernels()[dgp.select_kernel(2, 16384, 7168, dgp.BF16, dgp.SCALE_NONE)][0].tile_n == 64
-    assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dgp.FP8_E4M3, dgp.SCALE_TENSOR)][0].tile_n == 16
-    for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
-                   (dgp.FP4_E2M1, dgp.SCALE_MX32)):
-        assert dgp.kernels()[dgp.select_kernel(1, 16384, 7168, dt, sm)][0].tile_n == 64
-        assert dgp.kernels()[dgp.select_kernel(1, 8192, 7168, dt, sm)][0].tile_n == 16
-    # 512-1023 strips x splits at M = 16: mxfp8 and narrow blockscale K-split,
-    # wider blockscale and mxfp4 the 16x32 streaming tile
-    assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_MX128, 2)][0].tile_n == 16
-    assert dgp.kernels()[dgp.select_kernel(16, 2048, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128, 4)][0].tile_n == 16
-    assert dgp.kernels()[dgp.select_kernel(16, 4096, 7168, dgp.FP8_E4M3, dgp.SCALE_BLOCK128, 2)][0].tile_n == 32
-    assert dgp.kernels()[dgp.select_kernel(16, 8192, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 32
-    # mxfp4 follows the same rule as the other decode modes
-    assert dgp.kernels()[dgp.select_kernel(16, 16384, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 64
-    assert dgp.kernels()[dgp.select_kernel(1, 2048, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 8
-    assert dgp.kernels()[dgp.select_kernel(1, 4096, 7168, dgp.FP4_E2M1, dgp.SCALE_MX32)][0].tile_n == 16
+    # Decode-sized M, K = 7168: the per-shape table (M/N/split -> tile), from
+    # cold sweeps of every 16-row tile.
+    want = {
+        "tensor": "16/16384/1:k32 16/16384/2:k32 16/8192/1:k32 16/4096/1:k16 16/4096/4:k32 16/2048/1:k8 "
+                  "16/2048/2:k16 16/2048/8:k32 4/16384/1:k16 1/16384/1:k16 1/8192/1:k16 1/2048/1:k8 1/16384/2:s64",
+        "bf16": "16/16384/1:k64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/2048/8:k64 4/16384/1:k16 "
+                "1/16384/1:k16 1/16384/2:s64",
+        "mx32": "16/16384/1:s64 16/8192/1:s32 16/4096/2:s32 16/4096/4:s64 16/2048/4:k32 16/2048/2:k16 "
+                "4/16384/1:s64 4/8192/1:k16 1/16384/1:s64 1/2048/1:k8",
+        "block128": "16/16384/1:k64 16/8192/1:k32 16/4096/4:k64 16/2048/4:k32 4/2048/4:k32 1/16384/1:k32 "
+                    "1/8192/1:k32",
+        "mx128": "16/16384/1:k64 16/8192/1:k32 16/2048/8:k64 4/8192/1:k32 1/16384/1:k64 1/8192/1:k32",
+    }
+    modes = {"tensor": (dgp.FP8_E4M3, dgp.SCALE_TENSOR), "bf16": (dgp.BF16, dgp.SCALE_NONE),
+             "mx32": (dgp.FP4_E2M1, dgp.SCALE_MX32), "block128": (dgp.FP8_E4M3, dgp.SCALE_BLOCK128),
+             "mx128": (dgp.FP8_E4M3, dgp.SCALE_MX128)}
+    for mode, table in want.items():
+        dt, sm = modes[mode]
+        for entry in table.split():
+            shape, tile = entry.split(":")
+            M, N, split = (int(x) for x in shape.split("/"))
+            assert _pick(dgp, M, N, split, dt, sm) == tile, (mode, shape)
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
