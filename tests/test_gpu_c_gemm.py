@@ -210,6 +210,28 @@ def test_half_strip_writes_every_column(dtype, mode, M, split_k):
     assert np.array_equal(host_bits(out), c16)
 
 
+@pytest.mark.parametrize("tile_n,waves", [(64, 4), (32, 2), (16, 8), (8, 8), (32, 8), (64, 8)])
+@pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
+                                        ("fp8", "mx128"), ("fp4", "mx32")])
+def test_decode_tiles_ragged_width(dtype, mode, tile_n, waves):
+    """Every 16-row tile on widths that are not a whole number of tiles: the
+    last workgroup owns strips past N (loaded as zero, never stored).  C
+    starts as NaN, so a column left unwritten fails the bit-exact check."""
+    for N, M, split_k in ((400, 20, 1), (336, 5, 2), (144, 1, 1)):
+        if mode == "block128" and N % 128:
+            N = 640 if N > 256 else 128 * (N // 128 + 1)   # blockscale: whole 128-column blocks
+        K = 1024
+        A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 23)
+        a = dev_codes(A, dtype)
+        Bs_dev = dgp.preshuffle_b(dev_codes(B, dtype))
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        dgp.gemm_preshuffle_splitk(a, Bs_dev, split_k, dev_scales(sA, mode), dev_scales(sB, mode), dmode(mode),
+                                   out=out, config=dgp.Config(16, tile_n, 0, 0, 1, 0, 0, waves))
+        torch.cuda.synchronize()
+        _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split_k)
+        assert np.array_equal(host_bits(out), c16), (N, M, split_k)
+
+
 @pytest.mark.parametrize("dtype,mode", [("fp8", "tensor"), ("fp4", "mx32")])
 @pytest.mark.parametrize("split_k", [1, 2])
 def test_stream_multi_panel(dtype, mode, split_k):
