@@ -165,12 +165,9 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         if (M <= 4) {
             // A few rows: A is cheap to re-read, so one strip per workgroup
             // with K over 8 waves keeps the most of the weight in flight
-            // (10-36 % ahead of the streaming tiles); blockscale and mxfp8
-            // gain from 2 strips from 512 on; mxfp4's streaming tile, which
-            // stages its scales once per workgroup, leads from 1024.
-            if (mx4)
-                return u < 1024 ? ks(16) : st(64);
-            if (fp8t || dtype == DGP_BF16)
+            // (5-36 % ahead of the streaming tiles); blockscale and mxfp8
+            // gain from 2 strips from 512 on.
+            if (fp8t || dtype == DGP_BF16 || mx4)
                 return (u < 1024 || split_k == 1) ? ks(16) : st(64);
             if (u < 512)
                 return ks(16);
@@ -178,11 +175,12 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         }
         // More rows: A is read once per workgroup, so wider K-split tiles
         // (2 or 4 strips sharing each A fragment) lead from 512 strips x
-        // splits (6-18 %), except for mxfp4 past N = 2048.
+        // splits (4-22 %); for mxfp4 the streaming tile leads again from
+        // 2048.
         if (u < 512)
             return ks(16);
-        if (mx4)
-            return u < 1024 ? (N <= 2048 ? ks(32) : st(32)) : st(64);
+        if (mx4 && u >= 2048)
+            return st(64);
         if (u < 1024 || fp8t)
             return ks(32);
         return ks(64);

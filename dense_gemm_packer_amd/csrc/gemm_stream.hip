@@ -359,8 +359,8 @@ gemm_ksplit_kernel(const GemmArgs p)
     const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
     const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip0 * 16 / 128) * kblocks_row : nullptr;
     static_assert(SCALE != kScaleBlock || 128 % (16 * SPW) == 0, "a tile's strips in one 128-column block");
-    // mxfp8 / mxfp4: this lane's A row and its B column in each strip (A rows >= M: none).
-    constexpr bool kMx = SCALE == kScaleMx || SCALE == kScaleMx32;
+    // mxfp8: this lane's A row and its B column in each strip (A rows >= M: none).
+    constexpr bool kMx = SCALE == kScaleMx;
     const uint8_t *xa_row = (kMx && m < p.M) ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row
                                              : nullptr;
     const uint8_t *xb_row[SPW];
@@ -368,6 +368,37 @@ gemm_ksplit_kernel(const GemmArgs p)
     for (int sp = 0; sp < SPW; ++sp)
         xb_row[sp] = kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)((strip0 + sp) * 16 + (lane & 15)) * kblocks_row
                          : nullptr;
+
+    // mxfp4: the E8M0 bytes of a group of DEPTH = 4 steps are 16 contiguous
+    // bytes of each row (step st, lane l: byte 4*st + l/16 of the row's
+    // [K/32] scales, from byte kbase/16 on), so one 16-byte load per row and
+    // group replaces a byte load per step; the next group's words are loaded
+    // one group ahead (bytes past the wave's slice are read and unused).  The
+    // load is dword-aligned (rows are whole dwords), and the buffer unit
+    // range-checks each dword of such a load on its own: a group that runs
+    // past the end of the scale array reads zero in the dwords beyond it only.
+    // Rows past M and columns past N read as zero (2^-127, finite), which
+    // only ever scales zero data.
+    constexpr bool kXw = SCALE == kScaleMx32;
+    static_assert(!kXw || (DEPTH == 4 && kStepBytes == 64), "mxfp4 scale words: 4 bytes per step, one 16-byte load per 4 steps");
+    [[maybe_unused]] const auto rXa = make_rsrc(kXw ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblocks_row
+                                                    : nullptr,
+                                                kXw ? clamp_bytes((int64_t)(p.M - m0) * kblocks_row) : 0);
+    [[maybe_unused]] const auto rXb = make_rsrc(kXw ? static_cast<const uint8_t *>(p.sB) + (int64_t)strip0 * 16 * kblocks_row
+                                                    : nullptr,
+                                                kXw ? clamp_bytes((int64_t)(p.N - strip0 * 16) * kblocks_row) : 0);
+    [[maybe_unused]] i32x4 xw[2][1 + SPW];   // [group parity][A row, then each strip's column]
+    [[maybe_unused]] auto load_x = [&](auto setc, int st) {
+        if constexpr (kXw) {
+            constexpr int X = decltype(setc)::value;
+            const uint32_t gb = kbase / 16u + 4u * (uint32_t)st;
+            const uint32_t oa = (uint32_t)(lane & 15) * (uint32_t)kblocks_row + gb;
+            xw[X][0] = load16<kAuxNone>(rXa, oa);
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp)
+                xw[X][1 + sp] = load16<kAuxNone>(rXb, oa + (uint32_t)(sp * 16) * (uint32_t)kblocks_row);
+        }
+    };
 
     f32x4 acc[SPW];
 #pragma unroll
@@ -389,11 +420,18 @@ gemm_ksplit_kernel(const GemmArgs p)
     };
     // The ring loads only steps of this wave's slice (an empty slice, when
     // nsteps < NW, loads nothing), so no wave waits on loads it never uses.
+    // The loop runs two ring groups per iteration so that the parity of the
+    // mxfp4 scale words is a compile-time index.
+    if (s0 < s1)
+        load_x(std::integral_constant<int, 0>{}, s0);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
         if (s0 + d < s1)
             load_step(d, s0 + d);
-    for (int st0 = s0; st0 < s1; st0 += DEPTH) {
+    auto group = [&](auto setc, int st0) {
+        constexpr int X = decltype(setc)::value;
+        if (st0 + DEPTH < s1)
+            load_x(std::integral_constant<int, 1 - X>{}, st0 + DEPTH);
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int st = st0 + d;
@@ -412,9 +450,8 @@ gemm_ksplit_kernel(const GemmArgs p)
                     kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
                     ea = xa_row ? xa_row[kb] : 127;
                 } else if constexpr (SCALE == kScaleMx32) {
-                    // this lane's 16 bytes are one 32-element block: 16 bytes per block
-                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 16u) + (lane >> 4);
-                    ea = xa_row ? xa_row[kb] : 127;
+                    // this lane's 16 bytes are one 32-element block, byte l/16 of the step's word
+                    ea = (int)(((uint32_t)xw[X][0][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
                 }
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
@@ -432,7 +469,8 @@ gemm_ksplit_kernel(const GemmArgs p)
                     } else if constexpr (SCALE == kScaleMx) {
                         acc[sp] = mfma_mx(b, a, acc[sp], xb_row[sp][kb], ea);
                     } else if constexpr (SCALE == kScaleMx32) {
-                        acc[sp] = mfma_mx4(b, a, acc[sp], xb_row[sp][kb], ea);
+                        const int eb = (int)(((uint32_t)xw[X][1 + sp][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
+                        acc[sp] = mfma_mx4(b, a, acc[sp], eb, ea);
                     } else {
                         acc[sp] = mfma_op(b, a, acc[sp]);
                     }
@@ -441,6 +479,11 @@ gemm_ksplit_kernel(const GemmArgs p)
                     load_step(d, st + DEPTH);
             }
         }
+    };
+    for (int st0 = s0; st0 < s1; st0 += 2 * DEPTH) {
+        group(std::integral_constant<int, 0>{}, st0);
+        if (st0 + DEPTH < s1)
+            group(std::integral_constant<int, 1>{}, st0 + DEPTH);
     }
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp)

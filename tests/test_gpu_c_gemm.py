@@ -171,15 +171,15 @@ def test_stream_splitk(dtype, mode, M, split_k, tile_n, waves):
 
 @pytest.mark.parametrize("tile_n", [16, 8, 32, 64])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
-                                        ("fp8", "mx128")])
+                                        ("fp8", "mx128"), ("fp4", "mx32")])
 def test_ksplit_uneven_and_empty_slices(dtype, mode, tile_n):
     """K-split kernel (half, one, two and four strips): step counts not
     divisible by the 8 waves and fewer steps than waves (some waves own no
-    K), with splits.  (bf16 steps are 64 bytes and K rows must be whole 128
-    bytes, so its counts are even.)"""
+    K), with splits.  (bf16 and fp4 steps are 64 bytes and K rows must be
+    whole 128 bytes, so their counts are even.)"""
     cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0, 8)
-    step = 32 if dtype == "bf16" else 128    # K elements per MFMA step
-    cases = (((18, 1), (26, 1), (2, 1), (6, 1), (36, 2), (20, 2)) if dtype == "bf16" else
+    step = {"bf16": 32, "fp8": 128, "fp4": 128}[dtype]    # K elements per MFMA step
+    cases = (((18, 1), (26, 1), (2, 1), (6, 1), (36, 2), (20, 2)) if dtype != "fp8" else
              ((9, 1), (13, 1), (1, 1), (3, 1), (5, 1), (18, 2), (10, 2)))
     for steps, split in cases:
         K = steps * step
@@ -189,6 +189,24 @@ def test_ksplit_uneven_and_empty_slices(dtype, mode, tile_n):
         got = run_gpu(A, B, dtype, mode, sA, sB, split_k=split, config=cfg)
         _, c16 = run_oracle(A, B, dtype, mode, sA, sB, split_k=split)
         assert np.array_equal(got, c16), (steps, split)
+
+
+@pytest.mark.parametrize("tile_n", [16, 8, 32, 64])
+@pytest.mark.parametrize("M", [16, 7])
+def test_mx32_scale_groups_past_array_end(M, tile_n):
+    """mxfp4 K-split tiles load each row's E8M0 bytes four steps at a time,
+    one group ahead; when a wave's slice is not a multiple of 4 steps, the
+    last wave's group runs past the end of both scale arrays.  The final
+    scale bytes of the last row of A (M = 16: the tile's last row, M = 7: a
+    ragged tile) and of the last row of B must still be read: every element
+    of C, and so its last row and column, is bit-exact."""
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0, 8)
+    for steps, split, N in ((14, 1, 48), (22, 1, 64), (10, 1, 16), (28, 2, 48), (6, 1, 80)):
+        K = steps * 128
+        A, B, sA, sB = exact_inputs("fp4", "mx32", M, N, K, 41 + steps)
+        got = run_gpu(A, B, "fp4", "mx32", sA, sB, split_k=split, config=cfg)
+        _, c16 = run_oracle(A, B, "fp4", "mx32", sA, sB, split_k=split)
+        assert np.array_equal(got, c16), (steps, split, N)
 
 
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),

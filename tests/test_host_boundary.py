@@ -309,8 +309,8 @@ def test_default_selection(dgp):
                   "16/2048/2:k16 16/2048/8:k32 4/16384/1:k16 1/16384/1:k16 1/8192/1:k16 1/2048/1:k8 1/16384/2:s64",
         "bf16": "16/16384/1:k64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/2048/8:k64 4/16384/1:k16 "
                 "1/16384/1:k16 1/16384/2:s64",
-        "mx32": "16/16384/1:s64 16/8192/1:s32 16/4096/2:s32 16/4096/4:s64 16/2048/4:k32 16/2048/2:k16 "
-                "4/16384/1:s64 4/8192/1:k16 1/16384/1:s64 1/2048/1:k8",
+        "mx32": "16/16384/1:k64 16/16384/2:s64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/4096/4:k64 "
+                "16/2048/4:k32 16/2048/2:k16 4/16384/1:k16 4/8192/1:k16 1/16384/1:k16 1/16384/2:s64 1/2048/1:k8",
         "block128": "16/16384/1:k64 16/8192/1:k32 16/4096/4:k64 16/2048/4:k32 4/2048/4:k32 1/16384/1:k32 "
                     "1/8192/1:k32",
         "mx128": "16/16384/1:k64 16/8192/1:k32 16/2048/8:k64 4/8192/1:k32 1/16384/1:k64 1/8192/1:k32",
