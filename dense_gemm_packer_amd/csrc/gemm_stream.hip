@@ -359,15 +359,21 @@ gemm_ksplit_kernel(const GemmArgs p)
     const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
     const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip0 * 16 / 128) * kblocks_row : nullptr;
     static_assert(SCALE != kScaleBlock || 128 % (16 * SPW) == 0, "a tile's strips in one 128-column block");
-    // mxfp8: this lane's A row and its B column in each strip (A rows >= M: none).
+    // mxfp8: a step's E8M0 bytes (this lane's A row, its B column in each
+    // strip) are loaded with the step's operands into the same ring slot, so
+    // they arrive with them and waiting for them never drains the ring.  The
+    // resources cover rows m0.. < M and columns strip0*16.. < N: rows and
+    // strips past the edge read zero (2^-127), which only scales zero data.
     constexpr bool kMx = SCALE == kScaleMx;
-    const uint8_t *xa_row = (kMx && m < p.M) ? static_cast<const uint8_t *>(p.sA) + (int64_t)m * kblocks_row
-                                             : nullptr;
-    const uint8_t *xb_row[SPW];
-#pragma unroll
-    for (int sp = 0; sp < SPW; ++sp)
-        xb_row[sp] = kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)((strip0 + sp) * 16 + (lane & 15)) * kblocks_row
-                         : nullptr;
+    [[maybe_unused]] const auto rXa8 = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblocks_row
+                                                     : nullptr,
+                                                 kMx ? clamp_bytes((int64_t)(p.M - m0) * kblocks_row) : 0);
+    [[maybe_unused]] const auto rXb8 = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)strip0 * 16 * kblocks_row
+                                                     : nullptr,
+                                                 kMx ? clamp_bytes((int64_t)(p.N - strip0 * 16) * kblocks_row) : 0);
+    [[maybe_unused]] const uint32_t x8_off = (uint32_t)(lane & 15) * (uint32_t)kblocks_row;
+    [[maybe_unused]] int xs[DEPTH][1 + SPW];   // [ring slot][A row, then each strip's column]
+    static_assert(!kMx || kStepBytes == 128, "mxfp8: one 128-K scale block per MFMA step");
 
     // mxfp4: the E8M0 bytes of a group of DEPTH = 4 steps are 16 contiguous
     // bytes of each row (step st, lane l: byte 4*st + l/16 of the row's
@@ -409,6 +415,14 @@ gemm_ksplit_kernel(const GemmArgs p)
     // one 16-row x 64-byte operand read, B chunk cc of strip sp one 1 KiB block.
     auto load_step = [&](int d, int st) {
         const uint32_t k = kbase + (uint32_t)st * kStepBytes;
+        if constexpr (kMx) {
+            const uint32_t kb = k / 128u;   // one E8M0 byte per 128-K step
+            xs[d][0] = __builtin_amdgcn_raw_buffer_load_b8(rXa8, x8_off + kb, 0, kAuxNone);
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp)
+                xs[d][1 + sp] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rXb8, x8_off + (uint32_t)(sp * 16) * (uint32_t)kblocks_row + kb, 0, kAuxNone);
+        }
 #pragma unroll
         for (int cc = 0; cc < kStepCh; ++cc)
             areg[d][cc] = load16<kAuxNone>(rA, a_voff + k + cc * 64u);
@@ -447,8 +461,7 @@ gemm_ksplit_kernel(const GemmArgs p)
                     kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
                     sc = __fmul_rn(sa_row ? sa_row[kb] : 0.f, sb_row[kb]);
                 } else if constexpr (SCALE == kScaleMx) {
-                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
-                    ea = xa_row ? xa_row[kb] : 127;
+                    ea = xs[d][0];
                 } else if constexpr (SCALE == kScaleMx32) {
                     // this lane's 16 bytes are one 32-element block, byte l/16 of the step's word
                     ea = (int)(((uint32_t)xw[X][0][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
@@ -467,7 +480,7 @@ gemm_ksplit_kernel(const GemmArgs p)
                         acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, sc));
                         acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, sc));
                     } else if constexpr (SCALE == kScaleMx) {
-                        acc[sp] = mfma_mx(b, a, acc[sp], xb_row[sp][kb], ea);
+                        acc[sp] = mfma_mx(b, a, acc[sp], xs[d][1 + sp], ea);
                     } else if constexpr (SCALE == kScaleMx32) {
                         const int eb = (int)(((uint32_t)xw[X][1 + sp][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
                         acc[sp] = mfma_mx4(b, a, acc[sp], eb, ea);
