@@ -192,6 +192,24 @@ def test_ksplit_uneven_and_empty_slices(dtype, mode, tile_n):
 
 
 @pytest.mark.parametrize("tile_n", [16, 8, 32, 64])
+def test_mx128_ksplit_long_k_ragged_n(tile_n):
+    """mxfp8 K-split tiles on long K ranges (K = 8192, split 1; K = 16384,
+    split 2) with N = 80, which leaves the last tile's strips past N: every
+    element bit-exact.  A NaN byte (E8M0 255) in the last K block of one B
+    row poisons exactly that column of C."""
+    cfg = dgp.Config(16, tile_n, 0, 0, 1, 0, 0, 8)
+    for M, N, K, split in ((16, 80, 8192, 1), (5, 80, 16384, 2)):
+        A, B, sA, sB = exact_inputs("fp8", "mx128", M, N, K, 53)
+        got = run_gpu(A, B, "fp8", "mx128", sA, sB, split_k=split, config=cfg)
+        _, c16 = run_oracle(A, B, "fp8", "mx128", sA, sB, split_k=split)
+        assert np.array_equal(got, c16), (M, N, K, split)
+    sB2 = sB.copy()
+    sB2[70, 127] = 255
+    f = (run_gpu(A, B, "fp8", "mx128", sA, sB2, split_k=2, config=cfg).astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(f[:, 70])) and np.all(np.isfinite(np.delete(f, 70, axis=1)))
+
+
+@pytest.mark.parametrize("tile_n", [16, 8, 32, 64])
 @pytest.mark.parametrize("M", [16, 7])
 def test_mx32_scale_groups_past_array_end(M, tile_n):
     """mxfp4 K-split tiles load each row's E8M0 bytes four steps at a time,
