@@ -42,6 +42,52 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class GfxClock:
+    """Graphics (shader) clock of the benchmarked device, read in-process
+    through amdsmi (no child process), matched to torch device 0 by its PCI
+    address.  Every reading is None where amdsmi or the device is not
+    reachable; the benchmark never depends on it."""
+
+    def __init__(self, torch):
+        self.h = None
+        try:
+            import amdsmi
+            p = torch.cuda.get_device_properties(0)
+            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+            amdsmi.amdsmi_init()
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    self.h = h
+            self.amdsmi = amdsmi
+        except Exception as e:   # no amdsmi, no permission, no match
+            log(f"gfx clock: not readable ({e!r:.120})")
+
+    def mhz(self):
+        if self.h is None:
+            return None
+        try:
+            return int(self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)["clk"])
+        except Exception:
+            return None
+
+
+def launch_stats(np, launch_ms):
+    """Per-launch statistics (microseconds) of a list of event timings (ms)."""
+    us = np.asarray(launch_ms, dtype=np.float64) * 1e3
+    return {"n": int(us.size), "median": round(float(np.median(us)), 2), "min": round(float(us.min()), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "mean": round(float(us.mean()), 2)}
+
+
+def git_sha():
+    """HEAD of the checkout, or None where the tree carries no git metadata."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip()[:12] or None if r.returncode == 0 else None
+    except Exception:
+        return None
+
+
 def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for p in sources:
@@ -70,11 +116,13 @@ def read_traffic(path=PROFILE_FILE, sources=KERNEL_SOURCES):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # The chip's clocks settle after some 30 ms of load, so the default
-    # warm-up (~40 ms of GEMMs) is long enough for the timed steps to run at
-    # the clock the kernel sustains.
+    # The timed steps follow a clock settle (--settle-ms of the same GEMM)
+    # and the declared warm-up, so they run at the clock the kernel sustains
+    # whatever --warmup is.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="run the headline GEMM for at least this long before the warm-up (clock settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -89,6 +137,7 @@ def main():
                     help="run only a 256 MiB probe copy and three fp8 decode launches "
                          "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
     args = ap.parse_args()
+    sha = git_sha()   # before the GPU is touched: no child process after that
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -169,6 +218,22 @@ def main():
             "3 x the same GEMM with the plain raster (XCD remap off)")
         return 0
 
+    # Clock settle, outside the declared warm-up and the timed region: the
+    # shader clock ramps for tens of ms after the chip leaves idle, so the
+    # same GEMM runs for at least --settle-ms first (reported as settle_ms).
+    clock = GfxClock(torch)
+    sclk = {"idle": clock.mhz()}
+    t0 = time.perf_counter()
+    settle_launches = 0
+    while True:
+        for _ in range(10):
+            dgp.gemm_preshuffle(A, Bs, out=C)
+        settle_launches += 10
+        torch.cuda.synchronize()
+        settle_ms = (time.perf_counter() - t0) * 1e3
+        if settle_ms >= args.settle_ms:
+            break
+    sclk["after_settle"] = clock.mhz()
     for _ in range(args.warmup):
         dgp.gemm_preshuffle(A, Bs, out=C)
     torch.cuda.synchronize()
@@ -182,20 +247,27 @@ def main():
         e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk["after_timed"] = clock.mhz()
     launch_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
-    launch_avg_ms = float(np.mean(launch_ms))
-    achieved = flops / (launch_avg_ms * 1e-3) / 1e12
-    log(f"bf16 GEMM {M}x{N}x{K}: {ms_per_step*1e3:.1f} us/step wall, {launch_avg_ms*1e3:.1f} us/launch "
-        f"(median {np.median(launch_ms)*1e3:.1f}, min {np.min(launch_ms)*1e3:.1f}) -> {achieved:.0f} TFLOP/s")
+    stats = launch_stats(np, launch_ms)
+    # The pages time the median launch (FlyDSL PR #1008 "Performance": median
+    # of 20 after 5 warm-ups); achieved and frac use it.
+    achieved = flops / (stats["median"] * 1e-6) / 1e12
+    log(f"bf16 GEMM {M}x{N}x{K}: {ms_per_step*1e3:.1f} us/step wall, per launch {stats} us "
+        f"-> {achieved:.0f} TFLOP/s at the median; settle {settle_ms:.0f} ms ({settle_launches} launches); "
+        f"gfx clock MHz {sclk}")
 
     traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "frac_stat": "median launch", "launch_us": stats,
                 "kernel": dgp.describe_kernel(dgp.select_kernel(M, N, K, dgp.BF16, dgp.SCALE_NONE)),
-                "per_launch": f"{flops:.4g} FLOP = 2*M*N*K"}
+                "per_launch": f"{flops:.4g} FLOP = 2*M*N*K",
+                "settle_ms": round(settle_ms, 1), "gfx_clock_mhz": sclk,
+                "source_sha16": kernel_source_sha(), "git_sha": sha}
 
     # --------------------------------------------------------- CPU oracle
     cpu = None
@@ -225,6 +297,7 @@ def main():
         wall = secondary["mfma_wall_bf16"]["workload_data"]
         roofline["measured_wall"] = wall
         roofline["frac_measured_wall"] = round(achieved / wall, 4)
+        roofline["other_kernels"] = summarize(secondary)
 
     line = {
         "metric": METRIC,
@@ -249,8 +322,48 @@ def main():
     return 0
 
 
-def graph_time_us(torch, fn, iters):
-    """Per-iteration GPU time of fn(i), i = 0..iters-1, captured in one HIP graph."""
+def summarize(sec):
+    """The secondary kernels' headline figures, one short entry each."""
+    out = {}
+    f8 = sec.get("fp8_gemm_4096x4096x8192")
+    if f8:
+        out["fp8 tensor 4096x4096x8192"] = {"us_median": f8["us"], "TFLOP/s": f8["TFLOP/s"],
+                                            "frac": f8["frac_of_peak"], "peak": PEAK_FP8_TFLOPS}
+    for key, peak in (("fp8_block128_gemm_4096x4096x8192", PEAK_FP8_TFLOPS),
+                      ("fp8_mx128_gemm_4096x4096x8192", PEAK_FP8_TFLOPS),
+                      ("fp4_mx32_gemm_4096x4096x8192", PEAK_FP4_TFLOPS)):
+        v = sec.get(key)
+        if v:
+            out[key.replace("_gemm_", " ")] = {"us_median": v["us"], "TFLOP/s": v["TFLOP/s"],
+                                               "frac": v["frac_of_peak"], "peak": peak}
+    c1 = sec.get("bf16_gemm_128x256x256")
+    if c1:
+        out["bf16 128x256x256"] = {"us_median": c1["us"], "us_min": c1["launch_us"]["min"],
+                                   "us_p90": c1["launch_us"]["p90"]}
+    for k, v in sec.get("decode_cold_cache", {}).items():
+        if k.startswith("best ") and ("N=16384" in k or "N=2048" in k):
+            out["decode cold " + k[5:]] = {"split": v["split"], "GB/s": v["GB/s"], "frac": v["frac_hbm"],
+                                           "frac_read_wall": v["frac_measured_wall"]}
+    v = sec.get("vendor_library_same_process", {})
+    if "bf16_4096x4096x8192_TFLOP/s" in v:
+        out["context: vendor library, same process"] = {k: v[k] for k in v if k.endswith("TFLOP/s")}
+    return out
+
+
+def settle(torch, fn, ms):
+    """Run fn() repeatedly for at least `ms` milliseconds (clock settle)."""
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return
+
+
+def graph_time_us(torch, fn, iters, settle_ms=60.0, reps=7):
+    """Per-iteration GPU time of fn(i), i = 0..iters-1, captured in one HIP
+    graph: the graph is replayed for settle_ms first, then `reps` replays are
+    timed one by one and the median replay is divided by iters."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -262,16 +375,29 @@ def graph_time_us(torch, fn, iters):
     with torch.cuda.graph(g):
         for i in range(iters):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    e0.record()
-    for _ in range(reps):
+    settle(torch, g.replay, settle_ms)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
         g.replay()
-    e1.record()
+        e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * iters)
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return ms[len(ms) // 2] * 1e3 / iters
+
+
+def launch_time_us(torch, np, fn, n=20, settle_ms=60.0):
+    """Per-launch statistics (us) of fn() after a clock settle: n launches,
+    each bracketed by events on the current stream."""
+    settle(torch, fn, settle_ms)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return launch_stats(np, [e0.elapsed_time(e1) for e0, e1 in ev])
 
 
 def oracle_leg(np, w, rows, c_gpu_rows, threads, flop=None, nbytes=None):
@@ -304,6 +430,19 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     out["packer_bf16_4096x8192"] = {"us": round(us, 2), "GB/s": round(2 * N * K * 2 / (us * 1e-6) / 1e9, 1)}
     assert torch.equal(dst.view(torch.int16), Bs_bf16.view(torch.int16))
     del B_raw, dst
+
+    # The small bf16 parity workload, 128 x 256 x 256: one workgroup tile,
+    # launch-latency bound; per-launch time and the throughput it implies.
+    w1 = synth.workload_inputs("bf16_small")
+    A1 = to_dev(w1["A"], "bf16")
+    Bs1 = dgp.preshuffle_b(to_dev(w1["B"], "bf16"))
+    C1 = torch.empty((w1["M"], w1["N"]), dtype=torch.bfloat16, device=dev)
+    st = launch_time_us(torch, np, lambda: dgp.gemm_preshuffle(A1, Bs1, out=C1), n=50)
+    out["bf16_gemm_128x256x256"] = {
+        "us": st["median"], "launch_us": st,
+        "TFLOP/s": round(2.0 * w1["M"] * w1["N"] * w1["K"] / (st["median"] * 1e-6) / 1e12, 3),
+        "kernel": dgp.describe_kernel(dgp.select_kernel(w1["M"], w1["N"], w1["K"], dgp.BF16, dgp.SCALE_NONE))}
+    del A1, Bs1, C1
 
     # HBM walls: the best plain streaming read (a few grid sizes) of 1 GiB,
     # and, for each decode workload, of the same byte count cold (rotating
@@ -362,9 +501,10 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
     out["mfma_wall_fp8"] = mfma_wall(1, A8.view(torch.uint8).reshape(-1))
     out["mfma_wall_fp8"]["frac_of_peak"] = round(out["mfma_wall_fp8"]["workload_data"] / PEAK_FP8_TFLOPS, 4)
-    us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, out=C8), 10)
+    st = launch_time_us(torch, np, lambda: dgp.gemm_preshuffle(A8, Bs8, sA, sB, out=C8))
+    us = st["median"]
     tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
-    out["fp8_gemm_4096x4096x8192"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+    out["fp8_gemm_4096x4096x8192"] = {"us": round(us, 1), "launch_us": st, "TFLOP/s": round(tf, 1),
                                       "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                                       "frac_measured_wall": round(tf / out["mfma_wall_fp8"]["workload_data"], 4)}
     out["fp8_gemm_4096x4096x8192"]["kernel"] = dgp.describe_kernel(
@@ -377,17 +517,18 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
 
     # Context only: the vendor library (hipBLASLt through torch) on the same
     # shapes and bytes, in the same process, with B in its own row-major
-    # layout.  Not part of the path and not a baseline.
+    # layout, timed like ours (median launch after a clock settle).  Not part
+    # of the path and not a baseline.
     vend = {}
     try:
         Bb = dgp.unshuffle_b(Bs_bf16)
-        us = graph_time_us(torch, lambda i: torch.nn.functional.linear(A_bf16, Bb), 10)
+        us = launch_time_us(torch, np, lambda: torch.nn.functional.linear(A_bf16, Bb))["median"]
         vend["bf16_4096x4096x8192_TFLOP/s"] = round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)
         del Bb
         B8 = dgp.unshuffle_b(Bs8)
         one = torch.ones((), device=dev)
-        us = graph_time_us(torch, lambda i: torch._scaled_mm(A8, B8.t(), scale_a=one, scale_b=one,
-                                                             out_dtype=torch.bfloat16), 10)
+        us = launch_time_us(torch, np, lambda: torch._scaled_mm(A8, B8.t(), scale_a=one, scale_b=one,
+                                                                out_dtype=torch.bfloat16))["median"]
         vend["fp8_4096x4096x8192_TFLOP/s"] = round(2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12, 1)
         del B8
     except Exception as e:   # a torch build without these paths: report, do not fail
@@ -406,11 +547,12 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
         sA = torch.from_numpy(w["sA"]).to(dev)
         sB = torch.from_numpy(w["sB"]).to(dev)
         C8 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-        us = graph_time_us(torch, lambda i: dgp.gemm_preshuffle(A8, Bs8, sA, sB, smode, out=C8), 10)
+        st = launch_time_us(torch, np, lambda: dgp.gemm_preshuffle(A8, Bs8, sA, sB, smode, out=C8))
+        us = st["median"]
         tf = 2.0 * 4096 * 4096 * 8192 / (us * 1e-6) / 1e12
         key = f"{edt}_{mode}_gemm_4096x4096x8192"
         dcode = dgp.FP4_E2M1 if mode == "mx32" else dgp.FP8_E4M3
-        out[key] = {"us": round(us, 1), "TFLOP/s": round(tf, 1),
+        out[key] = {"us": round(us, 1), "launch_us": st, "TFLOP/s": round(tf, 1),
                     "kernel": dgp.describe_kernel(dgp.select_kernel(4096, 4096, 8192, dcode, smode))}
         if mode == "mx32":   # fp4 dense matrix-core peak (published); no fp4 wall is probed
             out[key]["frac_of_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)

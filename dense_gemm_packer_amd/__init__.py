@@ -142,6 +142,70 @@ def _dev(t: torch.Tensor, what: str):
         raise ValueError(f"{what} must be contiguous")
 
 
+def _same_device(ref: torch.Tensor, *named):
+    for t, what in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{what} is on {t.device}, A on {ref.device}")
+
+
+# Scale tensors per mode: (dtype, numel of sA, numel of sB) for an M x N x K
+# call, or None where K or N breaks the mode's divisibility rule (the C ABI
+# then rejects the call with its own status).
+def scale_shapes(mode: int, M: int, N: int, K: int):
+    if mode == SCALE_NONE:
+        return None
+    if mode == SCALE_TENSOR:
+        return torch.float32, 1, 1
+    if mode == SCALE_BLOCK128:
+        if K % 128 or N % 128:
+            return None
+        return torch.float32, M * (K // 128), (N // 128) * (K // 128)
+    if mode == SCALE_MX128:
+        if K % 128:
+            return None
+        return torch.uint8, M * (K // 128), N * (K // 128)
+    if mode == SCALE_MX32:
+        if K % 32:
+            return None
+        return torch.uint8, M * (K // 32), N * (K // 32)
+    return None
+
+
+def check_gemm_operands(A: torch.Tensor, Bs: torch.Tensor, sA, sB, mode: int, out) -> None:
+    """Shape and dtype checks the C ABI cannot make (it sees pointers only):
+    a buffer smaller than the call assumes would be read or written past its
+    end.  Raises ValueError; device-independent, so it runs before any
+    launch."""
+    if A.dim() != 2 or Bs.dim() != 2:
+        raise ValueError(f"A and Bs must be 2-D (got {A.dim()}-D and {Bs.dim()}-D)")
+    if Bs.dtype != A.dtype:
+        raise ValueError(f"Bs is {Bs.dtype}, A is {A.dtype}: both operands take one element type")
+    M, K, N = A.shape[0], k_elements(A), Bs.shape[0]
+    if k_elements(Bs) != K:
+        raise ValueError(f"Bs holds {k_elements(Bs)} elements per row, A {K}")
+    if out is not None:
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be a ({M}, {N}) bfloat16 tensor (got {tuple(out.shape)} {out.dtype})")
+    want = scale_shapes(mode, M, N, K)
+    if want is None:
+        return
+    dt, na, nb = want
+    for t, n, what in ((sA, na, "sA"), (sB, nb, "sB")):
+        if t is None:
+            continue   # a missing scale is the C ABI's DGP_ERR_NULL
+        if t.dtype != dt or t.numel() != n:
+            raise ValueError(f"{what} must hold {n} {dt} values for this scale mode and shape "
+                             f"(got {t.numel()} {t.dtype})")
+
+
+def _alloc_stream(stream):
+    """Context in which outputs and workspaces are allocated: the launch
+    stream, so the caching allocator never hands their memory to other work
+    while the kernels that use it are still queued there."""
+    import contextlib
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _config(config):
     if config is None:
         return None
@@ -155,9 +219,15 @@ def _config(config):
 def preshuffle_b(B: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Bs = dgp_preshuffle_b(B); B is [N][K] bf16 or e4m3, on the device."""
     _dev(B, "B")
+    if B.dim() != 2:
+        raise ValueError(f"B must be 2-D (got {B.dim()}-D)")
     if out is None:
-        out = torch.empty_like(B)
+        with _alloc_stream(stream):
+            out = torch.empty_like(B)
     _dev(out, "out")
+    if out.dtype != B.dtype or out.shape != B.shape:
+        raise ValueError(f"out must match B ({tuple(B.shape)} {B.dtype}), got {tuple(out.shape)} {out.dtype}")
+    _same_device(B, (out, "out"))
     _check(lib().dgp_preshuffle_b(_ptr(B), _ptr(out), B.shape[0], k_elements(B), dtype_code(B),
                                   _stream_handle(stream)))
     return out
@@ -165,17 +235,26 @@ def preshuffle_b(B: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 
 def unshuffle_b(Bs: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     _dev(Bs, "Bs")
+    if Bs.dim() != 2:
+        raise ValueError(f"Bs must be 2-D (got {Bs.dim()}-D)")
     if out is None:
-        out = torch.empty_like(Bs)
+        with _alloc_stream(stream):
+            out = torch.empty_like(Bs)
     _dev(out, "out")
+    if out.dtype != Bs.dtype or out.shape != Bs.shape:
+        raise ValueError(f"out must match Bs ({tuple(Bs.shape)} {Bs.dtype}), got {tuple(out.shape)} {out.dtype}")
+    _same_device(Bs, (out, "out"))
     _check(lib().dgp_unshuffle_b(_ptr(Bs), _ptr(out), Bs.shape[0], k_elements(Bs), dtype_code(Bs),
                                  _stream_handle(stream)))
     return out
 
 
-def _scale_mode(A, sA, scale_mode):
+def _scale_mode(A, sA, sB, scale_mode):
     """The scale mode of a call: given, or inferred from the scales (none for
-    bf16; uint8 E8M0 scales -> mxfp8; one fp32 -> per-tensor; else blockscale)."""
+    bf16; mxfp4 for fp4; uint8 E8M0 scales -> mxfp8; one fp32 in each of sA
+    and sB -> per-tensor; more in both -> blockscale).  A one-element sA with
+    a larger sB is ambiguous (blockscale with M = 1 and K = 128 has a
+    one-element sA too) and must name its mode."""
     if scale_mode is not None:
         return scale_mode
     if dtype_code(A) == BF16:
@@ -184,7 +263,14 @@ def _scale_mode(A, sA, scale_mode):
         return SCALE_MX32
     if sA is not None and sA.dtype == torch.uint8:
         return SCALE_MX128
-    return SCALE_TENSOR if sA is None or sA.numel() == 1 else SCALE_BLOCK128
+    if sA is None or sB is None:
+        return SCALE_TENSOR   # the C ABI rejects the missing scale
+    if sA.numel() == 1 and sB.numel() == 1:
+        return SCALE_TENSOR
+    if sA.numel() > 1 and sB.numel() > 1:
+        return SCALE_BLOCK128
+    raise ValueError("ambiguous fp8 scales (one of sA, sB holds a single value, the other more): "
+                     "pass scale_mode=SCALE_TENSOR or SCALE_BLOCK128")
 
 
 def gemm_preshuffle(A: torch.Tensor, Bs: torch.Tensor, sA: torch.Tensor | None = None,
@@ -192,15 +278,17 @@ def gemm_preshuffle(A: torch.Tensor, Bs: torch.Tensor, sA: torch.Tensor | None =
                     out: torch.Tensor | None = None, config=None, stream=None) -> torch.Tensor:
     """C = A * B^T (bf16 [M][N]) with Bs = preshuffle_b(B)."""
     _dev(A, "A"), _dev(Bs, "Bs")
+    for s, name in ((sA, "sA"), (sB, "sB"), (out, "out")):
+        if s is not None:
+            _dev(s, name)
+    _same_device(A, (Bs, "Bs"), (sA, "sA"), (sB, "sB"), (out, "out"))
+    mode = _scale_mode(A, sA, sB, scale_mode)
+    check_gemm_operands(A, Bs, sA, sB, mode, out)
     M, K = A.shape[0], k_elements(A)
     N = Bs.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    _dev(out, "out")
-    for s, name in ((sA, "sA"), (sB, "sB")):
-        if s is not None:
-            _dev(s, name)
-    mode = _scale_mode(A, sA, scale_mode)
+        with _alloc_stream(stream):
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _check(lib().dgp_gemm_preshuffle(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
                                      _ptr(sA), _ptr(sB), _config(config), _stream_handle(stream)))
     return out
@@ -215,18 +303,27 @@ def gemm_preshuffle_splitk(A: torch.Tensor, Bs: torch.Tensor, split_k: int,
                            scale_mode: int | None = None, out: torch.Tensor | None = None,
                            workspace: torch.Tensor | None = None, config=None,
                            stream=None) -> torch.Tensor:
-    """Two-pass split-K C = A * B^T; workspace (fp32) is allocated if not given."""
+    """Two-pass split-K C = A * B^T; workspace (fp32) is allocated if not given
+    (on the launch stream; it is freed on return, and the caching allocator
+    reuses it only for work queued behind this call on that stream)."""
     _dev(A, "A"), _dev(Bs, "Bs")
+    for s, name in ((sA, "sA"), (sB, "sB"), (out, "out"), (workspace, "workspace")):
+        if s is not None:
+            _dev(s, name)
+    _same_device(A, (Bs, "Bs"), (sA, "sA"), (sB, "sB"), (out, "out"), (workspace, "workspace"))
+    if workspace is not None and workspace.dtype != torch.float32:
+        raise ValueError(f"workspace must be float32 (got {workspace.dtype})")
+    mode = _scale_mode(A, sA, sB, scale_mode)
+    check_gemm_operands(A, Bs, sA, sB, mode, out)
     M, K = A.shape[0], k_elements(A)
     N = Bs.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    _dev(out, "out")
     need = splitk_workspace_bytes(M, N, split_k)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4, dtype=torch.float32, device=A.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=A.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    mode = _scale_mode(A, sA, scale_mode)
     _check(lib().dgp_gemm_preshuffle_splitk(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
                                             _ptr(sA), _ptr(sB), split_k, _ptr(workspace), ws_bytes,
                                             _config(config), _stream_handle(stream)))

@@ -6,6 +6,7 @@
 // allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -71,12 +72,14 @@ constexpr int64_t kMaxRowBytes = int64_t(1) << 23;
 
 dgp_status check_device_arch()
 {
-    static int cached[64];   // 0 unknown, 1 gfx950, 2 other
+    // Per-device answer, 0 unknown, 1 gfx950, 2 other.  Atomic: host threads
+    // may make their first calls concurrently (both then store the same value).
+    static std::atomic<int> cached[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return fail(DGP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64 && cached[dev] == 1)
+    if (dev >= 0 && dev < 64 && cached[dev].load(std::memory_order_acquire) == 1)
         return DGP_OK;
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
@@ -84,7 +87,7 @@ dgp_status check_device_arch()
         return fail(DGP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     dgp_status st = dgp_check_arch(prop.gcnArchName);
     if (dev >= 0 && dev < 64)
-        cached[dev] = st == DGP_OK ? 1 : 2;
+        cached[dev].store(st == DGP_OK ? 1 : 2, std::memory_order_release);
     if (st != DGP_OK)
         return fail(DGP_ERR_ARCH, "device %d is %s; this library runs on gfx950 only", dev,
                     prop.gcnArchName);

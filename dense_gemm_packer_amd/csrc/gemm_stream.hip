@@ -12,6 +12,8 @@
 // gemm_ksplit_kernel -- decode-sized M: a workgroup owns half a strip or 1,
 //    2 or 4 strips, its K range split over 8 waves, partials added in LDS.
 
+#include <atomic>
+
 #include "gemm_common.h"
 
 namespace dgp {
@@ -542,14 +544,16 @@ void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t s)
     const size_t lds = lds_bytes(panel);
     // The LDS allowance is a per-device attribute of the kernel: set it once
     // on each device this launcher runs on (a failure surfaces at the launch).
-    static bool attr_set[64];
+    // Host threads may launch concurrently: the flags are atomics, and two
+    // threads that both see a flag clear both set the same value.
+    static std::atomic<bool> attr_set[64];
     int dev = 0;
     (void)hipGetDevice(&dev);
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
         (void)hipFuncSetAttribute((const void *)gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes(kMax));
         if (dev >= 0 && dev < 64)
-            attr_set[dev] = true;
+            attr_set[dev].store(true, std::memory_order_release);
     }
     gemm_stream_kernel<DT, NW, SPW, DEPTH, SCALE, OUT><<<grid, NW * 64, lds, s>>>(a, panel);
 }

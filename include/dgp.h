@@ -30,6 +30,16 @@
  *   - Every argument is validated on the host before any HIP call.  On a bad
  *     argument the call returns a status != DGP_OK and enqueues nothing.
  *   - Aliasing between an output and any input is not supported.
+ *   - No input needs padding past its last element.  The kernels read
+ *     through gfx950 buffer resources whose range ends at the input's last
+ *     byte; a load at or past that end returns zero and touches no memory.
+ *     One kernel relies on a finer form of this rule: the 16-row K-split
+ *     decode tiles read mxfp4 (DGP_SCALE_MX32) scale bytes 16 at a time,
+ *     and such a 16-byte load near the end of sA or sB may run past it.  The
+ *     buffer unit range-checks each dword of an aligned multi-dword buffer
+ *     load on its own, so the dwords inside the range carry data and the
+ *     dwords past it read as zero.  (The compiler merges adjacent aligned
+ *     dword buffer loads into one wider load on the same rule.)
  */
 #ifndef DGP_H
 #define DGP_H

@@ -501,6 +501,53 @@ def test_k_zero_gives_zeros_and_empty_is_noop():
     assert dgp.gemm_preshuffle(A, Bs).shape == (0, 32)
 
 
+def test_binding_rejects_mismatched_operands_before_launch():
+    """An output, weight or scale tensor smaller than the call assumes is
+    refused by the binding (ValueError) and nothing runs: the output keeps
+    its contents."""
+    A = torch.ones((16, 1024), dtype=torch.bfloat16, device=DEV)
+    Bs = torch.ones((256, 1024), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((16, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        dgp.gemm_preshuffle(A, Bs, out=out)
+    with pytest.raises(ValueError):
+        dgp.gemm_preshuffle_splitk(A, Bs, 2, out=out)
+    with pytest.raises(ValueError):
+        dgp.gemm_preshuffle(A, torch.ones((256, 512), dtype=torch.bfloat16, device=DEV))
+    A8 = torch.zeros((16, 1024), dtype=torch.float8_e4m3fn, device=DEV)
+    B8 = torch.zeros((256, 1024), dtype=torch.float8_e4m3fn, device=DEV)
+    out2 = torch.full((16, 256), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):   # blockscale sB must be [N/128][K/128]
+        dgp.gemm_preshuffle(A8, B8, torch.ones((16, 8), device=DEV), torch.ones((1, 8), device=DEV),
+                            dgp.SCALE_BLOCK128, out=out2)
+    with pytest.raises(ValueError):
+        dgp.preshuffle_b(B8, out=torch.empty((128, 1024), dtype=torch.float8_e4m3fn, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0).item() and torch.all(out2 == 7.0).item()
+
+
+def test_side_stream_allocations():
+    """A call on a stream other than the current one allocates its output
+    and split-K workspace on that stream; the result equals the
+    current-stream result bit for bit."""
+    M, N, K = 16, 2048, 7168
+    A, B, sA, sB = exact_inputs("fp8", "tensor", M, N, K, 29)
+    a = dev_codes(A, "fp8")
+    Bs_dev = dgp.preshuffle_b(dev_codes(B, "fp8"))
+    dA, dB = dev_scales(sA, "tensor"), dev_scales(sB, "tensor")
+    want = dgp.gemm_preshuffle_splitk(a, Bs_dev, 4, dA, dB, dgp.SCALE_TENSOR)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = [dgp.gemm_preshuffle_splitk(a, Bs_dev, 4, dA, dB, dgp.SCALE_TENSOR, stream=s) for _ in range(4)]
+    with torch.cuda.stream(s):   # work queued behind the calls on their stream
+        junk = [torch.full((M * N * 4,), 3.0, device=DEV) for _ in range(4)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), want.view(torch.int16))
+
+
 def test_binding_rejects_bad_arguments():
     A = torch.zeros((16, 128), dtype=torch.float8_e4m3fn, device=DEV)
     Bs = torch.zeros((128, 128), dtype=torch.float8_e4m3fn, device=DEV)

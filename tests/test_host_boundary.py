@@ -382,3 +382,58 @@ def test_tune_spec_parsing(dgp):
     for spec in tune.DEFAULT_SHAPES:
         kind, dt, sm, M, N, K, split = tune.parse(spec)
         assert dgp.select_kernel(M, N, K, dt, sm, split) >= 0     # every default shape is valid
+
+
+def _t(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype)
+
+
+def test_binding_operand_checks(dgp):
+    """The binding's shape and dtype checks (the C ABI sees pointers only):
+    an undersized output, a mismatched weight or undersized scales raise
+    ValueError before anything is launched.  Pure host code on CPU tensors."""
+    import torch
+    f8, bf = torch.float8_e4m3fn, torch.bfloat16
+    chk = dgp.check_gemm_operands
+    A, Bs = _t((16, 1024), f8), _t((256, 1024), f8)
+    one = _t((1,), torch.float32)
+    chk(A, Bs, one, one, dgp.SCALE_TENSOR, _t((16, 256), bf))            # good call
+    bad = [
+        (A, Bs, one, one, dgp.SCALE_TENSOR, _t((16, 128), bf)),          # out too narrow
+        (A, Bs, one, one, dgp.SCALE_TENSOR, _t((16, 256), torch.float32)),  # out not bf16
+        (A, _t((256, 512), f8), one, one, dgp.SCALE_TENSOR, None),      # K of Bs differs
+        (A, _t((256, 1024), bf), one, one, dgp.SCALE_TENSOR, None),     # Bs dtype differs
+        (_t((16, 1024, 1), f8), Bs, one, one, dgp.SCALE_TENSOR, None),  # A not 2-D
+        (A, Bs, _t((16, 7), torch.float32), _t((2, 8), torch.float32), dgp.SCALE_BLOCK128, None),
+        (A, Bs, _t((16, 8), torch.float32), _t((256, 8), torch.float32), dgp.SCALE_BLOCK128, None),
+        (A, Bs, _t((16, 8), torch.float32), _t((2, 8), torch.float32), dgp.SCALE_MX128, None),
+        (A, Bs, _t((16, 8), torch.uint8), _t((255, 8), torch.uint8), dgp.SCALE_MX128, None),
+        (_t((16, 512), torch.float4_e2m1fn_x2), _t((256, 512), torch.float4_e2m1fn_x2),
+         _t((16, 8), torch.uint8), _t((256, 32), torch.uint8), dgp.SCALE_MX32, None),
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            chk(*args)
+    chk(A, Bs, _t((16, 8), torch.float32), _t((2, 8), torch.float32), dgp.SCALE_BLOCK128, None)
+    chk(A, Bs, _t((16, 8), torch.uint8), _t((256, 8), torch.uint8), dgp.SCALE_MX128, None)
+    chk(_t((16, 512), torch.float4_e2m1fn_x2), _t((256, 512), torch.float4_e2m1fn_x2),
+        _t((16, 32), torch.uint8), _t((256, 32), torch.uint8), dgp.SCALE_MX32, None)
+    # K that breaks the mode's rule is left to the C ABI's own status
+    chk(_t((16, 192), f8), _t((256, 192), f8), one, one, dgp.SCALE_BLOCK128, None)
+
+
+def test_binding_scale_mode_inference(dgp):
+    import torch
+    f8 = torch.float8_e4m3fn
+    A = _t((1, 128), f8)
+    one, many = _t((1,), torch.float32), _t((2, 1), torch.float32)
+    assert dgp._scale_mode(A, one, one, None) == dgp.SCALE_TENSOR
+    assert dgp._scale_mode(_t((4, 128), f8), _t((4, 1), torch.float32), many, None) == dgp.SCALE_BLOCK128
+    # blockscale with M = 1, K = 128: sA holds one value, sB more -- ambiguous, never per-tensor
+    with pytest.raises(ValueError):
+        dgp._scale_mode(A, one, many, None)
+    assert dgp._scale_mode(A, one, many, dgp.SCALE_BLOCK128) == dgp.SCALE_BLOCK128
+    assert dgp._scale_mode(A, _t((1, 1), torch.uint8), _t((16, 1), torch.uint8), None) == dgp.SCALE_MX128
+    assert dgp._scale_mode(_t((1, 128), torch.bfloat16), None, None, None) == dgp.SCALE_NONE
+    assert dgp._scale_mode(_t((1, 64), torch.float4_e2m1fn_x2), None, None, None) == dgp.SCALE_MX32
