@@ -52,7 +52,7 @@ class Config(ctypes.Structure):
 
 # Every symbol include/dgp.h and include/dgp_diag.h declare.
 EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_splitk_workspace_bytes",
-           "dgp_gemm_preshuffle_splitk", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
+           "dgp_gemm_preshuffle_splitk", "dgp_gemm_preshuffle_splitk_noalloc", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
            "dgp_tile_of_workgroup", "dgp_tile_map", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
            "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_lds_dma_narrow", "dgp_probe_copy",
            "dgp_probe_stream_read", "dgp_probe_mfma_peak")
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         "dgp_gemm_preshuffle": [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
         "dgp_gemm_preshuffle_splitk": [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp,
                                        _sz, _vp, _vp],
+        "dgp_gemm_preshuffle_splitk_noalloc": [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int,
+                                               _vp, _vp],
         "dgp_check_arch": [ctypes.c_char_p],
         "dgp_tile_of_workgroup": [_i64, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_i64)],
         "dgp_tile_map": [_i64, _i64, _i64, _int, _int, _vp, _i64],
@@ -327,6 +329,31 @@ def gemm_preshuffle_splitk(A: torch.Tensor, Bs: torch.Tensor, split_k: int,
     _check(lib().dgp_gemm_preshuffle_splitk(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
                                             _ptr(sA), _ptr(sB), split_k, _ptr(workspace), ws_bytes,
                                             _config(config), _stream_handle(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # DGP_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_preshuffle_splitk_noalloc(A: torch.Tensor, Bs: torch.Tensor, split_k: int, out: torch.Tensor,
+                                   sA: torch.Tensor | None = None, sB: torch.Tensor | None = None,
+                                   scale_mode: int | None = None, config=None, stream=None) -> torch.Tensor:
+    """Two-pass split-K C = A * B^T whose fp32 partials go to the library's
+    fixed per-GPU scratch (dgp_gemm_preshuffle_splitk_noalloc): nothing is
+    allocated, the caller passes `out`.  Calls that overlap on one GPU race on
+    that scratch."""
+    _dev(A, "A"), _dev(Bs, "Bs"), _dev(out, "out")
+    for s, name in ((sA, "sA"), (sB, "sB")):
+        if s is not None:
+            _dev(s, name)
+    _same_device(A, (Bs, "Bs"), (sA, "sA"), (sB, "sB"), (out, "out"))
+    mode = _scale_mode(A, sA, sB, scale_mode)
+    check_gemm_operands(A, Bs, sA, sB, mode, out)
+    M, K = A.shape[0], k_elements(A)
+    N = Bs.shape[0]
+    _check(lib().dgp_gemm_preshuffle_splitk_noalloc(_ptr(A), _ptr(Bs), _ptr(out), M, N, K, dtype_code(A), mode,
+                                                    _ptr(sA), _ptr(sB), split_k, _config(config),
+                                                    _stream_handle(stream)))
     return out
 
 

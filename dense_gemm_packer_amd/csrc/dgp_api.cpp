@@ -216,6 +216,7 @@ struct GemmCall {
     size_t ws_bytes;
     const dgp_config *cfg;
     bool select_only = false;   // shapes and configuration only: no buffers checked
+    bool lib_scratch = false;   // split-K partials go to the library's fixed array (ws unused)
 };
 
 // Kernel choice for a validated call: the configured tile, or the built-in
@@ -356,13 +357,21 @@ dgp_status validate(const GemmCall &c, Plan *plan)
             return fail(DGP_ERR_ALIGN, "fp32 scales sA and sB must be 4-byte aligned");
     }
     if (c.split_k > 1) {
-        if (!c.ws)
-            return fail(DGP_ERR_WORKSPACE, "split_k > 1 needs a workspace");
-        if (!aligned16(c.ws))
-            return fail(DGP_ERR_ALIGN, "workspace is not 16-byte aligned");
         const size_t need = dgp_splitk_workspace_bytes(c.M, c.N, c.split_k);
-        if (c.ws_bytes < need)
-            return fail(DGP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.ws_bytes, need);
+        if (c.lib_scratch) {
+            if (need > kNoAllocScratchBytes)
+                return fail(DGP_ERR_WORKSPACE,
+                            "split_k*M*N*4 = %zu bytes exceeds the library's fixed scratch of %zu bytes "
+                            "(DGP_NOALLOC_SCRATCH_BYTES); pass a workspace to dgp_gemm_preshuffle_splitk",
+                            need, kNoAllocScratchBytes);
+        } else {
+            if (!c.ws)
+                return fail(DGP_ERR_WORKSPACE, "split_k > 1 needs a workspace");
+            if (!aligned16(c.ws))
+                return fail(DGP_ERR_ALIGN, "workspace is not 16-byte aligned");
+            if (c.ws_bytes < need)
+                return fail(DGP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.ws_bytes, need);
+        }
     }
 
     return select_kernel(c, Ks, plan);
@@ -381,12 +390,18 @@ dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
         return st;
     if (c.K == 0)
         return hip_status(launch_splitk_reduce(nullptr, c.C, c.M, c.N, 0, stream), "zero fill");
+    float *ws = c.ws;
+    if (c.lib_scratch && c.split_k > 1) {
+        st = hip_status(noalloc_scratch(&ws), "address of the library's split-K scratch");
+        if (st != DGP_OK)
+            return st;
+    }
 
     GemmArgs a{};
     a.A = (const uint8_t *)c.A;
     a.Bs = (const uint8_t *)c.Bs;
     a.C = c.C;
-    a.ws = c.ws;
+    a.ws = ws;
     a.sA = c.sA;
     a.sB = c.sB;
     a.M = (int)c.M;
@@ -404,7 +419,7 @@ dgp_status run_gemm(const GemmCall &c, hipStream_t stream)
     st = hip_status(hipGetLastError(), "GEMM launch");
     if (st != DGP_OK || c.split_k == 1)
         return st;
-    return hip_status(launch_splitk_reduce(c.ws, c.C, c.M, c.N, c.split_k, stream), "split-K reduce launch");
+    return hip_status(launch_splitk_reduce(ws, c.C, c.M, c.N, c.split_k, stream), "split-K reduce launch");
 }
 
 dgp_status shuffle(const void *src, void *dst, int64_t N, int64_t K, int dtype, void *stream, bool inverse)
@@ -476,6 +491,15 @@ dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, in
                                       const dgp_config *cfg, void *stream)
 {
     GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, split_k, ws, ws_bytes, cfg};
+    return run_gemm(c, (hipStream_t)stream);
+}
+
+dgp_status dgp_gemm_preshuffle_splitk_noalloc(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
+                                              int64_t K, int dtype, int scale_mode, const void *sA,
+                                              const void *sB, int split_k, const dgp_config *cfg, void *stream)
+{
+    GemmCall c{A, Bs, C, M, N, K, dtype, scale_mode, sA, sB, split_k, nullptr, 0, cfg};
+    c.lib_scratch = true;
     return run_gemm(c, (hipStream_t)stream);
 }
 

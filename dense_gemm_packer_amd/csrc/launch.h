@@ -55,6 +55,13 @@ const KernelSpec *lds_kernels(int *count);
 const KernelSpec *stream_kernels(int *count);
 const KernelSpec *kernel_table(int *count);
 
+// Library-owned split-K workspace (noalloc.hip): the size of the fixed
+// per-device array, and its device address on the current device (taken
+// once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(float **out);
+
 hipError_t launch_preshuffle(const void *src, void *dst, int64_t N, int64_t Kb, bool inverse,
                              hipStream_t stream);
 hipError_t launch_splitk_reduce(const float *ws, void *C, int64_t M, int64_t N, int splits,

@@ -23,7 +23,8 @@
  *     (OCP e4m3fn codes, 1 byte).  Accumulation is always fp32.
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates, frees, synchronises or keeps a pointer past the
- *     call.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     call (one entry point, dgp_gemm_preshuffle_splitk_noalloc, uses a fixed
+ *     array of the library's own instead of a caller workspace).  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and runs asynchronously: outputs are ready when the stream is.
  *   - Scales are device pointers to fp32 as well (so a launch never needs a
  *     host synchronisation).
@@ -219,6 +220,33 @@ dgp_status dgp_gemm_preshuffle_splitk(const void *A, const void *Bs, void *C, in
                                       int64_t K, int dtype, int scale_mode, const void *sA,
                                       const void *sB, int split_k, float *ws, size_t ws_bytes,
                                       const dgp_config *cfg, void *stream);
+
+/*
+ * dgp_gemm_preshuffle_splitk_noalloc -- dgp_gemm_preshuffle_splitk without a
+ * caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation).
+ *
+ * Same arguments, rules, kernels and results as dgp_gemm_preshuffle_splitk
+ * (bit-identical output), except that pass 1's fp32 partials go to an array
+ * the library keeps in device memory: DGP_NOALLOC_SCRATCH_BYTES (16 MiB) per
+ * GPU, held from its first use on that GPU until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller passes A, Bs, C and the scales as usual.  Returns
+ * DGP_ERR_WORKSPACE, with nothing enqueued, when split_k > 1 and
+ * split_k * M * N * 4 > DGP_NOALLOC_SCRATCH_BYTES (e.g. M = 16, N = 16384
+ * fits up to split_k = 16).  split_k == 1 uses no scratch.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (on different streams, or from
+ * different host threads) race on it and may produce wrong results; order
+ * them on one stream or use dgp_gemm_preshuffle_splitk with a workspace each.
+ */
+#define DGP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dgp_status dgp_gemm_preshuffle_splitk_noalloc(const void *A, const void *Bs, void *C, int64_t M, int64_t N,
+                                              int64_t K, int dtype, int scale_mode, const void *sA,
+                                              const void *sB, int split_k, const dgp_config *cfg,
+                                              void *stream);
 
 /* dgp_check_arch -- DGP_OK if `gcn_arch_name` (as reported by the HIP device
  * properties, e.g. "gfx950:sramecc+:xnack-") names gfx950, else DGP_ERR_ARCH.

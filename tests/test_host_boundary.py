@@ -437,3 +437,17 @@ def test_binding_scale_mode_inference(dgp):
     assert dgp._scale_mode(A, _t((1, 1), torch.uint8), _t((16, 1), torch.uint8), None) == dgp.SCALE_MX128
     assert dgp._scale_mode(_t((1, 128), torch.bfloat16), None, None, None) == dgp.SCALE_NONE
     assert dgp._scale_mode(_t((1, 64), torch.float4_e2m1fn_x2), None, None, None) == dgp.SCALE_MX32
+
+
+def test_noalloc_rejects_sizes_past_its_scratch(dgp, L):
+    """dgp_gemm_preshuffle_splitk_noalloc refuses split_k * M * N * 4 bytes
+    beyond its fixed scratch before any HIP call (no device here)."""
+    f = L.dgp_gemm_preshuffle_splitk_noalloc
+    # 32 x 16384 x 14 partials = 28 MiB > 16 MiB
+    assert f(P, P, P, 32, 16384, 7168, FP8, TENSOR, P, P, 14, None, None) == WS
+    assert "scratch" in L.dgp_last_error().decode()
+    assert f(P, P, P, 32, 16384, 7168, FP8, TENSOR, P, P, 3, None, None) == SPLITK   # 7168 % 3
+    assert f(P, P, P, 32, 16384, 7168, FP8, TENSOR, P, None, 8, None, None) == NULL
+    assert dgp.NOALLOC_SCRATCH_BYTES == 16 << 20
+    hdr = open(os.path.join(INCLUDE, "dgp.h")).read()
+    assert "#define DGP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in hdr
