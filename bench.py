@@ -63,10 +63,25 @@ class GfxClock:
             log(f"gfx clock: not readable ({e!r:.120})")
 
     def mhz(self):
+        """Shader clock (MHz) and socket power (W) from the device's metrics
+        table: the mean of the per-XCD current clocks and the firmware's
+        average; meaningful when read while kernels are running."""
         if self.h is None:
             return None
         try:
-            return int(self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)["clk"])
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+            out = {}
+            cur = m.get("current_gfxclks")
+            if isinstance(cur, (list, tuple)):
+                vals = [int(v) for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
+                if vals:
+                    out["current"] = round(sum(vals) / len(vals))
+            for k, name in (("average_gfxclk_frequency", "average"), ("current_gfxclk", "current_single"),
+                            ("current_socket_power", "socket_W")):
+                v = m.get(k)
+                if isinstance(v, (int, float)) and 0 < v < 100000:
+                    out[name] = int(v)
+            return out or None
         except Exception:
             return None
 
@@ -229,11 +244,12 @@ def main():
         for _ in range(10):
             dgp.gemm_preshuffle(A, Bs, out=C)
         settle_launches += 10
+        if (time.perf_counter() - t0) * 1e3 >= 0.8 * args.settle_ms:
+            sclk["under_settle_load"] = clock.mhz()   # read while the queued GEMMs run
         torch.cuda.synchronize()
         settle_ms = (time.perf_counter() - t0) * 1e3
         if settle_ms >= args.settle_ms:
             break
-    sclk["after_settle"] = clock.mhz()
     for _ in range(args.warmup):
         dgp.gemm_preshuffle(A, Bs, out=C)
     torch.cuda.synchronize()
@@ -245,9 +261,10 @@ def main():
         s.record(stream)
         dgp.gemm_preshuffle(A, Bs, out=C)
         e.record(stream)
+    sclk["under_timed_load"] = clock.mhz()   # the timed launches are still queued
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sclk["after_timed"] = clock.mhz()
+    sclk["after"] = clock.mhz()
     launch_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
