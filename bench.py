@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--profile-splitk-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and three fp8 split-K decode calls "
                          "(M=16, N=16384, K=7168, split 4: pass 1 writing fp32 partials, then the reduce)")
+    ap.add_argument("--profile-compare", action="store_true",
+                    help="run only a 256 MiB probe copy, then for bf16 and fp8 4096x4096x8192: 3 launches each "
+                         "of the default kernel, the 4-wave kernel and the vendor library (for counter runs)")
     ap.add_argument("--profile-decode-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and three fp8 decode launches "
                          "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
@@ -172,6 +175,38 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16 if dtype == "bf16" else np.uint8).copy())
         return t.view({"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
                        "fp4": torch.float4_e2m1fn_x2}[dtype]).to(dev)
+
+    if args.profile_compare:
+        w4 = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8, schedule=4, prefetch=3)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dgp.probe_copy(src, dst)
+        del src, dst
+        for name in ("bf16_large", "fp8_large"):
+            wl = synth.workload_inputs(name)
+            dt = wl["dtype"]
+            Al = to_dev(wl["A"], dt)
+            Bsl = dgp.preshuffle_b(to_dev(wl["B"], dt))
+            Bl = dgp.unshuffle_b(Bsl)
+            Cl = torch.empty((wl["M"], wl["N"]), dtype=torch.bfloat16, device=dev)
+            sc = () if dt == "bf16" else (torch.from_numpy(wl["sA"]).to(dev), torch.from_numpy(wl["sB"]).to(dev))
+            one = torch.ones((), device=dev)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dgp.gemm_preshuffle(Al, Bsl, *sc, out=Cl)
+            for _ in range(3):
+                dgp.gemm_preshuffle(Al, Bsl, *sc, out=Cl, config=w4)
+            for _ in range(3):
+                if dt == "bf16":
+                    torch.nn.functional.linear(Al, Bl)
+                else:
+                    torch._scaled_mm(Al, Bl.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+            del Al, Bsl, Bl, Cl
+        log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 x default kernel, "
+            "3 x 4-wave kernel (B 3 k-tiles ahead), 3 x vendor library")
+        return 0
 
     if args.profile_decode_traffic:
         wd = synth.workload_inputs("fp8_decode", M=16, N=16384)

@@ -414,8 +414,9 @@ def describe_kernel(index: int) -> str:
         return (f"gemm_stream_kernel<{dts}, 16x{cfg.tile_n} tile, {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
     sched = {1: f"interleaved, LDS read-ahead {cfg.preload_dsrd}", 2: "ping-pong",
-             3: f"A and B in LDS, LDS read-ahead {cfg.preload_dsrd}"}[cfg.schedule]
-    kname = {1: "tiled", 2: "pingpong", 3: "lds"}[cfg.schedule]
+             3: f"A and B in LDS, LDS read-ahead {cfg.preload_dsrd}",
+             4: f"4 waves (1 per SIMD), AGPR accumulators, LDS read-ahead {cfg.preload_dsrd}"}[cfg.schedule]
+    kname = {1: "tiled", 2: "pingpong", 3: "lds", 4: "w4"}[cfg.schedule]
     return (f"gemm_{kname}_kernel<{dts}, {cfg.tile_m}x{cfg.tile_n} tile, "
             f"{cfg.tile_k}-byte k-tile, waves_m {cfg.waves_m}, prefetch {cfg.prefetch}, {sched}"
             f"{', fp32 partials' if so else ''}>")

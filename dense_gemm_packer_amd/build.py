@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdgp.so")
-SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_lds.hip", "gemm_stream.hip", "reduce.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_lds.hip", "gemm_stream.hip", "reduce.hip", "probe.hip", "noalloc.hip", "gemm_w4.hip"]
 HEADERS = ["common.h", "launch.h", "gemm_common.h"]
 ARCH = "gfx950"
 
@@ -26,7 +26,7 @@ CFLAGS = [
 # Keep MFMA accumulators in arch VGPRs (avoids accumulator copies at loop
 # latches) everywhere except in the kernels that need the AGPRs for them.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-AGPR_ACC_SOURCES = {"gemm_lds.hip"}
+AGPR_ACC_SOURCES = {"gemm_lds.hip", "gemm_w4.hip"}
 
 
 def flags(src):

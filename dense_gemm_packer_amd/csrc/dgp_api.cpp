@@ -30,6 +30,8 @@ const KernelSpec *kernel_table(int *count)
         v.insert(v.end(), t, t + n);
         t = lds_kernels(&n);
         v.insert(v.end(), t, t + n);
+        t = w4_kernels(&n);
+        v.insert(v.end(), t, t + n);
         t = stream_kernels(&n);
         v.insert(v.end(), t, t + n);
         return v;
@@ -229,8 +231,8 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
         const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
         if (c.cfg->waves_m < 0 || c.cfg->prefetch < 0)
             return fail(DGP_ERR_CONFIG, "waves_m and prefetch must be >= 0");
-        if (c.cfg->schedule < 0 || c.cfg->schedule > kSchedBothLds)
-            return fail(DGP_ERR_CONFIG, "schedule must be 0, 1, 2 or 3 (got %d)", c.cfg->schedule);
+        if (c.cfg->schedule < 0 || c.cfg->schedule > kSchedW4)
+            return fail(DGP_ERR_CONFIG, "schedule must be 0, 1, 2, 3 or 4 (got %d)", c.cfg->schedule);
         Query q{fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n};
         if (fam == kTiled) {
             q.kt = c.cfg->tile_k;

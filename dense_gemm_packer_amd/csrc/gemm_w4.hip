@@ -1,0 +1,346 @@
+// gemm_w4_kernel -- the 256 x 256 large-M tile with one wave per SIMD.
+//
+// Same operation, operand layouts and epilogue as gemm_tiled_kernel
+// (gemm_tiled.hip, gemm_common.h): per k-tile of 128 bytes the A tile goes
+// global -> LDS with the async buffer load (FlyDSL PR #1008 "Summary"), the
+// preshuffled B fragments go straight to VGPRs, and A fragments are read from
+// LDS per MFMA k-step (FlyDSL PR #974, follow-up commit item 2).  What
+// differs is the split of the workgroup: 4 waves (1 x 4), each owning all 256
+// rows and 64 columns of the tile, 256 fp32 accumulators per lane.  Against
+// the 8-wave tile this halves the LDS read traffic (each wave reads the whole
+// A tile once per k-tile, and there are half as many waves) while B still
+// passes through the L1 exactly once.
+//
+// Registers.  The accumulators live in the 256 AGPRs and every MFMA is
+// issued as inline assembly on its accumulator in place ("+a"), so the
+// compiler never moves them between register files.  Because the compiler
+// does not see these instructions as MFMAs, the code keeps to inputs whose
+// hazards the hardware or s_waitcnt covers: operands come straight from LDS
+// or buffer loads into the registers the MFMA reads, an accumulator is only
+// reused 64 MFMAs later, and the epilogue waits out the last MFMAs with
+// s_nop before reading the AGPRs.
+//
+// Schedule (one wave per SIMD: nothing else hides a stall, so the order is
+// fixed with scheduling fences).  A k-tile is kFr fragments (A fragment f =
+// row tile f % 16 of MFMA k-step f / 16), each followed by its 4 MFMAs (one
+// per 16-column strip).  The LDS read of fragment f + 7 is issued before the
+// MFMAs of fragment f.  A ring of 4 LDS stages: the workgroup barrier that
+// certifies tile t+1 sits 7 fragments before the end of tile t, right where
+// the reads of tile t+1 begin, and the copy of tile t+3 (into the stage tile
+// t-1 used) follows it.  Every global load has a fixed fragment position, so
+// the wait before the barrier is a compile-time count (kVmAtBarrier).
+#include "gemm_common.h"
+
+namespace dgp {
+
+namespace w4 {
+
+constexpr int TM = 256, TN = 256, NW = 4, KT = 128;
+constexpr int kMT = 16;                  // 16-row tiles per wave
+constexpr int kNT = 4;                   // 16-column strips per wave
+constexpr int kCH = KT / 64;             // 64-byte chunks per k-tile
+constexpr int kRing = 4;                 // LDS stages
+constexpr int kBuf = TM * KT;            // bytes per stage
+constexpr int kDma = (TM / 16) * kCH / NW;   // async copies per wave per k-tile
+constexpr int kRA = 7;                   // fragments read ahead of their MFMAs
+static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
+
+template <int DT>
+struct Plan {
+    static constexpr int kStepCh = Op<DT>::kBlocks;       // 64-byte chunks per MFMA step
+    static constexpr int kSteps = kCH / kStepCh;          // MFMA k-steps per k-tile
+    static constexpr int kFr = kSteps * kMT;              // A fragments per k-tile
+    static constexpr int kBar = kFr - kRA;                // barrier position
+    static_assert(kFr % (kRA + 1) == 0, "the fragment ring must wrap at the k-tile boundary");
+    // Global loads at fixed fragment positions.  Copy j of tile t+3 after the
+    // barrier, spread over the last kRA fragments.
+    static constexpr int dma_pos(int j) { return kBar + (j * kRA) / kDma; }
+    // B reloads: the chunks of a step are reloaded for tile t+kDB right after
+    // that step's last MFMA -- one load per fragment, starting at the next
+    // fragment; the last step's reloads wrap into the next k-tile.
+    static constexpr int kBLoads = kNT * kCH;
+    static constexpr int bload_pos(int i)   // i = step-major index (step, chunk of step, strip)
+    {
+        return ((i / (kNT * kStepCh)) * kMT + kMT + i % (kNT * kStepCh)) % kFr;
+    }
+    static constexpr bool bload_wraps(int i) { return (i / (kNT * kStepCh)) == kSteps - 1; }
+    // Loads issued after the last copy of tile t+1 (tile t-2, fragment kFr-1)
+    // up to the barrier of tile t+1 (tile t, fragment kBar): the rest of tile
+    // t-2, all of tile t-1, and tile t before the barrier.
+    static constexpr int vm_at_barrier()
+    {
+        int n = 0;
+        for (int j = 0; j < kDma; ++j) {   // tile t-2 after its last copy: later copies only
+            if (dma_pos(j) > dma_pos(kDma - 1))
+                ++n;
+        }
+        n += kDma + kBLoads;               // tile t-1
+        for (int i = 0; i < kBLoads; ++i)  // tile t before the barrier
+            n += bload_pos(i) < kBar ? 1 : 0;
+        for (int j = 0; j < kDma; ++j)
+            n += dma_pos(j) < kBar ? 1 : 0;
+        return n;
+    }
+    static_assert(kBar >= kMT || kSteps == 1, "");
+};
+
+}  // namespace w4
+
+// acc += B-fragment x A-fragment, in place on AGPRs: bf16 K32 ...
+__device__ inline void mfma_acc(f32x4 &acc, const i32x4 &b, const i32x4 &a)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// ... and e4m3 K128 (unscaled form: both operands OCP e4m3).
+__device__ inline void mfma_acc(f32x4 &acc, const i32x8 &b, const i32x8 &a)
+{
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// DB: B register sets = k-tiles of B loads in flight (2..4).
+// SWZ: A's LDS layout.  0 = the operand-block order of gemm_common.h (one
+// copy instruction = 16 rows x 64 bytes); 1 = row-major 128-byte rows with
+// the 16-byte chunks XOR-swizzled (one copy instruction = 8 whole rows, i.e.
+// 8 whole 128-byte lines): chunk c of tile row r is stored at chunk
+// c ^ ((r >> 1) & 7) of its row, so the 16 rows one fragment read touches
+// (rows 16mt + i, one chunk each) fall on 16 distinct 16-byte bank groups
+// -- the row-major tile with an XOR swizzle known to writer and reader of
+// FlyDSL PR #1008 "Changes" item 2.
+template <int DT, int SCALE, int OUT, int DB, int SWZ>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+gemm_w4_kernel(const GemmArgs p)
+{
+    static_assert(DB >= 2 && DB <= 4, "B sets");
+    constexpr int kDB = DB;
+    using namespace w4;
+    using P = Plan<DT>;
+    using Frag = typename Op<DT>::Frag;
+    constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
+    constexpr int kVm = P::vm_at_barrier();
+    static_assert(kVm <= 63, "vmcnt field is 6 bits");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
+    const int m0 = (int)tc.tm * TM;
+    const int n0 = (int)tc.tn * TN;
+    const int split = (int)tc.s;
+    const uint32_t Kb = (uint32_t)p.Kb;
+    const uint32_t kbase = (uint32_t)split * (uint32_t)p.Ks;
+    const int ntiles = p.Ks / KT;
+
+    // A copy: instruction j of this wave fills LDS block j*NW + wave = (row
+    // group rg, 64-byte chunk ch); lane l's global address selects row
+    // 16*rg + l%16, K-bytes 64*ch + 16*(l/16) (the operand-block order of
+    // gemm_common.h).  Rows >= M are past the range and load as zero.
+    const auto rA = make_rsrc(p.A + (int64_t)m0 * Kb, clamp_bytes((int64_t)(p.M - m0) * Kb));
+    uint32_t dma_voff[kDma];
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+        const int blk = j * NW + wave;
+        if constexpr (SWZ) {
+            // instruction j fills rows 8*blk .. 8*blk+7 (1 KiB, linear): lane l
+            // lands at row 8*blk + l/8, stored chunk l%8, so it fetches logical
+            // chunk (l%8) ^ swizzle(row)
+            const int r = 8 * blk + (lane >> 3);
+            dma_voff[j] = (uint32_t)r * Kb + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+        } else {
+            dma_voff[j] = (uint32_t)((blk / kCH) * 16 + (lane & 15)) * Kb +
+                          (uint32_t)((blk % kCH) * 64 + (lane >> 4) * 16);
+        }
+    }
+    // A fragment reads (SWZ): lane l reads row 16mt + l%16; logical chunk
+    // 4s + l/16 of step s sits at stored chunk (4s) ^ v with v = (l/16) ^
+    // ((l%16) >> 1 & 7), i.e. at lane offset a_off[0] (s = 0) or a_off[1]
+    // (s = 1; fp8: the upper 64 bytes of its one step).
+    [[maybe_unused]] uint32_t a_off[2];
+    if constexpr (SWZ) {
+        const uint32_t v = (uint32_t)((lane >> 4) ^ ((lane & 15) >> 1));
+        a_off[0] = (uint32_t)(lane & 15) * 128u + 16u * v;
+        a_off[1] = (uint32_t)(lane & 15) * 128u + 16u * (v ^ 4u);
+    }
+    // B: this wave's 4 strips; strips >= N/16 are past the range (zero).
+    const int strip0 = (n0 + wave * (TN / NW)) / 16;
+    const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
+    const uint32_t b_voff = (uint32_t)lane * 16u;
+
+    f32x4 acc[kMT][kNT];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (the zeroing stays ahead of the prologue's loads, far from the first MFMA)
+    __builtin_amdgcn_sched_barrier(0);
+
+    i32x4 breg[kDB][kNT][kCH];   // [set = tile % kDB][strip][chunk]
+    Frag ring[kRA + 1];          // A fragments: slot = fragment index % (kRA + 1)
+
+    auto kofs = [&](int t) { return kbase + (uint32_t)(t < ntiles ? t : ntiles - 1) * KT; };
+    auto stage = [&](int t) { return (uint32_t)(t & (kRing - 1)) * kBuf; };
+    auto load_b = [&](auto setc, int nt, int ch, uint32_t koff) {
+        constexpr int SET = decltype(setc)::value;
+        breg[SET][nt][ch] = load16<kAuxNone>(rB, b_voff + (uint32_t)nt * 16u * Kb + (uint32_t)ch * 1024u + koff * 16u);
+    };
+    auto dma = [&](int j, uint32_t st, uint32_t koff) {
+        lds_dma16(rA, lds + st + (j * NW + wave) * 1024, dma_voff[j], koff);
+    };
+    auto read_frag = [&](int f, uint32_t st) {   // fragment f of the tile in stage st
+        const int s = f / kMT, mt = f % kMT;
+        if constexpr (SWZ) {
+            const uint8_t *row = lds + st + mt * 2048;
+            if constexpr (DT == kDtypeBf16)
+                ring[f % (kRA + 1)] = *reinterpret_cast<const i32x4 *>(row + a_off[s]);
+            else
+                ring[f % (kRA + 1)] = cat(*reinterpret_cast<const i32x4 *>(row + a_off[0]),
+                                          *reinterpret_cast<const i32x4 *>(row + a_off[1]));
+        } else {
+            ring[f % (kRA + 1)] = lds_frag<DT>(lds + st + (mt * kCH + s * kStepCh) * 1024 + lane * 16);
+        }
+    };
+
+    // Prologue: copies of tiles 0..2, B of tiles 0..DB-1, all landed; then
+    // the first kRA fragments of tile 0.
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int j = 0; j < kDma; ++j)
+            dma(j, stage(t), kofs(t));
+    auto prologue_b = [&](auto setc) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int ch = 0; ch < kCH; ++ch)
+                load_b(setc, nt, ch, kofs(decltype(setc)::value));
+    };
+    prologue_b(std::integral_constant<int, 0>{});
+    prologue_b(std::integral_constant<int, 1>{});
+    if constexpr (DB > 2)
+        prologue_b(std::integral_constant<int, (DB > 2 ? 2 : 0)>{});
+    if constexpr (DB > 3)
+        prologue_b(std::integral_constant<int, (DB > 3 ? 3 : 0)>{});
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int f = 0; f < kRA; ++f)
+        read_frag(f, stage(0));
+
+    // One k-tile.  SET = t % kDB holds tile t's B (and receives tile t+kDB's
+    // as it is consumed); the wrapped reloads at its start refill set
+    // (t-1) % kDB with tile t-1+kDB.
+    auto tile = [&](auto setc, int t) {
+        constexpr int SET = decltype(setc)::value;
+        constexpr int PREV = (SET + kDB - 1) % kDB;
+        const uint32_t cur = stage(t), nx1 = stage(t + 1), nx3 = stage(t + 3);
+        const uint32_t k_prev = kofs(t - 1 + kDB), k_this = kofs(t + kDB), k_dma = kofs(t + 3);
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (f == kBar)
+                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+            // this position's global loads
+#pragma unroll
+            for (int i = 0; i < P::kBLoads; ++i) {
+                if (P::bload_pos(i) == f) {
+                    const int st = i / (kNT * kStepCh), r = i % (kNT * kStepCh);
+                    const int ch = st * kStepCh + r / kNT, nt = r % kNT;
+                    if (P::bload_wraps(i))
+                        load_b(std::integral_constant<int, PREV>{}, nt, ch, k_prev);
+                    else
+                        load_b(setc, nt, ch, k_this);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kDma; ++j)
+                if (P::dma_pos(j) == f)
+                    dma(j, nx3, k_dma);
+            // the LDS read kRA fragments ahead (into tile t+1 past the barrier)
+            if (f + kRA < kFr)
+                read_frag(f + kRA, cur);
+            else
+                read_frag(f + kRA - kFr, nx1);
+            // this fragment's MFMAs
+            const int st = f / kMT, mt = f % kMT;
+            const Frag &a = ring[f % (kRA + 1)];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                if constexpr (DT == kDtypeBf16)
+                    mfma_acc(acc[mt][nt], breg[SET][nt][st], a);
+                else
+                    mfma_acc(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Main loop unrolled by DB (the B set of every k-tile is a compile-time
+    // index); the remaining ntiles % DB k-tiles follow.
+    int t = 0;
+    for (; t + DB <= ntiles; t += DB) {
+        tile(std::integral_constant<int, 0>{}, t);
+        tile(std::integral_constant<int, 1>{}, t + 1);
+        if constexpr (DB > 2)
+            tile(std::integral_constant<int, (DB > 2 ? 2 : 0)>{}, t + 2);
+        if constexpr (DB > 3)
+            tile(std::integral_constant<int, (DB > 3 ? 3 : 0)>{}, t + 3);
+    }
+    if (t < ntiles)
+        tile(std::integral_constant<int, 0>{}, t++);
+    if constexpr (DB > 2)
+        if (t < ntiles)
+            tile(std::integral_constant<int, 1>{}, t++);
+    if constexpr (DB > 3)
+        if (t < ntiles)
+            tile(std::integral_constant<int, (DB > 3 ? 2 : 0)>{}, t++);
+    // Drain: outstanding copies write LDS; the last MFMAs must finish before
+    // their accumulators are read (the compiler does not count these
+    // instructions as MFMAs, so it inserts no wait states for them).
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    float scale = 1.0f;
+    if constexpr (SCALE == kScaleTensor)
+        scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+        const int m = m0 + mt * 16 + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const int n = n0 + wave * (TN / NW) + nt * 16 + (lane >> 4) * 4;
+            f32x4 v = acc[mt][nt];
+            if constexpr (SCALE == kScaleTensor)
+                v = v * scale;
+            store_tile<OUT>(p, split, m, n, v);
+        }
+    }
+}
+
+template <int DT, int SCALE, int OUT, int DB, int SWZ>
+void launch_w4(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ><<<grid, 256, 0, s>>>(a);
+}
+
+// Table entries: the LDS layout rides in preload_vmem (0 operand blocks,
+// 1 swizzled rows) until the schedule settles on one.
+#define DGP_W4(DT, SC, OUT, DB, SWZ)                                                          \
+    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, SWZ, w4::kRA, DB, kSchedW4, &launch_w4<DT, SC, OUT, DB, SWZ>}
+#define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ) DGP_W4(DT, SC, kOutBf16, DB, SWZ), DGP_W4(DT, SC, kOutPartial, DB, SWZ)
+
+static const KernelSpec kW4Kernels[] = {
+    // one wave per SIMD, 256 x 256 (B k-tiles in flight, A layout)
+    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 0),
+    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 1),
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 0),
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 1),
+};
+
+const KernelSpec *w4_kernels(int *count)
+{
+    *count = (int)(sizeof(kW4Kernels) / sizeof(kW4Kernels[0]));
+    return kW4Kernels;
+}
+
+}  // namespace dgp

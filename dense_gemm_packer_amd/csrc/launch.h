@@ -28,7 +28,7 @@ struct GemmArgs {
 enum Family { kTiled = 0, kStream = 1 };
 
 // Wave schedules of the tiled family (dgp_config.schedule).
-enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3 };
+enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3, kSchedW4 = 4 };
 
 // One compiled kernel configuration.
 struct KernelSpec {
@@ -47,11 +47,13 @@ struct KernelSpec {
 };
 
 // The compiled GEMM kernels: the tiled family (gemm_tiled.hip), its
-// both-in-LDS schedule (gemm_lds.hip), the streaming family
-// (gemm_stream.hip), and all of them in one table in that order
-// (dgp_api.cpp) -- the numbering dgp_kernel_info uses.
+// both-in-LDS schedule (gemm_lds.hip), its one-wave-per-SIMD schedule
+// (gemm_w4.hip), the streaming family (gemm_stream.hip), and all of them in
+// one table in that order (dgp_api.cpp) -- the numbering dgp_kernel_info
+// uses.
 const KernelSpec *tiled_kernels(int *count);
 const KernelSpec *lds_kernels(int *count);
+const KernelSpec *w4_kernels(int *count);
 const KernelSpec *stream_kernels(int *count);
 const KernelSpec *kernel_table(int *count);
 

@@ -330,10 +330,10 @@ def test_default_selection(dgp):
 
 def test_schedule_validation(dgp):
     base = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8)
-    for sched in (1, 2, 3):
+    for sched in (1, 2, 3, 4):
         i = dgp.select_kernel(1024, 1024, 1024, dgp.BF16, dgp.SCALE_NONE, 1, dgp.Config(**base, schedule=sched))
         assert dgp.kernels()[i][0].schedule == sched
-    bad = (dgp.Config(**base, schedule=4), dgp.Config(**base, schedule=-1),
+    bad = (dgp.Config(**base, schedule=5), dgp.Config(**base, schedule=-1),
            dgp.Config(**base, schedule=2, preload_dsrd=8),
            dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 1))
     for cfg in bad:
