@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 MALL_BYTES = 256 << 20         # Infinity Cache; cold-cache rotation exceeds 2x this
 METRIC = "TFLOP/s (large M) and GB/s (decode M≤16) at 1 GPU; % of MFMA / HBM roofline"
 PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_4096x4096x8192_traffic.md")
-KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_tiled.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
+KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_w4.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
                   "dense_gemm_packer_amd/csrc/common.h"]
 DECODE_PROFILE_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_decode_16x16384x7168_traffic.md")
 DECODE_KERNEL_SOURCES = ["dense_gemm_packer_amd/csrc/gemm_stream.hip", "dense_gemm_packer_amd/csrc/gemm_common.h",
@@ -150,7 +150,8 @@ def main():
                          "(M=16, N=16384, K=7168, split 4: pass 1 writing fp32 partials, then the reduce)")
     ap.add_argument("--profile-compare", action="store_true",
                     help="run only a 256 MiB probe copy, then for bf16 and fp8 4096x4096x8192: 3 launches each "
-                         "of the default kernel, the 4-wave kernel and the vendor library (for counter runs)")
+                         "of the built-in kernel, the 4-wave kernel with A in operand blocks, the 8-wave kernel "
+                         "and the vendor library (for counter runs)")
     ap.add_argument("--profile-decode-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and three fp8 decode launches "
                          "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
@@ -177,7 +178,10 @@ def main():
                        "fp4": torch.float4_e2m1fn_x2}[dtype]).to(dev)
 
     if args.profile_compare:
-        w4 = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8, schedule=4, prefetch=3)
+        base = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8)
+        variants = (None,                                          # built-in: 4 waves, swizzled A rows
+                    dict(base, schedule=4, a_layout=1),            # 4 waves, A in operand blocks
+                    dict(base, schedule=1, prefetch=2))            # 8 waves, interleaved
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -193,10 +197,9 @@ def main():
             sc = () if dt == "bf16" else (torch.from_numpy(wl["sA"]).to(dev), torch.from_numpy(wl["sB"]).to(dev))
             one = torch.ones((), device=dev)
             torch.cuda.synchronize()
-            for _ in range(3):
-                dgp.gemm_preshuffle(Al, Bsl, *sc, out=Cl)
-            for _ in range(3):
-                dgp.gemm_preshuffle(Al, Bsl, *sc, out=Cl, config=w4)
+            for cfg in variants:
+                for _ in range(3):
+                    dgp.gemm_preshuffle(Al, Bsl, *sc, out=Cl, config=cfg)
             for _ in range(3):
                 if dt == "bf16":
                     torch.nn.functional.linear(Al, Bl)
@@ -204,8 +207,9 @@ def main():
                     torch._scaled_mm(Al, Bl.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
             torch.cuda.synchronize()
             del Al, Bsl, Bl, Cl
-        log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 x default kernel, "
-            "3 x 4-wave kernel (B 3 k-tiles ahead), 3 x vendor library")
+        log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 launches each of the "
+            "built-in kernel (4 waves, swizzled A rows), the 4-wave kernel with A in operand blocks, the 8-wave "
+            "interleaved kernel, and the vendor library")
         return 0
 
     if args.profile_decode_traffic:
@@ -365,7 +369,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(K) rounded to bf16)",
         "config": {"workload": "bf16 GEMM C=A*B^T, M=N=4096, K=8192, B preshuffled, fp32 accumulate, bf16 out",
-                   "M": M, "N": N, "K": K, "tile": "256x256x128", "parallelism": "single GPU"},
+                   "M": M, "N": N, "K": K, "tile": "256x256x128, 4 waves", "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -22,9 +22,9 @@
 //
 // Schedule (one wave per SIMD: nothing else hides a stall, so the order is
 // fixed with scheduling fences).  A k-tile is kFr fragments (A fragment f =
-// row tile f % 16 of MFMA k-step f / 16), each followed by its 4 MFMAs (one
-// per 16-column strip).  The LDS read of fragment f + 7 is issued before the
-// MFMAs of fragment f.  A ring of 4 LDS stages: the workgroup barrier that
+// row tile f % 16 of MFMA k-step f / 16), each with its 4 MFMAs (one per
+// 16-column strip).  The LDS read of fragment f + 7 is issued after the
+// first MFMA of fragment f, global loads after the second and third.  A ring of 4 LDS stages: the workgroup barrier that
 // certifies tile t+1 sits 7 fragments before the end of tile t, right where
 // the reads of tile t+1 begin, and the copy of tile t+3 (into the stage tile
 // t-1 used) follows it.  Every global load has a fixed fragment position, so
@@ -239,37 +239,48 @@ gemm_w4_kernel(const GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
             if (f == kBar)
                 asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
-            // this position's global loads
+            // The fragment's 4 MFMAs with one slot of other work between each
+            // two (one wave per SIMD issues in order: work bunched between
+            // two fragments would leave the matrix pipe idle): the LDS read
+            // kRA fragments ahead (into tile t+1 past the barrier), then
+            // this position's B reloads, then its A copies.
+            const int st = f / kMT, mt = f % kMT;
+            const Frag &a = ring[f % (kRA + 1)];
+            auto mf = [&](int nt) {
+                if constexpr (DT == kDtypeBf16)
+                    mfma_acc(acc[mt][nt], breg[SET][nt][st], a);
+                else
+                    mfma_acc(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a);
+            };
+            mf(0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (f + kRA < kFr)
+                read_frag(f + kRA, cur);
+            else
+                read_frag(f + kRA - kFr, nx1);
+            __builtin_amdgcn_sched_barrier(0);
+            mf(1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < P::kBLoads; ++i) {
                 if (P::bload_pos(i) == f) {
-                    const int st = i / (kNT * kStepCh), r = i % (kNT * kStepCh);
-                    const int ch = st * kStepCh + r / kNT, nt = r % kNT;
+                    const int st2 = i / (kNT * kStepCh), r = i % (kNT * kStepCh);
+                    const int ch = st2 * kStepCh + r / kNT, nt = r % kNT;
                     if (P::bload_wraps(i))
                         load_b(std::integral_constant<int, PREV>{}, nt, ch, k_prev);
                     else
                         load_b(setc, nt, ch, k_this);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            mf(2);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kDma; ++j)
                 if (P::dma_pos(j) == f)
                     dma(j, nx3, k_dma);
-            // the LDS read kRA fragments ahead (into tile t+1 past the barrier)
-            if (f + kRA < kFr)
-                read_frag(f + kRA, cur);
-            else
-                read_frag(f + kRA - kFr, nx1);
-            // this fragment's MFMAs
-            const int st = f / kMT, mt = f % kMT;
-            const Frag &a = ring[f % (kRA + 1)];
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                if constexpr (DT == kDtypeBf16)
-                    mfma_acc(acc[mt][nt], breg[SET][nt][st], a);
-                else
-                    mfma_acc(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            mf(3);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -303,16 +314,58 @@ gemm_w4_kernel(const GemmArgs p)
     float scale = 1.0f;
     if constexpr (SCALE == kScaleTensor)
         scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
+    if constexpr (OUT == kOutBf16) {
+        // bf16 C through LDS, so that every store writes whole 128-byte
+        // lines: the wave's 256 x 64 block is exactly one line per row.
+        // Each wave stages its block in its own 32 KiB of the (now idle) A
+        // ring, row r at byte 128r with 16-byte chunk c stored at chunk
+        // c ^ ((r >> 1) & 7), the swizzle of the A tile: the 8-byte writes
+        // (lane l: row l%16 of a row tile, columns 4(l/16)..+3 of a strip)
+        // and the 16-byte reads (8 lanes per row) are both conflict-free.
+        // All waves must be done with the ring first (their last LDS reads
+        // and copies): the wait above drained this wave's copies, the
+        // barrier covers the others'.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        uint8_t *cst = lds + wave * (TM * 128);
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        const int m = m0 + mt * 16 + (lane & 15);
+        for (int mt = 0; mt < kMT; ++mt) {
+            const int r = mt * 16 + (lane & 15);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const int n = n0 + wave * (TN / NW) + nt * 16 + (lane >> 4) * 4;
-            f32x4 v = acc[mt][nt];
-            if constexpr (SCALE == kScaleTensor)
-                v = v * scale;
-            store_tile<OUT>(p, split, m, n, v);
+            for (int nt = 0; nt < kNT; ++nt) {
+                f32x4 v = acc[mt][nt];
+                if constexpr (SCALE == kScaleTensor)
+                    v = v * scale;
+                u32x2 packed;
+                packed.x = pack_bf16x2(v.x, v.y);
+                packed.y = pack_bf16x2(v.z, v.w);
+                const int c = 2 * nt + (lane >> 5);              // 16-byte chunk of the row
+                *reinterpret_cast<u32x2 *>(cst + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * ((lane >> 4) & 1)) =
+                    packed;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own rows only: no barrier needed
+        const int ncol = n0 + wave * (TN / NW) + 8 * (lane & 7);
+        const bool col_ok = ncol < p.N;                       // N % 16 == 0: 8 columns in or out together
+#pragma unroll
+        for (int q = 0; q < TM / 8; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            const i32x4 d = *reinterpret_cast<const i32x4 *>(cst + r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+            const int m = m0 + r;
+            if (col_ok && m < p.M)
+                *reinterpret_cast<i32x4 *>(static_cast<uint8_t *>(p.C) + ((int64_t)m * p.N + ncol) * 2) = d;
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+            const int m = m0 + mt * 16 + (lane & 15);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const int n = n0 + wave * (TN / NW) + nt * 16 + (lane >> 4) * 4;
+                f32x4 v = acc[mt][nt];
+                if constexpr (SCALE == kScaleTensor)
+                    v = v * scale;
+                store_tile<OUT>(p, split, m, n, v);
+            }
         }
     }
 }
@@ -323,18 +376,19 @@ void launch_w4(const GemmArgs &a, dim3 grid, hipStream_t s)
     gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ><<<grid, 256, 0, s>>>(a);
 }
 
-// Table entries: the LDS layout rides in preload_vmem (0 operand blocks,
-// 1 swizzled rows) until the schedule settles on one.
 #define DGP_W4(DT, SC, OUT, DB, SWZ)                                                          \
-    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, SWZ, w4::kRA, DB, kSchedW4, &launch_w4<DT, SC, OUT, DB, SWZ>}
+    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, 0, w4::kRA, DB, kSchedW4, &launch_w4<DT, SC, OUT, DB, SWZ>, \
+     SWZ ? kLaySwizzled : kLayBlocks}
 #define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ) DGP_W4(DT, SC, kOutBf16, DB, SWZ), DGP_W4(DT, SC, kOutPartial, DB, SWZ)
 
 static const KernelSpec kW4Kernels[] = {
-    // one wave per SIMD, 256 x 256 (B k-tiles in flight, A layout)
-    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 0),
+    // one wave per SIMD, 256 x 256 (B k-tiles in flight, A layout); the
+    // swizzled-row layout first: it is the tuned one (whole-line copies),
+    // the operand-block layout is kept to measure against
     DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 1),
-    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 0),
+    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 0),
     DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 1),
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 0),
 };
 
 const KernelSpec *w4_kernels(int *count)

@@ -30,6 +30,11 @@ enum Family { kTiled = 0, kStream = 1 };
 // Wave schedules of the tiled family (dgp_config.schedule).
 enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3, kSchedW4 = 4 };
 
+// A's layout in LDS (tiled kernels; dgp_config.a_layout - 1): 1 KiB operand
+// blocks (gemm_common.h), or row-major 128-byte rows with XOR-swizzled
+// 16-byte chunks (gemm_w4.hip).
+enum ALayout { kLayBlocks = 0, kLaySwizzled = 1 };
+
 // One compiled kernel configuration.
 struct KernelSpec {
     int family;
@@ -42,8 +47,9 @@ struct KernelSpec {
     int p0, p1;     // family-specific: tiled = (wm, wn); stream = (strips per wave, depth)
     int pv, pd;     // scheduling hint pair (tiled)
     int depth;      // prefetch distance: k-tiles (tiled) / steps (stream)
-    int sched;      // tiled: kSchedInterleaved or kSchedPingPong; stream: 0
+    int sched;      // tiled: kSchedInterleaved, kSchedPingPong, kSchedBothLds or kSchedW4; stream: 0
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
+    int lay = 0;    // tiled: A's LDS layout, kLayBlocks or kLaySwizzled
 };
 
 // The compiled GEMM kernels: the tiled family (gemm_tiled.hip), its

@@ -138,6 +138,14 @@ typedef enum dgp_scale_mode {
  *                    Must be 0 for the streaming kernel.  Zero-initialising
  *                    the whole struct and setting tile_m = 0 selects the
  *                    built-in table, like NULL. */
+/*   a_layout       : tiled kernels: A's layout in LDS.  1 = 1 KiB operand
+ *                    blocks (one async copy instruction = 16 rows x 64
+ *                    bytes); 2 = row-major 128-byte rows with the 16-byte
+ *                    chunks XOR-swizzled (one instruction = 8 whole rows,
+ *                    the layout of [P1] "Changes" item 2); 0 = the tile's
+ *                    tuned choice.  Schedules 1-3 use operand blocks;
+ *                    schedule 4 compiles both.  Must be 0 for the 16-row
+ *                    kernels. */
 typedef struct dgp_config {
     int tile_m;
     int tile_n;
@@ -149,6 +157,7 @@ typedef struct dgp_config {
     int waves_m;
     int prefetch;
     int schedule;
+    int a_layout;
 } dgp_config;
 
 /*

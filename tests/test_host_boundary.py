@@ -254,7 +254,7 @@ def test_kernel_table(dgp, L):
     seen = set()
     for cfg, dt, sm, split_out in ks:
         key = (cfg.tile_m, cfg.tile_n, cfg.tile_k, cfg.waves_m, cfg.prefetch, cfg.preload_vmem,
-               cfg.preload_dsrd, cfg.schedule, dt, sm, split_out)
+               cfg.preload_dsrd, cfg.schedule, cfg.a_layout, dt, sm, split_out)
         assert key not in seen
         seen.add(key)
         assert (dt, sm) in ((0, 0), (1, 1), (1, 2), (1, 3), (2, 4))
@@ -292,7 +292,8 @@ def test_default_selection(dgp):
     # Headline shapes take a 256x256 tile; empty calls launch nothing.
     for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
         cfg = dgp.kernels()[dgp.select_kernel(4096, 4096, 8192, dt, sm)][0]
-        assert (cfg.tile_m, cfg.tile_n) == (256, 256)
+        # the one-wave-per-SIMD tile with swizzled A rows
+        assert (cfg.tile_m, cfg.tile_n, cfg.schedule, cfg.a_layout) == (256, 256, 4, 2)
     # blockscale, mxfp8 and mxfp4: the tiled kernels above decode-sized M,
     # the 16-row tiles at it
     for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
@@ -333,7 +334,13 @@ def test_schedule_validation(dgp):
     for sched in (1, 2, 3, 4):
         i = dgp.select_kernel(1024, 1024, 1024, dgp.BF16, dgp.SCALE_NONE, 1, dgp.Config(**base, schedule=sched))
         assert dgp.kernels()[i][0].schedule == sched
+    for lay in (1, 2):
+        i = dgp.select_kernel(1024, 1024, 1024, dgp.BF16, dgp.SCALE_NONE, 1,
+                              dgp.Config(**base, schedule=4, a_layout=lay))
+        assert dgp.kernels()[i][0].a_layout == lay
     bad = (dgp.Config(**base, schedule=5), dgp.Config(**base, schedule=-1),
+           dgp.Config(**base, schedule=4, a_layout=3), dgp.Config(**base, schedule=1, a_layout=2),
+           dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 0, 1),
            dgp.Config(**base, schedule=2, preload_dsrd=8),
            dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 1))
     for cfg in bad:
