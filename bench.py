@@ -64,8 +64,9 @@ class GfxClock:
 
     def mhz(self):
         """Shader clock (MHz) and socket power (W) from the device's metrics
-        table: the mean of the per-XCD current clocks and the firmware's
-        average; meaningful when read while kernels are running."""
+        table: the mean of the per-XCD current clocks; meaningful when read
+        while kernels are running.  The table is refreshed at intervals of
+        tens to hundreds of ms, so reads close together repeat a value."""
         if self.h is None:
             return None
         try:
@@ -84,6 +85,27 @@ class GfxClock:
             return out or None
         except Exception:
             return None
+
+
+def clock_under_load(torch, clock, fn, ms):
+    """Sample the gfx clock every ~100 ms while fn() runs back to back for
+    `ms` milliseconds (outside any timed region).  The metrics table refreshes
+    at intervals of its own, so only the distinct readings are kept."""
+    seen = []
+    t0 = time.perf_counter()
+    next_read = 0.0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            fn()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= next_read:
+            r = clock.mhz()
+            if r and r not in seen:
+                seen.append(r)
+            next_read = el + 100.0
+        torch.cuda.synchronize()
+    cur = [r["current"] for r in seen if "current" in r]
+    return {"readings": seen, "max_current": max(cur) if cur else None}
 
 
 def launch_stats(np, launch_ms):
@@ -136,7 +158,10 @@ def main():
     # whatever --warmup is.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--settle-ms", type=float, default=250.0,
+    ap.add_argument("--clock-ms", type=float, default=1500.0,
+                    help="after the timed steps, run the same GEMM this long while sampling the gfx clock "
+                         "(0: skip)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="run the headline GEMM for at least this long before the warm-up (clock settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
@@ -264,7 +289,7 @@ def main():
             dgp.probe_copy(src, dst)
         for _ in range(3):
             dgp.gemm_preshuffle(A, Bs, out=C)
-        plain = dgp.Config(tile_m=256, tile_n=256, tile_k=128, xcd_remap=0, group_m=1)
+        plain = dgp.Config(tile_m=256, tile_n=256, tile_k=128, xcd_remap=0, group_m=1, schedule=4, a_layout=2)
         for _ in range(3):
             dgp.gemm_preshuffle(A, Bs, out=C, config=plain)
         torch.cuda.synchronize()
@@ -276,15 +301,13 @@ def main():
     # shader clock ramps for tens of ms after the chip leaves idle, so the
     # same GEMM runs for at least --settle-ms first (reported as settle_ms).
     clock = GfxClock(torch)
-    sclk = {"idle": clock.mhz()}
+    sclk = {"before": clock.mhz()}
     t0 = time.perf_counter()
     settle_launches = 0
     while True:
         for _ in range(10):
             dgp.gemm_preshuffle(A, Bs, out=C)
         settle_launches += 10
-        if (time.perf_counter() - t0) * 1e3 >= 0.8 * args.settle_ms:
-            sclk["under_settle_load"] = clock.mhz()   # read while the queued GEMMs run
         torch.cuda.synchronize()
         settle_ms = (time.perf_counter() - t0) * 1e3
         if settle_ms >= args.settle_ms:
@@ -300,10 +323,11 @@ def main():
         s.record(stream)
         dgp.gemm_preshuffle(A, Bs, out=C)
         e.record(stream)
-    sclk["under_timed_load"] = clock.mhz()   # the timed launches are still queued
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sclk["after"] = clock.mhz()
+    if args.clock_ms > 0:
+        sclk["under_load"] = clock_under_load(torch, clock, lambda: dgp.gemm_preshuffle(A, Bs, out=C),
+                                              args.clock_ms)
     launch_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K

@@ -43,6 +43,10 @@ constexpr int kRing = 4;                 // LDS stages
 constexpr int kBuf = TM * KT;            // bytes per stage
 constexpr int kDma = (TM / 16) * kCH / NW;   // async copies per wave per k-tile
 constexpr int kRA = 7;                   // fragments read ahead of their MFMAs
+// Where a k-tile's A copy is issued: right after the barrier that frees its
+// stage, 3 k-tiles ahead (false), or early in the next k-tile, 2 ahead (true).
+constexpr bool kDmaLate = false;
+constexpr int kDmaAhead = kDmaLate ? 2 : 3;
 static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
 
 template <int DT>
@@ -52,9 +56,10 @@ struct Plan {
     static constexpr int kFr = kSteps * kMT;              // A fragments per k-tile
     static constexpr int kBar = kFr - kRA;                // barrier position
     static_assert(kFr % (kRA + 1) == 0, "the fragment ring must wrap at the k-tile boundary");
-    // Global loads at fixed fragment positions.  Copy j of tile t+3 after the
-    // barrier, spread over the last kRA fragments.
-    static constexpr int dma_pos(int j) { return kBar + (j * kRA) / kDma; }
+    // Global loads at fixed fragment positions.  Copy j of tile t+kDmaAhead:
+    // after the barrier, spread over the last kRA fragments, or (kDmaLate)
+    // spread over the fragments before the barrier.
+    static constexpr int dma_pos(int j) { return kDmaLate ? (j * kBar) / kDma : kBar + (j * kRA) / kDma; }
     // B reloads: the chunks of a step are reloaded for tile t+kDB right after
     // that step's last MFMA -- one load per fragment, starting at the next
     // fragment; the last step's reloads wrap into the next k-tile.
@@ -64,18 +69,16 @@ struct Plan {
         return ((i / (kNT * kStepCh)) * kMT + kMT + i % (kNT * kStepCh)) % kFr;
     }
     static constexpr bool bload_wraps(int i) { return (i / (kNT * kStepCh)) == kSteps - 1; }
-    // Loads issued after the last copy of tile t+1 (tile t-2, fragment kFr-1)
-    // up to the barrier of tile t+1 (tile t, fragment kBar): the rest of tile
-    // t-2, all of tile t-1, and tile t before the barrier.
+    // Loads issued after the last copy of tile t+1 (in tile t+1-kDmaAhead)
+    // up to the barrier of tile t+1 (tile t, fragment kBar).  Within a
+    // fragment position the B reloads precede the copies.
     static constexpr int vm_at_barrier()
     {
         int n = 0;
-        for (int j = 0; j < kDma; ++j) {   // tile t-2 after its last copy: later copies only
-            if (dma_pos(j) > dma_pos(kDma - 1))
-                ++n;
-        }
-        n += kDma + kBLoads;               // tile t-1
-        for (int i = 0; i < kBLoads; ++i)  // tile t before the barrier
+        for (int i = 0; i < kBLoads; ++i)   // the copies' tile, after its last copy
+            n += bload_pos(i) > dma_pos(kDma - 1) ? 1 : 0;
+        n += (kDmaAhead - 2) * (kDma + kBLoads);   // whole k-tiles in between
+        for (int i = 0; i < kBLoads; ++i)   // tile t before the barrier
             n += bload_pos(i) < kBar ? 1 : 0;
         for (int j = 0; j < kDma; ++j)
             n += dma_pos(j) < kBar ? 1 : 0;
@@ -201,10 +204,10 @@ gemm_w4_kernel(const GemmArgs p)
         }
     };
 
-    // Prologue: copies of tiles 0..2, B of tiles 0..DB-1, all landed; then
-    // the first kRA fragments of tile 0.
+    // Prologue: copies of tiles 0..kDmaAhead-1, B of tiles 0..DB-1, all
+    // landed; then the first kRA fragments of tile 0.
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < kDmaAhead; ++t)
 #pragma unroll
         for (int j = 0; j < kDma; ++j)
             dma(j, stage(t), kofs(t));
@@ -232,8 +235,8 @@ gemm_w4_kernel(const GemmArgs p)
     auto tile = [&](auto setc, int t) {
         constexpr int SET = decltype(setc)::value;
         constexpr int PREV = (SET + kDB - 1) % kDB;
-        const uint32_t cur = stage(t), nx1 = stage(t + 1), nx3 = stage(t + 3);
-        const uint32_t k_prev = kofs(t - 1 + kDB), k_this = kofs(t + kDB), k_dma = kofs(t + 3);
+        const uint32_t cur = stage(t), nx1 = stage(t + 1), nx3 = stage(t + kDmaAhead);
+        const uint32_t k_prev = kofs(t - 1 + kDB), k_this = kofs(t + kDB), k_dma = kofs(t + kDmaAhead);
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
             __builtin_amdgcn_sched_barrier(0);
