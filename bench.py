@@ -150,6 +150,52 @@ def read_traffic(path=PROFILE_FILE, sources=KERNEL_SOURCES):
         return None
 
 
+# The built-in large-M kernel and the design choices it is measured against
+# (dgp_config fields; None = the built-in choice).
+_W4 = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8, schedule=4)
+ABLATIONS = (
+    ("built-in (4 waves, swizzled A rows, async copy, read-ahead 7, interleaved issue)", None),
+    ("A in operand blocks (16 rows x 64 bytes per copy instruction)", dict(_W4, a_layout=1)),
+    ("A copied through registers (buffer load + ds_write)", dict(_W4, a_layout=2, a_copy=2)),
+    ("LDS read-ahead 3", dict(_W4, a_layout=2, preload_vmem=1, preload_dsrd=3)),
+    ("LDS read-ahead 1", dict(_W4, a_layout=2, preload_vmem=1, preload_dsrd=1)),
+    ("fragment work bunched ahead of its MFMAs", dict(_W4, a_layout=2, preload_vmem=0, preload_dsrd=7)),
+    ("8 waves (2 per SIMD), interleaved", dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8,
+                                                schedule=1, prefetch=2)),
+)
+
+
+def run_ablations(dgp, torch, np, synth, to_dev, dev):
+    """Median launch (us) of every ablation, bf16 and fp8 4096x4096x8192,
+    three alternating rounds; every output equals the built-in one bit for bit."""
+    out = {}
+    for name in ("bf16_large", "fp8_large"):
+        w = synth.workload_inputs(name)
+        dt = w["dtype"]
+        A = to_dev(w["A"], dt)
+        Bs = dgp.preshuffle_b(to_dev(w["B"], dt))
+        sc = () if dt == "bf16" else (torch.from_numpy(w["sA"]).to(dev), torch.from_numpy(w["sB"]).to(dev))
+        res = {n: [] for n, _ in ABLATIONS}
+        ref = None
+        for rnd in range(3):
+            order = ABLATIONS if rnd % 2 == 0 else ABLATIONS[::-1]
+            for n, cfg in order:
+                C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device=dev)
+                st = launch_time_us(torch, np, lambda: dgp.gemm_preshuffle(A, Bs, *sc, out=C, config=cfg),
+                                    n=20, settle_ms=100.0)
+                res[n].append(st["median"])
+                if ref is None:
+                    ref = C
+                elif not torch.equal(C.view(torch.int16), ref.view(torch.int16)):
+                    raise RuntimeError(f"{name}: {n} differs from the first variant")
+        fl = 2.0 * w["M"] * w["N"] * w["K"]
+        out[dt] = {n: {"us_median_of_rounds": round(float(np.median(v)), 1),
+                       "TFLOP/s": round(fl / (np.median(v) * 1e-6) / 1e12, 1)} for n, v in res.items()}
+        log(f"ablations {dt}: " + "; ".join(f"{n}: {v['us_median_of_rounds']} us" for n, v in out[dt].items()))
+        del A, Bs
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,8 +221,10 @@ def main():
                          "(M=16, N=16384, K=7168, split 4: pass 1 writing fp32 partials, then the reduce)")
     ap.add_argument("--profile-compare", action="store_true",
                     help="run only a 256 MiB probe copy, then for bf16 and fp8 4096x4096x8192: 3 launches each "
-                         "of the built-in kernel, the 4-wave kernel with A in operand blocks, the 8-wave kernel "
-                         "and the vendor library (for counter runs)")
+                         "of the built-in kernel, each design ablation and the vendor library (for counter runs)")
+    ap.add_argument("--ablations", action="store_true",
+                    help="time the built-in 4096x4096x8192 kernel against each design ablation (bf16 and fp8; "
+                         "median launch after a clock settle, alternating rounds) and print one JSON line")
     ap.add_argument("--profile-decode-traffic", action="store_true",
                     help="run only a 256 MiB probe copy and three fp8 decode launches "
                          "(M=16, N=16384, K=7168, split 1; each on its own copy of the weight)")
@@ -203,10 +251,7 @@ def main():
                        "fp4": torch.float4_e2m1fn_x2}[dtype]).to(dev)
 
     if args.profile_compare:
-        base = dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8)
-        variants = (None,                                          # built-in: 4 waves, swizzled A rows
-                    dict(base, schedule=4, a_layout=1),            # 4 waves, A in operand blocks
-                    dict(base, schedule=1, prefetch=2))            # 8 waves, interleaved
+        variants = tuple(v for _, v in ABLATIONS)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -232,9 +277,13 @@ def main():
                     torch._scaled_mm(Al, Bl.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
             torch.cuda.synchronize()
             del Al, Bsl, Bl, Cl
-        log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 launches each of the "
-            "built-in kernel (4 waves, swizzled A rows), the 4-wave kernel with A in operand blocks, the 8-wave "
-            "interleaved kernel, and the vendor library")
+        log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 launches each of "
+            + ", ".join(n for n, _ in ABLATIONS) + ", then the vendor library")
+        return 0
+
+    if args.ablations:
+        print(json.dumps({"ablations_4096x4096x8192": run_ablations(dgp, torch, np, synth, to_dev, dev)}),
+              flush=True)
         return 0
 
     if args.profile_decode_traffic:

@@ -44,12 +44,12 @@ class DgpError(RuntimeError):
 
 class Config(ctypes.Structure):
     """dgp_config: tile_m/tile_n/tile_k, xcd_remap, group_m, preload pair, waves_m, prefetch, schedule,
-    a_layout."""
+    a_layout, a_copy."""
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("xcd_remap", ctypes.c_int), ("group_m", ctypes.c_int),
                 ("preload_vmem", ctypes.c_int), ("preload_dsrd", ctypes.c_int),
                 ("waves_m", ctypes.c_int), ("prefetch", ctypes.c_int), ("schedule", ctypes.c_int),
-                ("a_layout", ctypes.c_int)]
+                ("a_layout", ctypes.c_int), ("a_copy", ctypes.c_int)]
 
 
 # Every symbol include/dgp.h and include/dgp_diag.h declare.
@@ -417,9 +417,12 @@ def describe_kernel(index: int) -> str:
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
     sched = {1: f"interleaved, LDS read-ahead {cfg.preload_dsrd}", 2: "ping-pong",
              3: f"A and B in LDS, LDS read-ahead {cfg.preload_dsrd}",
-             4: f"4 waves (1 per SIMD), AGPR accumulators, LDS read-ahead {cfg.preload_dsrd}"}[cfg.schedule]
+             4: f"4 waves (1 per SIMD), AGPR accumulators, LDS read-ahead {cfg.preload_dsrd}, "
+                f"{'interleaved' if cfg.preload_vmem else 'bunched'} issue"}[cfg.schedule]
     lay = {1: "A in operand blocks", 2: "A in swizzled rows"}.get(cfg.a_layout, "")
     sched = f"{sched}, {lay}" if cfg.schedule == 4 and lay else sched
+    if cfg.a_copy == 2:
+        sched += ", A copied through registers"
     kname = {1: "tiled", 2: "pingpong", 3: "lds", 4: "w4"}[cfg.schedule]
     return (f"gemm_{kname}_kernel<{dts}, {cfg.tile_m}x{cfg.tile_n} tile, "
             f"{cfg.tile_k}-byte k-tile, waves_m {cfg.waves_m}, prefetch {cfg.prefetch}, {sched}"

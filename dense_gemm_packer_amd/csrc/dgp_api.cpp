@@ -121,7 +121,7 @@ bool spec_fits(const KernelSpec &k, int64_t Ks)
 // A kernel-table query; -1 in a field means "any".
 struct Query {
     int family, dtype, scale, out, tm, tn;
-    int kt = -1, wm = -1, depth = -1, pv = -1, pd = -1, sched = -1, lay = -1;
+    int kt = -1, wm = -1, depth = -1, pv = -1, pd = -1, sched = -1, lay = -1, copy = -1;
 };
 
 const KernelSpec *find_spec(const Query &q)
@@ -134,7 +134,8 @@ const KernelSpec *find_spec(const Query &q)
         if (k.family == q.family && k.dtype == q.dtype && k.scale == q.scale && k.out == q.out && k.tm == q.tm &&
             k.tn == q.tn && (q.kt < 0 || k.kt == q.kt) && (q.wm < 0 || wm == q.wm) &&
             (q.depth < 0 || k.depth == q.depth) && (q.pv < 0 || k.pv == q.pv) && (q.pd < 0 || k.pd == q.pd) &&
-            (q.sched < 0 || k.sched == q.sched) && (q.lay < 0 || (k.family == kTiled && k.lay == q.lay)))
+            (q.sched < 0 || k.sched == q.sched) && (q.lay < 0 || (k.family == kTiled && k.lay == q.lay)) &&
+            (q.copy < 0 || (k.family == kTiled && k.copy == q.copy)))
             return &k;
     }
     return nullptr;
@@ -243,6 +244,8 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
             return fail(DGP_ERR_CONFIG, "schedule must be 0, 1, 2, 3 or 4 (got %d)", c.cfg->schedule);
         if (c.cfg->a_layout < 0 || c.cfg->a_layout > 2)
             return fail(DGP_ERR_CONFIG, "a_layout must be 0, 1 or 2 (got %d)", c.cfg->a_layout);
+        if (c.cfg->a_copy < 0 || c.cfg->a_copy > 2)
+            return fail(DGP_ERR_CONFIG, "a_copy must be 0, 1 or 2 (got %d)", c.cfg->a_copy);
         Query q{fam, c.dtype, c.scale, out, c.cfg->tile_m, c.cfg->tile_n};
         if (fam == kTiled) {
             q.kt = c.cfg->tile_k;
@@ -258,13 +261,14 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
                 q.sched = c.cfg->schedule;
             if (c.cfg->a_layout > 0)
                 q.lay = c.cfg->a_layout - 1;
+            q.copy = c.cfg->a_copy > 0 ? c.cfg->a_copy - 1 : kCopyAsync;
         } else {
             if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0)
                 return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
             if (c.cfg->schedule != 0)
                 return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel has no schedule choice");
-            if (c.cfg->a_layout != 0)
-                return fail(DGP_ERR_CONFIG, "the 16-row kernels have no A layout choice");
+            if (c.cfg->a_layout != 0 || c.cfg->a_copy != 0)
+                return fail(DGP_ERR_CONFIG, "the 16-row kernels have no A layout or copy choice");
             q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;   // matched against waves per workgroup
             q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
         }
@@ -272,8 +276,9 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
         if (!spec)
             return fail(DGP_ERR_CONFIG,
                         "no compiled kernel for tile %dx%dx%d (waves_m %d, prefetch %d, preload %d,%d, schedule %d, "
-                        "a_layout %d) with this dtype/scale", c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k, c.cfg->waves_m,
-                        c.cfg->prefetch, c.cfg->preload_vmem, c.cfg->preload_dsrd, c.cfg->schedule, c.cfg->a_layout);
+                        "a_layout %d, a_copy %d) with this dtype/scale", c.cfg->tile_m, c.cfg->tile_n, c.cfg->tile_k,
+                        c.cfg->waves_m, c.cfg->prefetch, c.cfg->preload_vmem, c.cfg->preload_dsrd, c.cfg->schedule,
+                        c.cfg->a_layout, c.cfg->a_copy);
         if (!spec_fits(*spec, Ks))
             return fail(DGP_ERR_CONFIG, "tile_k=%d does not divide the K range of a split (%lld bytes)",
                         spec->kt, (long long)Ks);
@@ -614,6 +619,7 @@ dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mo
     cfg->prefetch = k.depth;
     cfg->schedule = k.sched;
     cfg->a_layout = k.family == kTiled ? k.lay + 1 : 0;
+    cfg->a_copy = k.family == kTiled ? k.copy + 1 : 0;
     *dtype = k.dtype;
     *scale_mode = k.scale;
     *split_out = k.out == kOutPartial ? 1 : 0;

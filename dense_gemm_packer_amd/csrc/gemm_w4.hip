@@ -42,24 +42,28 @@ constexpr int kCH = KT / 64;             // 64-byte chunks per k-tile
 constexpr int kRing = 4;                 // LDS stages
 constexpr int kBuf = TM * KT;            // bytes per stage
 constexpr int kDma = (TM / 16) * kCH / NW;   // async copies per wave per k-tile
-constexpr int kRA = 7;                   // fragments read ahead of their MFMAs
+constexpr int kRA = 7;                   // tuned LDS read-ahead (fragments ahead of their MFMAs)
 // Where a k-tile's A copy is issued: right after the barrier that frees its
 // stage, 3 k-tiles ahead (false), or early in the next k-tile, 2 ahead (true).
 constexpr bool kDmaLate = false;
 constexpr int kDmaAhead = kDmaLate ? 2 : 3;
 static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
 
-template <int DT>
+template <int DT, int RA>
 struct Plan {
     static constexpr int kStepCh = Op<DT>::kBlocks;       // 64-byte chunks per MFMA step
     static constexpr int kSteps = kCH / kStepCh;          // MFMA k-steps per k-tile
     static constexpr int kFr = kSteps * kMT;              // A fragments per k-tile
-    static constexpr int kBar = kFr - kRA;                // barrier position
-    static_assert(kFr % (kRA + 1) == 0, "the fragment ring must wrap at the k-tile boundary");
+    static constexpr int kBar = kFr - RA;                 // barrier position
+    static_assert(RA >= 1 && kFr % (RA + 1) == 0, "the fragment ring must wrap at the k-tile boundary");
     // Global loads at fixed fragment positions.  Copy j of tile t+kDmaAhead:
-    // after the barrier, spread over the last kRA fragments, or (kDmaLate)
+    // after the barrier, spread over the last RA fragments, or (kDmaLate)
     // spread over the fragments before the barrier.
-    static constexpr int dma_pos(int j) { return kDmaLate ? (j * kBar) / kDma : kBar + (j * kRA) / kDma; }
+    static constexpr int dma_pos(int j) { return kDmaLate ? (j * kBar) / kDma : kBar + (j * RA) / kDma; }
+    // The copy through registers (ablation): the loads sit where the async
+    // copies would, their LDS writes RA fragments earlier in the next k-tile
+    // (before that k-tile's barrier, which waits for them).
+    static constexpr int write_pos(int j) { return dma_pos(j) - RA; }
     // B reloads: the chunks of a step are reloaded for tile t+kDB right after
     // that step's last MFMA -- one load per fragment, starting at the next
     // fragment; the last step's reloads wrap into the next k-tile.
@@ -102,6 +106,13 @@ __device__ inline void mfma_acc(f32x4 &acc, const i32x8 &b, const i32x8 &a)
 }
 
 // DB: B register sets = k-tiles of B loads in flight (2..4).
+// RA: A fragments read from LDS ahead of the MFMAs that consume them.
+// ILV: 1 = a fragment's 4 MFMAs with one slot of other work between each
+// two (the LDS read, the B reloads, the A copies); 0 = all of that work
+// first, then the 4 MFMAs.
+// SYNC: 0 = A copied global -> LDS by the async buffer load; 1 = through
+// registers (buffer load into VGPRs, ds_write a k-tile later): the copy
+// path FlyDSL PR #1008 replaced, kept to measure against.
 // SWZ: A's LDS layout.  0 = the operand-block order of gemm_common.h (one
 // copy instruction = 16 rows x 64 bytes); 1 = row-major 128-byte rows with
 // the 16-byte chunks XOR-swizzled (one copy instruction = 8 whole rows, i.e.
@@ -110,14 +121,16 @@ __device__ inline void mfma_acc(f32x4 &acc, const i32x8 &b, const i32x8 &a)
 // (rows 16mt + i, one chunk each) fall on 16 distinct 16-byte bank groups
 // -- the row-major tile with an XOR swizzle known to writer and reader of
 // FlyDSL PR #1008 "Changes" item 2.
-template <int DT, int SCALE, int OUT, int DB, int SWZ>
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_w4_kernel(const GemmArgs p)
 {
     static_assert(DB >= 2 && DB <= 4, "B sets");
     constexpr int kDB = DB;
     using namespace w4;
-    using P = Plan<DT>;
+    static_assert(!SYNC || (SWZ && !kDmaLate), "the register copy: swizzled rows, copies after the barrier");
+    constexpr int kRA = RA;
+    using P = Plan<DT, RA>;
     using Frag = typename Op<DT>::Frag;
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
     constexpr int kVm = P::vm_at_barrier();
@@ -190,6 +203,12 @@ gemm_w4_kernel(const GemmArgs p)
     auto dma = [&](int j, uint32_t st, uint32_t koff) {
         lds_dma16(rA, lds + st + (j * NW + wave) * 1024, dma_voff[j], koff);
     };
+    // The register copy: the same 16 bytes per lane, to the same LDS place.
+    [[maybe_unused]] i32x4 cp[SYNC ? kDma : 1];
+    auto copy_load = [&](int j, uint32_t koff) { cp[j] = load16<kAuxNone>(rA, dma_voff[j] + koff); };
+    auto copy_write = [&](int j, uint32_t st) {
+        *reinterpret_cast<i32x4 *>(lds + st + (j * NW + wave) * 1024 + lane * 16) = cp[j];
+    };
     auto read_frag = [&](int f, uint32_t st) {   // fragment f of the tile in stage st
         const int s = f / kMT, mt = f % kMT;
         if constexpr (SWZ) {
@@ -205,12 +224,20 @@ gemm_w4_kernel(const GemmArgs p)
     };
 
     // Prologue: copies of tiles 0..kDmaAhead-1, B of tiles 0..DB-1, all
-    // landed; then the first kRA fragments of tile 0.
+    // landed; then the first kRA fragments of tile 0.  (The register copy
+    // loads its last prologue tile into registers: tile 0 writes it.)
 #pragma unroll
     for (int t = 0; t < kDmaAhead; ++t)
 #pragma unroll
-        for (int j = 0; j < kDma; ++j)
+        for (int j = 0; j < kDma; ++j) {
+            if constexpr (SYNC) {
+                if (t == kDmaAhead - 1) {
+                    copy_load(j, kofs(t));
+                    continue;
+                }
+            }
             dma(j, stage(t), kofs(t));
+        }
     auto prologue_b = [&](auto setc) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
@@ -237,11 +264,16 @@ gemm_w4_kernel(const GemmArgs p)
         constexpr int PREV = (SET + kDB - 1) % kDB;
         const uint32_t cur = stage(t), nx1 = stage(t + 1), nx3 = stage(t + kDmaAhead);
         const uint32_t k_prev = kofs(t - 1 + kDB), k_this = kofs(t + kDB), k_dma = kofs(t + kDmaAhead);
+        [[maybe_unused]] const uint32_t nx2 = stage(t + kDmaAhead - 1);   // the register copy's write stage
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
             __builtin_amdgcn_sched_barrier(0);
-            if (f == kBar)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+            if (f == kBar) {
+                if constexpr (SYNC)   // this wave's LDS writes of tile t+1 (and earlier) are done
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else                  // this wave's async copy of tile t+1 has landed
+                    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+            }
             // The fragment's 4 MFMAs with one slot of other work between each
             // two (one wave per SIMD issues in order: work bunched between
             // two fragments would leave the matrix pipe idle): the LDS read
@@ -255,34 +287,60 @@ gemm_w4_kernel(const GemmArgs p)
                 else
                     mfma_acc(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a);
             };
-            mf(0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (f + kRA < kFr)
-                read_frag(f + kRA, cur);
-            else
-                read_frag(f + kRA - kFr, nx1);
-            __builtin_amdgcn_sched_barrier(0);
-            mf(1);
-            __builtin_amdgcn_sched_barrier(0);
+            auto lds_read = [&]() {
+                if (f + kRA < kFr)
+                    read_frag(f + kRA, cur);
+                else
+                    read_frag(f + kRA - kFr, nx1);
+            };
+            auto b_loads = [&]() {
 #pragma unroll
-            for (int i = 0; i < P::kBLoads; ++i) {
-                if (P::bload_pos(i) == f) {
-                    const int st2 = i / (kNT * kStepCh), r = i % (kNT * kStepCh);
-                    const int ch = st2 * kStepCh + r / kNT, nt = r % kNT;
-                    if (P::bload_wraps(i))
-                        load_b(std::integral_constant<int, PREV>{}, nt, ch, k_prev);
-                    else
-                        load_b(setc, nt, ch, k_this);
+                for (int i = 0; i < P::kBLoads; ++i) {
+                    if (P::bload_pos(i) == f) {
+                        const int st2 = i / (kNT * kStepCh), r = i % (kNT * kStepCh);
+                        const int ch = st2 * kStepCh + r / kNT, nt = r % kNT;
+                        if (P::bload_wraps(i))
+                            load_b(std::integral_constant<int, PREV>{}, nt, ch, k_prev);
+                        else
+                            load_b(setc, nt, ch, k_this);
+                    }
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            mf(2);
-            __builtin_amdgcn_sched_barrier(0);
+            };
+            auto a_copies = [&]() {
 #pragma unroll
-            for (int j = 0; j < kDma; ++j)
-                if (P::dma_pos(j) == f)
-                    dma(j, nx3, k_dma);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < kDma; ++j) {
+                    if constexpr (SYNC) {
+                        if (P::write_pos(j) == f)
+                            copy_write(j, nx2);
+                        if (P::dma_pos(j) == f)
+                            copy_load(j, k_dma);
+                    } else if (P::dma_pos(j) == f) {
+                        dma(j, nx3, k_dma);
+                    }
+                }
+            };
+            if constexpr (ILV) {
+                mf(0);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_read();
+                __builtin_amdgcn_sched_barrier(0);
+                mf(1);
+                __builtin_amdgcn_sched_barrier(0);
+                b_loads();
+                __builtin_amdgcn_sched_barrier(0);
+                mf(2);
+                __builtin_amdgcn_sched_barrier(0);
+                a_copies();
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                lds_read();
+                b_loads();
+                a_copies();
+                __builtin_amdgcn_sched_barrier(0);
+                mf(0);
+                mf(1);
+                mf(2);
+            }
             mf(3);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -373,25 +431,38 @@ gemm_w4_kernel(const GemmArgs p)
     }
 }
 
-template <int DT, int SCALE, int OUT, int DB, int SWZ>
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
 void launch_w4(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ><<<grid, 256, 0, s>>>(a);
+    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ, RA, ILV, SYNC><<<grid, 256, 0, s>>>(a);
 }
 
-#define DGP_W4(DT, SC, OUT, DB, SWZ)                                                          \
-    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, 0, w4::kRA, DB, kSchedW4, &launch_w4<DT, SC, OUT, DB, SWZ>, \
-     SWZ ? kLaySwizzled : kLayBlocks}
-#define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ) DGP_W4(DT, SC, kOutBf16, DB, SWZ), DGP_W4(DT, SC, kOutPartial, DB, SWZ)
+// Table entries: preload pair = (ILV, RA), layout, copy path.
+#define DGP_W4(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC)                                           \
+    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, ILV, RA, DB, kSchedW4,                        \
+     &launch_w4<DT, SC, OUT, DB, SWZ, RA, ILV, SYNC>, SWZ ? kLaySwizzled : kLayBlocks,          \
+     SYNC ? kCopyRegs : kCopyAsync}
+#define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ, RA, ILV, SYNC)                                       \
+    DGP_W4(DT, SC, kOutBf16, DB, SWZ, RA, ILV, SYNC), DGP_W4(DT, SC, kOutPartial, DB, SWZ, RA, ILV, SYNC)
 
 static const KernelSpec kW4Kernels[] = {
-    // one wave per SIMD, 256 x 256 (B k-tiles in flight, A layout); the
-    // swizzled-row layout first: it is the tuned one (whole-line copies),
-    // the operand-block layout is kept to measure against
-    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 1),
-    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 0),
-    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 1),
-    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 0),
+    // one wave per SIMD, 256 x 256 (B k-tiles in flight, A layout, LDS
+    // read-ahead, interleaved issue, register copy); the tuned kernel
+    // first, then the ablations the design was measured against: A in
+    // operand blocks, LDS read-ahead 3 and 1, the fragment's work bunched
+    // ahead of its MFMAs, A copied through registers
+    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 1, w4::kRA, 1, 0),
+    DGP_W4_BOTH_OUT(kDtypeBf16, kScaleNone, 3, 0, w4::kRA, 1, 0),
+    DGP_W4(kDtypeBf16, kScaleNone, kOutBf16, 3, 1, 3, 1, 0),
+    DGP_W4(kDtypeBf16, kScaleNone, kOutBf16, 3, 1, 1, 1, 0),
+    DGP_W4(kDtypeBf16, kScaleNone, kOutBf16, 3, 1, w4::kRA, 0, 0),
+    DGP_W4(kDtypeBf16, kScaleNone, kOutBf16, 3, 1, w4::kRA, 1, 1),
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 1, w4::kRA, 1, 0),
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleTensor, 3, 0, w4::kRA, 1, 0),
+    DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, 3, 1, 0),
+    DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, 1, 1, 0),
+    DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 0, 0),
+    DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 1, 1),
 };
 
 const KernelSpec *w4_kernels(int *count)

@@ -35,6 +35,11 @@ enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3, kS
 // 16-byte chunks (gemm_w4.hip).
 enum ALayout { kLayBlocks = 0, kLaySwizzled = 1 };
 
+// A's global -> LDS copy (tiled kernels; dgp_config.a_copy - 1): the async
+// buffer load that writes LDS directly, or a buffer load into registers and
+// an LDS write (gemm_w4.hip keeps it as an ablation).
+enum ACopy { kCopyAsync = 0, kCopyRegs = 1 };
+
 // One compiled kernel configuration.
 struct KernelSpec {
     int family;
@@ -50,6 +55,7 @@ struct KernelSpec {
     int sched;      // tiled: kSchedInterleaved, kSchedPingPong, kSchedBothLds or kSchedW4; stream: 0
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
     int lay = 0;    // tiled: A's LDS layout, kLayBlocks or kLaySwizzled
+    int copy = 0;   // tiled: A's global -> LDS path, kCopyAsync or kCopyRegs
 };
 
 // The compiled GEMM kernels: the tiled family (gemm_tiled.hip), its

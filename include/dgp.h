@@ -145,7 +145,17 @@ typedef enum dgp_scale_mode {
  *                    the layout of [P1] "Changes" item 2); 0 = the tile's
  *                    tuned choice.  Schedules 1-3 use operand blocks;
  *                    schedule 4 compiles both.  Must be 0 for the 16-row
- *                    kernels. */
+ *                    kernels.
+ *   a_copy         : tiled kernels: how A reaches LDS.  1 = the async
+ *                    global -> LDS buffer load ([P1] "Summary"); 2 = a
+ *                    buffer load into registers and an LDS write (the path
+ *                    [P1] replaced; schedule 4 keeps it to measure against);
+ *                    0 = the tile's tuned choice (1).  Must be 0 for the
+ *                    16-row kernels.
+ *   preload pair, schedule 4: preload_dsrd = the LDS read-ahead in A
+ *                    fragments (7 tuned; 3 and 1 compiled); preload_vmem =
+ *                    1: a fragment's LDS read, B reloads and A copies sit
+ *                    between its MFMAs, 0: all ahead of them. */
 typedef struct dgp_config {
     int tile_m;
     int tile_n;
@@ -158,6 +168,7 @@ typedef struct dgp_config {
     int prefetch;
     int schedule;
     int a_layout;
+    int a_copy;
 } dgp_config;
 
 /*

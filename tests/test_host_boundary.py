@@ -254,7 +254,7 @@ def test_kernel_table(dgp, L):
     seen = set()
     for cfg, dt, sm, split_out in ks:
         key = (cfg.tile_m, cfg.tile_n, cfg.tile_k, cfg.waves_m, cfg.prefetch, cfg.preload_vmem,
-               cfg.preload_dsrd, cfg.schedule, cfg.a_layout, dt, sm, split_out)
+               cfg.preload_dsrd, cfg.schedule, cfg.a_layout, cfg.a_copy, dt, sm, split_out)
         assert key not in seen
         seen.add(key)
         assert (dt, sm) in ((0, 0), (1, 1), (1, 2), (1, 3), (2, 4))
@@ -340,7 +340,8 @@ def test_schedule_validation(dgp):
         assert dgp.kernels()[i][0].a_layout == lay
     bad = (dgp.Config(**base, schedule=5), dgp.Config(**base, schedule=-1),
            dgp.Config(**base, schedule=4, a_layout=3), dgp.Config(**base, schedule=1, a_layout=2),
-           dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 0, 1),
+           dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 0, 1), dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 0, 0, 1),
+           dgp.Config(**base, schedule=4, a_copy=3), dgp.Config(**base, schedule=1, a_copy=2),
            dgp.Config(**base, schedule=2, preload_dsrd=8),
            dgp.Config(16, 64, 0, 0, 1, 0, 0, 0, 0, 1))
     for cfg in bad:
