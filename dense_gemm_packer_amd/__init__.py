@@ -412,6 +412,10 @@ def describe_kernel(index: int) -> str:
         half = ", half a strip" if cfg.tile_n == 8 else ""
         return (f"gemm_ksplit_kernel<{dts}, 16x{cfg.tile_n} tile{half}, K split over {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
+    if cfg.tile_m == 1:
+        half = ", half a strip" if cfg.tile_n == 8 else ""
+        return (f"gemm_wave_kernel<{dts}, 1x{cfg.tile_n} tile{half}, VALU dot products, K split over "
+                f"{cfg.waves_m} waves, {cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
     if cfg.tile_m == 16:
         return (f"gemm_stream_kernel<{dts}, 16x{cfg.tile_n} tile, {cfg.waves_m} waves, "
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdgp.so")
-SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_lds.hip", "gemm_stream.hip", "reduce.hip", "probe.hip", "noalloc.hip", "gemm_w4.hip"]
+SOURCES = ["dgp_api.cpp", "packer.hip", "gemm_tiled.hip", "gemm_lds.hip", "gemm_stream.hip", "reduce.hip", "probe.hip", "noalloc.hip", "gemm_w4.hip", "gemm_wave.hip"]
 HEADERS = ["common.h", "launch.h", "gemm_common.h"]
 ARCH = "gfx950"
 

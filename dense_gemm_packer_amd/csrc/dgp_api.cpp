@@ -34,6 +34,8 @@ const KernelSpec *kernel_table(int *count)
         v.insert(v.end(), t, t + n);
         t = stream_kernels(&n);
         v.insert(v.end(), t, t + n);
+        t = wave_kernels(&n);
+        v.insert(v.end(), t, t + n);
         return v;
     }();
     *count = (int)all.size();
@@ -164,6 +166,19 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             q.wm = tn == 64 ? 4 : 2;
             return find_spec(q);
         };
+        // One row, one pass, bf16 or per-tensor fp8: the one-row VALU kernel
+        // (measured cold at K = 7168 against every 16-row tile: N = 2048
+        // 6.5 vs 8.2 us bf16, 4.5 vs 5.3 us fp8; 2-4 % ahead at N = 4096,
+        // level at 16384).  Half strips while the strips are fewer than the
+        // CUs.
+        if (M == 1 && split_k == 1 && (dtype == DGP_BF16 || fp8t)) {
+            const bool half = N / 16 < 256;
+            Query q{kWave, dtype, scale, out, 1, half ? 8 : 16};
+            q.wm = (half || dtype != DGP_BF16) ? 4 : 8;
+            q.depth = 8;
+            if (const KernelSpec *k = find_spec(q))
+                return k;
+        }
         // Fewer strips x splits than CUs: half a strip per workgroup doubles
         // the workgroups with no second pass.
         if (u < 256)
@@ -237,7 +252,7 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
     const int out = c.split_k > 1 ? kOutPartial : kOutBf16;
     const KernelSpec *spec = nullptr;
     if (c.cfg && c.cfg->tile_m > 0) {
-        const int fam = (c.cfg->tile_m == 16) ? kStream : kTiled;
+        const int fam = c.cfg->tile_m == 16 ? kStream : c.cfg->tile_m == 1 ? kWave : kTiled;
         if (c.cfg->waves_m < 0 || c.cfg->prefetch < 0)
             return fail(DGP_ERR_CONFIG, "waves_m and prefetch must be >= 0");
         if (c.cfg->schedule < 0 || c.cfg->schedule > kSchedW4)
@@ -264,11 +279,11 @@ dgp_status select_kernel(const GemmCall &c, int64_t Ks, Plan *plan)
             q.copy = c.cfg->a_copy > 0 ? c.cfg->a_copy - 1 : kCopyAsync;
         } else {
             if (c.cfg->preload_vmem != 0 || c.cfg->preload_dsrd != 0)
-                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel takes no preload hints");
+                return fail(DGP_ERR_CONFIG, "the 16-row and one-row kernels take no preload hints");
             if (c.cfg->schedule != 0)
-                return fail(DGP_ERR_CONFIG, "the 16-row streaming kernel has no schedule choice");
+                return fail(DGP_ERR_CONFIG, "the 16-row and one-row kernels have no schedule choice");
             if (c.cfg->a_layout != 0 || c.cfg->a_copy != 0)
-                return fail(DGP_ERR_CONFIG, "the 16-row kernels have no A layout or copy choice");
+                return fail(DGP_ERR_CONFIG, "the 16-row and one-row kernels have no A layout or copy choice");
             q.wm = c.cfg->waves_m > 0 ? c.cfg->waves_m : -1;   // matched against waves per workgroup
             q.depth = c.cfg->prefetch > 0 ? c.cfg->prefetch : -1;
         }

@@ -27,6 +27,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -106,6 +107,78 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_dst, uin
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// ------------------------------------------------------------ load ring
+//
+// ring_run<DEPTH>(n, load, consume) -- one wave's slice of n steps through a
+// ring of DEPTH slots: load(d, i) issues step i's loads into slot d and
+// consume(d, i) uses them, slot d = i % DEPTH (a compile-time index).  Loads
+// run DEPTH steps ahead and are issued for steps < n only.  Every stretch of
+// code is branch-free with loads and consumes in slot order (scheduling
+// fences), so the compiler waits for exactly the slot a step needs: a loop
+// whose iterations consume and refill DEPTH slots while at least 2*DEPTH
+// steps remain, then one of 2*DEPTH straight-line tails chosen by the count
+// left (a wave-uniform branch).
+
+// The last t < 2*DEPTH steps from step i0; with PRE their first min(t, DEPTH)
+// loads are issued here, else they are already in flight in slot order.
+template <int DEPTH, int T, bool PRE, class Load, class Consume>
+__device__ __attribute__((always_inline)) inline void ring_tail(int i0, Load &load, Consume &consume)
+{
+    constexpr int L = T < DEPTH ? T : DEPTH;
+    if constexpr (PRE) {
+#pragma unroll
+        for (int d = 0; d < L; ++d) {
+            load(d, i0 + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < L; ++d) {
+        consume(d, i0 + d);
+        if constexpr (DEPTH < T) {
+            if (d + DEPTH < T)   // compile-time after unrolling
+                load(d, i0 + DEPTH + d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int d = 0; d + DEPTH < T; ++d) {
+        consume(d, i0 + DEPTH + d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int DEPTH, bool PRE, class Load, class Consume, int... Ts>
+__device__ __attribute__((always_inline)) inline void ring_tail_of(int t, int i0, Load &load, Consume &consume, std::integer_sequence<int, Ts...>)
+{
+    ((t == Ts ? ring_tail<DEPTH, Ts, PRE>(i0, load, consume) : void()), ...);
+}
+
+template <int DEPTH, class Load, class Consume>
+__device__ __attribute__((always_inline)) inline void ring_run(int n, Load &&load, Consume &&consume)
+{
+    using Counts = std::make_integer_sequence<int, 2 * DEPTH>;
+    if (n < 2 * DEPTH) {
+        ring_tail_of<DEPTH, true>(n, 0, load, consume, Counts{});
+        return;
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        load(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int i0 = 0;
+    for (; i0 + 2 * DEPTH <= n; i0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            consume(d, i0 + d);
+            load(d, i0 + DEPTH + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    ring_tail_of<DEPTH, false>(n - i0, i0, load, consume, Counts{});
 }
 
 // ------------------------------------------------------------- epilogue

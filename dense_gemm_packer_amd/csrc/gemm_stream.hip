@@ -358,9 +358,18 @@ gemm_ksplit_kernel(const GemmArgs p)
     for (int sp = 0; sp < SPW; ++sp)
         b_voff[sp] = (uint32_t)sp * 16u * Kb + (uint32_t)lane * 16u + (row_on ? 0u : 0x80000000u);
     const int m = m0 + (lane & 15);
-    const float *sa_row = (SCALE == kScaleBlock && m < p.M) ? static_cast<const float *>(p.sA) + (int64_t)m * kblocks_row : nullptr;
-    const float *sb_row = SCALE == kScaleBlock ? static_cast<const float *>(p.sB) + (int64_t)(strip0 * 16 / 128) * kblocks_row : nullptr;
+    // Blockscale: a step's two scales (this lane's A row of sA, rows past M
+    // reading zero; the tile's row of sB, whose strips lie in one 128-column
+    // block): loaded into the step's ring slot with its operands (ordered
+    // ring) or read where the step is multiplied (guarded loop).
     static_assert(SCALE != kScaleBlock || 128 % (16 * SPW) == 0, "a tile's strips in one 128-column block");
+    constexpr bool kBs = SCALE == kScaleBlock;
+    [[maybe_unused]] const auto rSa = make_rsrc(kBs ? static_cast<const float *>(p.sA) + (int64_t)m0 * kblocks_row : nullptr,
+                                                kBs ? clamp_bytes((int64_t)(p.M - m0) * kblocks_row * 4) : 0);
+    [[maybe_unused]] const auto rSb = make_rsrc(kBs ? static_cast<const float *>(p.sB) + (int64_t)(strip0 * 16 / 128) * kblocks_row
+                                                    : nullptr,
+                                                kBs ? (uint32_t)kblocks_row * 4u : 0u);
+    [[maybe_unused]] const uint32_t sa_off = (uint32_t)(lane & 15) * (uint32_t)kblocks_row * 4u;
     // mxfp8: a step's E8M0 bytes (this lane's A row, its B column in each
     // strip) are loaded with the step's operands into the same ring slot, so
     // they arrive with them and waiting for them never drains the ring.  The
@@ -412,7 +421,15 @@ gemm_ksplit_kernel(const GemmArgs p)
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp)
         acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Ring schedule, chosen per tile from cold sweeps of both: the 16-column
+    // tiles and the fp8 half-strip tiles keep their ring in order with exact
+    // waits (ring_run, 1-15 % faster there); the wider tiles, whose ordered
+    // ring needs too many registers for two workgroups per CU, the bf16
+    // half strips and mxfp4 (scale words per group of 4 steps) run the
+    // guarded loop below, which waits for a whole group at a time.
+    constexpr bool kRing = !kXw && (TN == 16 || (TN == 8 && DT != kDtypeBf16));
     i32x4 areg[DEPTH][kStepCh], breg[DEPTH][SPW][kStepCh];
+    [[maybe_unused]] float sav[DEPTH], sbv[DEPTH];
     // Step st of the split: K bytes kbase + st*kStepBytes; A chunk cc of it is
     // one 16-row x 64-byte operand read, B chunk cc of strip sp one 1 KiB block.
     auto load_step = [&](int d, int st) {
@@ -425,6 +442,11 @@ gemm_ksplit_kernel(const GemmArgs p)
                 xs[d][1 + sp] = __builtin_amdgcn_raw_buffer_load_b8(
                     rXb8, x8_off + (uint32_t)(sp * 16) * (uint32_t)kblocks_row + kb, 0, kAuxNone);
         }
+        if constexpr (kBs && kRing) {
+            const uint32_t kb = k / 128u;   // one fp32 scale per 128-K step
+            sav[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSa, sa_off + 4u * kb, 0, kAuxNone));
+            sbv[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSb, 4u * kb, 0, kAuxNone));
+        }
 #pragma unroll
         for (int cc = 0; cc < kStepCh; ++cc)
             areg[d][cc] = load16<kAuxNone>(rA, a_voff + k + cc * 64u);
@@ -434,71 +456,86 @@ gemm_ksplit_kernel(const GemmArgs p)
             for (int cc = 0; cc < kStepCh; ++cc)
                 breg[d][sp][cc] = load16<kAuxNonTemporal>(rB, b_voff[sp] + k * 16u + cc * 1024u);
     };
-    // The ring loads only steps of this wave's slice (an empty slice, when
-    // nsteps < NW, loads nothing), so no wave waits on loads it never uses.
-    // The loop runs two ring groups per iteration so that the parity of the
-    // mxfp4 scale words is a compile-time index.
-    if (s0 < s1)
-        load_x(std::integral_constant<int, 0>{}, s0);
+    // The MFMAs of step st in slot d (X: the mxfp4 scale words' parity).
+    auto consume = [&](auto setc, int d, [[maybe_unused]] int st) {
+        [[maybe_unused]] constexpr int X = decltype(setc)::value;
+        Frag a;
+        if constexpr (kStepCh == 1)
+            a = areg[d][0];
+        else
+            a = cat(areg[d][0], areg[d][1]);
+        [[maybe_unused]] float sc = 0.f;
+        [[maybe_unused]] int ea = 127;
+        if constexpr (kBs && kRing) {
+            sc = __fmul_rn(sav[d], sbv[d]);
+        } else if constexpr (kBs) {   // the guarded loop reads the two scales here
+            const uint32_t kb = (kbase + (uint32_t)st * kStepBytes) / 128u;
+            sc = __fmul_rn(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSa, sa_off + 4u * kb, 0, kAuxNone)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rSb, 4u * kb, 0, kAuxNone)));
+        } else if constexpr (kMx) {
+            ea = xs[d][0];
+        } else if constexpr (kXw) {
+            // this lane's 16 bytes are one 32-element block, byte l/16 of the step's word
+            ea = (int)(((uint32_t)xw[X][0][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
+        }
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (s0 + d < s1)
-            load_step(d, s0 + d);
-    auto group = [&](auto setc, int st0) {
-        constexpr int X = decltype(setc)::value;
-        if (st0 + DEPTH < s1)
-            load_x(std::integral_constant<int, 1 - X>{}, st0 + DEPTH);
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int st = st0 + d;
-            if (st < s1) {
-                Frag a;
-                if constexpr (kStepCh == 1)
-                    a = areg[d][0];
-                else
-                    a = cat(areg[d][0], areg[d][1]);
-                [[maybe_unused]] float sc = 0.f;
-                [[maybe_unused]] int kb = 0, ea = 127;
-                if constexpr (SCALE == kScaleBlock) {
-                    kb = (int)((kbase + (uint32_t)st * kStepBytes) / 128u);
-                    sc = __fmul_rn(sa_row ? sa_row[kb] : 0.f, sb_row[kb]);
-                } else if constexpr (SCALE == kScaleMx) {
-                    ea = xs[d][0];
-                } else if constexpr (SCALE == kScaleMx32) {
-                    // this lane's 16 bytes are one 32-element block, byte l/16 of the step's word
-                    ea = (int)(((uint32_t)xw[X][0][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
-                }
-#pragma unroll
-                for (int sp = 0; sp < SPW; ++sp) {
-                    Frag b;
-                    if constexpr (kStepCh == 1)
-                        b = breg[d][sp][0];
-                    else
-                        b = cat(breg[d][sp][0], breg[d][sp][1]);
-                    if constexpr (SCALE == kScaleBlock) {
-                        const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
-                        acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, sc));
-                        acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, sc));
-                        acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, sc));
-                        acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, sc));
-                    } else if constexpr (SCALE == kScaleMx) {
-                        acc[sp] = mfma_mx(b, a, acc[sp], xs[d][1 + sp], ea);
-                    } else if constexpr (SCALE == kScaleMx32) {
-                        const int eb = (int)(((uint32_t)xw[X][1 + sp][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
-                        acc[sp] = mfma_mx4(b, a, acc[sp], eb, ea);
-                    } else {
-                        acc[sp] = mfma_op(b, a, acc[sp]);
-                    }
-                }
-                if (st + DEPTH < s1)
-                    load_step(d, st + DEPTH);
+        for (int sp = 0; sp < SPW; ++sp) {
+            Frag b;
+            if constexpr (kStepCh == 1)
+                b = breg[d][sp][0];
+            else
+                b = cat(breg[d][sp][0], breg[d][sp][1]);
+            if constexpr (kBs) {
+                const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
+                acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, sc));
+                acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, sc));
+                acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, sc));
+                acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, sc));
+            } else if constexpr (kMx) {
+                acc[sp] = mfma_mx(b, a, acc[sp], xs[d][1 + sp], ea);
+            } else if constexpr (kXw) {
+                const int eb = (int)(((uint32_t)xw[X][1 + sp][d] >> (8u * (uint32_t)(lane >> 4))) & 0xFFu);
+                acc[sp] = mfma_mx4(b, a, acc[sp], eb, ea);
+            } else {
+                acc[sp] = mfma_op(b, a, acc[sp]);
             }
         }
     };
-    for (int st0 = s0; st0 < s1; st0 += 2 * DEPTH) {
-        group(std::integral_constant<int, 0>{}, st0);
-        if (st0 + DEPTH < s1)
-            group(std::integral_constant<int, 1>{}, st0 + DEPTH);
+    if constexpr (kRing) {
+        // The ring loads only steps of this wave's slice (an empty slice, when
+        // nsteps < NW, loads nothing).
+        ring_run<DEPTH>(
+            s1 - s0, [&](int d, int i) { load_step(d, s0 + i); },
+            [&](int d, int i) { consume(std::integral_constant<int, 0>{}, d, s0 + i); });
+    } else {
+        // Two ring groups per iteration, so the parity of the mxfp4 scale
+        // words (loaded a group ahead) is a compile-time index; the ring
+        // loads only steps of the wave's slice.
+        if (s0 < s1)
+            load_x(std::integral_constant<int, 0>{}, s0);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            if (s0 + d < s1)
+                load_step(d, s0 + d);
+        auto group = [&](auto setc, int st0) {
+            constexpr int X = decltype(setc)::value;
+            if (st0 + DEPTH < s1)
+                load_x(std::integral_constant<int, 1 - X>{}, st0 + DEPTH);
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int st = st0 + d;
+                if (st < s1) {
+                    consume(setc, d, st);
+                    if (st + DEPTH < s1)
+                        load_step(d, st + DEPTH);
+                }
+            }
+        };
+        for (int st0 = s0; st0 < s1; st0 += 2 * DEPTH) {
+            group(std::integral_constant<int, 0>{}, st0);
+            if (st0 + DEPTH < s1)
+                group(std::integral_constant<int, 1>{}, st0 + DEPTH);
+        }
     }
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp)

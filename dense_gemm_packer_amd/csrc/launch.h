@@ -25,7 +25,7 @@ struct GemmArgs {
 };
 
 // Kernel family selectors.
-enum Family { kTiled = 0, kStream = 1 };
+enum Family { kTiled = 0, kStream = 1, kWave = 2 };
 
 // Wave schedules of the tiled family (dgp_config.schedule).
 enum Schedule { kSchedInterleaved = 1, kSchedPingPong = 2, kSchedBothLds = 3, kSchedW4 = 4 };
@@ -52,7 +52,7 @@ struct KernelSpec {
     int p0, p1;     // family-specific: tiled = (wm, wn); stream = (strips per wave, depth)
     int pv, pd;     // scheduling hint pair (tiled)
     int depth;      // prefetch distance: k-tiles (tiled) / steps (stream)
-    int sched;      // tiled: kSchedInterleaved, kSchedPingPong, kSchedBothLds or kSchedW4; stream: 0
+    int sched;      // tiled: kSchedInterleaved, kSchedPingPong, kSchedBothLds or kSchedW4; stream, wave: 0
     void (*launch)(const GemmArgs &, dim3 grid, hipStream_t);
     int lay = 0;    // tiled: A's LDS layout, kLayBlocks or kLaySwizzled
     int copy = 0;   // tiled: A's global -> LDS path, kCopyAsync or kCopyRegs
@@ -60,13 +60,14 @@ struct KernelSpec {
 
 // The compiled GEMM kernels: the tiled family (gemm_tiled.hip), its
 // both-in-LDS schedule (gemm_lds.hip), its one-wave-per-SIMD schedule
-// (gemm_w4.hip), the streaming family (gemm_stream.hip), and all of them in
-// one table in that order (dgp_api.cpp) -- the numbering dgp_kernel_info
-// uses.
+// (gemm_w4.hip), the streaming family (gemm_stream.hip), the one-row VALU
+// kernels (gemm_wave.hip), and all of them in one table in that order
+// (dgp_api.cpp) -- the numbering dgp_kernel_info uses.
 const KernelSpec *tiled_kernels(int *count);
 const KernelSpec *lds_kernels(int *count);
 const KernelSpec *w4_kernels(int *count);
 const KernelSpec *stream_kernels(int *count);
+const KernelSpec *wave_kernels(int *count);
 const KernelSpec *kernel_table(int *count);
 
 // Library-owned split-K workspace (noalloc.hip): the size of the fixed

@@ -100,7 +100,10 @@ typedef enum dgp_scale_mode {
  *                    16x64 and 16x32 streaming (4 and 2 waves); K-split
  *                    (8 waves) over 16x8 -- half a strip, two workgroups
  *                    per 16-column strip -- 16x16, 16x32 and 16x64; every
- *                    16-row tile for every mode)
+ *                    16-row tile for every mode; one-row VALU tiles 1x16
+ *                    and 1x8 for bf16 and per-tensor fp8 -- [P3] file
+ *                    table, the "Wave" decode policy -- one workgroup per
+ *                    row of C, meant for M = 1)
  *   tile_k         : tiled kernels: K bytes staged per main-loop step (128,
  *                    the k-tile of every compiled tiled kernel); ignored by
  *                    the 16-row kernels
@@ -121,10 +124,13 @@ typedef enum dgp_scale_mode {
  *                    strips; the K-split kernel (8 waves): waves sharing
  *                    the tile's K range, which also tells the 16x32 and
  *                    16x64 K-split tiles from the streaming ones (0 = the
- *                    first compiled kernel for this tile: the streaming one).
+ *                    first compiled kernel for this tile: the streaming one);
+ *                    the one-row tiles: waves sharing the K range (4, 8 or
+ *                    16 compiled).
  *   prefetch       : tiled kernels: k-tiles loaded ahead of the one being
- *                    multiplied; streaming kernel: MFMA steps of loads in
- *                    flight per wave (0 = any compiled depth for this tile).
+ *                    multiplied; 16-row and one-row kernels: steps of loads
+ *                    in flight per wave (0 = any compiled depth for this
+ *                    tile).
  *   schedule       : tiled kernels: how one workgroup's waves order their
  *                    work.  1 = interleaved: every wave mixes its LDS reads,
  *                    global loads and MFMAs, placed by the preload hints;

@@ -148,6 +148,46 @@ def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):
             assert np.array_equal(got, c16), (k, cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule)
 
 
+# Ordered load rings: the one-row VALU kernel (every compiled form) and the
+# K-split tiles that use the ordered ring (16 columns; fp8 half strips):
+# (config, dtype, mode, K bytes per step, waves, ring depth).
+RING_CASES = [
+    (dgp.Config(tile_m=1, tile_n=16, waves_m=4, prefetch=8), "bf16", "none", 64, 4, 8),
+    (dgp.Config(tile_m=1, tile_n=8, waves_m=8, prefetch=4), "bf16", "none", 128, 8, 4),
+    (dgp.Config(tile_m=1, tile_n=16, waves_m=8, prefetch=8), "fp8", "tensor", 64, 8, 8),
+    (dgp.Config(tile_m=1, tile_n=8, waves_m=4, prefetch=8), "fp8", "tensor", 128, 4, 8),
+    (dgp.Config(tile_m=16, tile_n=16, waves_m=8, prefetch=4), "bf16", "none", 64, 8, 4),
+    (dgp.Config(tile_m=16, tile_n=16, waves_m=8, prefetch=4), "fp8", "tensor", 128, 8, 4),
+    (dgp.Config(tile_m=16, tile_n=8, waves_m=8, prefetch=4), "fp8", "block128", 128, 8, 4),
+    (dgp.Config(tile_m=16, tile_n=16, waves_m=8, prefetch=4), "fp8", "mx128", 128, 8, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RING_CASES)))
+def test_ring_slice_lengths(case):
+    """Every slice length a wave can get, 0 .. 3 x the ring depth steps (empty
+    slices, each of the 2 x depth straight-line tails, one and two
+    main-loop iterations before a tail), with equal and unequal slices
+    across the waves; exact-integer inputs, bit-exact."""
+    cfg, dtype, mode, step_bytes, nw, depth = RING_CASES[case]
+    eb = 2 if dtype == "bf16" else 1
+    M, N = (3 if cfg.tile_m == 1 else 19), 256
+    seen = set()
+    for n in range(0, 3 * depth + 1):
+        for extra in (0, nw // 2, nw - 1):
+            steps = nw * n + extra
+            kb = steps * step_bytes
+            if kb == 0 or kb % 128 or (kb // eb) % 128 and mode in ("block128", "mx128") or kb in seen:
+                continue
+            seen.add(kb)
+            K = kb // eb
+            A, B, sA, sB = exact_inputs(dtype, mode, M, N, K, 29)
+            got = run_gpu(A, B, dtype, mode, sA, sB, config=cfg)
+            _, c16 = run_oracle(A, B, dtype, mode, sA, sB)
+            assert np.array_equal(got, c16), (dtype, mode, cfg.tile_m, cfg.tile_n, K)
+    assert len(seen) > 2 * depth
+
+
 @pytest.mark.parametrize("tile_n,waves", [(64, 0), (32, 0), (16, 0), (8, 0), (32, 8), (64, 8)])
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128"), ("fp4", "mx32")])
