@@ -146,16 +146,18 @@ const KernelSpec *find_spec(const Query &q)
 // Built-in per-shape choice.
 const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t N, int64_t Ks, int split_k)
 {
-    // Decode-sized M streams the weight through the 16-row tiles.  Larger M
-    // takes the tiled kernels, every scale mode included.
+    // Decode-sized M streams the weight through the 16-row and one-row
+    // tiles.  Larger M takes the tiled kernels, every scale mode included.
     if (M <= 32) {
-        // Rules from cold-cache sweeps of the 16-row tiles at K = 7168 (every
-        // mode; M = 1, 4 and 16; N 2048-16384; split 1-8).  u = strips x
-        // splits; ks(t) = the K-split tile t columns wide (8 waves), st(t) =
-        // the streaming tile.
+        // Rules from cold sweeps of every 16-row and one-row tile at K = 7168
+        // (every mode; M = 1, 2, 4 and 16; N 2048-16384; split 1-4).
+        // u = strips x splits; ks(t) = the K-split tile t columns wide (8
+        // waves), st(t) = the streaming tile, wv(t, w, d) = the one-row VALU
+        // tile with w waves and a d-step ring.
         const int64_t u = N / 16 * split_k;
         const bool fp8t = dtype == DGP_FP8_E4M3 && scale == DGP_SCALE_TENSOR;
         const bool mx4 = scale == DGP_SCALE_MX32;
+        const bool bs = scale == DGP_SCALE_BLOCK128, mx8 = scale == DGP_SCALE_MX128;
         const auto ks = [&](int tn) {
             Query q{kStream, dtype, scale, out, 16, tn};
             q.wm = 8;
@@ -166,33 +168,53 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             q.wm = tn == 64 ? 4 : 2;
             return find_spec(q);
         };
-        // One row, one pass, bf16 or per-tensor fp8: the one-row VALU kernel
-        // (measured cold at K = 7168 against every 16-row tile: N = 2048
-        // 6.5 vs 8.2 us bf16, 4.5 vs 5.3 us fp8; 2-4 % ahead at N = 4096,
-        // level at 16384).  Half strips while the strips are fewer than the
-        // CUs.
-        if (M == 1 && split_k == 1 && (dtype == DGP_BF16 || fp8t)) {
-            const bool half = N / 16 < 256;
-            Query q{kWave, dtype, scale, out, 1, half ? 8 : 16};
-            q.wm = (half || dtype != DGP_BF16) ? 4 : 8;
-            q.depth = 8;
-            if (const KernelSpec *k = find_spec(q))
+        const auto wv = [&](int tn, int waves, int depth) {
+            Query q{kWave, dtype, scale, out, 1, tn};
+            q.wm = waves, q.depth = depth;
+            return find_spec(q);
+        };
+        // One row, bf16 or per-tensor fp8: the one-row VALU tile (split 1 at
+        // N = 2048: 6.4 vs 8.3 us bf16, 4.5 vs 5.3 us fp8; 0-4 % ahead of
+        // the 16-row tiles at larger N and 1-11 % with splits), half strips
+        // while one pass has fewer strips than CUs.
+        if (M == 1 && (dtype == DGP_BF16 || fp8t)) {
+            const KernelSpec *k = nullptr;
+            if (split_k == 1 && N / 16 < 256)
+                k = wv(8, 4, 8);
+            else if (split_k == 1)
+                k = dtype == DGP_BF16 ? wv(16, 8, 8) : wv(16, 4, 8);
+            else
+                k = (dtype == DGP_BF16 || split_k == 2) ? wv(16, 4, 8) : wv(16, 4, 4);
+            if (k)
                 return k;
         }
+        // Blockscale from 4 splits and mxfp8 from 2 over at least 2048
+        // strips x splits: the streaming 16x64 tile (5-19 % ahead), whose A
+        // panel in LDS serves four strips per wave.
+        if (u >= 2048 && ((bs && split_k >= 4) || (mx8 && split_k >= 2)))
+            return st(64);
         // Fewer strips x splits than CUs: half a strip per workgroup doubles
         // the workgroups with no second pass.
         if (u < 256)
             return ks(8);
         if (M <= 4) {
-            // A few rows: A is cheap to re-read, so one strip per workgroup
-            // with K over 8 waves keeps the most of the weight in flight
-            // (5-36 % ahead of the streaming tiles); blockscale and mxfp8
-            // gain from 2 strips from 512 on.
-            if (fp8t || dtype == DGP_BF16 || mx4)
-                return (u < 1024 || split_k == 1) ? ks(16) : st(64);
+            // A few rows: A is cheap to re-read.  One pass: one strip per
+            // workgroup with K over 8 waves.  With splits each wave's slice
+            // is short, so 2 strips per workgroup lead (4-13 %), until the
+            // streaming tile takes over from 2048 strips x splits at 4
+            // splits; bf16 keeps one strip at 2 splits.
+            if (fp8t || dtype == DGP_BF16 || mx4) {
+                if (split_k == 1)
+                    return ks(16);
+                if (dtype == DGP_BF16)
+                    return split_k == 2 ? ks(16) : ks(32);
+                if (u < 1024)
+                    return ks(16);
+                return (split_k == 2 || u == 1024) ? ks(32) : st(64);
+            }
             if (u < 512)
                 return ks(16);
-            return (scale == DGP_SCALE_MX128 && u >= 1024) ? ks(64) : ks(32);
+            return (mx8 && u >= 1024) ? ks(64) : ks(32);
         }
         // More rows: A is read once per workgroup, so wider K-split tiles
         // (2 or 4 strips sharing each A fragment) lead from 512 strips x
