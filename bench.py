@@ -703,7 +703,7 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
         edt = {"bf16": "bf16", "mx32": "fp4"}.get(mode, "fp8")
         eb = {"bf16": 2.0, "mx32": 0.5}.get(mode, 1.0)     # bytes per element
         Ms = (1, 16) if mode in ("tensor", "bf16", "mx32") else (16,)
-        Ns = (2048, 16384) if mode in ("tensor", "bf16", "mx32") else (16384,)
+        Ns = (2048, 16384)
         for n_ in Ns:
             base = synth.workload_inputs(name, M=16, N=n_)
             kk = base["K"]
