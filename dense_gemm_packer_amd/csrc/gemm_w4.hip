@@ -1,4 +1,5 @@
-// gemm_w4_kernel -- the 256 x 256 large-M tile with one wave per SIMD.
+// gemm_w4_kernel -- the 256 x 256 large-M tile with one wave per SIMD
+// (bf16, per-tensor fp8 and mxfp8).
 //
 // Same operation, operand layouts and epilogue as gemm_tiled_kernel
 // (gemm_tiled.hip, gemm_common.h): per k-tile of 128 bytes the A tile goes
@@ -105,6 +106,16 @@ __device__ inline void mfma_acc(f32x4 &acc, const i32x8 &b, const i32x8 &a)
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
+// ... and the hardware-scaled e4m3 K128 form (mxfp8): eb scales the B
+// fragment (first operand: lane l's byte for its column), ea the A fragment
+// (its row), both E8M0 in the low byte (op_sel byte 0).
+__device__ inline void mfma_acc_mx(f32x4 &acc, const i32x8 &b, const i32x8 &a, int eb, int ea)
+{
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc)
+                 : "v"(b), "v"(a), "v"(eb), "v"(ea));
+}
+
 // DB: B register sets = k-tiles of B loads in flight (2..4).
 // RA: A fragments read from LDS ahead of the MFMAs that consume them.
 // ILV: 1 = a fragment's 4 MFMAs with one slot of other work between each
@@ -121,6 +132,17 @@ __device__ inline void mfma_acc(f32x4 &acc, const i32x8 &b, const i32x8 &a)
 // (rows 16mt + i, one chunk each) fall on 16 distinct 16-byte bank groups
 // -- the row-major tile with an XOR swizzle known to writer and reader of
 // FlyDSL PR #1008 "Changes" item 2.
+//
+// mxfp8 (SCALE = kScaleMx): a 128-byte k-tile is one 128-K scale block, so
+// each k-tile carries one E8M0 byte per A row (sA [M][K/128]) and per column
+// (sB [N][K/128]).  They are staged per stage of the LDS ring beside the A
+// tile by two 1-byte async copies per wave (one dword per lane, the byte
+// zero-extended), issued with the tile's first A copy so the barrier that
+// certifies the tile certifies them.  The staging order lets a lane read its
+// scales in 16-byte pieces: A row 16mt + i at dword 16i + mt (a lane reads the
+// 4 row tiles of a quad at once, one read per 4 fragments, 4 fragments of
+// ring), column 64w + 16s + i at dword 256 + 4(16w + i) + s (one read per
+// k-tile, right after the barrier, for the next tile).
 template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_w4_kernel(const GemmArgs p)
@@ -129,13 +151,24 @@ gemm_w4_kernel(const GemmArgs p)
     constexpr int kDB = DB;
     using namespace w4;
     static_assert(!SYNC || (SWZ && !kDmaLate), "the register copy: swizzled rows, copies after the barrier");
+    constexpr bool kMx = SCALE == kScaleMx;
+    static_assert(!kMx || (DT == kDtypeFp8 && SWZ && !SYNC && !kDmaLate), "mxfp8: fp8, swizzled rows, async copies");
     constexpr int kRA = RA;
     using P = Plan<DT, RA>;
     using Frag = typename Op<DT>::Frag;
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
-    constexpr int kVm = P::vm_at_barrier();
+    static_assert(!kMx || (kFr == kMT && kMT % 4 == 0 && kRA < kFr - 4), "mxfp8: one k-step per k-tile, quad ring");
+    // The barrier's count: the scale copies of the k-tiles in between are
+    // 2 more loads per k-tile (those of the barrier's own tile precede its
+    // last A copy).
+    constexpr int kVm = P::vm_at_barrier() + (kMx ? 2 * (kDmaAhead - 2) : 0);
     static_assert(kVm <= 63, "vmcnt field is 6 bits");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf];
+    // One LDS object (the A ring, then for mxfp8 the scale stages): the
+    // compiler's wait insertion keeps the async copies and the LDS reads of
+    // one object apart by their order, where a second object made it wait
+    // for every copy in flight before each read.
+    constexpr int kXBytes = kMx ? kRing * 2048 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf + kXBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,6 +210,36 @@ gemm_w4_kernel(const GemmArgs p)
         a_off[0] = (uint32_t)(lane & 15) * 128u + 16u * v;
         a_off[1] = (uint32_t)(lane & 15) * 128u + 16u * (v ^ 4u);
     }
+    // mxfp8 scale staging: copy lane e = 64*wave + lane fetches A row
+    // 16*(e%16) + e/16 and column 64*wave + 16*(lane%4) + lane/4 of this
+    // k-tile's scale block; rows >= M and columns >= N are past the ranges and
+    // stage 0 (2^-127, finite), which only ever scales zero data.
+    [[maybe_unused]] const int kblk = p.K / 128;
+    [[maybe_unused]] const auto rXa = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblk : nullptr,
+                                                kMx ? clamp_bytes((int64_t)(p.M - m0) * kblk) : 0);
+    [[maybe_unused]] const auto rXb = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)n0 * kblk : nullptr,
+                                                kMx ? clamp_bytes((int64_t)(p.N - n0) * kblk) : 0);
+    [[maybe_unused]] const uint32_t xa_voff =
+        (uint32_t)(16 * ((wave * 64 + lane) % 16) + (wave * 64 + lane) / 16) * (uint32_t)kblk;
+    [[maybe_unused]] const uint32_t xb_voff = (uint32_t)(64 * wave + 16 * (lane & 3) + (lane >> 2)) * (uint32_t)kblk;
+    auto xstage = [&](int t) -> uint32_t * {
+        return reinterpret_cast<uint32_t *>(lds + kRing * kBuf + (kMx ? (t & (kRing - 1)) * 2048 : 0));
+    };
+    auto dma_scales = [&](int t, uint32_t koff) {
+        if constexpr (kMx) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rXa, (__attribute__((address_space(3))) void *)(xstage(t) + wave * 64), 1, xa_voff, koff / 128u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rXb, (__attribute__((address_space(3))) void *)(xstage(t) + 256 + wave * 64), 1, xb_voff, koff / 128u, 0, 0);
+        }
+    };
+    [[maybe_unused]] i32x4 xq[4];              // A scales of row tiles 4q..4q+3 (slot q)
+    [[maybe_unused]] i32x4 xb_cur, xb_next;    // B scales of this and the next k-tile, one per strip
+    auto read_xb = [&](int t) {
+        if constexpr (kMx)
+            xb_next = *reinterpret_cast<const i32x4 *>(xstage(t) + 256 + 4 * (wave * 16 + (lane & 15)));
+    };
+
     // B: this wave's 4 strips; strips >= N/16 are past the range (zero).
     const int strip0 = (n0 + wave * (TN / NW)) / 16;
     const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
@@ -211,6 +274,11 @@ gemm_w4_kernel(const GemmArgs p)
     };
     auto read_frag = [&](int f, uint32_t st) {   // fragment f of the tile in stage st
         const int s = f / kMT, mt = f % kMT;
+        if constexpr (kMx) {
+            if (mt % 4 == 0)
+                xq[mt / 4] = *reinterpret_cast<const i32x4 *>(lds + kRing * kBuf + (st / kBuf) * 2048 +
+                                                              4 * (16 * (lane & 15) + mt));
+        }
         if constexpr (SWZ) {
             const uint8_t *row = lds + st + mt * 2048;
             if constexpr (DT == kDtypeBf16)
@@ -237,6 +305,8 @@ gemm_w4_kernel(const GemmArgs p)
                 }
             }
             dma(j, stage(t), kofs(t));
+            if (j == 0)
+                dma_scales(t, kofs(t));
         }
     auto prologue_b = [&](auto setc) {
 #pragma unroll
@@ -252,6 +322,7 @@ gemm_w4_kernel(const GemmArgs p)
     if constexpr (DB > 3)
         prologue_b(std::integral_constant<int, (DB > 3 ? 3 : 0)>{});
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    read_xb(0);
 #pragma unroll
     for (int f = 0; f < kRA; ++f)
         read_frag(f, stage(0));
@@ -268,6 +339,10 @@ gemm_w4_kernel(const GemmArgs p)
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kMx) {
+                if (f == 0)
+                    xb_cur = xb_next;
+            }
             if (f == kBar) {
                 if constexpr (SYNC)   // this wave's LDS writes of tile t+1 (and earlier) are done
                     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -284,10 +359,14 @@ gemm_w4_kernel(const GemmArgs p)
             auto mf = [&](int nt) {
                 if constexpr (DT == kDtypeBf16)
                     mfma_acc(acc[mt][nt], breg[SET][nt][st], a);
+                else if constexpr (kMx)
+                    mfma_acc_mx(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a, xb_cur[nt], xq[mt / 4][mt % 4]);
                 else
                     mfma_acc(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a);
             };
             auto lds_read = [&]() {
+                if (f == kBar)   // past the barrier: the next k-tile's column scales
+                    read_xb(t + 1);
                 if (f + kRA < kFr)
                     read_frag(f + kRA, cur);
                 else
@@ -316,6 +395,8 @@ gemm_w4_kernel(const GemmArgs p)
                             copy_load(j, k_dma);
                     } else if (P::dma_pos(j) == f) {
                         dma(j, nx3, k_dma);
+                        if (j == 0)
+                            dma_scales(t + kDmaAhead, k_dma);
                     }
                 }
             };
@@ -463,6 +544,9 @@ static const KernelSpec kW4Kernels[] = {
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, 1, 1, 0),
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 0, 0),
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 1, 1),
+    // mxfp8: the hardware-scaled MFMA with the k-tile's E8M0 bytes staged
+    // beside the A tile
+    DGP_W4_BOTH_OUT(kDtypeFp8, kScaleMx, 3, 1, w4::kRA, 1, 0),
 };
 
 const KernelSpec *w4_kernels(int *count)
