@@ -230,16 +230,15 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     }
     const KernelSpec *k = nullptr;
     if (M >= 1024 && N >= 1024) {
-        // bf16, per-tensor fp8 and mxfp8: the one-wave-per-SIMD tile with
-        // swizzled A rows (measured 8-18 % ahead of the 8-wave tile at 4096 x
-        // 4096 x 8192); blockscale and mxfp4: the 8-wave tile.
+        // bf16, per-tensor fp8, mxfp8 and mxfp4: the one-wave-per-SIMD tile
+        // with swizzled A rows (measured 8-18 % ahead of the 8-wave tile at
+        // 4096 x 4096 x 8192); blockscale: the 8-wave tile.
         Query q{kTiled, dtype, scale, out, 256, 256};
         q.kt = 128;
-        if (scale == DGP_SCALE_NONE || scale == DGP_SCALE_TENSOR || scale == DGP_SCALE_MX128) {
+        if (scale != DGP_SCALE_BLOCK128) {
             q.sched = kSchedW4, q.lay = kLaySwizzled;
         } else {
-            q.wm = 1, q.depth = 2, q.pv = 0;
-            q.pd = (scale == DGP_SCALE_BLOCK128 || scale == DGP_SCALE_MX128) ? 4 : 8;
+            q.wm = 1, q.depth = 2, q.pv = 0, q.pd = 4;
         }
         k = find_spec(q);
     }

@@ -116,6 +116,15 @@ __device__ inline void mfma_acc_mx(f32x4 &acc, const i32x8 &b, const i32x8 &a, i
                  : "v"(b), "v"(a), "v"(eb), "v"(ea));
 }
 
+// ... and the hardware-scaled E2M1 K128 form (mxfp4: 16 bytes = 32 values per
+// lane, one 32-value block, cbsz = blgp = 4).
+__device__ inline void mfma_acc_mx4(f32x4 &acc, const i32x4 &b, const i32x4 &a, int eb, int ea)
+{
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                 : "+a"(acc)
+                 : "v"(b), "v"(a), "v"(eb), "v"(ea));
+}
+
 // DB: B register sets = k-tiles of B loads in flight (2..4).
 // RA: A fragments read from LDS ahead of the MFMAs that consume them.
 // ILV: 1 = a fragment's 4 MFMAs with one slot of other work between each
@@ -143,6 +152,15 @@ __device__ inline void mfma_acc_mx(f32x4 &acc, const i32x8 &b, const i32x8 &a, i
 // 4 row tiles of a quad at once, one read per 4 fragments, 4 fragments of
 // ring), column 64w + 16s + i at dword 256 + 4(16w + i) + s (one read per
 // k-tile, right after the barrier, for the next tile).
+//
+// mxfp4 (SCALE = kScaleMx32): a 128-byte k-tile is 256 values = 8 blocks of
+// 32, two MFMA k-steps whose lane l holds block 4s + l/16 of its row.  Each
+// row and column has 2 scale dwords per k-tile (bytes 4s..4s+3 = the blocks
+// of step s), staged by 4-byte async copies (2 for rows, 2 for columns per
+// wave): row 16mt + i, dword s at dword 2(16i + mt) + s, so a lane reads a
+// quad of row tiles' 8 dwords in two 16-byte reads, and column 64w + 16c + i
+// at dword 512 + 2(4(16w + i) + c) + s; a lane's byte is taken with one
+// bit-field extract per fragment.
 template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_w4_kernel(const GemmArgs p)
@@ -152,22 +170,27 @@ gemm_w4_kernel(const GemmArgs p)
     using namespace w4;
     static_assert(!SYNC || (SWZ && !kDmaLate), "the register copy: swizzled rows, copies after the barrier");
     constexpr bool kMx = SCALE == kScaleMx;
+    constexpr bool kMx4 = SCALE == kScaleMx32;
     static_assert(!kMx || (DT == kDtypeFp8 && SWZ && !SYNC && !kDmaLate), "mxfp8: fp8, swizzled rows, async copies");
+    static_assert(!kMx4 || (DT == kDtypeFp4 && SWZ && !SYNC && !kDmaLate), "mxfp4: fp4, swizzled rows, async copies");
     constexpr int kRA = RA;
     using P = Plan<DT, RA>;
     using Frag = typename Op<DT>::Frag;
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
     static_assert(!kMx || (kFr == kMT && kMT % 4 == 0 && kRA < kFr - 4), "mxfp8: one k-step per k-tile, quad ring");
+    static_assert(!kMx4 || (kFr == 2 * kMT && kRA < kMT - 4), "mxfp4: two k-steps per k-tile, quad ring");
     // The barrier's count: the scale copies of the k-tiles in between are
-    // 2 more loads per k-tile (those of the barrier's own tile precede its
-    // last A copy).
-    constexpr int kVm = P::vm_at_barrier() + (kMx ? 2 * (kDmaAhead - 2) : 0);
+    // 2 (mxfp8) or 4 (mxfp4) more loads per k-tile (those of the barrier's
+    // own tile precede its last A copy).
+    constexpr int kXCopies = kMx ? 2 : kMx4 ? 4 : 0;
+    constexpr int kVm = P::vm_at_barrier() + kXCopies * (kDmaAhead - 2);
     static_assert(kVm <= 63, "vmcnt field is 6 bits");
     // One LDS object (the A ring, then for mxfp8 the scale stages): the
     // compiler's wait insertion keeps the async copies and the LDS reads of
     // one object apart by their order, where a second object made it wait
     // for every copy in flight before each read.
-    constexpr int kXBytes = kMx ? kRing * 2048 : 0;
+    constexpr int kXStage = kMx ? 2048 : kMx4 ? 4096 : 0;   // scale bytes per stage
+    constexpr int kXBytes = kRing * kXStage;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf + kXBytes];
 
     const int lane = threadIdx.x & 63;
@@ -214,16 +237,31 @@ gemm_w4_kernel(const GemmArgs p)
     // 16*(e%16) + e/16 and column 64*wave + 16*(lane%4) + lane/4 of this
     // k-tile's scale block; rows >= M and columns >= N are past the ranges and
     // stage 0 (2^-127, finite), which only ever scales zero data.
-    [[maybe_unused]] const int kblk = p.K / 128;
-    [[maybe_unused]] const auto rXa = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblk : nullptr,
-                                                kMx ? clamp_bytes((int64_t)(p.M - m0) * kblk) : 0);
-    [[maybe_unused]] const auto rXb = make_rsrc(kMx ? static_cast<const uint8_t *>(p.sB) + (int64_t)n0 * kblk : nullptr,
-                                                kMx ? clamp_bytes((int64_t)(p.N - n0) * kblk) : 0);
+    // (mxfp4: rows of the scale arrays are K/32 bytes, and a k-tile's dwords
+    // start at byte koff / 16 of a row, koff in K-bytes of two values each.)
+    [[maybe_unused]] const int kblk = kMx4 ? p.K / 32 : p.K / 128;
+    constexpr bool kX = kMx || kMx4;
+    [[maybe_unused]] const auto rXa = make_rsrc(kX ? static_cast<const uint8_t *>(p.sA) + (int64_t)m0 * kblk : nullptr,
+                                                kX ? clamp_bytes((int64_t)(p.M - m0) * kblk) : 0);
+    [[maybe_unused]] const auto rXb = make_rsrc(kX ? static_cast<const uint8_t *>(p.sB) + (int64_t)n0 * kblk : nullptr,
+                                                kX ? clamp_bytes((int64_t)(p.N - n0) * kblk) : 0);
     [[maybe_unused]] const uint32_t xa_voff =
         (uint32_t)(16 * ((wave * 64 + lane) % 16) + (wave * 64 + lane) / 16) * (uint32_t)kblk;
     [[maybe_unused]] const uint32_t xb_voff = (uint32_t)(64 * wave + 16 * (lane & 3) + (lane >> 2)) * (uint32_t)kblk;
+    // mxfp4 copy j (0, 1) of this wave: dword e = 128*wave + 64*j + lane of the
+    // row region (row 16*((e/2)%16) + e/32, dword e%2) and dword e' = 64*j +
+    // lane of this wave's part of the column region (column 64*wave +
+    // 16*((e'/2)%4) + (e'/8)%16, dword e'%2).
+    [[maybe_unused]] uint32_t xa4_voff[2], xb4_voff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = 128 * wave + 64 * j + lane, e2 = 64 * j + lane;
+        xa4_voff[j] = (uint32_t)(16 * ((e / 2) % 16) + e / 32) * (uint32_t)kblk + 4u * (uint32_t)(e % 2);
+        xb4_voff[j] = (uint32_t)(64 * wave + 16 * ((e2 / 2) % 4) + (e2 / 8) % 16) * (uint32_t)kblk +
+                      4u * (uint32_t)(e2 % 2);
+    }
     auto xstage = [&](int t) -> uint32_t * {
-        return reinterpret_cast<uint32_t *>(lds + kRing * kBuf + (kMx ? (t & (kRing - 1)) * 2048 : 0));
+        return reinterpret_cast<uint32_t *>(lds + kRing * kBuf + (kX ? (t & (kRing - 1)) * kXStage : 0));
     };
     auto dma_scales = [&](int t, uint32_t koff) {
         if constexpr (kMx) {
@@ -231,13 +269,32 @@ gemm_w4_kernel(const GemmArgs p)
                 rXa, (__attribute__((address_space(3))) void *)(xstage(t) + wave * 64), 1, xa_voff, koff / 128u, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rXb, (__attribute__((address_space(3))) void *)(xstage(t) + 256 + wave * 64), 1, xb_voff, koff / 128u, 0, 0);
+        } else if constexpr (kMx4) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rXa, (__attribute__((address_space(3))) void *)(xstage(t) + 128 * wave + 64 * j), 4, xa4_voff[j],
+                    koff / 16u, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rXb, (__attribute__((address_space(3))) void *)(xstage(t) + 512 + 128 * wave + 64 * j), 4,
+                    xb4_voff[j], koff / 16u, 0, 0);
+            }
         }
     };
-    [[maybe_unused]] i32x4 xq[4];              // A scales of row tiles 4q..4q+3 (slot q)
-    [[maybe_unused]] i32x4 xb_cur, xb_next;    // B scales of this and the next k-tile, one per strip
+    [[maybe_unused]] i32x4 xq[4];              // mxfp8: A scales of row tiles 4q..4q+3 (slot q)
+    [[maybe_unused]] i32x4 xb_cur, xb_next;    // mxfp8: B scales of this and the next k-tile, one per strip
+    [[maybe_unused]] i32x4 xq4[4][2];          // mxfp4: A scale dwords of row tiles 4q..4q+3, both steps
+    [[maybe_unused]] i32x4 xb4_next[2];        // mxfp4: the next k-tile's column dwords [strip][step]
+    [[maybe_unused]] int eb4[4][2];            // mxfp4: this k-tile's column scale bytes [strip][step]
+    [[maybe_unused]] const uint32_t xsh = 8u * (uint32_t)(lane >> 4);   // mxfp4: this lane's byte of a dword
     auto read_xb = [&](int t) {
-        if constexpr (kMx)
+        if constexpr (kMx) {
             xb_next = *reinterpret_cast<const i32x4 *>(xstage(t) + 256 + 4 * (wave * 16 + (lane & 15)));
+        } else if constexpr (kMx4) {
+            const uint32_t *b = xstage(t) + 512 + 8 * (wave * 16 + (lane & 15));
+            xb4_next[0] = *reinterpret_cast<const i32x4 *>(b);
+            xb4_next[1] = *reinterpret_cast<const i32x4 *>(b + 4);
+        }
     };
 
     // B: this wave's 4 strips; strips >= N/16 are past the range (zero).
@@ -276,12 +333,18 @@ gemm_w4_kernel(const GemmArgs p)
         const int s = f / kMT, mt = f % kMT;
         if constexpr (kMx) {
             if (mt % 4 == 0)
-                xq[mt / 4] = *reinterpret_cast<const i32x4 *>(lds + kRing * kBuf + (st / kBuf) * 2048 +
+                xq[mt / 4] = *reinterpret_cast<const i32x4 *>(lds + kRing * kBuf + (st / kBuf) * kXStage +
                                                               4 * (16 * (lane & 15) + mt));
+        } else if constexpr (kMx4) {
+            if (s == 0 && mt % 4 == 0) {
+                const uint8_t *q = lds + kRing * kBuf + (st / kBuf) * kXStage + 8 * (16 * (lane & 15) + mt);
+                xq4[mt / 4][0] = *reinterpret_cast<const i32x4 *>(q);
+                xq4[mt / 4][1] = *reinterpret_cast<const i32x4 *>(q + 16);
+            }
         }
         if constexpr (SWZ) {
             const uint8_t *row = lds + st + mt * 2048;
-            if constexpr (DT == kDtypeBf16)
+            if constexpr (kStepCh == 1)
                 ring[f % (kRA + 1)] = *reinterpret_cast<const i32x4 *>(row + a_off[s]);
             else
                 ring[f % (kRA + 1)] = cat(*reinterpret_cast<const i32x4 *>(row + a_off[0]),
@@ -342,6 +405,14 @@ gemm_w4_kernel(const GemmArgs p)
             if constexpr (kMx) {
                 if (f == 0)
                     xb_cur = xb_next;
+            } else if constexpr (kMx4) {
+                if (f == 0) {
+#pragma unroll
+                    for (int c = 0; c < kNT; ++c)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            eb4[c][s2] = (int)__builtin_amdgcn_ubfe((uint32_t)xb4_next[c / 2][(c % 2) * 2 + s2], xsh, 8u);
+                }
             }
             if (f == kBar) {
                 if constexpr (SYNC)   // this wave's LDS writes of tile t+1 (and earlier) are done
@@ -356,8 +427,13 @@ gemm_w4_kernel(const GemmArgs p)
             // this position's B reloads, then its A copies.
             const int st = f / kMT, mt = f % kMT;
             const Frag &a = ring[f % (kRA + 1)];
+            [[maybe_unused]] int ea4 = 0;
+            if constexpr (kMx4)   // this fragment's row scale byte
+                ea4 = (int)__builtin_amdgcn_ubfe((uint32_t)xq4[mt / 4][(mt % 4) / 2][(mt % 2) * 2 + st], xsh, 8u);
             auto mf = [&](int nt) {
-                if constexpr (DT == kDtypeBf16)
+                if constexpr (kMx4)
+                    mfma_acc_mx4(acc[mt][nt], breg[SET][nt][st], a, eb4[nt][st], ea4);
+                else if constexpr (DT == kDtypeBf16)
                     mfma_acc(acc[mt][nt], breg[SET][nt][st], a);
                 else if constexpr (kMx)
                     mfma_acc_mx(acc[mt][nt], cat(breg[SET][nt][0], breg[SET][nt][1]), a, xb_cur[nt], xq[mt / 4][mt % 4]);
@@ -544,9 +620,10 @@ static const KernelSpec kW4Kernels[] = {
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, 1, 1, 0),
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 0, 0),
     DGP_W4(kDtypeFp8, kScaleTensor, kOutBf16, 3, 1, w4::kRA, 1, 1),
-    // mxfp8: the hardware-scaled MFMA with the k-tile's E8M0 bytes staged
-    // beside the A tile
+    // mxfp8 and mxfp4: the hardware-scaled MFMA with the k-tile's E8M0
+    // bytes staged beside the A tile
     DGP_W4_BOTH_OUT(kDtypeFp8, kScaleMx, 3, 1, w4::kRA, 1, 0),
+    DGP_W4_BOTH_OUT(kDtypeFp4, kScaleMx32, 3, 1, w4::kRA, 1, 0),
 };
 
 const KernelSpec *w4_kernels(int *count)

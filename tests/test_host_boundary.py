@@ -297,13 +297,13 @@ def test_default_selection(dgp):
         # the one-wave-per-SIMD tile with swizzled A rows
         assert (cfg.tile_m, cfg.tile_n, cfg.schedule, cfg.a_layout) == (256, 256, 4, 2)
     # blockscale, mxfp8 and mxfp4: the tiled kernels above decode-sized M
-    # (mxfp8 on the one-wave-per-SIMD tile, the others on the 8-wave tile),
-    # the 16-row tiles at it
+    # (the MX modes on the one-wave-per-SIMD tile, blockscale on the 8-wave
+    # tile), the 16-row tiles at it
     for dt, sm in ((dgp.FP8_E4M3, dgp.SCALE_BLOCK128), (dgp.FP8_E4M3, dgp.SCALE_MX128),
                    (dgp.FP4_E2M1, dgp.SCALE_MX32)):
         i = dgp.select_kernel(4096, 4096, 7168, dt, sm)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][0].tile_n, dgp.kernels()[i][2]) == (256, 256, sm)
-        assert dgp.kernels()[i][0].schedule == (4 if sm == dgp.SCALE_MX128 else 1)
+        assert dgp.kernels()[i][0].schedule == (1 if sm == dgp.SCALE_BLOCK128 else 4)
         i = dgp.select_kernel(300, 1024, 7168, dt, sm, 2)
         assert (dgp.kernels()[i][0].tile_m, dgp.kernels()[i][3]) == (128, True)
         assert dgp.kernels()[dgp.select_kernel(32, 16384, 7168, dt, sm)][0].tile_m == 16
