@@ -151,16 +151,16 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     if (M <= 32) {
         // Rules from cold sweeps of every 16-row and one-row tile at K = 7168
         // (every mode; M = 1, 2, 4 and 16; N 2048-16384; split 1-4).
-        // u = strips x splits; ks(t) = the K-split tile t columns wide (8
-        // waves), st(t) = the streaming tile, wv(t, w, d) = the one-row VALU
+        // u = strips x splits; ks(t, w) = the K-split tile t columns wide
+        // (w waves, 8 unless given), st(t) = the streaming tile, wv(t, w, d) = the one-row VALU
         // tile with w waves and a d-step ring.
         const int64_t u = N / 16 * split_k;
         const bool fp8t = dtype == DGP_FP8_E4M3 && scale == DGP_SCALE_TENSOR;
         const bool mx4 = scale == DGP_SCALE_MX32;
         const bool bs = scale == DGP_SCALE_BLOCK128, mx8 = scale == DGP_SCALE_MX128;
-        const auto ks = [&](int tn) {
+        const auto ks = [&](int tn, int waves = 8) {
             Query q{kStream, dtype, scale, out, 16, tn};
-            q.wm = 8;
+            q.wm = waves;
             return find_spec(q);
         };
         const auto st = [&](int tn) {
@@ -226,6 +226,11 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             return st(64);
         if (u < 1024 || fp8t)
             return ks(32);
+        // bf16 in one pass: the same 4 strips over 16 waves (M = 16, N =
+        // 16384: 37.5 vs 38.8 us)
+        if (dtype == DGP_BF16 && split_k == 1)
+            if (const KernelSpec *k = ks(64, 16))
+                return k;
         return ks(64);
     }
     const KernelSpec *k = nullptr;

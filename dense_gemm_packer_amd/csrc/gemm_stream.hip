@@ -651,6 +651,9 @@ static const KernelSpec kStreamKernels[] = {
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleBlock, 64),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp8, 8, 4, kScaleMx, 64),
     DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 8, 4, kScaleMx32, 64),
+    // bf16, four strips, 16 waves (4 per SIMD where the 8-wave tile has 2;
+    // the fp8 modes spill or lose with 16)
+    DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 16, 4, kScaleNone, 64),
 };
 
 const KernelSpec *stream_kernels(int *count)

@@ -1,5 +1,5 @@
 // gemm_w4_kernel -- the 256 x 256 large-M tile with one wave per SIMD
-// (bf16, per-tensor fp8 and mxfp8).
+// (bf16, per-tensor fp8, mxfp8 and mxfp4).
 //
 // Same operation, operand layouts and epilogue as gemm_tiled_kernel
 // (gemm_tiled.hip, gemm_common.h): per k-tile of 128 bytes the A tile goes

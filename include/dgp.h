@@ -98,7 +98,8 @@ typedef enum dgp_scale_mode {
  *                    256x256, 128x256, 128x128 for bf16 and per-tensor fp8;
  *                    256x256 and 128x128 for fp8 blockscale, mxfp8 and mxfp4;
  *                    16x64 and 16x32 streaming (4 and 2 waves); K-split
- *                    (8 waves) over 16x8 -- half a strip, two workgroups
+ *                    (8 waves; bf16 16x64 also 16) over 16x8 -- half a
+ *                    strip, two workgroups
  *                    per 16-column strip -- 16x16, 16x32 and 16x64; every
  *                    16-row tile for every mode; one-row VALU tiles 1x16
  *                    and 1x8 for bf16 and per-tensor fp8 -- [P3] file
@@ -121,7 +122,7 @@ typedef enum dgp_scale_mode {
  *   waves_m        : tiled kernels: waves along M inside the workgroup; the
  *                    16-row streaming kernel (tile_m = 16, tile_n 32 or 64):
  *                    waves per workgroup, each owning tile_n / (16 * waves)
- *                    strips; the K-split kernel (8 waves): waves sharing
+ *                    strips; the K-split kernel (8 or 16 waves): waves sharing
  *                    the tile's K range, which also tells the 16x32 and
  *                    16x64 K-split tiles from the streaming ones (0 = the
  *                    first compiled kernel for this tile: the streaming one);

@@ -281,13 +281,14 @@ def test_every_kernel_is_selected_by_its_reported_config(dgp):
 
 
 def _pick(dgp, M, N, split, dt, sm):
-    """The built-in choice as 'k<tile_n>' (K-split tiles, 8 waves) or 's<tile_n>' (streaming)."""
+    """The built-in choice as 'k<tile_n>' (K-split tiles, 8 waves; 'K<tile_n>' with 16) or
+    's<tile_n>' (streaming)."""
     c = dgp.kernels()[dgp.select_kernel(M, N, 7168, dt, sm, split)][0]
     if c.tile_m == 1:   # one-row VALU tile
         return f"w{c.tile_n}"
     if c.tile_m != 16:
         return f"t{c.tile_m}x{c.tile_n}"
-    return ("k" if c.waves_m == 8 else "s") + str(c.tile_n)
+    return {8: "k", 16: "K"}.get(c.waves_m, "s") + str(c.tile_n)
 
 
 def test_default_selection(dgp):
@@ -313,7 +314,7 @@ def test_default_selection(dgp):
         "tensor": "16/16384/1:k32 16/16384/2:k32 16/8192/1:k32 16/4096/1:k16 16/4096/4:k32 16/2048/1:k8 "
                   "16/2048/2:k16 16/2048/8:k32 4/16384/1:k16 1/16384/1:w16 1/8192/1:w16 1/2048/1:w8 1/16384/2:w16 "
                   "1/2048/2:w16 4/16384/2:k32 4/4096/4:k32 4/16384/4:s64 2/2048/1:k8",
-        "bf16": "16/16384/1:k64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/2048/8:k64 4/16384/1:k16 "
+        "bf16": "16/16384/1:K64 32/16384/1:K64 16/16384/2:k64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/2048/8:k64 4/16384/1:k16 "
                 "1/16384/1:w16 1/2048/1:w8 1/16384/2:w16 2/2048/1:k8 4/16384/2:k16 4/8192/4:k32",
         "mx32": "16/16384/1:k64 16/16384/2:s64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/4096/4:k64 "
                 "16/2048/4:k32 16/2048/2:k16 4/16384/1:k16 4/8192/1:k16 1/16384/1:k16 1/16384/2:k32 1/2048/1:k8 "
