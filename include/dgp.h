@@ -141,7 +141,11 @@ typedef enum dgp_scale_mode {
  *                    (preload must be (0, 0)); 3 = both in LDS: A and the
  *                    preshuffled B tile both go global -> LDS with the async
  *                    copy (two stages), and the waves read both operands from
- *                    LDS; 0 = the tile's tuned default.
+ *                    LDS; 4 = one wave per SIMD: 4 waves each owning all
+ *                    256 rows and 64 columns of the 256x256 tile, 256
+ *                    accumulators per lane in AGPRs (the built-in large-M
+ *                    kernel for bf16, per-tensor fp8, mxfp8 and mxfp4);
+ *                    0 = the tile's tuned default.
  *                    Must be 0 for the streaming kernel.  Zero-initialising
  *                    the whole struct and setting tile_m = 0 selects the
  *                    built-in table, like NULL. */
