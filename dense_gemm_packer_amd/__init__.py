@@ -13,13 +13,17 @@ DGP_FP4_E2M1.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdgp.so")
+# The LDS-poison debug build of the same sources (see lds_poison_build).
+LDS_POISON_LIB_PATH = os.path.join(_HERE, "libdgp_lds_poison.so")
 
 BF16 = 0
 FP8_E4M3 = 1
@@ -57,21 +61,52 @@ EXPORTS = ("dgp_preshuffle_b", "dgp_unshuffle_b", "dgp_gemm_preshuffle", "dgp_sp
            "dgp_gemm_preshuffle_splitk", "dgp_gemm_preshuffle_splitk_noalloc", "dgp_check_arch", "dgp_status_string", "dgp_last_error",
            "dgp_tile_of_workgroup", "dgp_tile_map", "dgp_kernel_count", "dgp_kernel_info", "dgp_select_kernel",
            "dgp_probe_mfma_layout", "dgp_probe_mfma_scaled", "dgp_probe_lds_dma", "dgp_probe_lds_dma_narrow", "dgp_probe_copy",
-           "dgp_probe_stream_read", "dgp_probe_mfma_peak")
+           "dgp_probe_stream_read", "dgp_probe_mfma_peak", "dgp_lds_poison")
 
 _lib = None
+_loaded = {}                 # path -> CDLL
+_swap = threading.Lock()     # serialises lds_poison_build's switch of the active library
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libdgp.so.  Raises if it has not been built."""
+    """The active library: libdgp.so unless inside lds_poison_build().  Raises
+    if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def lds_poison_build():
+    """Run every call made inside the block on the LDS-poison debug build
+    (libdgp_lds_poison.so, built beside libdgp.so by the same build step): the
+    same entry points and kernels, with each kernel's LDS filled with 0xFF
+    bytes before use and each global -> LDS copy's destination poisoned until
+    the copy lands, so a read of LDS no copy filled shows up as NaN or a wrong
+    value in a bit-exact comparison.  For tests; the switch is process-wide
+    (one block at a time)."""
+    global _lib
+    with _swap:
+        saved = lib()
+        poison = _load(LDS_POISON_LIB_PATH)
+        if poison.dgp_lds_poison() != 1:
+            raise ImportError(f"{LDS_POISON_LIB_PATH} is not an LDS-poison build")
+        _lib = poison
+        try:
+            yield poison
+        finally:
+            _lib = saved
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
                           "(or python dense_gemm_packer_amd/build.py)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     sigs = {
         "dgp_preshuffle_b": [_vp, _vp, _i64, _i64, _int, _vp],
         "dgp_unshuffle_b": [_vp, _vp, _i64, _i64, _int, _vp],
@@ -105,7 +140,9 @@ def lib() -> ctypes.CDLL:
     L.dgp_status_string.restype = ctypes.c_char_p
     L.dgp_last_error.argtypes = []
     L.dgp_last_error.restype = ctypes.c_char_p
-    _lib = L
+    L.dgp_lds_poison.argtypes = []
+    L.dgp_lds_poison.restype = _int
+    _loaded[path] = L
     return L
 
 

@@ -6,6 +6,13 @@
 
 namespace dgp {
 
+// The LDS-poison debug build compiles every source with DGP_LDS_POISON=1
+// (gemm_common.h: lds_poison_fill, lds_dma).
+#ifndef DGP_LDS_POISON
+#define DGP_LDS_POISON 0
+#endif
+constexpr bool kLdsPoison = DGP_LDS_POISON != 0;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -633,6 +633,11 @@ dgp_status dgp_tile_map(int64_t tiles_m, int64_t tiles_n, int64_t splits, int xc
     return ok();
 }
 
+int dgp_lds_poison(void)
+{
+    return dgp::kLdsPoison ? 1 : 0;
+}
+
 int dgp_kernel_count(void)
 {
     int n = 0;

@@ -103,10 +103,62 @@ __device__ inline typename Op<DT>::Frag lds_frag(const uint8_t *p)
     }
 }
 
+// ------------------------------------------------------------ LDS poison
+//
+// The LDS-poison debug build (the library compiled a second time with
+// DGP_LDS_POISON=1, libdgp_lds_poison.so) turns a kernel that reads LDS its
+// copies have not filled -- a tile only partly loaded, or a read that runs
+// ahead of the wait for its copy -- into a parity failure instead of a quiet
+// wrong answer at full speed.  Every kernel fills its LDS with 0xFF bytes
+// before its first copy (a NaN in bf16, e4m3, E8M0 and fp32; -6 in E2M1),
+// and every global -> LDS copy first overwrites its own destination with
+// 0xFF and waits for that write, so LDS holds poison from the moment a
+// stage is handed to a copy until the copy lands.  The library built
+// without the flag (kLdsPoison false, common.h) compiles none of it.
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) int lds_i32;
+
+// Poison build: fill bytes [0, bytes) of an LDS array (bytes a multiple of
+// 16) with 0xFF, spread over the workgroup's threads.  The caller
+// synchronises the workgroup before the first copy.
+__device__ inline void lds_poison_fill(void *lds_base, int bytes)
+{
+    if constexpr (kLdsPoison) {
+        lds_i32x4 *d = (lds_i32x4 *)lds_base;
+        for (int i = (int)threadIdx.x; i < bytes / 16; i += (int)(blockDim.x * blockDim.y * blockDim.z))
+            d[i] = i32x4{-1, -1, -1, -1};
+    }
+}
+
+// Async global -> LDS copy of BYTES (16, 4, 2 or 1) per lane: lane l's
+// 16 bytes land at lds_dst + 16 l, a narrow copy's value zero-extended in
+// dword l.  Poison build: that destination is overwritten with 0xFF first.
+template <int BYTES>
+__device__ inline void lds_dma(__amdgpu_buffer_rsrc_t r, void *lds_dst, uint32_t voff, uint32_t soff)
+{
+    static_assert(BYTES == 16 || BYTES == 4 || BYTES == 2 || BYTES == 1, "copy width");
+    if constexpr (kLdsPoison) {
+        const int lane = (int)(threadIdx.x & 63);
+        if constexpr (BYTES == 16)
+            ((lds_i32x4 *)lds_dst)[lane] = i32x4{-1, -1, -1, -1};
+        else
+            ((lds_i32 *)lds_dst)[lane] = -1;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    auto *d = (__attribute__((address_space(3))) void *)lds_dst;
+    if constexpr (BYTES == 16)   // (the size operand must be a literal)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, voff, soff, 0, 0);
+    else if constexpr (BYTES == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, voff, soff, 0, 0);
+    else if constexpr (BYTES == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 2, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 1, voff, soff, 0, 0);
+}
+
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_dst, uint32_t voff, uint32_t soff)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, soff, 0, 0);
+    lds_dma<16>(r, lds_dst, voff, soff);
 }
 
 // ------------------------------------------------------------ load ring

@@ -60,6 +60,10 @@ gemm_lds_kernel(const GemmArgs p)
     static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
     static_assert(kMfmaPh % 2 == 0 && kMfmaPh >= kDma, "phase too short for its copies");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+    if constexpr (kLdsPoison) {   // debug build: all of LDS poisoned before the first copy
+        lds_poison_fill(lds, (int)sizeof(lds));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -54,6 +54,14 @@ gemm_stream_kernel(const GemmArgs p, int panel)
     // then one of the workgroup's columns (row stride nsteps + 1 dwords).
     constexpr int kCols = NW * SPW * 16;
     uint32_t *lds_x4 = reinterpret_cast<uint32_t *>(lds_a + 16 * panel);
+    if constexpr (kLdsPoison) {   // debug build: all of LDS poisoned before the first copy
+        lds_poison_fill(lds_a, 16 * panel + (SCALE == kScaleMx32 ? (int)stream_mx32_scale_bytes(kCols, panel) : 0));
+        lds_poison_fill(lds_sa, (int)sizeof(lds_sa));
+        lds_poison_fill(lds_sb, (int)sizeof(lds_sb));
+        lds_poison_fill(lds_xa, (int)sizeof(lds_xa));
+        lds_poison_fill(lds_xb, (int)sizeof(lds_xb));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -171,9 +179,7 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                     const int e = j * 64 + lane;
                     const int r = e / stride < rows ? e / stride : rows - 1;
                     const int st = e % stride < nsteps ? e % stride : nsteps - 1;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rs, (__attribute__((address_space(3))) void *)(dst + j * 64), 4,
-                        (uint32_t)r * (uint32_t)kblocks_row + kb0 + 4u * (uint32_t)st, 0, 0, 0);
+                    lds_dma<4>(rs, dst + j * 64, (uint32_t)r * (uint32_t)kblocks_row + kb0 + 4u * (uint32_t)st, 0u);
                 }
             };
             stage(rXa, lds_x4, 16);
@@ -324,6 +330,10 @@ gemm_ksplit_kernel(const GemmArgs p)
     constexpr int kStepCh = Op<DT>::kBlocks;
     constexpr int kStepBytes = 64 * kStepCh;
     __shared__ f32x4 red[NW][SPW][64];
+    if constexpr (kLdsPoison) {   // debug build: the partial-sum array poisoned before its writes
+        lds_poison_fill(red, (int)sizeof(red));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -59,6 +59,10 @@ gemm_tiled_kernel(const GemmArgs p)
     // DEPTH sets of B registers.
     constexpr int kRing = DEPTH + 1;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kStageBytes];
+    if constexpr (kLdsPoison) {   // debug build: all of LDS poisoned before the first copy
+        lds_poison_fill(lds, (int)sizeof(lds));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -164,14 +168,13 @@ gemm_tiled_kernel(const GemmArgs p)
         if constexpr (kXS) {
 #pragma unroll
             for (int j = 0; j < kXDma; ++j) {
-                auto *d = (__attribute__((address_space(3))) void *)(lds + buf_off + S::kBufBytes +
-                                                                     (j * S::kWaves + wave) * 256);
-                if constexpr (kX4)   // the size operand must be a literal
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 4, x_voff[j], koff / 16u, 0, 0);
+                uint8_t *d = lds + buf_off + S::kBufBytes + (j * S::kWaves + wave) * 256;
+                if constexpr (kX4)
+                    lds_dma<4>(x_rsrc[j], d, x_voff[j], koff / 16u);
                 else if constexpr (kES == 4)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 4, x_voff[j], (koff / 128u) * 4u, 0, 0);
+                    lds_dma<4>(x_rsrc[j], d, x_voff[j], (koff / 128u) * 4u);
                 else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc[j], d, 1, x_voff[j], koff / 128u, 0, 0);
+                    lds_dma<1>(x_rsrc[j], d, x_voff[j], koff / 128u);
             }
         }
     };
@@ -523,6 +526,10 @@ gemm_pingpong_kernel(const GemmArgs p)
     constexpr int kRing = 3;
     constexpr int kFrP = DT == kDtypeBf16 ? 16 : 8;   // A fragments per phase: 16 LDS reads either way
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * S::kBufBytes];
+    if constexpr (kLdsPoison) {   // debug build: all of LDS poisoned before the first copy
+        lds_poison_fill(lds, (int)sizeof(lds));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -192,6 +192,10 @@ gemm_w4_kernel(const GemmArgs p)
     constexpr int kXStage = kMx ? 2048 : kMx4 ? 4096 : 0;   // scale bytes per stage
     constexpr int kXBytes = kRing * kXStage;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBuf + kXBytes];
+    if constexpr (kLdsPoison) {   // debug build: all of LDS poisoned before the first copy
+        lds_poison_fill(lds, (int)sizeof(lds));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -265,19 +269,13 @@ gemm_w4_kernel(const GemmArgs p)
     };
     auto dma_scales = [&](int t, uint32_t koff) {
         if constexpr (kMx) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rXa, (__attribute__((address_space(3))) void *)(xstage(t) + wave * 64), 1, xa_voff, koff / 128u, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rXb, (__attribute__((address_space(3))) void *)(xstage(t) + 256 + wave * 64), 1, xb_voff, koff / 128u, 0, 0);
+            lds_dma<1>(rXa, xstage(t) + wave * 64, xa_voff, koff / 128u);
+            lds_dma<1>(rXb, xstage(t) + 256 + wave * 64, xb_voff, koff / 128u);
         } else if constexpr (kMx4) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rXa, (__attribute__((address_space(3))) void *)(xstage(t) + 128 * wave + 64 * j), 4, xa4_voff[j],
-                    koff / 16u, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rXb, (__attribute__((address_space(3))) void *)(xstage(t) + 512 + 128 * wave + 64 * j), 4,
-                    xb4_voff[j], koff / 16u, 0, 0);
+                lds_dma<4>(rXa, xstage(t) + 128 * wave + 64 * j, xa4_voff[j], koff / 16u);
+                lds_dma<4>(rXb, xstage(t) + 512 + 128 * wave + 64 * j, xb4_voff[j], koff / 16u);
             }
         }
     };

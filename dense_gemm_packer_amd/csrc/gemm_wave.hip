@@ -89,6 +89,10 @@ gemm_wave_kernel(const GemmArgs p)
     constexpr bool kHalf = TN == 8;
     constexpr uint32_t kStepBytes = kHalf ? 128u : 64u;   // K-bytes per step
     __shared__ float red[NW][TN];
+    if constexpr (kLdsPoison) {   // debug build: the partial-sum array poisoned before its writes
+        lds_poison_fill(red, (int)sizeof(red));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -58,6 +58,21 @@ int dgp_kernel_count(void);
 dgp_status dgp_kernel_info(int index, dgp_config *cfg, int *dtype, int *scale_mode, int *split_out);
 
 /*
+ * dgp_lds_poison -- 1 in the LDS-poison debug build of the library
+ * (libdgp_lds_poison.so: the same sources compiled with DGP_LDS_POISON=1),
+ * 0 in the release build.  In the debug build every GEMM kernel fills its
+ * LDS with 0xFF bytes before its first global -> LDS copy, and every copy
+ * first overwrites its own destination with 0xFF and waits for that write:
+ * a read of LDS that no copy filled, or one that runs ahead of the wait for
+ * its copy, yields NaN (bf16, e4m3, E8M0 and fp32 bytes) or -6 (E2M1) and
+ * fails a bit-exact parity check, instead of giving a plausible wrong
+ * answer at full speed -- the failure mode of a tile only partly loaded
+ * ([P2] follow-up commit, item 1).  Same entry points, same results on
+ * correct kernels; slower, for tests only.  Pure host function.
+ */
+int dgp_lds_poison(void);
+
+/*
  * dgp_select_kernel -- which compiled GEMM kernel a call would launch.
  *
  * Runs the shape and configuration checks of dgp_gemm_preshuffle_splitk

@@ -56,6 +56,28 @@ def test_library_exports_every_declared_symbol(dgp, L):
     assert names <= exported
 
 
+def test_lds_poison_build_exports_the_same_symbols(dgp, L):
+    """The debug build is the same library with the LDS poison compiled in:
+    every declared symbol, the same kernel table, and dgp_lds_poison() = 1
+    (0 in the release build)."""
+    names = declared_symbols()
+    out = subprocess.run(["nm", "-D", "--defined-only", dgp.LDS_POISON_LIB_PATH], capture_output=True,
+                         text=True).stdout
+    assert names <= set(re.findall(r"\bT (dgp_\w+)", out))
+    assert L.dgp_lds_poison() == 0
+    release = [(c.tile_m, c.tile_n, c.waves_m, c.prefetch, c.schedule, dt, sm, so)
+               for c, dt, sm, so in dgp.kernels()]
+    with dgp.lds_poison_build() as P:
+        assert P.dgp_lds_poison() == 1 and dgp.lib() is P
+        assert P.dgp_kernel_count() == L.dgp_kernel_count() == len(release)
+        for i, (tm, tn, wm, pf, sch, dt, sm, so) in enumerate(release):
+            cfg, d, m, o = dgp.Config(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+            assert P.dgp_kernel_info(i, ctypes.byref(cfg), ctypes.byref(d), ctypes.byref(m), ctypes.byref(o)) == OK
+            assert (cfg.tile_m, cfg.tile_n, cfg.waves_m, cfg.prefetch, cfg.schedule, d.value, m.value,
+                    bool(o.value)) == (tm, tn, wm, pf, sch, dt, sm, bool(so))
+    assert dgp.lib() is L
+
+
 def test_check_arch(L):
     assert L.dgp_check_arch(b"gfx950") == OK
     assert L.dgp_check_arch(b"gfx950:sramecc+:xnack-") == OK
