@@ -444,8 +444,8 @@ def describe_kernel(index: int) -> str:
     """One-line description of compiled kernel `index`."""
     cfg, dt, sm, so = kernels()[index]
     dts = {BF16: "bf16", FP8_E4M3: "fp8", FP4_E2M1: "fp4"}[dt]
-    # the K-split tiles run 8 waves per workgroup (16 for one bf16 tile), the
-    # streaming tiles 2 or 4
+    # the K-split tiles run 8 waves per workgroup (16 for a bf16 tile and three
+    # mxfp4 tiles), the streaming tiles 2 or 4
     if cfg.tile_m == 16 and (cfg.tile_n in (8, 16) or cfg.waves_m in (8, 16)):
         half = ", half a strip" if cfg.tile_n == 8 else ""
         return (f"gemm_ksplit_kernel<{dts}, 16x{cfg.tile_n} tile{half}, K split over {cfg.waves_m} waves, "

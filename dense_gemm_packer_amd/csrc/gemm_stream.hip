@@ -664,6 +664,11 @@ static const KernelSpec kStreamKernels[] = {
     // bf16, four strips, 16 waves (4 per SIMD where the 8-wave tile has 2;
     // the fp8 modes spill or lose with 16)
     DGP_KSPLIT_BOTH_OUT(kDtypeBf16, 16, 4, kScaleNone, 64),
+    // mxfp4, 16 waves over half a strip, one or two strips: each wave's slice
+    // of one pass fits one 4-step group of its guarded loop
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 16, 4, kScaleMx32, 8),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 16, 4, kScaleMx32, 16),
+    DGP_KSPLIT_BOTH_OUT(kDtypeFp4, 16, 4, kScaleMx32, 32),
 };
 
 const KernelSpec *stream_kernels(int *count)

@@ -98,8 +98,9 @@ typedef enum dgp_scale_mode {
  *                    256x256, 128x256, 128x128 for bf16 and per-tensor fp8;
  *                    256x256 and 128x128 for fp8 blockscale, mxfp8 and mxfp4;
  *                    16x64 and 16x32 streaming (4 and 2 waves); K-split
- *                    (8 waves; bf16 16x64 also 16) over 16x8 -- half a
- *                    strip, two workgroups
+ *                    (8 waves; also 16 for bf16 16x64 and for mxfp4
+ *                    16x8, 16x16 and 16x32) over 16x8 -- half a strip, two
+ *                    workgroups
  *                    per 16-column strip -- 16x16, 16x32 and 16x64; every
  *                    16-row tile for every mode; one-row VALU tiles 1x16
  *                    and 1x8 for bf16 and per-tensor fp8 -- [P3] file

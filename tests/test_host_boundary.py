@@ -338,9 +338,9 @@ def test_default_selection(dgp):
                   "1/2048/2:w16 4/16384/2:k32 4/4096/4:k32 4/16384/4:s64 2/2048/1:k8",
         "bf16": "16/16384/1:K64 32/16384/1:K64 16/16384/2:k64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/2048/8:k64 4/16384/1:k16 "
                 "1/16384/1:w16 1/2048/1:w8 1/16384/2:w16 2/2048/1:k8 4/16384/2:k16 4/8192/4:k32",
-        "mx32": "16/16384/1:k64 16/16384/2:s64 16/8192/1:k32 16/8192/2:k64 16/4096/2:k32 16/4096/4:k64 "
-                "16/2048/4:k32 16/2048/2:k16 4/16384/1:k16 4/8192/1:k16 1/16384/1:k16 1/16384/2:k32 1/2048/1:k8 "
-                "4/16384/4:s64",
+        "mx32": "16/16384/1:k64 16/16384/2:s64 16/8192/1:K32 16/8192/2:k64 16/4096/2:k32 16/4096/4:k64 "
+                "16/2048/4:k32 16/2048/2:k16 4/16384/1:k16 4/8192/1:K32 1/16384/1:k16 1/16384/2:k32 1/2048/1:K16 "
+                "4/16384/4:s64 16/2048/1:K8 16/4096/1:K16 4/4096/1:K16 1/8192/1:K32",
         "block128": "16/16384/1:k64 16/8192/1:k32 16/4096/4:k64 16/2048/4:k32 4/2048/4:k32 1/16384/1:k32 "
                     "1/8192/1:k32 16/16384/4:s64 16/8192/4:s64 16/16384/2:k64",
         "mx128": "16/16384/1:k64 16/8192/1:k32 16/2048/8:k64 4/8192/1:k32 1/16384/1:k64 1/8192/1:k32 "
