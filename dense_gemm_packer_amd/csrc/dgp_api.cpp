@@ -188,10 +188,10 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             if (k)
                 return k;
         }
-        // Blockscale from 4 splits and mxfp8 from 2 over at least 2048
-        // strips x splits: the streaming 16x64 tile (5-19 % ahead), whose A
-        // panel in LDS serves four strips per wave.
-        if (u >= 2048 && ((bs && split_k >= 4) || (mx8 && split_k >= 2)))
+        // Blockscale and mxfp8 from 4 splits over at least 2048 strips x
+        // splits: the streaming 16x64 tile (5-19 % ahead), whose A panel in
+        // LDS serves four strips per wave.
+        if (u >= 2048 && (bs || mx8) && split_k >= 4)
             return st(64);
         // mxfp4 in one pass over at most 512 strips: 16 waves per workgroup,
         // so each wave's K slice is one 4-step group of the guarded loop
@@ -223,7 +223,10 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             }
             if (u < 512)
                 return ks(16);
-            return (mx8 && u >= 1024) ? ks(64) : ks(32);
+            // (mxfp8 in one or two passes: the 32-column tile, whose 3-step
+            // ring keeps two workgroups per CU: 20.3-20.7 vs 20.9-21.1 us at
+            // N = 16384)
+            return (mx8 && u >= 1024 && split_k > 2) ? ks(64) : ks(32);
         }
         // More rows: A is read once per workgroup, so wider K-split tiles
         // (2 or 4 strips sharing each A fragment) lead from 512 strips x
@@ -233,7 +236,9 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
             return ks(16);
         if (mx4 && u >= 2048)
             return st(64);
-        if (u < 1024 || fp8t)
+        // (mxfp8 at 2 splits: 24.9 vs 25.6 us for the streaming tile at M =
+        // 16, N = 16384)
+        if (u < 1024 || fp8t || (mx8 && split_k == 2))
             return ks(32);
         // bf16 in one pass: the same 4 strips over 16 waves (M = 16, N =
         // 16384: 37.5 vs 38.8 us)

@@ -343,8 +343,8 @@ def test_default_selection(dgp):
                 "4/16384/4:s64 16/2048/1:K8 16/4096/1:K16 4/4096/1:K16 1/8192/1:K32",
         "block128": "16/16384/1:k64 16/8192/1:k32 16/4096/4:k64 16/2048/4:k32 4/2048/4:k32 1/16384/1:k32 "
                     "1/8192/1:k32 16/16384/4:s64 16/8192/4:s64 16/16384/2:k64",
-        "mx128": "16/16384/1:k64 16/8192/1:k32 16/2048/8:k64 4/8192/1:k32 1/16384/1:k64 1/8192/1:k32 "
-                 "16/16384/2:s64 1/16384/4:s64 16/8192/2:k64",
+        "mx128": "16/16384/1:k64 16/8192/1:k32 16/2048/8:k64 4/8192/1:k32 1/16384/1:k32 1/8192/1:k32 "
+                 "16/16384/2:k32 1/16384/4:s64 16/8192/2:k32 4/16384/2:k32 16/16384/4:s64",
     }
     modes = {"tensor": (dgp.FP8_E4M3, dgp.SCALE_TENSOR), "bf16": (dgp.BF16, dgp.SCALE_NONE),
              "mx32": (dgp.FP4_E2M1, dgp.SCALE_MX32), "block128": (dgp.FP8_E4M3, dgp.SCALE_BLOCK128),
