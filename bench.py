@@ -162,6 +162,8 @@ ABLATIONS = (
     ("fragment work bunched ahead of its MFMAs", dict(_W4, a_layout=2, preload_vmem=0, preload_dsrd=7)),
     ("8 waves (2 per SIMD), interleaved", dict(tile_m=256, tile_n=256, tile_k=128, xcd_remap=1, group_m=8,
                                                 schedule=1, prefetch=2)),
+    ("2 x 2 waves (each 128 x 128), B 2 k-tiles deep", dict(_W4, a_layout=2, waves_m=2, prefetch=2,
+                                                            preload_vmem=1, preload_dsrd=7)),
 )
 
 

@@ -37,8 +37,6 @@ namespace dgp {
 namespace w4 {
 
 constexpr int TM = 256, TN = 256, NW = 4, KT = 128;
-constexpr int kMT = 16;                  // 16-row tiles per wave
-constexpr int kNT = 4;                   // 16-column strips per wave
 constexpr int kCH = KT / 64;             // 64-byte chunks per k-tile
 constexpr int kRing = 4;                 // LDS stages
 constexpr int kBuf = TM * KT;            // bytes per stage
@@ -50,8 +48,12 @@ constexpr bool kDmaLate = false;
 constexpr int kDmaAhead = kDmaLate ? 2 : 3;
 static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
 
-template <int DT, int RA>
+// WM = waves along M: 1 = the 1 x 4 split (each wave all 256 rows, 64
+// columns), 2 = 2 x 2 (each wave 128 rows, 128 columns).
+template <int DT, int RA, int WM = 1>
 struct Plan {
+    static constexpr int kMT = 16 / WM;                   // 16-row tiles per wave
+    static constexpr int kNT = 4 * WM;                    // 16-column strips per wave
     static constexpr int kStepCh = Op<DT>::kBlocks;       // 64-byte chunks per MFMA step
     static constexpr int kSteps = kCH / kStepCh;          // MFMA k-steps per k-tile
     static constexpr int kFr = kSteps * kMT;              // A fragments per k-tile
@@ -161,7 +163,7 @@ __device__ inline void mfma_acc_mx4(f32x4 &acc, const i32x4 &b, const i32x4 &a, 
 // quad of row tiles' 8 dwords in two 16-byte reads, and column 64w + 16c + i
 // at dword 512 + 2(4(16w + i) + c) + s; a lane's byte is taken with one
 // bit-field extract per fragment.
-template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_w4_kernel(const GemmArgs p)
 {
@@ -174,7 +176,10 @@ gemm_w4_kernel(const GemmArgs p)
     static_assert(!kMx || (DT == kDtypeFp8 && SWZ && !SYNC && !kDmaLate), "mxfp8: fp8, swizzled rows, async copies");
     static_assert(!kMx4 || (DT == kDtypeFp4 && SWZ && !SYNC && !kDmaLate), "mxfp4: fp4, swizzled rows, async copies");
     constexpr int kRA = RA;
-    using P = Plan<DT, RA>;
+    static_assert(WM == 1 || WM == 2, "waves along M: 1 (1 x 4) or 2 (2 x 2)");
+    static_assert(WM == 1 || !(kMx || kMx4), "the MX scale staging assumes the 1 x 4 split");
+    using P = Plan<DT, RA, WM>;
+    constexpr int kMT = P::kMT, kNT = P::kNT;
     using Frag = typename Op<DT>::Frag;
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
     static_assert(!kMx || (kFr == kMT && kMT % 4 == 0 && kRA < kFr - 4), "mxfp8: one k-step per k-tile, quad ring");
@@ -199,6 +204,8 @@ gemm_w4_kernel(const GemmArgs p)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // This wave's place in the tile: rows wm*TM/WM.., columns wn*64*WM..
+    const int wm = WM == 1 ? 0 : wave / 2, wn = WM == 1 ? wave : wave % 2;
     const auto tc = tile_of_workgroup<int>((int)blockIdx.x, p.tiles_m, p.tiles_n, p.splits, p.remap, p.group_m);
     const int m0 = (int)tc.tm * TM;
     const int n0 = (int)tc.tn * TN;
@@ -295,8 +302,8 @@ gemm_w4_kernel(const GemmArgs p)
         }
     };
 
-    // B: this wave's 4 strips; strips >= N/16 are past the range (zero).
-    const int strip0 = (n0 + wave * (TN / NW)) / 16;
+    // B: this wave's kNT strips; strips >= N/16 are past the range (zero).
+    const int strip0 = (n0 + wn * 16 * kNT) / 16;
     const auto rB = make_rsrc(p.Bs + (int64_t)strip0 * 16 * Kb, clamp_bytes((int64_t)(p.N / 16 - strip0) * 16 * Kb));
     const uint32_t b_voff = (uint32_t)lane * 16u;
 
@@ -341,14 +348,14 @@ gemm_w4_kernel(const GemmArgs p)
             }
         }
         if constexpr (SWZ) {
-            const uint8_t *row = lds + st + mt * 2048;
+            const uint8_t *row = lds + st + (wm * kMT + mt) * 2048;
             if constexpr (kStepCh == 1)
                 ring[f % (kRA + 1)] = *reinterpret_cast<const i32x4 *>(row + a_off[s]);
             else
                 ring[f % (kRA + 1)] = cat(*reinterpret_cast<const i32x4 *>(row + a_off[0]),
                                           *reinterpret_cast<const i32x4 *>(row + a_off[1]));
         } else {
-            ring[f % (kRA + 1)] = lds_frag<DT>(lds + st + (mt * kCH + s * kStepCh) * 1024 + lane * 16);
+            ring[f % (kRA + 1)] = lds_frag<DT>(lds + st + ((wm * kMT + mt) * kCH + s * kStepCh) * 1024 + lane * 16);
         }
     };
 
@@ -474,29 +481,54 @@ gemm_w4_kernel(const GemmArgs p)
                     }
                 }
             };
-            if constexpr (ILV) {
+            if constexpr (ILV && WM == 2) {
+                // 8 MFMAs per fragment: its LDS read after the first, B
+                // reloads after the third, A copies after the fifth
                 mf(0);
                 __builtin_amdgcn_sched_barrier(0);
                 lds_read();
                 __builtin_amdgcn_sched_barrier(0);
                 mf(1);
+                mf(2);
                 __builtin_amdgcn_sched_barrier(0);
                 b_loads();
                 __builtin_amdgcn_sched_barrier(0);
-                mf(2);
+                mf(3);
+                mf(4);
                 __builtin_amdgcn_sched_barrier(0);
                 a_copies();
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 5; nt < kNT; ++nt)
+                    mf(nt);
             } else {
-                lds_read();
-                b_loads();
-                a_copies();
-                __builtin_amdgcn_sched_barrier(0);
-                mf(0);
-                mf(1);
-                mf(2);
+                if constexpr (ILV) {
+                    mf(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    lds_read();
+                    __builtin_amdgcn_sched_barrier(0);
+                    mf(1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    b_loads();
+                    __builtin_amdgcn_sched_barrier(0);
+                    mf(2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    a_copies();
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    lds_read();
+                    b_loads();
+                    a_copies();
+                    __builtin_amdgcn_sched_barrier(0);
+                    mf(0);
+                    mf(1);
+                    mf(2);
+                }
+                mf(3);
+#pragma unroll
+                for (int nt = 4; nt < kNT; ++nt)
+                    mf(nt);
             }
-            mf(3);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -532,9 +564,10 @@ gemm_w4_kernel(const GemmArgs p)
         scale = static_cast<const float *>(p.sA)[0] * static_cast<const float *>(p.sB)[0];
     if constexpr (OUT == kOutBf16) {
         // bf16 C through LDS, so that every store writes whole 128-byte
-        // lines: the wave's 256 x 64 block is exactly one line per row.
-        // Each wave stages its block in its own 32 KiB of the (now idle) A
-        // ring, row r at byte 128r with 16-byte chunk c stored at chunk
+        // lines: the wave's block (256 x 64, or 128 x 128 as two 128 x 64
+        // halves) is one line per row of each 64-column half.  Each wave
+        // stages its block in its own 32 KiB of the (now idle) A ring, half
+        // h row r at byte 128 (h kRowsW + r) with 16-byte chunk c stored at chunk
         // c ^ ((r >> 1) & 7), the swizzle of the A tile: the 8-byte writes
         // (lane l: row l%16 of a row tile, columns 4(l/16)..+3 of a strip)
         // and the 16-byte reads (8 lanes per row) are both conflict-free.
@@ -542,6 +575,7 @@ gemm_w4_kernel(const GemmArgs p)
         // and copies): the wait above drained this wave's copies, the
         // barrier covers the others'.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        constexpr int kRowsW = TM / WM;                        // rows of the wave's block
         uint8_t *cst = lds + wave * (TM * 128);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
@@ -554,29 +588,33 @@ gemm_w4_kernel(const GemmArgs p)
                 u32x2 packed;
                 packed.x = pack_bf16x2(v.x, v.y);
                 packed.y = pack_bf16x2(v.z, v.w);
-                const int c = 2 * nt + (lane >> 5);              // 16-byte chunk of the row
-                *reinterpret_cast<u32x2 *>(cst + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * ((lane >> 4) & 1)) =
-                    packed;
+                const int c = 2 * (nt % 4) + (lane >> 5);        // 16-byte chunk of the half row
+                *reinterpret_cast<u32x2 *>(cst + (nt / 4) * (kRowsW * 128) + r * 128 + 16 * (c ^ ((r >> 1) & 7)) +
+                                           8 * ((lane >> 4) & 1)) = packed;
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own rows only: no barrier needed
-        const int ncol = n0 + wave * (TN / NW) + 8 * (lane & 7);
-        const bool col_ok = ncol < p.N;                       // N % 16 == 0: 8 columns in or out together
 #pragma unroll
-        for (int q = 0; q < TM / 8; ++q) {
-            const int r = 8 * q + (lane >> 3);
-            const i32x4 d = *reinterpret_cast<const i32x4 *>(cst + r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
-            const int m = m0 + r;
-            if (col_ok && m < p.M)
-                *reinterpret_cast<i32x4 *>(static_cast<uint8_t *>(p.C) + ((int64_t)m * p.N + ncol) * 2) = d;
+        for (int h = 0; h < kNT / 4; ++h) {
+            const int ncol = n0 + wn * 16 * kNT + 64 * h + 8 * (lane & 7);
+            const bool col_ok = ncol < p.N;                   // N % 16 == 0: 8 columns in or out together
+#pragma unroll
+            for (int q = 0; q < kRowsW / 8; ++q) {
+                const int r = 8 * q + (lane >> 3);
+                const i32x4 d = *reinterpret_cast<const i32x4 *>(cst + h * (kRowsW * 128) + r * 128 +
+                                                                 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+                const int m = m0 + wm * kRowsW + r;
+                if (col_ok && m < p.M)
+                    *reinterpret_cast<i32x4 *>(static_cast<uint8_t *>(p.C) + ((int64_t)m * p.N + ncol) * 2) = d;
+            }
         }
     } else {
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-            const int m = m0 + mt * 16 + (lane & 15);
+            const int m = m0 + wm * (TM / WM) + mt * 16 + (lane & 15);
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                const int n = n0 + wave * (TN / NW) + nt * 16 + (lane >> 4) * 4;
+                const int n = n0 + wn * 16 * kNT + nt * 16 + (lane >> 4) * 4;
                 f32x4 v = acc[mt][nt];
                 if constexpr (SCALE == kScaleTensor)
                     v = v * scale;
@@ -586,17 +624,18 @@ gemm_w4_kernel(const GemmArgs p)
     }
 }
 
-template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC>
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM>
 void launch_w4(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ, RA, ILV, SYNC><<<grid, 256, 0, s>>>(a);
+    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ, RA, ILV, SYNC, WM><<<grid, 256, 0, s>>>(a);
 }
 
-// Table entries: preload pair = (ILV, RA), layout, copy path.
-#define DGP_W4(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC)                                           \
-    {kTiled, DT, SC, OUT, 256, 256, 128, 4, 1, 4, ILV, RA, DB, kSchedW4,                        \
-     &launch_w4<DT, SC, OUT, DB, SWZ, RA, ILV, SYNC>, SWZ ? kLaySwizzled : kLayBlocks,          \
+// Table entries: waves (WM x 4/WM), preload pair = (ILV, RA), layout, copy path.
+#define DGP_W4X(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM)                                      \
+    {kTiled, DT, SC, OUT, 256, 256, 128, 4, WM, 4 / WM, ILV, RA, DB, kSchedW4,                  \
+     &launch_w4<DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM>, SWZ ? kLaySwizzled : kLayBlocks,      \
      SYNC ? kCopyRegs : kCopyAsync}
+#define DGP_W4(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC) DGP_W4X(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, 1)
 #define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ, RA, ILV, SYNC)                                       \
     DGP_W4(DT, SC, kOutBf16, DB, SWZ, RA, ILV, SYNC), DGP_W4(DT, SC, kOutPartial, DB, SWZ, RA, ILV, SYNC)
 
@@ -622,6 +661,15 @@ static const KernelSpec kW4Kernels[] = {
     // bytes staged beside the A tile
     DGP_W4_BOTH_OUT(kDtypeFp8, kScaleMx, 3, 1, w4::kRA, 1, 0),
     DGP_W4_BOTH_OUT(kDtypeFp4, kScaleMx32, 3, 1, w4::kRA, 1, 0),
+    // 2 x 2 waves (each 128 x 128: half the A fragment reads per wave, twice
+    // the B strips), B two k-tiles deep
+    DGP_W4X(kDtypeBf16, kScaleNone, kOutBf16, 2, 1, 7, 1, 0, 2),
+    DGP_W4X(kDtypeBf16, kScaleNone, kOutPartial, 2, 1, 7, 1, 0, 2),
+    DGP_W4X(kDtypeBf16, kScaleNone, kOutBf16, 3, 1, 7, 1, 0, 2),
+    DGP_W4X(kDtypeBf16, kScaleNone, kOutBf16, 2, 1, 3, 1, 0, 2),
+    DGP_W4X(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 7, 1, 0, 2),
+    DGP_W4X(kDtypeFp8, kScaleTensor, kOutPartial, 2, 1, 7, 1, 0, 2),
+    DGP_W4X(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 3, 1, 0, 2),
 };
 
 const KernelSpec *w4_kernels(int *count)
