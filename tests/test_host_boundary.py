@@ -355,6 +355,12 @@ def test_default_selection(dgp):
             shape, tile = entry.split(":")
             M, N, split = (int(x) for x in shape.split("/"))
             assert _pick(dgp, M, N, split, dt, sm) == tile, (mode, shape)
+    # Small grids above 32 rows: the 16-row K-split tile (C1 = 128 x 256 x 256), until the 128 x 128
+    # grid has 64 tiles, the weight passes 8 MiB, M passes 256 or the call splits K
+    for M, N, K, split, want in ((128, 256, 256, 1, 16), (256, 2048, 2048, 1, 16), (256, 4096, 2048, 1, 128),
+                                 (128, 4096, 4096, 1, 128), (300, 256, 256, 1, 128), (128, 256, 256, 2, 128)):
+        i = dgp.select_kernel(M, N, K, dgp.BF16, dgp.SCALE_NONE, split)
+        assert dgp.kernels()[i][0].tile_m == want, (M, N, K, split)
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
