@@ -222,6 +222,13 @@ dgp_status dgp_unshuffle_b(const void *Bs, void *B, int64_t N, int64_t K, int dt
  * on [P3] flags the silent ceil-division), mxfp8 K % 128 == 0; A, Bs, C
  * 16-byte aligned.  sA, sB: device pointers to the scales of `scale_mode`.
  * M = 0 or N = 0 is a no-op returning DGP_OK.  The device must be gfx950.
+ *
+ * One pass puts the whole K range of a tile in one workgroup.  Decode-sized
+ * M and small grids (M <= 256 with a weight of at most 8 MiB) take 16-row
+ * tiles that spread K over the waves of each workgroup; other shapes whose
+ * tile grid has fewer tiles than the GPU has CUs (256) leave CUs idle, and
+ * for them dgp_gemm_preshuffle_splitk with split_k > 1 fills more of the
+ * GPU (the library allocates no workspace of its own to split K here).
  */
 dgp_status dgp_gemm_preshuffle(const void *A, const void *Bs, void *C, int64_t M, int64_t N, int64_t K,
                                int dtype, int scale_mode, const void *sA, const void *sB,
