@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -260,8 +262,21 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         if (const KernelSpec *k = find_spec(q))
             return k;
     }
+    // Larger M: the tile whose grid finishes first.  A grid of t tiles (x
+    // splits) runs in ceil(t / 256) rounds over the 256 CUs, and one round of
+    // a 256x256, 128x256 or 128x128 tile takes about 1.45 : 1.12 : 1 (bf16,
+    // fp8, mxfp8, mxfp4; K = 2048 and 8192; blockscale's 8-wave 256x256 tile
+    // about 2.05 : 1): 4096 x 4096 and 3072 x 3072 take the 256x256 tile,
+    // 2048 x 4096 the 128x256 tile (99 vs 137 us at K = 8192), 2048 x 2048
+    // the 128x128 tile (91 vs 134 us).  Ties go to the larger tile.
+    const auto rounds = [&](int64_t tm, int64_t tn) {
+        return ((M + tm - 1) / tm * ((N + tn - 1) / tn) * split_k + 255) / 256;
+    };
+    const bool has_128x256 = scale == DGP_SCALE_NONE || scale == DGP_SCALE_TENSOR;   // (bf16 and fp8 per-tensor)
+    const int64_t c256 = (scale == DGP_SCALE_BLOCK128 ? 205 : 145) * rounds(256, 256),
+                  c128x256 = has_128x256 ? 112 * rounds(128, 256) : INT64_MAX, c128 = 100 * rounds(128, 128);
     const KernelSpec *k = nullptr;
-    if (M >= 1024 && N >= 1024) {
+    if (c256 <= c128x256 && c256 <= c128) {
         // bf16, per-tensor fp8, mxfp8 and mxfp4: the one-wave-per-SIMD tile
         // with swizzled A rows (measured 8-18 % ahead of the 8-wave tile at
         // 4096 x 4096 x 8192); blockscale: the 8-wave tile.
@@ -272,6 +287,10 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         } else {
             q.wm = 1, q.depth = 2, q.pv = 0, q.pd = 4;
         }
+        k = find_spec(q);
+    } else if (c128x256 < c128) {
+        Query q{kTiled, dtype, scale, out, 128, 256};
+        q.kt = 128;
         k = find_spec(q);
     }
     if (!k || !spec_fits(*k, Ks)) {

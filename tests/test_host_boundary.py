@@ -361,6 +361,14 @@ def test_default_selection(dgp):
                                  (128, 4096, 4096, 1, 128), (300, 256, 256, 1, 128), (128, 256, 256, 2, 128)):
         i = dgp.select_kernel(M, N, K, dgp.BF16, dgp.SCALE_NONE, split)
         assert dgp.kernels()[i][0].tile_m == want, (M, N, K, split)
+    # Larger M: the tile whose grid needs the fewest weighted rounds over 256 CUs
+    for M, N, K, sm, want in ((4096, 4096, 8192, dgp.SCALE_NONE, (256, 256)), (3072, 3072, 8192, dgp.SCALE_NONE, (256, 256)),
+                              (2048, 4096, 8192, dgp.SCALE_NONE, (128, 256)), (2048, 2048, 8192, dgp.SCALE_NONE, (128, 128)),
+                              (768, 16384, 4096, dgp.SCALE_NONE, (256, 256)), (1536, 1536, 8192, dgp.SCALE_NONE, (128, 128)),
+                              (2048, 4096, 8192, dgp.SCALE_BLOCK128, (128, 128)), (3072, 3072, 8192, dgp.SCALE_BLOCK128, (256, 256))):
+        dt = dgp.BF16 if sm == dgp.SCALE_NONE else dgp.FP8_E4M3
+        c = dgp.kernels()[dgp.select_kernel(M, N, K, dt, sm)][0]
+        assert (c.tile_m, c.tile_n) == want, (M, N, K, sm)
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
