@@ -459,14 +459,16 @@ def summarize(sec):
     f8 = sec.get("fp8_gemm_4096x4096x8192")
     if f8:
         out["fp8 tensor 4096x4096x8192"] = {"us_median": f8["us"], "TFLOP/s": f8["TFLOP/s"],
-                                            "frac": f8["frac_of_peak"], "peak": PEAK_FP8_TFLOPS}
+                                            "frac": f8["frac_of_peak"], "peak": PEAK_FP8_TFLOPS,
+                                            "frac_wall": f8.get("frac_measured_wall")}
     for key, peak in (("fp8_block128_gemm_4096x4096x8192", PEAK_FP8_TFLOPS),
                       ("fp8_mx128_gemm_4096x4096x8192", PEAK_FP8_TFLOPS),
                       ("fp4_mx32_gemm_4096x4096x8192", PEAK_FP4_TFLOPS)):
         v = sec.get(key)
         if v:
             out[key.replace("_gemm_", " ")] = {"us_median": v["us"], "TFLOP/s": v["TFLOP/s"],
-                                               "frac": v["frac_of_peak"], "peak": peak}
+                                               "frac": v["frac_of_peak"], "peak": peak,
+                                               "frac_wall": v.get("frac_measured_wall")}
     c1 = sec.get("bf16_gemm_128x256x256")
     if c1:
         out["bf16 128x256x256"] = {"us_median": c1["us"], "us_min": c1["launch_us"]["min"],
@@ -603,7 +605,7 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     # clock it holds for that data; constant operands (1.0) give the rate near
     # the spec clock.
     def mfma_wall(which, data_bytes):
-        rounds = 1024 if which == 0 else 512
+        rounds = 512 if which == 1 else 1024   # about 0.9 ms at the spec rate
         need = dgp.MFMA_PEAK_OPERAND_BYTES[which]
         res = {}
         for kind in ("workload_data", "constant_1.0"):
@@ -613,8 +615,8 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
                 ops = torch.empty(need, dtype=torch.uint8, device=dev)
                 if which == 0:
                     ops.view(torch.int16).fill_(0x3F80)
-                else:
-                    ops.fill_(0x38)
+                else:   # e4m3 1.0, or two E2M1 1.0 codes per byte
+                    ops.fill_(0x38 if which == 1 else 0x22)
             flop = dgp.MFMA_PEAK_FLOP[which] * 512 * 4 * rounds * 64
             us = graph_time_us(torch, lambda i: dgp.probe_mfma_peak(which, rounds, 512, ops, sink), 8)
             res[kind] = round(flop / (us * 1e-6) / 1e12, 1)
@@ -685,8 +687,12 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
         dcode = dgp.FP4_E2M1 if mode == "mx32" else dgp.FP8_E4M3
         out[key] = {"us": round(us, 1), "launch_us": st, "TFLOP/s": round(tf, 1),
                     "kernel": dgp.describe_kernel(dgp.select_kernel(4096, 4096, 8192, dcode, smode))}
-        if mode == "mx32":   # fp4 dense matrix-core peak (published); no fp4 wall is probed
+        if mode == "mx32":   # the E2M1 wall, probed on this workload's A bytes
+            out["mfma_wall_fp4"] = mfma_wall(2, A8.view(torch.uint8).reshape(-1))
+            out["mfma_wall_fp4"]["frac_of_peak"] = round(out["mfma_wall_fp4"]["workload_data"] / PEAK_FP4_TFLOPS,
+                                                         4)
             out[key]["frac_of_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
+            out[key]["frac_measured_wall"] = round(tf / out["mfma_wall_fp4"]["workload_data"], 4)
         else:
             out[key]["frac_of_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
             out[key]["frac_measured_wall"] = round(tf / out["mfma_wall_fp8"]["workload_data"], 4)

@@ -514,16 +514,19 @@ def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 1024,
     _check(lib().dgp_probe_stream_read(_ptr(src), nbytes, blocks, _ptr(sink), _stream_handle(stream)))
 
 
-# FLOP per matrix-core instruction of dgp_probe_mfma_peak (which = 0, 1), and
-# the operand buffer it reads (256 sets x 16 fragments x 64 lanes x 16|32 B).
-MFMA_PEAK_FLOP = (16384, 65536)
-MFMA_PEAK_OPERAND_BYTES = (256 * 16 * 64 * 16, 256 * 16 * 64 * 32)
+# FLOP per matrix-core instruction of dgp_probe_mfma_peak (which = 0 bf16,
+# 1 e4m3, 2 E2M1), and the operand buffer it reads (256 sets x 16 fragments
+# x 64 lanes x 16|32|16 B).
+MFMA_PEAK_FLOP = (16384, 65536, 65536)
+MFMA_PEAK_OPERAND_BYTES = (256 * 16 * 64 * 16, 256 * 16 * 64 * 32, 256 * 16 * 64 * 16)
 
 
 def probe_mfma_peak(which: int, rounds: int, blocks: int, operands: torch.Tensor, sink: torch.Tensor,
                     stream=None) -> int:
     """Launch the register-only MFMA loop on `operands`; returns the FLOP it performs."""
     _dev(operands, "operands")
+    if which not in (0, 1, 2):
+        raise ValueError("which must be 0, 1 or 2")
     if operands.numel() * operands.element_size() < MFMA_PEAK_OPERAND_BYTES[which]:
         raise ValueError(f"operands must hold {MFMA_PEAK_OPERAND_BYTES[which]} bytes")
     _check(lib().dgp_probe_mfma_peak(which, rounds, blocks, _ptr(operands), _ptr(sink), _stream_handle(stream)))

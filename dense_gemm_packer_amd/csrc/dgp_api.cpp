@@ -829,8 +829,8 @@ dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, int blocks, uin
 dgp_status dgp_probe_mfma_peak(int which, int rounds, int blocks, const void *operands, uint32_t *sink,
                                void *stream)
 {
-    if (which != 0 && which != 1)
-        return fail(DGP_ERR_CONFIG, "which must be 0 or 1");
+    if (which < 0 || which > 2)
+        return fail(DGP_ERR_CONFIG, "which must be 0, 1 or 2");
     if (rounds < 1 || rounds > (1 << 24) || blocks < 1 || blocks > 65536)
         return fail(DGP_ERR_SHAPE, "rounds must be in [1, 2^24] and blocks in [1, 65536]");
     if (!operands || !sink)

@@ -134,13 +134,29 @@ constexpr int kPeakSets = 256;      // operand sets in the caller's buffer
 // traffic in the loop.  The matrix units draw more power on operands that
 // toggle, so the rate depends on the data: random operands hold a lower
 // clock than constant ones.  which = 0: v_mfma_f32_16x16x32_bf16,
-// 1: the e4m3 16x16x128 form.
+// 1: the e4m3 16x16x128 form, 2: the E2M1 16x16x128 form; both scaled forms
+// take unit block scales (E8M0 127).
+template <int WHICH, typename F>
+__device__ inline void peak_mfma(f32x4 &acc, const F &b, const F &a, int unit)
+{
+    if constexpr (WHICH == 0)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    else if constexpr (WHICH == 1)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                     : "+a"(acc)
+                     : "v"(b), "v"(a), "v"(unit));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(acc)
+                     : "v"(b), "v"(a), "v"(unit));
+}
+
 template <int WHICH>
 __global__ __launch_bounds__(kPeakThreads) void probe_mfma_peak_kernel(int rounds, const uint8_t *__restrict__ ops,
                                                                        uint32_t *sink)
 {
-    constexpr int kFB = WHICH == 0 ? 16 : 32;   // bytes per lane per fragment
-    using F = typename std::conditional<WHICH == 0, i32x4, i32x8>::type;
+    constexpr int kFB = WHICH == 1 ? 32 : 16;   // bytes per lane per fragment
+    using F = typename std::conditional<WHICH == 1, i32x8, i32x4>::type;
     const int l = threadIdx.x & 63;
     const int set = (int)((blockIdx.x * (kPeakThreads / 64) + (threadIdx.x >> 6)) % kPeakSets);
     const uint8_t *base = ops + (size_t)set * 16 * 64 * kFB + l * kFB;
@@ -154,18 +170,16 @@ __global__ __launch_bounds__(kPeakThreads) void probe_mfma_peak_kernel(int round
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int unit = 127;   // E8M0 2^0
+    // Each accumulator is pinned to its AGPRs by the asm operand, so the
+    // loop holds nothing but the 64 MFMAs and its branch (the builtins let
+    // the register allocator rotate accumulators and add copies).
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                if constexpr (WHICH == 0)
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf[j]),
-                                                                     __builtin_bit_cast(bf16x8, af[(j + s) & 7]),
-                                                                     acc[j], 0, 0, 0);
-                else
-                    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[(j + s) & 7], acc[j],
-                                                                              0, 0, 0, 0, 0, 0);
+                peak_mfma<WHICH>(acc[j], bf[j], af[(j + s) & 7], unit);
             }
         }
     }
@@ -231,8 +245,10 @@ hipError_t launch_probe_mfma_peak(int which, int rounds, int blocks, const void 
 {
     if (which == 0)
         probe_mfma_peak_kernel<0><<<blocks, kPeakThreads, 0, s>>>(rounds, (const uint8_t *)ops, sink);
-    else
+    else if (which == 1)
         probe_mfma_peak_kernel<1><<<blocks, kPeakThreads, 0, s>>>(rounds, (const uint8_t *)ops, sink);
+    else
+        probe_mfma_peak_kernel<2><<<blocks, kPeakThreads, 0, s>>>(rounds, (const uint8_t *)ops, sink);
     return hipGetLastError();
 }
 

@@ -153,17 +153,19 @@ dgp_status dgp_probe_stream_read(const void *src, int64_t bytes, int blocks, uin
  * (operand set w % 256 for wave w) into registers and runs `rounds` rounds of
  * 64 MFMAs over 8 independent accumulators, with no memory traffic in the
  * loop.  which = 0 issues v_mfma_f32_16x16x32_bf16 (16384 FLOP each),
- * which = 1 the e4m3 16x16x128 form (65536 FLOP each); total FLOP =
- * blocks*4*rounds*64*that.  The matrix units draw more power on operands that
+ * which = 1 the block-scaled e4m3 16x16x128 form and which = 2 the
+ * block-scaled E2M1 16x16x128 form (65536 FLOP each; unit E8M0 scales);
+ * total FLOP = blocks*4*rounds*64*that.  The matrix units draw more power on operands that
  * toggle, so timing this on the workload's own data gives the MFMA wall at
  * the clock the chip holds for that data; constant operands give the rate
  * near the spec clock.
  *   operands: device buffer of 256 sets x 16 fragments x 64 lanes x 16 bytes
- *             (which 0: 4 MiB) or x 32 bytes (which 1: 8 MiB), set-major,
+ *             (which 0 and 2: 4 MiB) or x 32 bytes (which 1: 8 MiB), set-major,
  *             A fragments 0..7 then B fragments 0..7, lane-major inside a
  *             fragment.  Read once per wave.
  *   sink: >= 4096 uint32, normally left untouched.
- * rounds in [1, 2^24], blocks in [1, 65536], else DGP_ERR_SHAPE.
+ * which outside 0..2: DGP_ERR_CONFIG.  rounds in [1, 2^24], blocks in
+ * [1, 65536], else DGP_ERR_SHAPE.
  */
 dgp_status dgp_probe_mfma_peak(int which, int rounds, int blocks, const void *operands, uint32_t *sink,
                                void *stream);

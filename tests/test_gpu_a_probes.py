@@ -170,7 +170,7 @@ def test_probe_copy_copies():
     assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("which", [0, 1, 2])
 def test_probe_mfma_peak_runs_and_leaves_sink(which):
     # The register-only loop touches memory only on a practically impossible
     # value, so the sink stays as written; the FLOP count is the documented one.
@@ -181,4 +181,5 @@ def test_probe_mfma_peak_runs_and_leaves_sink(which):
     flop = dgp.probe_mfma_peak(which, 16, 8, ops, sink)
     torch.cuda.synchronize()
     assert flop == 8 * 4 * 16 * 64 * (16384 if which == 0 else 65536)
+    assert dgp.MFMA_PEAK_OPERAND_BYTES[which] == 256 * 16 * 64 * (32 if which == 1 else 16)
     assert bool((sink == 7).all())

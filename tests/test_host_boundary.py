@@ -193,7 +193,8 @@ def test_probe_validation(L):
     assert L.dgp_probe_stream_read(P, 4096, 65537, P, None) == SHAPE
     assert L.dgp_probe_stream_read(0, 4096, 512, P, None) == NULL
     assert L.dgp_probe_stream_read(P, 0, 512, P, None) == OK
-    assert L.dgp_probe_mfma_peak(2, 1, 1, P, P, None) == CONFIG
+    assert L.dgp_probe_mfma_peak(3, 1, 1, P, P, None) == CONFIG
+    assert L.dgp_probe_mfma_peak(-1, 1, 1, P, P, None) == CONFIG
     assert L.dgp_probe_mfma_peak(0, 0, 1, P, P, None) == SHAPE
     assert L.dgp_probe_mfma_peak(1, 1, 0, P, P, None) == SHAPE
     assert L.dgp_probe_mfma_peak(0, 1, 65537, P, P, None) == SHAPE
