@@ -235,14 +235,15 @@ gemm_stream_kernel(const GemmArgs p, int panel)
                         else
                             b = cat(breg[d][sp][0], breg[d][sp][1]);
                         if constexpr (SCALE == kScaleBlock) {
-                            // One MFMA is exactly one 128-wide K block: scale its
-                            // fp32 partial, then add (blockscale, aiter PR #5148).
+                            // One MFMA is exactly one 128-wide K block: its fp32
+                            // partial scaled and added in one fused multiply-add
+                            // (blockscale, aiter PR #5148).
                             const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
                             const float s = __fmul_rn(lds_sa[lane & 15][st], lds_sb[wave * SPW + sp][st]);
-                            acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, s));
-                            acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, s));
-                            acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, s));
-                            acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, s));
+                            acc[sp].x = __builtin_fmaf(part.x, s, acc[sp].x);
+                            acc[sp].y = __builtin_fmaf(part.y, s, acc[sp].y);
+                            acc[sp].z = __builtin_fmaf(part.z, s, acc[sp].z);
+                            acc[sp].w = __builtin_fmaf(part.w, s, acc[sp].w);
                         } else if constexpr (SCALE == kScaleMx) {
                             acc[sp] = mfma_mx(b, a, acc[sp], lds_xb[(wave * SPW + sp) * 16 + (lane & 15)][st],
                                               lds_xa[lane & 15][st]);
@@ -506,10 +507,10 @@ gemm_ksplit_kernel(const GemmArgs p)
                 b = cat(breg[d][sp][0], breg[d][sp][1]);
             if constexpr (kBs) {
                 const f32x4 part = mfma_op(b, a, f32x4{0.f, 0.f, 0.f, 0.f});
-                acc[sp].x = __fadd_rn(acc[sp].x, __fmul_rn(part.x, sc));
-                acc[sp].y = __fadd_rn(acc[sp].y, __fmul_rn(part.y, sc));
-                acc[sp].z = __fadd_rn(acc[sp].z, __fmul_rn(part.z, sc));
-                acc[sp].w = __fadd_rn(acc[sp].w, __fmul_rn(part.w, sc));
+                acc[sp].x = __builtin_fmaf(part.x, sc, acc[sp].x);
+                acc[sp].y = __builtin_fmaf(part.y, sc, acc[sp].y);
+                acc[sp].z = __builtin_fmaf(part.z, sc, acc[sp].z);
+                acc[sp].w = __builtin_fmaf(part.w, sc, acc[sp].w);
             } else if constexpr (kMx) {
                 // (2 or 4 strips: strip sp's column bytes sit in lanes 16 sp + i)
                 acc[sp] = mfma_mx(b, a, acc[sp], SPW >= 2 ? __shfl(xs[d][1], 16 * sp + (lane & 15)) : xs[d][1 + sp], ea);

@@ -214,7 +214,8 @@ gemm_tiled_kernel(const GemmArgs p)
     uint32_t nxt = (uint32_t)DEPTH * kStageBytes;       // LDS offset of tile t+DEPTH
     // Blockscale k-tile (one 128-K scale block per k-tile).  Each fragment's
     // MFMAs start from a zero accumulator; the fp32 partial is multiplied by
-    // sA[row][kb] * sB[col / 128][kb] and added to the running sum.  The order
+    // sA[row][kb] * sB[col / 128][kb] and added to the running sum in one
+    // fused multiply-add (one rounding per block).  The order
     // is fixed by scheduling fences, one fragment at a time: issue the LDS
     // reads (A fragment and the row's A scale) of fragment f + PD, issue the
     // MFMAs of fragment f, then scale and add the partials of fragment f - 1,
@@ -272,10 +273,10 @@ gemm_tiled_kernel(const GemmArgs p)
                         f32x4 &a = acc[f - 1][nt];
                         const f32x4 &q = part[(f - 1) & 1][nt];
                         const float c = sc[(f - 1) & 1];
-                        a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
-                        a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
-                        a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
-                        a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+                        a.x = __builtin_fmaf(q.x, c, a.x);
+                        a.y = __builtin_fmaf(q.y, c, a.y);
+                        a.z = __builtin_fmaf(q.z, c, a.z);
+                        a.w = __builtin_fmaf(q.w, c, a.w);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -286,10 +287,10 @@ gemm_tiled_kernel(const GemmArgs p)
                 f32x4 &a = acc[kFr - 1][nt];
                 const f32x4 &q = part[(kFr - 1) & 1][nt];
                 const float c = sc[(kFr - 1) & 1];
-                a.x = __fadd_rn(a.x, __fmul_rn(q.x, c));
-                a.y = __fadd_rn(a.y, __fmul_rn(q.y, c));
-                a.z = __fadd_rn(a.z, __fmul_rn(q.z, c));
-                a.w = __fadd_rn(a.w, __fmul_rn(q.w, c));
+                a.x = __builtin_fmaf(q.x, c, a.x);
+                a.y = __builtin_fmaf(q.y, c, a.y);
+                a.z = __builtin_fmaf(q.z, c, a.z);
+                a.w = __builtin_fmaf(q.w, c, a.w);
             }
         }
     };

@@ -74,9 +74,11 @@ typedef enum dgp_dtype { DGP_BF16 = 0, DGP_FP8_E4M3 = 1, DGP_FP4_E2M1 = 2 } dgp_
  * sB each point to one fp32 and C = bf16(acc * (sA*sB)).  DGP_SCALE_BLOCK128:
  * fp8 only; sA is [M][K/128] fp32 (A per row per 128-wide K block), sB is
  * [N/128][K/128] fp32 (B per 128x128 block), both row-major; each 128-K
- * block's fp32 partial sum is multiplied by sA[m][kb]*sB[n/128][kb] and added
- * to the fp32 accumulator ([P3] "Summary"; scale shapes from the
- * run_torch_blockscale review).  DGP_SCALE_MX128 (mxfp8): fp8 only; sA is
+ * block's fp32 partial sum p is multiplied by s = sA[m][kb]*sB[n/128][kb]
+ * (rounded to fp32) and added to the fp32 accumulator in one fused
+ * multiply-add, acc = fma(p, s, acc), one rounding per block ([P3] "Summary";
+ * scale shapes from the run_torch_blockscale review; the rounding is not
+ * stated there).  DGP_SCALE_MX128 (mxfp8): fp8 only; sA is
  * [M][K/128] and sB [N][K/128] bytes, both row-major, each an E8M0 scale
  * 2^(e-127) (255: NaN) for one row of A or one row of B (= one column of C)
  * over one 128-wide K block; the matrix-core instruction applies them to each

@@ -35,7 +35,9 @@
  *  - per-tensor scaling multiplies the fp32 sum by (sA*sB), the product of the
  *    two scales formed once in fp32; blockscale multiplies each 128-K block's
  *    fp32 partial sum by (sA[m][kb]*sB[n/128][kb]) and adds it to the running
- *    fp32 sum.
+ *    fp32 sum in one fused multiply-add (fmaf: one rounding per block; the
+ *    pages leave that rounding open, and the fused form is what a GPU's
+ *    fp32 multiply-add instruction computes).
  *  - split s covers K range [s*K/S, (s+1)*K/S); partials carry the scales; the
  *    reduce adds P_0 + P_1 + ... + P_{S-1} in that order.
  *  - mxfp8: an E8M0 byte e means 2^(e-127) (e = 255: NaN), as in the OCP
@@ -52,7 +54,8 @@
  *    is scaled and added.
  *
  * Build: plain C11, -O2 -ffp-contract=off, no fast-math (so that every fp32
- * multiply and add rounds separately, in the order written here).
+ * multiply and add rounds separately, in the order written here, and only
+ * the explicit fmaf fuses).
  */
 #include <math.h>
 #include <pthread.h>
@@ -223,7 +226,7 @@ static float partial_sum(const gemm_job *j, int64_t m, int64_t n, int64_t k0, in
             for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
                 p += arow[k] * brow[k];
             float s = j->sA[m * kblocks + kb] * j->sB[(n / 128) * kblocks + kb];
-            acc += p * s;
+            acc = fmaf(p, s, acc);
         }
         return acc;
     }

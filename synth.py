@@ -205,6 +205,12 @@ def exact_block_scales(shape, seed) -> np.ndarray:
     return rng(seed).choice(np.array([0.5, 1.0, 2.0], dtype=np.float32), size=shape)
 
 
+def random_block_scales(shape, seed) -> np.ndarray:
+    """fp32 scales uniform in [0.5, 2): with exact-integer operands every
+    128-K partial sum is exact, and scaling it rounds."""
+    return rng(seed).uniform(0.5, 2.0, size=shape).astype(np.float32)
+
+
 def workload_inputs(name: str, M=None, N=None, K=None):
     """Inputs of a named workload: dict(A, B, sA, sB, dtype, scale_mode, M, N, K).
 

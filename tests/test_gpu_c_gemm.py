@@ -128,6 +128,40 @@ def test_every_compiled_kernel():
         assert_close(got, c32, what=what)
 
 
+def test_blockscale_fused_accumulate_bit_exact():
+    """Exact-integer operands with random fp32 block scales: every 128-K
+    partial is exact and each scaled accumulate rounds, so only the same
+    fused multiply-add in the same order reproduces the oracle bit for bit.
+    Kernels that walk K in order (large tiles, streaming tiles) match the
+    oracle at their split; a K-split tile at split 1 sums its waves' slices
+    (one 128-K block each at K = 1024) in wave order, which is the oracle's
+    split-K over as many ranges as waves."""
+    count = 0
+    for cfg, dt, sm, split_out in dgp.kernels():
+        if sm != dgp.SCALE_BLOCK128:
+            continue
+        if cfg.tile_m == 16:
+            M, N = 37, 384
+        else:
+            M, N = 2 * cfg.tile_m + 44, 2 * cfg.tile_n + 128
+        K = 1024
+        ksplit = cfg.tile_m == 16 and (cfg.tile_n in (8, 16) or cfg.waves_m in (8, 16))
+        if ksplit and split_out:
+            continue   # partials of partials: no single oracle order
+        split = 2 if split_out else 1
+        what = f"tile {cfg.tile_m}x{cfg.tile_n} wm{cfg.waves_m} d{cfg.prefetch} s{cfg.schedule} split {split}"
+        print(what, flush=True)
+        A = synth.exact_ints((M, K), 81, "fp8")
+        B = synth.exact_ints((N, K), 82, "fp8")
+        sA = synth.random_block_scales((M, K // 128), 83)
+        sB = synth.random_block_scales((N // 128, K // 128), 84)
+        got = run_gpu(A, B, "fp8", "block128", sA, sB, split_k=split, config=cfg)
+        _, c16 = run_oracle(A, B, "fp8", "block128", sA, sB, split_k=cfg.waves_m if ksplit else split)
+        assert np.array_equal(got, c16), what
+        count += 1
+    assert count >= 8
+
+
 @pytest.mark.parametrize("dtype,mode", [("bf16", "none"), ("fp8", "tensor"), ("fp8", "block128"),
                                         ("fp8", "mx128"), ("fp4", "mx32")])
 def test_k_tile_counts_not_multiple_of_prefetch_depth(dtype, mode):

@@ -172,6 +172,45 @@ def test_blockscale_exact_against_integer_arithmetic(orc):
     assert np.array_equal(c32.astype(np.float64), want)
 
 
+def _round_f32(x: Fraction) -> np.float32:
+    """x rounded to the nearest fp32, ties to even, by exact comparison of
+    the neighbours of a first guess (normal range only)."""
+    g = np.float32(float(x))
+    cands = [np.nextafter(g, np.float32(-np.inf)), g, np.nextafter(g, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - x), int(c.view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_blockscale_accumulates_with_one_rounding_per_block(orc):
+    """Exact-integer operands make every 128-K partial p exact; random fp32
+    scales make p*s inexact.  The oracle's sum is then, bit for bit, the
+    sequence acc <- round(p*s + acc) over the blocks in K order (s = sA*sB
+    rounded once), computed here in exact rational arithmetic, and it differs
+    from the two-rounding sequence acc <- round(acc + round(p*s))."""
+    M, N, K = 3, 256, 1280
+    A = synth.exact_ints((M, K), 65, "fp8")
+    B = synth.exact_ints((N, K), 66, "fp8")
+    sA = synth.random_block_scales((M, K // 128), 67)
+    sB = synth.random_block_scales((N // 128, K // 128), 68)
+    a = dec_torch(A, "fp8").astype(np.int64)
+    b = dec_torch(B, "fp8").astype(np.int64)
+    c32, _ = orc.gemm(A, B, orc.FP8_E4M3, orc.SCALE_BLOCK128, sA, sB)
+    two_roundings_differ = 0
+    for m in range(M):
+        for n in range(N):
+            fused = np.float32(0.0)
+            split = np.float32(0.0)
+            for kb in range(K // 128):
+                sl = slice(kb * 128, kb * 128 + 128)
+                p = int(a[m, sl] @ b[n, sl])
+                s = np.float32(sA[m, kb]) * np.float32(sB[n // 128, kb])
+                fused = _round_f32(Fraction(p) * Fraction(float(s)) + Fraction(float(fused)))
+                split = np.float32(split + np.float32(np.float32(p) * s))
+            assert c32[m, n] == fused, (m, n)
+            two_roundings_differ += int(split != fused)
+    assert two_roundings_differ > 0
+
+
 # ---------------------------------------------------- one-hot / identity
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
