@@ -55,6 +55,33 @@ def test_large_workload_sampled_rows(name):
     assert_close(host_bits(C)[rows], c32, what=name)
 
 
+@pytest.mark.parametrize("M", [4096, 16])
+def test_blockscale_full_size_fused_accumulate_bit_exact(M):
+    """The blockscale shapes the benchmark times (4096 x 4096 x 8192 and the
+    M = 16 decode at N = 16384, K = 7168) through the built-in selection, on
+    exact-integer operands with random fp32 block scales: every scaled
+    accumulate rounds, so sampled rows must match the oracle bit for bit
+    (same fused multiply-add, same K order; the decode tile's wave slices
+    against the oracle's split-K over as many ranges)."""
+    N, K = (4096, 8192) if M == 4096 else (16384, 7168)
+    A = synth.exact_ints((M, K), 91, "fp8")
+    B = synth.exact_ints((N, K), 92, "fp8")
+    sA = synth.random_block_scales((M, K // 128), 93)
+    sB = synth.random_block_scales((N // 128, K // 128), 94)
+    a = dev_codes(A, "fp8")
+    Bs = dgp.preshuffle_b(dev_codes(B, "fp8"))
+    C = dgp.gemm_preshuffle(a, Bs, dev_scales(sA, "block128"), dev_scales(sB, "block128"), dgp.SCALE_BLOCK128)
+    torch.cuda.synchronize()
+    cfg, _, _, _ = dgp.kernels()[dgp.select_kernel(M, N, K, dgp.FP8_E4M3, dgp.SCALE_BLOCK128)]
+    ksplit = cfg.tile_m == 16 and (cfg.tile_n in (8, 16) or cfg.waves_m in (8, 16))
+    if ksplit:   # the oracle's split-K over the waves' slices: equal whole 128-K blocks
+        assert (K // 128) % cfg.waves_m == 0
+    rows = np.arange(M) if M <= 16 else np.unique(np.concatenate([np.linspace(0, M - 1, 24).astype(np.int64),
+                                                                     np.array([255, 256, 2047, 2048])]))
+    _, c16 = run_oracle(A, B, "fp8", "block128", sA, sB, split_k=cfg.waves_m if ksplit else 1, rows=rows)
+    assert np.array_equal(host_bits(C)[rows], c16)
+
+
 DECODE = [("fp8_decode", 2048), ("fp8_decode", 16384), ("bf16_decode", 2048), ("bf16_decode", 16384),
           ("fp4_mx32", 2048), ("fp4_mx32", 16384), ("fp8_blockscale", 16384), ("fp8_mx128", 16384)]
 
