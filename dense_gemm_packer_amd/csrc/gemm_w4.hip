@@ -184,6 +184,7 @@ gemm_w4_kernel(const GemmArgs p)
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
     static_assert(!kMx || (kFr == kMT && kMT % 4 == 0 && kRA < kFr - 4), "mxfp8: one k-step per k-tile, quad ring");
     static_assert(!kMx4 || (kFr == 2 * kMT && kRA < kMT - 4), "mxfp4: two k-steps per k-tile, quad ring");
+    static_assert(!kMx4 || kFr % 2 == 0, "mxfp4: the row-scale slot of fragment f is f % 2 across k-tiles");
     // The barrier's count: the scale copies of the k-tiles in between are
     // 2 (mxfp8) or 4 (mxfp4) more loads per k-tile (those of the barrier's
     // own tile precede its last A copy).
@@ -394,6 +395,13 @@ gemm_w4_kernel(const GemmArgs p)
 #pragma unroll
     for (int f = 0; f < kRA; ++f)
         read_frag(f, stage(0));
+    // mxfp4: fragment f's row scale byte, extracted (VALU) one fragment
+    // ahead into slot f % 2 -- the hardware-scaled MFMA needs 2 wait states
+    // after a vector-ALU write of its scale register, and the extraction sits
+    // three MFMAs before the first one that reads it.
+    [[maybe_unused]] int ea4v[2] = {0, 0};
+    if constexpr (kMx4)
+        ea4v[0] = (int)__builtin_amdgcn_ubfe((uint32_t)xq4[0][0][0], xsh, 8u);
 
     // One k-tile.  SET = t % kDB holds tile t's B (and receives tile t+kDB's
     // as it is consumed); the wrapped reloads at its start refill set
@@ -432,9 +440,14 @@ gemm_w4_kernel(const GemmArgs p)
             // this position's B reloads, then its A copies.
             const int st = f / kMT, mt = f % kMT;
             const Frag &a = ring[f % (kRA + 1)];
-            [[maybe_unused]] int ea4 = 0;
-            if constexpr (kMx4)   // this fragment's row scale byte
-                ea4 = (int)__builtin_amdgcn_ubfe((uint32_t)xq4[mt / 4][(mt % 4) / 2][(mt % 2) * 2 + st], xsh, 8u);
+            [[maybe_unused]] const int ea4 = ea4v[f & 1];   // this fragment's row scale byte
+            auto next_ea4 = [&]() {   // the next fragment's (that of the next k-tile after the last)
+                if constexpr (kMx4) {
+                    const int g = (f + 1) % kFr, st1 = g / kMT, mt1 = g % kMT;
+                    ea4v[(f + 1) & 1] =
+                        (int)__builtin_amdgcn_ubfe((uint32_t)xq4[mt1 / 4][(mt1 % 4) / 2][(mt1 % 2) * 2 + st1], xsh, 8u);
+                }
+            };
             auto mf = [&](int nt) {
                 if constexpr (kMx4)
                     mfma_acc_mx4(acc[mt][nt], breg[SET][nt][st], a, eb4[nt][st], ea4);
@@ -486,6 +499,7 @@ gemm_w4_kernel(const GemmArgs p)
                 // reloads after the third, A copies after the fifth
                 mf(0);
                 __builtin_amdgcn_sched_barrier(0);
+                next_ea4();
                 lds_read();
                 __builtin_amdgcn_sched_barrier(0);
                 mf(1);
@@ -505,6 +519,7 @@ gemm_w4_kernel(const GemmArgs p)
                 if constexpr (ILV) {
                     mf(0);
                     __builtin_amdgcn_sched_barrier(0);
+                    next_ea4();
                     lds_read();
                     __builtin_amdgcn_sched_barrier(0);
                     mf(1);
@@ -521,6 +536,9 @@ gemm_w4_kernel(const GemmArgs p)
                     a_copies();
                     __builtin_amdgcn_sched_barrier(0);
                     mf(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    next_ea4();
+                    __builtin_amdgcn_sched_barrier(0);
                     mf(1);
                     mf(2);
                 }

@@ -170,7 +170,10 @@ __global__ __launch_bounds__(kPeakThreads) void probe_mfma_peak_kernel(int round
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int unit = 127;   // E8M0 2^0
+    int unit = 127;   // E8M0 2^0
+    // 2 wait states between the vector-ALU write of the scale register and
+    // the first scaled MFMA that reads it (the asm ties the nop to it).
+    asm volatile("s_nop 1" : "+v"(unit));
     // Each accumulator is pinned to its AGPRs by the asm operand, so the
     // loop holds nothing but the 64 MFMAs and its branch (the builtins let
     // the register allocator rotate accumulators and add copies).
