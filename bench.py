@@ -600,10 +600,9 @@ def run_secondary(dgp, torch, np, synth, to_dev, dev, stream, Bs_bf16, A_bf16, C
     size_walls = {}
 
     # MFMA walls: a register-only matrix-core loop (512 workgroups x 4 waves,
-    # two waves per SIMD like the GEMM) timed like the GEMMs.  On the
-    # workload's own operand bytes it gives the rate the chip sustains at the
-    # clock it holds for that data; constant operands (1.0) give the rate near
-    # the spec clock.
+    # two waves per SIMD) timed like the GEMMs.  On the workload's own operand
+    # bytes it gives the rate the chip sustains at the clock it holds for that
+    # data; constant operands (1.0) give the rate near the spec clock.
     def mfma_wall(which, data_bytes):
         rounds = 512 if which == 1 else 1024   # about 0.9 ms at the spec rate
         need = dgp.MFMA_PEAK_OPERAND_BYTES[which]
