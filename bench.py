@@ -279,8 +279,23 @@ def main():
                     torch._scaled_mm(Al, Bl.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
             torch.cuda.synchronize()
             del Al, Bsl, Bl, Cl
+        # the block-scaled modes' built-in kernels at the same size, for the
+        # same counters (the scale copies beside the A and B traffic)
+        for name, smode in (("fp8_mx128", dgp.SCALE_MX128), ("fp4_mx32", dgp.SCALE_MX32)):
+            wl = synth.workload_inputs(name, M=4096, N=4096, K=8192)
+            dt = "fp4" if smode == dgp.SCALE_MX32 else "fp8"
+            Al = to_dev(wl["A"], dt)
+            Bsl = dgp.preshuffle_b(to_dev(wl["B"], dt))
+            sc = (torch.from_numpy(wl["sA"]).to(dev), torch.from_numpy(wl["sB"]).to(dev))
+            Cl = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dgp.gemm_preshuffle(Al, Bsl, *sc, smode, out=Cl)
+            torch.cuda.synchronize()
+            del Al, Bsl, Cl
         log("profile-compare: 3 x probe copy of 256 MiB; bf16 then fp8 4096x4096x8192: 3 launches each of "
-            + ", ".join(n for n, _ in ABLATIONS) + ", then the vendor library")
+            + ", ".join(n for n, _ in ABLATIONS) + ", then the vendor library; then 3 launches each of the "
+            "mxfp8 and mxfp4 built-in kernels at the same size")
         return 0
 
     if args.ablations:
