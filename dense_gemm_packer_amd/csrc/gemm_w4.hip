@@ -425,6 +425,11 @@ gemm_w4_kernel(const GemmArgs p)
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2)
                             eb4[c][s2] = (int)__builtin_amdgcn_ubfe((uint32_t)xb4_next[c / 2][(c % 2) * 2 + s2], xsh, 8u);
+                    // the first MFMA below reads one of these: 2 wait states
+                    // after the extractions, in whatever order they issue
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("s_nop 1");
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             if (f == kBar) {
