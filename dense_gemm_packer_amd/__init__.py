@@ -459,7 +459,8 @@ def describe_kernel(index: int) -> str:
                 f"{cfg.prefetch}-step ring{', fp32 partials' if so else ''}>")
     sched = {1: f"interleaved, LDS read-ahead {cfg.preload_dsrd}", 2: "ping-pong",
              3: f"A and B in LDS, LDS read-ahead {cfg.preload_dsrd}",
-             4: f"4 waves (1 per SIMD{', 2x2' if cfg.waves_m == 2 else ''}), AGPR accumulators, "
+             4: f"4 waves (1 per SIMD{', 2x2' if cfg.waves_m == 2 else ''}"
+                f"{', up to 2 workgroups per CU' if cfg.tile_m == 128 else ''}), AGPR accumulators, "
                 f"LDS read-ahead {cfg.preload_dsrd}, "
                 f"{'interleaved' if cfg.preload_vmem else 'bunched'} issue"}[cfg.schedule]
     lay = {1: "A in operand blocks", 2: "A in swizzled rows"}.get(cfg.a_layout, "")

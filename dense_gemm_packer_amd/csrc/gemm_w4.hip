@@ -1,5 +1,6 @@
-// gemm_w4_kernel -- the 256 x 256 large-M tile with one wave per SIMD
-// (bf16, per-tensor fp8, mxfp8 and mxfp4).
+// gemm_w4_kernel -- the large-M tile with one wave per SIMD: 256 x 256 (bf16,
+// per-tensor fp8, mxfp8 and mxfp4) and 128 x 256 (bf16 and per-tensor fp8;
+// two waves per SIMD when two workgroups share a CU).
 //
 // Same operation, operand layouts and epilogue as gemm_tiled_kernel
 // (gemm_tiled.hip, gemm_common.h): per k-tile of 128 bytes the A tile goes
@@ -7,7 +8,8 @@
 // preshuffled B fragments go straight to VGPRs, and A fragments are read from
 // LDS per MFMA k-step (FlyDSL PR #974, follow-up commit item 2).  What
 // differs is the split of the workgroup: 4 waves (1 x 4), each owning all 256
-// rows and 64 columns of the tile, 256 fp32 accumulators per lane.  Against
+// rows and 64 columns of the tile, 256 fp32 accumulators per lane (128 rows and
+// 128 accumulators in the 128-row form).  Against
 // the 8-wave tile this halves the LDS read traffic (each wave reads the whole
 // A tile once per k-tile, and there are half as many waves) while B still
 // passes through the L1 exactly once.
@@ -36,23 +38,24 @@ namespace dgp {
 
 namespace w4 {
 
-constexpr int TM = 256, TN = 256, NW = 4, KT = 128;
+constexpr int TN = 256, NW = 4, KT = 128;
 constexpr int kCH = KT / 64;             // 64-byte chunks per k-tile
 constexpr int kRing = 4;                 // LDS stages
-constexpr int kBuf = TM * KT;            // bytes per stage
-constexpr int kDma = (TM / 16) * kCH / NW;   // async copies per wave per k-tile
 constexpr int kRA = 7;                   // tuned LDS read-ahead (fragments ahead of their MFMAs)
 // Where a k-tile's A copy is issued: right after the barrier that frees its
 // stage, 3 k-tiles ahead (false), or early in the next k-tile, 2 ahead (true).
 constexpr bool kDmaLate = false;
 constexpr int kDmaAhead = kDmaLate ? 2 : 3;
-static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
 
-// WM = waves along M: 1 = the 1 x 4 split (each wave all 256 rows, 64
-// columns), 2 = 2 x 2 (each wave 128 rows, 128 columns).
-template <int DT, int RA, int WM = 1>
+// WM = waves along M: 1 = the 1 x 4 split (each wave all TM rows, 64
+// columns), 2 = 2 x 2 (each wave TM/2 rows, 128 columns).  TM = tile rows:
+// 256, or 128 (two workgroups per CU, two waves per SIMD).
+template <int DT, int RA, int WM = 1, int TM = 256>
 struct Plan {
-    static constexpr int kMT = 16 / WM;                   // 16-row tiles per wave
+    static constexpr int kBuf = TM * KT;                  // bytes per LDS stage
+    static constexpr int kDma = (TM / 16) * kCH / NW;     // async copies per wave per k-tile
+    static_assert((TM * KT) % (NW * 64 * 16) == 0, "A tile must split into whole 16-byte loads");
+    static constexpr int kMT = TM / 16 / WM;              // 16-row tiles per wave
     static constexpr int kNT = 4 * WM;                    // 16-column strips per wave
     static constexpr int kStepCh = Op<DT>::kBlocks;       // 64-byte chunks per MFMA step
     static constexpr int kSteps = kCH / kStepCh;          // MFMA k-steps per k-tile
@@ -163,8 +166,8 @@ __device__ inline void mfma_acc_mx4(f32x4 &acc, const i32x4 &b, const i32x4 &a, 
 // quad of row tiles' 8 dwords in two 16-byte reads, and column 64w + 16c + i
 // at dword 512 + 2(4(16w + i) + c) + s; a lane's byte is taken with one
 // bit-field extract per fragment.
-template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM, int TM>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(256 / TM, 256 / TM)))
 gemm_w4_kernel(const GemmArgs p)
 {
     static_assert(DB >= 2 && DB <= 4, "B sets");
@@ -178,7 +181,9 @@ gemm_w4_kernel(const GemmArgs p)
     constexpr int kRA = RA;
     static_assert(WM == 1 || WM == 2, "waves along M: 1 (1 x 4) or 2 (2 x 2)");
     static_assert(WM == 1 || !(kMx || kMx4), "the MX scale staging assumes the 1 x 4 split");
-    using P = Plan<DT, RA, WM>;
+    static_assert(TM == 256 || (TM == 128 && !(kMx || kMx4)), "tile rows: 256, or 128 without MX scales");
+    using P = Plan<DT, RA, WM, TM>;
+    constexpr int kBuf = P::kBuf, kDma = P::kDma;
     constexpr int kMT = P::kMT, kNT = P::kNT;
     using Frag = typename Op<DT>::Frag;
     constexpr int kFr = P::kFr, kBar = P::kBar, kStepCh = P::kStepCh;
@@ -647,17 +652,18 @@ gemm_w4_kernel(const GemmArgs p)
     }
 }
 
-template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM>
+template <int DT, int SCALE, int OUT, int DB, int SWZ, int RA, int ILV, int SYNC, int WM, int TM>
 void launch_w4(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ, RA, ILV, SYNC, WM><<<grid, 256, 0, s>>>(a);
+    gemm_w4_kernel<DT, SCALE, OUT, DB, SWZ, RA, ILV, SYNC, WM, TM><<<grid, 256, 0, s>>>(a);
 }
 
 // Table entries: waves (WM x 4/WM), preload pair = (ILV, RA), layout, copy path.
-#define DGP_W4X(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM)                                      \
-    {kTiled, DT, SC, OUT, 256, 256, 128, 4, WM, 4 / WM, ILV, RA, DB, kSchedW4,                  \
-     &launch_w4<DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM>, SWZ ? kLaySwizzled : kLayBlocks,      \
+#define DGP_W4T(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM, TM)                                  \
+    {kTiled, DT, SC, OUT, TM, 256, 128, 4, WM, 4 / WM, ILV, RA, DB, kSchedW4,                   \
+     &launch_w4<DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM, TM>, SWZ ? kLaySwizzled : kLayBlocks,  \
      SYNC ? kCopyRegs : kCopyAsync}
+#define DGP_W4X(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM) DGP_W4T(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, WM, 256)
 #define DGP_W4(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC) DGP_W4X(DT, SC, OUT, DB, SWZ, RA, ILV, SYNC, 1)
 #define DGP_W4_BOTH_OUT(DT, SC, DB, SWZ, RA, ILV, SYNC)                                       \
     DGP_W4(DT, SC, kOutBf16, DB, SWZ, RA, ILV, SYNC), DGP_W4(DT, SC, kOutPartial, DB, SWZ, RA, ILV, SYNC)
@@ -693,6 +699,14 @@ static const KernelSpec kW4Kernels[] = {
     DGP_W4X(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 7, 1, 0, 2),
     DGP_W4X(kDtypeFp8, kScaleTensor, kOutPartial, 2, 1, 7, 1, 0, 2),
     DGP_W4X(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 3, 1, 0, 2),
+    // 128 x 256 (up to two workgroups per CU, two waves per SIMD: 128 AGPR
+    // accumulators per lane, B two k-tiles deep); the tuned read-ahead first
+    DGP_W4T(kDtypeBf16, kScaleNone, kOutBf16, 2, 1, 7, 1, 0, 1, 128),
+    DGP_W4T(kDtypeBf16, kScaleNone, kOutPartial, 2, 1, 7, 1, 0, 1, 128),
+    DGP_W4T(kDtypeBf16, kScaleNone, kOutBf16, 2, 1, 3, 1, 0, 1, 128),
+    DGP_W4T(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 1, 1, 0, 1, 128),
+    DGP_W4T(kDtypeFp8, kScaleTensor, kOutPartial, 2, 1, 1, 1, 0, 1, 128),
+    DGP_W4T(kDtypeFp8, kScaleTensor, kOutBf16, 2, 1, 3, 1, 0, 1, 128),
 };
 
 const KernelSpec *w4_kernels(int *count)
