@@ -370,6 +370,12 @@ def test_default_selection(dgp):
         dt = dgp.BF16 if sm == dgp.SCALE_NONE else dgp.FP8_E4M3
         c = dgp.kernels()[dgp.select_kernel(M, N, K, dt, sm)][0]
         assert (c.tile_m, c.tile_n) == want, (M, N, K, sm)
+    # bf16 and per-tensor fp8 take the 128 x 256 tile in its one-wave-per-SIMD form, split-K
+    # partials included
+    for dt, sm in ((dgp.BF16, dgp.SCALE_NONE), (dgp.FP8_E4M3, dgp.SCALE_TENSOR)):
+        for M, split in ((2048, 1), (1024, 2)):
+            c, _, _, so = dgp.kernels()[dgp.select_kernel(M, 4096, 8192, dt, sm, split)]
+            assert (c.tile_m, c.tile_n, c.schedule, bool(so)) == (128, 256, 4, split > 1), (dt, M, split)
     assert dgp.select_kernel(0, 4096, 8192, dgp.BF16, dgp.SCALE_NONE) == -1
     assert dgp.select_kernel(16, 4096, 0, dgp.BF16, dgp.SCALE_NONE) == -1
 
