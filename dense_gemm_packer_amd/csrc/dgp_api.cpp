@@ -269,12 +269,19 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     // about 2.05 : 1): 4096 x 4096 and 3072 x 3072 take the 256x256 tile,
     // 2048 x 4096 the 128x256 tile (99 vs 137 us at K = 8192), 2048 x 2048
     // the 128x128 tile (91 vs 134 us).  Ties go to the larger tile.
+    // bf16 and per-tensor fp8 run their 128x256 tile one wave per SIMD, two
+    // workgroups per CU at once: the busiest CU's k tiles cost about 1.05
+    // rounds of the 256x256 tile per pair and 0.74 for one alone (K = 8192:
+    // 4096 x 6144 281 vs 314 us for the 256x256 tile, 4096 x 5120 260 vs
+    // 307, 3072 x 4096 168 vs 153, 4096 x 4096 187 vs 178; fp8 alike).
     const auto rounds = [&](int64_t tm, int64_t tn) {
         return ((M + tm - 1) / tm * ((N + tn - 1) / tn) * split_k + 255) / 256;
     };
     const bool has_128x256 = scale == DGP_SCALE_NONE || scale == DGP_SCALE_TENSOR;   // (bf16 and fp8 per-tensor)
+    const int64_t k128x256 = rounds(128, 256);   // 128x256 tiles on the busiest CU
     const int64_t c256 = (scale == DGP_SCALE_BLOCK128 ? 205 : 145) * rounds(256, 256),
-                  c128x256 = has_128x256 ? 112 * rounds(128, 256) : INT64_MAX, c128 = 100 * rounds(128, 128);
+                  c128x256 = has_128x256 ? 153 * (k128x256 / 2) + 107 * (k128x256 % 2) : INT64_MAX,
+                  c128 = 100 * rounds(128, 128);
     const KernelSpec *k = nullptr;
     if (c256 <= c128x256 && c256 <= c128) {
         // bf16, per-tensor fp8, mxfp8 and mxfp4: the one-wave-per-SIMD tile

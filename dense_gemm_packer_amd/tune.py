@@ -34,13 +34,15 @@ from . import (BF16, FP4_E2M1, FP8_E4M3, SCALE_BLOCK128, SCALE_MX32, SCALE_MX128
                select_kernel, splitk_workspace_bytes)
 
 LLC_BYTES = 256 << 20
-# The headline shapes, bf16 and per-tensor fp8 at 2048 x 4096 (the 128-row
-# large-M tile's range), then the decode grid (K = 7168): bf16 and per-tensor
+# The headline shapes, bf16 and per-tensor fp8 at 2048 x 4096 and 4096 x 6144
+# (the 128-row large-M tile's range: one tile per CU, and two at once), then
+# the decode grid (K = 7168): bf16 and per-tensor
 # fp8 at M = 1, 4, 16, N = 2048 and 16384, 1, 2 and 4 splits; blockscale and
 # mxfp8 at M = 1 and 16 with 1 and 4 splits; mxfp4 at M = 1 and 16 with 1
 # and 2 splits.
 DEFAULT_SHAPES = (["bf16:4096x4096x8192", "fp8:4096x4096x8192", "fp8b:4096x4096x8192", "mx8:4096x4096x8192",
-                   "mx4:4096x4096x8192", "bf16:2048x4096x8192", "fp8:2048x4096x8192"]
+                   "mx4:4096x4096x8192", "bf16:2048x4096x8192", "fp8:2048x4096x8192", "bf16:4096x6144x8192",
+                   "fp8:4096x6144x8192"]
                   + [f"{k}:{m}x{n}x7168:{s}" for k in ("bf16", "fp8") for m in (1, 4, 16) for n in (2048, 16384)
                      for s in (1, 2, 4)]
                   + [f"{k}:{m}x{n}x7168:{s}" for k in ("fp8b", "mx8") for m in (1, 16) for n in (2048, 16384)

@@ -366,7 +366,11 @@ def test_default_selection(dgp):
     for M, N, K, sm, want in ((4096, 4096, 8192, dgp.SCALE_NONE, (256, 256)), (3072, 3072, 8192, dgp.SCALE_NONE, (256, 256)),
                               (2048, 4096, 8192, dgp.SCALE_NONE, (128, 256)), (2048, 2048, 8192, dgp.SCALE_NONE, (128, 128)),
                               (768, 16384, 4096, dgp.SCALE_NONE, (256, 256)), (1536, 1536, 8192, dgp.SCALE_NONE, (128, 128)),
-                              (2048, 4096, 8192, dgp.SCALE_BLOCK128, (128, 128)), (3072, 3072, 8192, dgp.SCALE_BLOCK128, (256, 256))):
+                              (2048, 4096, 8192, dgp.SCALE_BLOCK128, (128, 128)), (3072, 3072, 8192, dgp.SCALE_BLOCK128, (256, 256)),
+                              # two 256x256 rounds against three 128x256 tiles on the busiest CU, two at once
+                              (4096, 6144, 8192, dgp.SCALE_NONE, (128, 256)), (6144, 4096, 8192, dgp.SCALE_TENSOR, (128, 256)),
+                              (4096, 5120, 8192, dgp.SCALE_NONE, (128, 256)), (3072, 4096, 8192, dgp.SCALE_TENSOR, (256, 256)),
+                              (4096, 6144, 8192, dgp.SCALE_BLOCK128, (256, 256))):
         dt = dgp.BF16 if sm == dgp.SCALE_NONE else dgp.FP8_E4M3
         c = dgp.kernels()[dgp.select_kernel(M, N, K, dt, sm)][0]
         assert (c.tile_m, c.tile_n) == want, (M, N, K, sm)
