@@ -297,8 +297,8 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
         k = find_spec(q);
     } else if (c128x256 < c128) {
         // bf16 and per-tensor fp8: the one-wave-per-SIMD tile, 128 rows
-        // (2048 x 4096 x 8192: 98.6 vs 106.3 us bf16, 55.0 vs 58.7 us fp8
-        // against the 8-wave 128x256 tile; bit-identical results)
+        // (2048 x 4096 x 8192: 105.9 vs 123.8 us bf16, 60.5 vs 66.6 us fp8
+        // against the 8-wave 128x256 tile in a sweep; bit-identical results)
         Query q{kTiled, dtype, scale, out, 128, 256};
         q.kt = 128, q.sched = kSchedW4, q.lay = kLaySwizzled;
         k = find_spec(q);
