@@ -272,14 +272,17 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     // workgroups per CU at once: the busiest CU's k tiles cost about 1.05
     // rounds of the 256x256 tile per pair and 0.74 for one alone (K = 8192:
     // 4096 x 6144 281 vs 314 us for the 256x256 tile, 4096 x 5120 260 vs
-    // 307, 3072 x 4096 168 vs 153, 4096 x 4096 187 vs 178; fp8 alike).
+    // 307, 3072 x 4096 168 vs 153, 4096 x 4096 187 vs 178; fp8 alike).  A
+    // lone tile against a 128x128 round: bf16 0.95 (2048 x 2048 x 8192: 77.8
+    // vs 89.7 us), fp8 1.07 (51.0 vs 48.1 us).
     const auto rounds = [&](int64_t tm, int64_t tn) {
         return ((M + tm - 1) / tm * ((N + tn - 1) / tn) * split_k + 255) / 256;
     };
     const bool has_128x256 = scale == DGP_SCALE_NONE || scale == DGP_SCALE_TENSOR;   // (bf16 and fp8 per-tensor)
     const int64_t k128x256 = rounds(128, 256);   // 128x256 tiles on the busiest CU
     const int64_t c256 = (scale == DGP_SCALE_BLOCK128 ? 205 : 145) * rounds(256, 256),
-                  c128x256 = has_128x256 ? 153 * (k128x256 / 2) + 107 * (k128x256 % 2) : INT64_MAX,
+                  c128x256 = has_128x256 ? 153 * (k128x256 / 2) + (dtype == DGP_BF16 ? 95 : 107) * (k128x256 % 2)
+                                         : INT64_MAX,
                   c128 = 100 * rounds(128, 128);
     const KernelSpec *k = nullptr;
     if (c256 <= c128x256 && c256 <= c128) {

@@ -364,8 +364,10 @@ def test_default_selection(dgp):
         assert dgp.kernels()[i][0].tile_m == want, (M, N, K, split)
     # Larger M: the tile whose grid needs the fewest weighted rounds over 256 CUs
     for M, N, K, sm, want in ((4096, 4096, 8192, dgp.SCALE_NONE, (256, 256)), (3072, 3072, 8192, dgp.SCALE_NONE, (256, 256)),
-                              (2048, 4096, 8192, dgp.SCALE_NONE, (128, 256)), (2048, 2048, 8192, dgp.SCALE_NONE, (128, 128)),
-                              (768, 16384, 4096, dgp.SCALE_NONE, (256, 256)), (1536, 1536, 8192, dgp.SCALE_NONE, (128, 128)),
+                              (2048, 4096, 8192, dgp.SCALE_NONE, (128, 256)), (2048, 2048, 8192, dgp.SCALE_TENSOR, (128, 128)),
+                              (768, 16384, 4096, dgp.SCALE_NONE, (256, 256)), (1536, 1536, 8192, dgp.SCALE_TENSOR, (128, 128)),
+                              # a lone bf16 128x256 tile one wave per SIMD beats a 128x128 round
+                              (2048, 2048, 8192, dgp.SCALE_NONE, (128, 256)), (1536, 1536, 8192, dgp.SCALE_NONE, (128, 256)),
                               (2048, 4096, 8192, dgp.SCALE_BLOCK128, (128, 128)), (3072, 3072, 8192, dgp.SCALE_BLOCK128, (256, 256)),
                               # two 256x256 rounds against three 128x256 tiles on the busiest CU, two at once
                               (4096, 6144, 8192, dgp.SCALE_NONE, (128, 256)), (6144, 4096, 8192, dgp.SCALE_TENSOR, (128, 256)),
