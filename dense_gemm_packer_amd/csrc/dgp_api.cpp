@@ -267,7 +267,8 @@ const KernelSpec *default_spec(int dtype, int scale, int out, int64_t M, int64_t
     // a 256x256 or 128x128 tile takes about 1.45 : 1 (bf16, fp8, mxfp8,
     // mxfp4; K = 2048 and 8192; blockscale's 8-wave 256x256 tile about
     // 2.05 : 1): 4096 x 4096 and 3072 x 3072 take the 256x256 tile, 2048 x
-    // 2048 the 128x128 tile (91 vs 134 us).  Ties go to the larger tile.
+    // 2048 the 128x128 tile (91 vs 134 us; bf16 there now takes the 128x256
+    // tile below).  Ties go to the larger tile.
     // bf16 and per-tensor fp8 run their 128x256 tile one wave per SIMD, two
     // workgroups per CU at once: the busiest CU's k tiles cost about 1.05
     // rounds of the 256x256 tile per pair and 0.74 for one alone (K = 8192:
